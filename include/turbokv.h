@@ -1,0 +1,158 @@
+/*
+ * libturbokv: TurboQuant / TurboQuant+ KV-cache codec and decode attention
+ * for AMD Instinct MI355X (gfx950).  C ABI: plain pointers, sizes and a HIP
+ * stream passed as void*.  No C++ exceptions cross this boundary.
+ *
+ * Method sources (web pages, cited by title and section):
+ *   [QPQ] quidproquo.cc, "TurboQuant+ KV cache compression": Stage 1
+ *         (PolarQuant: L2 norm, random Walsh-Hadamard rotation, Lloyd-Max
+ *         Gaussian codebook, per-coordinate indices), Stage 2 (QJL: residual,
+ *         residual norm, 1-bit sign of a random projection), format table
+ *         (turbo2/3/4), K/V asymmetric strategy (K = both stages, V = Stage 1).
+ *   [CXT] chenxutan.com, "TurboQuant+ deep dive": 1.1 cached decode attention,
+ *         1.2 KV-cache size, 2.3 QJL (one fixed-seed matrix at both ends,
+ *         bit = projection > 0), 3.3 sparse V (no renormalisation).
+ *   [YYL] yeyulingfeng.com, TurboQuant+ introduction: core item 3 (Boundary V:
+ *         first 2 + last 2 layers at q8_0), item 4 (Sparse V below 1e-6).
+ *   [MAC] mac-code GitHub issue #1, technical analysis, section 2.1
+ *         (per-group asymmetric min-max quantisation, group 64).
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer (inputs, packed planes, outputs,
+ *     workspace).  The library allocates device memory only inside
+ *     tq_codebook_init and frees it in tq_ctx_destroy.  A ctx is immutable
+ *     after init and may be shared by calls on different streams.
+ *   - Memory: "device" pointers must be HIP device (or managed) memory on the
+ *     current device; "host" pointers are ordinary CPU memory.
+ *   - Layout: a K or V tensor of one layer is [n_vec, head_dim] fp16 row-major
+ *     (row = one token of one KV head; for attention n_vec = B*Hkv*T in
+ *     [B, Hkv, T] order).  Packed tensors are described by tq_packed_layout.
+ *   - Errors: every call validates all arguments on the host before any HIP
+ *     call and returns a negative tq_status on failure without launching.
+ *     Launch failures return TQ_ERR_HIP.  Faults inside a kernel surface at
+ *     the caller's next synchronisation of the stream.
+ *   - Async: all compute calls are stream-ordered and return immediately.
+ */
+#ifndef TURBOKV_H
+#define TURBOKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or format */
+    TQ_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+    TQ_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
+    TQ_ERR_ALLOC = -4,        /* device or host allocation failed */
+    TQ_ERR_WORKSPACE = -5     /* workspace pointer null or too small */
+} tq_status;
+
+/* Codec of one packed tensor.
+ *   TQ_KIND_MSE : Stage 1 only ("TurboQuantMSE", the V codec of [QPQ]):
+ *                 b-bit codebook indices + fp16 norm.          bits = 1..4
+ *   TQ_KIND_PROD: Stage 1 + QJL (the K codec of [QPQ]): b-bit indices,
+ *                 1 sign bit per projection, fp16 norm, fp16 residual norm.
+ *                 turboN K = {TQ_KIND_PROD, N-1}.              bits = 1..3
+ *   TQ_KIND_Q8  : boundary-layer blocks ([YYL] item 3): int8 per element,
+ *                 fp16 absmax/127 scale per block of 32.       bits = 8     */
+typedef enum tq_kind { TQ_KIND_MSE = 0, TQ_KIND_PROD = 1, TQ_KIND_Q8 = 2 } tq_kind;
+
+typedef struct tq_format {
+    int32_t kind; /* tq_kind */
+    int32_t bits;
+} tq_format;
+
+typedef struct tq_ctx tq_ctx;
+
+/* Byte offsets (from the start of one packed buffer) and sizes of its planes.
+ * Every plane starts on a 256-byte boundary.
+ *   MSE : idx plane   n_vec * bits*d/8 bytes, LSB-first bitstream per row
+ *                     (bit j of the code of coordinate i is row bit i*bits+j);
+ *         norm plane  n_vec * 2 bytes (fp16 ||x||).
+ *   PROD: idx plane as MSE; sign plane n_vec * m/8 bytes (bit p = [(S e)_p > 0]);
+ *         norm plane  n_vec * 4 bytes (fp16 ||x|| then fp16 residual norm).
+ *   Q8  : idx plane   n_vec * d int8 values; norm plane n_vec * d/32 fp16
+ *         block scales; no sign plane.                                      */
+typedef struct tq_planes_desc {
+    int64_t idx_offset, idx_bytes;
+    int64_t sign_offset, sign_bytes;
+    int64_t norm_offset, norm_bytes;
+    int64_t total_bytes;
+} tq_planes_desc;
+
+/* Build the codec tables for head_dim d and QJL dimension m from a seed
+ * ([QPQ] Stage 1 "precomputed Lloyd-Max codebook"; [CXT] 2.3 fixed-seed
+ * matrix): Lloyd-Max levels and boundaries of N(0,1) for 1..4 bits (float64
+ * on the host, stored as float32), the random sign diagonal D and the
+ * m x d Gaussian matrix S (fp16), both drawn from a splitmix64 counter stream
+ * (counter i = 1..d -> signs, d+1.. -> Box-Muller pairs, row-major S).
+ * Uploads them to the current device and synchronises `stream`.
+ * This build supports d = m = 128.  *ctx receives an owning handle. */
+tq_status tq_codebook_init(tq_ctx **ctx, int head_dim, int qjl_dim, uint64_t seed, void *stream);
+tq_status tq_ctx_destroy(tq_ctx *ctx);
+
+/* Host-only copy of the tables tq_codebook_init would build (no GPU needed).
+ * levels: 4*16 doubles (row b-1 holds the 2^b ascending levels of b bits);
+ * bounds: 4*16 doubles (row b-1 holds the 2^b - 1 midpoints);
+ * signs:  head_dim floats (+1/-1);  S: qjl_dim*head_dim fp16 bit patterns.
+ * Any output pointer may be NULL. */
+tq_status tq_host_tables(int head_dim, int qjl_dim, uint64_t seed, double *levels, double *bounds,
+                         float *signs, uint16_t *S);
+
+/* Plane layout of n_vec packed vectors in format f (host only). */
+tq_status tq_packed_layout(tq_format f, int head_dim, int64_t n_vec, tq_planes_desc *out);
+
+/* Encode per-token K and V rows ([QPQ] Stage 1 and Stage 2; K/V asymmetric).
+ * k_f16, v_f16: device, [n_vec, d] fp16 (either may be NULL to skip it);
+ * k_packed, v_packed: device, tq_packed_layout(kf|vf, d, n_vec).total_bytes
+ * each, 256-byte aligned.  Formats: MSE, PROD or Q8 for either tensor. */
+tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, int64_t n_vec,
+                       tq_format kf, tq_format vf, void *k_packed, void *v_packed, void *stream);
+
+/* Reconstruct fp16 rows from one packed tensor: MSE -> n R^T c[idx]/sqrt(d);
+ * PROD -> R^T (n c[idx]/sqrt(d) + sqrt(pi/2)/m * gamma * S^T (2 bit - 1));
+ * Q8 -> int8 * block scale.  packed: device; out_f16: device [n_vec, d]. */
+tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64_t n_vec,
+                       void *out_f16, void *stream);
+
+/* Single-token decode attention over a packed cache ([CXT] 1.1, [YYL] item 4,
+ * [CXT] 3.3).  q_f16: device [B, Hq, d]; k_packed / v_packed: device, one
+ * packed tensor each over n_vec = B*Hkv*T rows in [B, Hkv, T] order.
+ * seq_lens: device int32 [B] (values clamped to [0, T]) or NULL (= T).
+ * Scores <q, k_hat>/sqrt(d) with q head h reading kv head h/(Hq/Hkv); full
+ * softmax over each sequence; V rows whose normalised weight is below tau
+ * are skipped and not renormalised (tau = 0 keeps every row).
+ * out_f32: device [B, Hq, d].  workspace: device, at least
+ * tq_attn_workspace_bytes(...) bytes, 256-byte aligned; its contents need no
+ * initialisation and are clobbered.  K: MSE, PROD or Q8; V: MSE or Q8.
+ * Calls that share one workspace must be ordered on one stream. */
+tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                         const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                         int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                         void *workspace, size_t ws_bytes, void *stream);
+size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_format vf);
+
+/* Per-group asymmetric min-max quantisation ([MAC] 2.1): for each group of
+ * group_size consecutive elements, fp16 scale = (max-min)/(2^bits-1) (from the
+ * exact fp16 extremes, rounded once), fp16 zero = min, code =
+ * clamp(rint((x - zero)/scale), 0, 2^bits-1) in float32 (0 when scale = 0).
+ * x_f16: device [n]; codes: device, n*bits/8 bytes, one LSB-first bitstream;
+ * scale_f16, zero_f16: device [n/group_size].  This build: group_size 64,
+ * bits 2..4, n a multiple of group_size. */
+tq_status tq_minmax_quant(const void *x_f16, int64_t n, int group_size, int bits, void *codes,
+                          void *scale_f16, void *zero_f16, void *stream);
+/* x_hat = code*scale + zero (float32, rounded to fp16). */
+tq_status tq_minmax_dequant(const void *codes, const void *scale_f16, const void *zero_f16,
+                            int64_t n, int group_size, int bits, void *out_f16, void *stream);
+
+const char *tq_status_str(tq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TURBOKV_H */

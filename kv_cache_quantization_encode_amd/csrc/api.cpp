@@ -1,0 +1,266 @@
+// libturbokv C ABI: argument validation, plane layouts, table upload and
+// dispatch to the HIP kernels.  Every check runs on the host before any HIP
+// call, so all error paths can be exercised without a GPU.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+namespace tq {
+
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static bool format_ok(tq_format f) {
+    switch (f.kind) {
+        case TQ_KIND_MSE: return f.bits >= 1 && f.bits <= 4;
+        case TQ_KIND_PROD: return f.bits >= 1 && f.bits <= 3;
+        case TQ_KIND_Q8: return f.bits == 8;
+        default: return false;
+    }
+}
+
+bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out) {
+    if (!format_ok(f) || d != kHeadDim || n_vec < 0) return false;
+    if (n_vec > (int64_t(1) << 40)) return false;
+    tq_planes_desc p{};
+    int64_t off = 0;
+    if (f.kind == TQ_KIND_Q8) {
+        p.idx_offset = 0;
+        p.idx_bytes = n_vec * d;
+        off = align256(p.idx_bytes);
+        p.norm_offset = off;
+        p.norm_bytes = n_vec * (d / 32) * 2;
+        off = align256(off + p.norm_bytes);
+    } else {
+        p.idx_offset = 0;
+        p.idx_bytes = n_vec * f.bits * d / 8;
+        off = align256(p.idx_bytes);
+        if (f.kind == TQ_KIND_PROD) {
+            p.sign_offset = off;
+            p.sign_bytes = n_vec * d / 8;
+            off = align256(off + p.sign_bytes);
+            p.norm_offset = off;
+            p.norm_bytes = n_vec * 4;
+        } else {
+            p.norm_offset = off;
+            p.norm_bytes = n_vec * 2;
+        }
+        off = align256(off + p.norm_bytes);
+    }
+    p.total_bytes = off;
+    *out = p;
+    return true;
+}
+
+AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
+    AttnPlan p{};
+    const int64_t rows = int64_t(B) * Hkv;
+    int64_t want = (2048 + rows - 1) / rows;  // aim for ~2048 blocks per pass
+    int64_t maxc = (int64_t(T) + 255) / 256;
+    int64_t nc = want < maxc ? want : maxc;
+    if (nc < 1) nc = 1;
+    int64_t chunk = (int64_t(T) + nc - 1) / nc;
+    chunk = (chunk + 255) / 256 * 256;
+    nc = (int64_t(T) + chunk - 1) / chunk;
+    if (nc < 1) nc = 1;
+    p.n_chunks = int(nc);
+    p.chunk = int(chunk);
+    const int64_t heads = int64_t(B) * Hq;
+    int64_t off = 0;
+    p.off_qr = size_t(off); off = align256(off + heads * kHeadDim * 4);
+    p.off_qp = size_t(off); off = align256(off + heads * kHeadDim * 4);
+    p.off_qsum = size_t(off); off = align256(off + heads * 4);
+    p.off_scores = size_t(off); off = align256(off + heads * int64_t(T) * 4);
+    p.off_stats = size_t(off); off = align256(off + heads * nc * 2 * 4);
+    p.off_part = size_t(off); off = align256(off + heads * nc * kHeadDim * 4);
+    p.off_cnt = size_t(off); off = align256(off + rows * 4);
+    p.total = size_t(off);
+    return p;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char *tq_status_str(tq_status s) {
+    switch (s) {
+        case TQ_OK: return "ok";
+        case TQ_ERR_INVALID_ARG: return "invalid argument";
+        case TQ_ERR_UNSUPPORTED: return "unsupported by this build";
+        case TQ_ERR_HIP: return "HIP runtime error";
+        case TQ_ERR_ALLOC: return "allocation failed";
+        case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+tq_status tq_host_tables(int head_dim, int qjl_dim, uint64_t seed, double *levels, double *bounds,
+                         float *signs, uint16_t *S) {
+    if (head_dim < 2 || head_dim > 256 || (head_dim & (head_dim - 1))) return TQ_ERR_INVALID_ARG;
+    if (qjl_dim < 1 || qjl_dim > 4096 || (int64_t(qjl_dim) * head_dim) % 2) return TQ_ERR_INVALID_ARG;
+    if (levels || bounds) {
+        for (int b = 1; b <= 4; ++b) {
+            double lv[16] = {0}, bd[16] = {0};
+            lloyd_max_gaussian(b, lv, bd);
+            if (levels) std::memcpy(levels + 16 * (b - 1), lv, sizeof lv);
+            if (bounds) std::memcpy(bounds + 16 * (b - 1), bd, sizeof bd);
+        }
+    }
+    if (signs || S) {
+        float *sg = new (std::nothrow) float[head_dim];
+        uint16_t *ss = new (std::nothrow) uint16_t[size_t(qjl_dim) * head_dim];
+        if (!sg || !ss) { delete[] sg; delete[] ss; return TQ_ERR_ALLOC; }
+        random_tables(head_dim, qjl_dim, seed, sg, ss);
+        if (signs) std::memcpy(signs, sg, sizeof(float) * head_dim);
+        if (S) std::memcpy(S, ss, sizeof(uint16_t) * size_t(qjl_dim) * head_dim);
+        delete[] sg;
+        delete[] ss;
+    }
+    return TQ_OK;
+}
+
+tq_status tq_packed_layout(tq_format f, int head_dim, int64_t n_vec, tq_planes_desc *out) {
+    if (!out) return TQ_ERR_INVALID_ARG;
+    if (!format_ok(f) || n_vec < 0) return TQ_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim) return TQ_ERR_UNSUPPORTED;
+    return plane_layout(f, head_dim, n_vec, out) ? TQ_OK : TQ_ERR_INVALID_ARG;
+}
+
+tq_status tq_codebook_init(tq_ctx **ctx, int head_dim, int qjl_dim, uint64_t seed, void *stream) {
+    if (!ctx) return TQ_ERR_INVALID_ARG;
+    *ctx = nullptr;
+    if (head_dim < 2 || head_dim > 256 || (head_dim & (head_dim - 1))) return TQ_ERR_INVALID_ARG;
+    if (qjl_dim < 1) return TQ_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim || qjl_dim != kHeadDim) return TQ_ERR_UNSUPPORTED;
+    DevTables *host = new (std::nothrow) DevTables;
+    tq_ctx *c = new (std::nothrow) tq_ctx;
+    if (!host || !c) { delete host; delete c; return TQ_ERR_ALLOC; }
+    build_device_tables(head_dim, qjl_dim, seed, host);
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        delete host; delete c; return TQ_ERR_HIP;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) { delete host; delete c; return TQ_ERR_UNSUPPORTED; }
+    void *d = nullptr;
+    if (hipMalloc(&d, sizeof(DevTables)) != hipSuccess) { delete host; delete c; return TQ_ERR_ALLOC; }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(d, host, sizeof(DevTables), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        (void)hipFree(d); delete host; delete c; return TQ_ERR_HIP;
+    }
+    delete host;
+    c->head_dim = head_dim;
+    c->qjl_dim = qjl_dim;
+    c->seed = seed;
+    c->device = dev;
+    c->dev = static_cast<DevTables *>(d);
+    *ctx = c;
+    return TQ_OK;
+}
+
+tq_status tq_ctx_destroy(tq_ctx *ctx) {
+    if (!ctx) return TQ_ERR_INVALID_ARG;
+    hipError_t e = hipFree(ctx->dev);
+    delete ctx;
+    return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, int64_t n_vec,
+                       tq_format kf, tq_format vf, void *k_packed, void *v_packed, void *stream) {
+    if (!ctx || n_vec < 0) return TQ_ERR_INVALID_ARG;
+    if (!k_f16 && !v_f16) return TQ_ERR_INVALID_ARG;
+    tq_planes_desc kl{}, vl{};
+    if (k_f16) {
+        if (!k_packed || !aligned(k_f16, 16) || !aligned(k_packed, 256)) return TQ_ERR_INVALID_ARG;
+        if (!plane_layout(kf, ctx->head_dim, n_vec, &kl)) return TQ_ERR_INVALID_ARG;
+    }
+    if (v_f16) {
+        if (!v_packed || !aligned(v_f16, 16) || !aligned(v_packed, 256)) return TQ_ERR_INVALID_ARG;
+        if (!plane_layout(vf, ctx->head_dim, n_vec, &vl)) return TQ_ERR_INVALID_ARG;
+    }
+    if (n_vec == 0) return TQ_OK;
+    if (k_f16 && launch_encode(ctx->dev, k_f16, n_vec, kf, k_packed, kl, stream) != 0) return TQ_ERR_HIP;
+    if (v_f16 && launch_encode(ctx->dev, v_f16, n_vec, vf, v_packed, vl, stream) != 0) return TQ_ERR_HIP;
+    return TQ_OK;
+}
+
+tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64_t n_vec,
+                       void *out_f16, void *stream) {
+    if (!ctx || !packed || !out_f16 || n_vec < 0) return TQ_ERR_INVALID_ARG;
+    if (!aligned(packed, 256) || !aligned(out_f16, 16)) return TQ_ERR_INVALID_ARG;
+    tq_planes_desc l{};
+    if (!plane_layout(f, ctx->head_dim, n_vec, &l)) return TQ_ERR_INVALID_ARG;
+    if (n_vec == 0) return TQ_OK;
+    return launch_decode(ctx->dev, packed, f, n_vec, l, out_f16, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_format vf) {
+    (void)kf;
+    (void)vf;
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv) return 0;
+    return attn_plan(B, Hq, Hkv, T).total;
+}
+
+tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                         const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                         int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    if (!ctx || !q_f16 || !k_packed || !v_packed || !out_f32) return TQ_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv) return TQ_ERR_INVALID_ARG;
+    if (!(sparse_v_tau >= 0.0f) || !std::isfinite(sparse_v_tau)) return TQ_ERR_INVALID_ARG;
+    if (!aligned(q_f16, 16) || !aligned(k_packed, 256) || !aligned(v_packed, 256) ||
+        !aligned(out_f32, 16) || (seq_lens && !aligned(seq_lens, 4)))
+        return TQ_ERR_INVALID_ARG;
+    if (!format_ok(kf) || !format_ok(vf)) return TQ_ERR_INVALID_ARG;
+    if (vf.kind == TQ_KIND_PROD) return TQ_ERR_UNSUPPORTED;
+    const int g = Hq / Hkv;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return TQ_ERR_UNSUPPORTED;
+    if (int64_t(B) * Hkv * T > (int64_t(1) << 36)) return TQ_ERR_UNSUPPORTED;
+    const int64_t n_vec = int64_t(B) * Hkv * T;
+    tq_planes_desc kl{}, vl{};
+    if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))
+        return TQ_ERR_INVALID_ARG;
+    const AttnPlan plan = attn_plan(B, Hq, Hkv, T);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < plan.total) return TQ_ERR_WORKSPACE;
+    return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, seq_lens,
+                       sparse_v_tau, out_f32, workspace, plan, stream) == 0
+               ? TQ_OK
+               : TQ_ERR_HIP;
+}
+
+tq_status tq_minmax_quant(const void *x_f16, int64_t n, int group_size, int bits, void *codes,
+                          void *scale_f16, void *zero_f16, void *stream) {
+    if (!x_f16 || !codes || !scale_f16 || !zero_f16 || n < 0) return TQ_ERR_INVALID_ARG;
+    if (bits < 1 || bits > 8 || group_size < 1) return TQ_ERR_INVALID_ARG;
+    if (group_size != 64 || bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (n % group_size) return TQ_ERR_INVALID_ARG;
+    if (!aligned(x_f16, 16) || !aligned(codes, 4) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2))
+        return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    return launch_minmax_quant(x_f16, n, bits, codes, scale_f16, zero_f16, stream) == 0 ? TQ_OK
+                                                                                       : TQ_ERR_HIP;
+}
+
+tq_status tq_minmax_dequant(const void *codes, const void *scale_f16, const void *zero_f16,
+                            int64_t n, int group_size, int bits, void *out_f16, void *stream) {
+    if (!codes || !scale_f16 || !zero_f16 || !out_f16 || n < 0) return TQ_ERR_INVALID_ARG;
+    if (bits < 1 || bits > 8 || group_size < 1) return TQ_ERR_INVALID_ARG;
+    if (group_size != 64 || bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (n % group_size) return TQ_ERR_INVALID_ARG;
+    if (!aligned(codes, 4) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) || !aligned(out_f16, 16))
+        return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    return launch_minmax_dequant(codes, scale_f16, zero_f16, n, bits, out_f16, stream) == 0
+               ? TQ_OK
+               : TQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/turbokv.h"
+
+namespace tq {
+
+constexpr int kHeadDim = 128;  // head_dim (= QJL dimension m) of this build
+
+// Tables uploaded once per ctx.  Plain data, identical on host and device.
+struct DevTables {
+    float levels[4][16];             // row b-1: 2^b ascending N(0,1) Lloyd-Max levels
+    float bounds[4][16];             // row b-1: 2^b-1 midpoints, then +inf padding
+    uint32_t sign_pair_xor[4][16];   // fp16-pair sign flips of D per lane quarter
+    float signs[kHeadDim];           // D
+    uint16_t S[kHeadDim * kHeadDim]; // QJL matrix, fp16 bits, row-major [m][d]
+    uint16_t S_enc[32 * 64 * 8];     // S as encode MFMA A-fragments
+    uint16_t St_dec[32 * 64 * 8];    // S^T as dequant MFMA A-fragments
+};
+
+// tables.cpp (host only)
+uint16_t double_to_half_rne(double v);
+double half_to_double(uint16_t h);
+void lloyd_max_gaussian(int bits, double *levels, double *bounds);
+void random_tables(int d, int m, uint64_t seed, float *signs, uint16_t *S);
+void build_device_tables(int d, int m, uint64_t seed, DevTables *t);
+
+// Plane layout (api.cpp); returns false for an invalid format/size.
+bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out);
+
+// Attention partitioning shared by the host (workspace size) and launchers.
+struct AttnPlan {
+    int n_chunks;    // token chunks per (batch, kv head)
+    int chunk;       // tokens per chunk (multiple of 256)
+    size_t off_qr, off_qp, off_qsum, off_scores, off_stats, off_part, off_cnt, total;
+};
+AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
+
+// Kernel launchers (HIP translation units).  All return a hipError_t as int.
+int launch_encode(const DevTables *tab, const void *x, int64_t n_vec, tq_format f, void *packed,
+                  const tq_planes_desc &lay, void *stream);
+int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t n_vec,
+                  const tq_planes_desc &lay, void *out, void *stream);
+int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
+                tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
+                int Hkv, int T, const int32_t *seq_lens, float tau, float *out, void *ws,
+                const AttnPlan &plan, void *stream);
+int launch_minmax_quant(const void *x, int64_t n, int bits, void *codes, void *scale, void *zero,
+                        void *stream);
+int launch_minmax_dequant(const void *codes, const void *scale, const void *zero, int64_t n,
+                          int bits, void *out, void *stream);
+
+}  // namespace tq
+
+struct tq_ctx {
+    int head_dim;
+    int qjl_dim;
+    uint64_t seed;
+    int device;
+    tq::DevTables *dev;  // device copy
+};

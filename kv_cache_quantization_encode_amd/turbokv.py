@@ -1,0 +1,214 @@
+"""Thin ctypes binding of libturbokv (argument marshalling only).
+
+Every function here mirrors one C entry point of include/turbokv.h under the
+same name.  Tensors are PyTorch tensors on the GPU (PyTorch supplies device
+memory and streams); the library does all the computing.  The library must
+have been built (kv_cache_quantization_encode_amd.build) -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libturbokv.so")
+
+TQ_OK = 0
+TQ_ERR_INVALID_ARG = -1
+TQ_ERR_UNSUPPORTED = -2
+TQ_ERR_HIP = -3
+TQ_ERR_ALLOC = -4
+TQ_ERR_WORKSPACE = -5
+
+KIND_MSE, KIND_PROD, KIND_Q8 = 0, 1, 2
+HEAD_DIM = 128
+
+
+class TqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+class tq_format(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"tq_format(kind={self.kind}, bits={self.bits})"
+
+
+class tq_planes_desc(ctypes.Structure):
+    _fields_ = [("idx_offset", ctypes.c_int64), ("idx_bytes", ctypes.c_int64),
+                ("sign_offset", ctypes.c_int64), ("sign_bytes", ctypes.c_int64),
+                ("norm_offset", ctypes.c_int64), ("norm_bytes", ctypes.c_int64),
+                ("total_bytes", ctypes.c_int64)]
+
+
+def fmt(kind: int, bits: int) -> tq_format:
+    return tq_format(kind, bits)
+
+
+def turbo_k(n: int) -> tq_format:
+    """turboN K: (N-1)-bit codebook + 1-bit QJL."""
+    return tq_format(KIND_PROD, n - 1)
+
+
+def mse(bits: int) -> tq_format:
+    """b-bit codebook only (the V codec)."""
+    return tq_format(KIND_MSE, bits)
+
+
+Q8 = tq_format(KIND_Q8, 8)
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libturbokv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: run `python -m kv_cache_quantization_encode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
+    lib.tq_codebook_init.argtypes = [ctypes.POINTER(vp), i32, i32, u64, vp]
+    lib.tq_ctx_destroy.argtypes = [vp]
+    lib.tq_host_tables.argtypes = [i32, i32, u64, vp, vp, vp, vp]
+    lib.tq_packed_layout.argtypes = [tq_format, i32, i64, ctypes.POINTER(tq_planes_desc)]
+    lib.tq_encode_kv.argtypes = [vp, vp, vp, i64, tq_format, tq_format, vp, vp, vp]
+    lib.tq_decode_kv.argtypes = [vp, vp, tq_format, i64, vp, vp]
+    lib.tq_attn_decode.argtypes = [vp, vp, vp, vp, tq_format, tq_format, i32, i32, i32, i32, vp,
+                                   ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.tq_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, tq_format, tq_format]
+    lib.tq_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq_minmax_quant.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+    lib.tq_minmax_dequant.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp]
+    lib.tq_status_str.argtypes = [i32]
+    lib.tq_status_str.restype = ctypes.c_char_p
+    for name in ("tq_codebook_init", "tq_ctx_destroy", "tq_host_tables", "tq_packed_layout",
+                 "tq_encode_kv", "tq_decode_kv", "tq_attn_decode", "tq_minmax_quant",
+                 "tq_minmax_dequant"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().tq_status_str(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TqError(status, where)
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ----------------------------------------------------------------------------
+# C entry points
+# ----------------------------------------------------------------------------
+def tq_codebook_init(head_dim: int = HEAD_DIM, qjl_dim: int = HEAD_DIM, seed: int = 42, stream=None) -> int:
+    ctx = ctypes.c_void_p()
+    _check(load().tq_codebook_init(ctypes.byref(ctx), head_dim, qjl_dim, seed, _stream(stream)),
+           "tq_codebook_init")
+    return ctx.value
+
+
+def tq_ctx_destroy(ctx: int) -> None:
+    _check(load().tq_ctx_destroy(ctx), "tq_ctx_destroy")
+
+
+def tq_host_tables(head_dim: int = HEAD_DIM, qjl_dim: int = HEAD_DIM, seed: int = 42):
+    """(levels[4,16] f64, bounds[4,16] f64, signs[d] f32, S[m,d] fp16-bits u16) as numpy."""
+    import numpy as np
+    levels = np.zeros((4, 16), np.float64)
+    bounds = np.zeros((4, 16), np.float64)
+    signs = np.zeros(head_dim, np.float32)
+    S = np.zeros((qjl_dim, head_dim), np.uint16)
+    _check(load().tq_host_tables(head_dim, qjl_dim, seed, levels.ctypes.data, bounds.ctypes.data,
+                                 signs.ctypes.data, S.ctypes.data), "tq_host_tables")
+    return levels, bounds, signs, S
+
+
+def tq_packed_layout(f: tq_format, head_dim: int, n_vec: int) -> tq_planes_desc:
+    out = tq_planes_desc()
+    _check(load().tq_packed_layout(f, head_dim, n_vec, ctypes.byref(out)), "tq_packed_layout")
+    return out
+
+
+def tq_encode_kv(ctx, k, v, n_vec, kf: tq_format, vf: tq_format, k_packed, v_packed, stream=None) -> None:
+    _check(load().tq_encode_kv(ctx, _ptr(k), _ptr(v), n_vec, kf, vf, _ptr(k_packed), _ptr(v_packed),
+                               _stream(stream)), "tq_encode_kv")
+
+
+def tq_decode_kv(ctx, packed, f: tq_format, n_vec, out, stream=None) -> None:
+    _check(load().tq_decode_kv(ctx, _ptr(packed), f, n_vec, _ptr(out), _stream(stream)), "tq_decode_kv")
+
+
+def tq_attn_workspace_bytes(B, Hq, Hkv, T, kf: tq_format, vf: tq_format) -> int:
+    return int(load().tq_attn_workspace_bytes(B, Hq, Hkv, T, kf, vf))
+
+
+def tq_attn_decode(ctx, q, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, seq_lens, tau, out, workspace,
+                   ws_bytes, stream=None) -> None:
+    _check(load().tq_attn_decode(ctx, _ptr(q), _ptr(k_packed), _ptr(v_packed), kf, vf, B, Hq, Hkv, T,
+                                 _ptr(seq_lens), float(tau), _ptr(out), _ptr(workspace), ws_bytes,
+                                 _stream(stream)), "tq_attn_decode")
+
+
+def tq_minmax_quant(x, n, group_size, bits, codes, scale, zero, stream=None) -> None:
+    _check(load().tq_minmax_quant(_ptr(x), n, group_size, bits, _ptr(codes), _ptr(scale), _ptr(zero),
+                                  _stream(stream)), "tq_minmax_quant")
+
+
+def tq_minmax_dequant(codes, scale, zero, n, group_size, bits, out, stream=None) -> None:
+    _check(load().tq_minmax_dequant(_ptr(codes), _ptr(scale), _ptr(zero), n, group_size, bits, _ptr(out),
+                                    _stream(stream)), "tq_minmax_dequant")
+
+
+# ----------------------------------------------------------------------------
+# Allocation helpers (PyTorch device memory)
+# ----------------------------------------------------------------------------
+@dataclass
+class Packed:
+    """A packed tensor: one uint8 device buffer plus its plane layout."""
+    buf: "object"
+    fmt: tq_format
+    n_vec: int
+    layout: tq_planes_desc
+
+
+def alloc_packed(f: tq_format, n_vec: int, device="cuda") -> Packed:
+    import torch
+    lay = tq_packed_layout(f, HEAD_DIM, n_vec)
+    # torch's caching allocator hands out 512-byte aligned blocks
+    buf = torch.empty(max(int(lay.total_bytes), 256), dtype=torch.uint8, device=device)
+    assert buf.data_ptr() % 256 == 0
+    return Packed(buf, f, n_vec, lay)
+
+
+def alloc_workspace(B, Hq, Hkv, T, kf, vf, device="cuda"):
+    import torch
+    n = tq_attn_workspace_bytes(B, Hq, Hkv, T, kf, vf)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws, n
