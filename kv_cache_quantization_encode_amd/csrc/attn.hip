@@ -14,16 +14,15 @@
 // accumulated in the rotated domain and rotated back once per head.
 //
 // Passes (one stream, no host synchronisation):
-//   1. prologue   one wave per (batch, q head): q_rot, q_proj, their sums;
-//                 zeroes the per-(batch, kv head) completion counters.
-//   2. scores     grid (chunk, batch*kv head); one token per lane, the g query
-//                 heads of the kv head share one unpack; scores go to the
+//   1. prologue   one wave per (batch, q head): q_rot and q_proj.
+//   2. scores     grid (chunk, batch*kv head); MFMA over 16-token tiles with
+//                 the g query heads of the kv head as rows; scores go to the
 //                 workspace with per-chunk (max, sum exp) per head.
 //   3. values     same grid; combines the chunk statistics into the exact
 //                 softmax normaliser, keeps tokens with some weight >= tau,
 //                 compacts them, accumulates weight * level over 8 coordinates
-//                 per lane, writes the chunk's partial sum; the last block of
-//                 each (batch, kv head) sums the partials and applies R^T.
+//                 per lane, writes the chunk's partial sum.
+//   4. merge      one wave per (batch, q head): sum of the partials, then R^T.
 #include <type_traits>
 
 #include "device_common.h"
@@ -33,12 +32,7 @@ namespace tq {
 constexpr float kRsqrtD = 0.08838834764831845f;            // 1/sqrt(128)
 constexpr float kQjlOverSqrtD = 1.2533141373155003f / 128.0f * 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQc = 8;  // query coordinates per scalar-load chunk
 
-// Read-only data in the constant address space: uniform loads from it become
-// scalar (s_load) loads into SGPRs.
-typedef const __attribute__((address_space(4))) float *const_fp;
-__device__ __forceinline__ const_fp as_const(const float *p) { return (const_fp)p; }
 
 struct AttnArgs {
     const DevTables *tab;
@@ -46,8 +40,7 @@ struct AttnArgs {
     const uint8_t *kidx, *ksign, *knorm;  // K planes
     const uint8_t *vidx, *vnorm;          // V planes
     const int32_t *seq_lens;
-    float *qr, *qp, *qsum, *scores, *stats, *part;
-    uint32_t *cnt;
+    float *qr, *qp, *scores, *stats, *part;
     float *out;
     float tau;
     int B, Hq, Hkv, T, chunk, n_chunks;
@@ -62,11 +55,12 @@ __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
 }
 
 // ---------------------------------------------------------------- prologue
+// q_rot = R q = H D q / sqrt(d) for rotated keys (q itself for q8 keys) and
+// q_proj = S q_rot, both unscaled fp32; the score scales are applied per token.
 __global__ __launch_bounds__(64) void attn_prologue_kernel(AttnArgs a, int want_proj) {
     __shared__ float s_q[128];
     const int head = blockIdx.x;  // b * Hq + h
     const int lane = threadIdx.x;
-    const int g = a.Hq / a.Hkv;
     const uint16_t *q = a.q + int64_t(head) * 128;
     float v0 = h2f(q[lane]), v1 = h2f(q[lane + 64]);
     if (a.k_rotated) {
@@ -83,173 +77,204 @@ __global__ __launch_bounds__(64) void attn_prologue_kernel(AttnArgs a, int want_
             v0 = fmaf(sg, v0, p0);
             v1 = fmaf(sg, v1, p1);
         }
-        v0 *= kRsqrtD;  // q_rot = H D q / sqrt(d)
+        v0 *= kRsqrtD;
         v1 *= kRsqrtD;
     }
-    // rotated keys: s = (1/sqrt d)(n/sqrt d) <q_rot, c> = n <q_rot/d, c>;
-    // q8 keys: s = <q/sqrt(d), k> on the unrotated query
-    const float f = a.k_rotated ? (1.0f / 128.0f) : kRsqrtD;
-    a.qr[int64_t(head) * 128 + lane] = v0 * f;
-    a.qr[int64_t(head) * 128 + lane + 64] = v1 * f;
+    a.qr[int64_t(head) * 128 + lane] = v0;
+    a.qr[int64_t(head) * 128 + lane + 64] = v1;
     if (want_proj) {
         s_q[lane] = v0;
         s_q[lane + 64] = v1;
         __syncthreads();
-        const uint16_t *S = a.tab->S;
+        const uint16_t *ST = a.tab->ST;  // S^T: lanes read consecutive projections
         float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll 8
         for (int i = 0; i < 128; ++i) {
             const float qi = s_q[i];
-            p0 = fmaf(h2f(S[lane * 128 + i]), qi, p0);
-            p1 = fmaf(h2f(S[(lane + 64) * 128 + i]), qi, p1);
+            p0 = fmaf(h2f(ST[i * 128 + lane]), qi, p0);
+            p1 = fmaf(h2f(ST[i * 128 + lane + 64]), qi, p1);
         }
-        p0 *= kQjlOverSqrtD;
-        p1 *= kQjlOverSqrtD;
         a.qp[int64_t(head) * 128 + lane] = p0;
         a.qp[int64_t(head) * 128 + lane + 64] = p1;
-        float sum = p0 + p1;
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) sum += __shfl_xor(sum, s);
-        if (lane == 0) a.qsum[head] = sum;
     }
-    if (lane == 0 && (head % a.Hq) % g == 0) a.cnt[(head / a.Hq) * a.Hkv + (head % a.Hq) / g] = 0u;
 }
 
 // ------------------------------------------------------------------ scores
+// One wavefront scores 16 tokens of one kv head at a time with
+// v_mfma_f32_16x16x32_f16: rows = query heads of the group (zero-padded to
+// 16), columns = tokens, k = coordinates.  Lane l supplies token l&15 and the
+// 32 coordinates 32*(l>>4)+[0,32) of its packed row (8 per MFMA k-step), so a
+// lane unpacks exactly the b dwords it loaded.  fp32 accuracy from fp16 MFMA:
+// the query is split into hi + lo fp16 halves and every codebook level into
+// hi + lo halves (three products, dropping lo*lo); the QJL operand is +-1,
+// exact in fp16.  q8 keys use k-steps = the four 32-element scale blocks.
+__device__ __forceinline__ void split_half8(const float *src, half8 &hi, half8 &lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const _Float16 h = _Float16(src[j]);
+        hi[j] = h;
+        lo[j] = _Float16(src[j] - float(h));
+    }
+}
+
 template <int G, int KIND, int BITS>
 __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const float *__restrict__ qr_all,
                                                           const float *__restrict__ qp_all,
                                                           const uint8_t *__restrict__ kidx,
+                                                          const uint8_t *__restrict__ ksign,
+                                                          const uint8_t *__restrict__ knorm,
                                                           float *__restrict__ scores) {
-    __shared__ float s_levels[16];
-    __shared__ float s_red[4][G][2];
+    static_assert(G <= 16, "at most 16 query heads per kv head");
+    __shared__ uint32_t s_lut[16];          // level k as fp16 hi | fp16 lo << 16
+    __shared__ float s_red[4][16][2];       // per wave, per head: (max, sum)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = lane & 15, kq = lane >> 4;
     const int chunk_id = blockIdx.x, row = blockIdx.y;  // row = b*Hkv + kvh
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
-    const int hq0 = kvh * G;
+    const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
     if constexpr (KIND != TQ_KIND_Q8) {
-        if (tid < 16) s_levels[tid] = a.tab->levels[BITS - 1][tid];
+        if (tid < 16) {
+            const float c = a.tab->levels[BITS - 1][tid];
+            const _Float16 hi = _Float16(c);
+            const _Float16 lo = _Float16(c - float(hi));
+            s_lut[tid] = uint32_t(__builtin_bit_cast(uint16_t, hi)) |
+                         (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
+        }
+    }
+    // A operands: lane (h = l&15, kq) holds 8 query values per k-step
+    half8 arh[4], arl[4], aph[4], apl[4];
+    {
+        const int h = lane & 15;
+        float buf[8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c0 = (KIND == TQ_KIND_Q8) ? 32 * s + 8 * kq : 32 * kq + 8 * s;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) buf[j] = h < G ? qr_all[(head0 + h) * 128 + c0 + j] : 0.0f;
+            split_half8(buf, arh[s], arl[s]);
+            if constexpr (KIND == TQ_KIND_PROD) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) buf[j] = h < G ? qp_all[(head0 + h) * 128 + c0 + j] : 0.0f;
+                split_half8(buf, aph[s], apl[s]);
+            }
+        }
     }
     __syncthreads();
     const int L = seq_len_of(a, b);
     const int t0 = chunk_id * a.chunk;
     const int t1 = min(t0 + a.chunk, L);
-    const int64_t head0 = int64_t(b) * a.Hq + hq0;
-    const float *qr_base = qr_all + head0 * 128;
-    const float *qp_base = qp_all + head0 * 128;
-    float qsum[G];
-    if constexpr (KIND == TQ_KIND_PROD) {
+    float m[4], l[4];
 #pragma unroll
-        for (int g = 0; g < G; ++g) qsum[g] = a.qsum[head0 + g];
-    }
-    float m[G], l[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) { m[g] = -INFINITY; l[g] = 0.0f; }
+    for (int j = 0; j < 4; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
+    const _Float16 one = _Float16(1.0f), mone = _Float16(-1.0f);
 
-    for (int t = t0 + tid; t < t1; t += 256) {
-        const int64_t vec = int64_t(row) * a.T + t;
-        float sc[G];
+    for (int tb = t0 + wave * 16; tb < t1; tb += 64) {
+        const int tok = tb + t;
+        const bool valid = tok < t1;
+        const int64_t vec = int64_t(row) * a.T + tok;
+        floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+        float sc[4];
         if constexpr (KIND == TQ_KIND_Q8) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(kidx + vec * 128);
-            const uint2 sc2 = *reinterpret_cast<const uint2 *>(a.knorm + vec * 8);
-            const float bs[4] = {h2f(sc2.x & 0xFFFFu), h2f(sc2.x >> 16), h2f(sc2.y & 0xFFFFu), h2f(sc2.y >> 16)};
+            uint2 raw[4] = {};
+            uint2 scl = {};
+            if (valid) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) sc[g] = 0.0f;
-            Unroll<16>::run([&](auto K) {  // 16 chunks of 8 int8 values
-                constexpr int k = decltype(K)::value;
-                const_fp qk = as_const(qr_base + k * 8);
-                asm volatile("" : "+s"(qk));
-                const uint4 u = src[k >> 1];
-                const uint32_t w0 = (k & 1) ? u.z : u.x, w1 = (k & 1) ? u.w : u.y;
-                float part[G];
+                for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const uint2 *>(kidx + vec * 128 + 32 * s + 8 * kq);
+                scl = *reinterpret_cast<const uint2 *>(knorm + vec * 8);
+            }
+            const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int g = 0; g < G; ++g) part[g] = 0.0f;
+            for (int s = 0; s < 4; ++s) {
+                half8 bv;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t ww = i < 4 ? w0 : w1;
-                    const float kv = float(int8_t((ww >> (8 * (i & 3))) & 0xFFu));
-#pragma unroll
-                    for (int g = 0; g < G; ++g) part[g] = fmaf(qk[g * 128 + i], kv, part[g]);
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t w = j < 4 ? raw[s].x : raw[s].y;
+                    bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
                 }
+                floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
+                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bv, ds, 0, 0, 0);
+                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bv, ds, 0, 0, 0);
+                // lane (t, kq) holds heads 4kq + j of token t; scale of block s for token t
 #pragma unroll
-                for (int g = 0; g < G; ++g) sc[g] = fmaf(bs[k >> 2], part[g], sc[g]);
-            });
+                for (int j = 0; j < 4; ++j) acc[j] = fmaf(bs[s], ds[j], acc[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = acc[j] * kRsqrtD;
         } else {
-            uint32_t w[4 * BITS];
-            const uint4 *src = reinterpret_cast<const uint4 *>(kidx + vec * (16 * BITS));
+            uint32_t w[BITS];
+            uint32_t sw = 0, nn = 0;
+            if (valid) {
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(kidx + vec * (16 * BITS) + 4 * BITS * kq);
 #pragma unroll
-            for (int c = 0; c < BITS; ++c) {
-                const uint4 u = src[c];
-                w[4 * c] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
+                for (int i = 0; i < BITS; ++i) w[i] = src[i];
+                if constexpr (KIND == TQ_KIND_PROD) {
+                    sw = reinterpret_cast<const uint32_t *>(ksign + vec * 16)[kq];
+                    nn = reinterpret_cast<const uint32_t *>(knorm)[vec];
+                } else {
+                    nn = reinterpret_cast<const uint16_t *>(knorm)[vec];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < BITS; ++i) w[i] = 0;
             }
-            float acc[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-            // the query values are read from the scalar cache in chunks of
-            // kQc coordinates; the empty asm re-derives the pointer per chunk so
-            // the compiler cannot hoist all 128*G loads into registers at once
-            Unroll<128 / kQc>::run([&](auto K) {
-                constexpr int k = decltype(K)::value;
-                const_fp qk = as_const(qr_base + k * kQc);
-                asm volatile("" : "+s"(qk));
-                Unroll<kQc>::run([&](auto I) {
-                    constexpr int i = decltype(I)::value;
-                    const float lv = s_levels[code_at<BITS, k * kQc + i>(w)];
-#pragma unroll
-                    for (int g = 0; g < G; ++g) acc[g] = fmaf(qk[g * 128 + i], lv, acc[g]);
+            Unroll<4>::run([&](auto S) {
+                constexpr int s = decltype(S)::value;
+                half8 bh, bl;
+                Unroll<8>::run([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    const uint32_t e = s_lut[code_at<BITS, 8 * s + j>(w)];
+                    bh[j] = __builtin_bit_cast(_Float16, uint16_t(e & 0xFFFFu));
+                    bl[j] = __builtin_bit_cast(_Float16, uint16_t(e >> 16));
                 });
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bh, d0, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bl, d0, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bh, d0, 0, 0, 0);
+                if constexpr (KIND == TQ_KIND_PROD) {
+                    half8 sg;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sg[j] = ((sw >> (8 * s + j)) & 1u) ? one : mone;
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aph[s], sg, d1, 0, 0, 0);
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[s], sg, d1, 0, 0, 0);
+                }
             });
-            if constexpr (KIND == TQ_KIND_PROD) {
-                const uint32_t nn = reinterpret_cast<const uint32_t *>(a.knorm)[vec];
-                const float n = h2f(nn & 0xFFFFu), gam = h2f(nn >> 16);
-                const uint4 su = *reinterpret_cast<const uint4 *>(a.ksign + vec * 16);
-                const uint32_t sw[4] = {su.x, su.y, su.z, su.w};
-                float aj[G];
+            // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
+            const float n = h2f(nn & 0xFFFFu) * (1.0f / 128.0f);
+            const float gq = h2f(nn >> 16) * kQjlOverSqrtD;
 #pragma unroll
-                for (int g = 0; g < G; ++g) aj[g] = 0.0f;
-                Unroll<128 / kQc>::run([&](auto K) {
-                    constexpr int k = decltype(K)::value;
-                    const_fp qk = as_const(qp_base + k * kQc);
-                    asm volatile("" : "+s"(qk));
-#pragma unroll
-                    for (int i = 0; i < kQc; ++i) {
-                        const int p = k * kQc + i;
-                        const float bf = float((sw[p >> 5] >> (p & 31)) & 1u);
-#pragma unroll
-                        for (int g = 0; g < G; ++g) aj[g] = fmaf(qk[g * 128 + i], bf, aj[g]);
-                    }
-                });
-#pragma unroll
-                for (int g = 0; g < G; ++g) sc[g] = fmaf(n, acc[g], gam * fmaf(2.0f, aj[g], -qsum[g]));
-            } else {
-                const float n = h2f(reinterpret_cast<const uint16_t *>(a.knorm)[vec]);
-#pragma unroll
-                for (int g = 0; g < G; ++g) sc[g] = n * acc[g];
-            }
+            for (int j = 0; j < 4; ++j) sc[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
         }
+        // lane (t, kq) holds heads 4kq + j of token tok
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            scores[(head0 + g) * a.T + t] = sc[g];
-            if (sc[g] > m[g]) {
-                l[g] = l[g] * exp2f((m[g] - sc[g]) * kLog2e) + 1.0f;
-                m[g] = sc[g];
-            } else {
-                l[g] += exp2f((sc[g] - m[g]) * kLog2e);
+        for (int j = 0; j < 4; ++j) {
+            const int h = 4 * kq + j;
+            if (h < G && valid) {
+                scores[(head0 + h) * a.T + tok] = sc[j];
+                if (sc[j] > m[j]) {
+                    l[j] = l[j] * exp2f((m[j] - sc[j]) * kLog2e) + 1.0f;
+                    m[j] = sc[j];
+                } else {
+                    l[j] += exp2f((sc[j] - m[j]) * kLog2e);
+                }
             }
         }
     }
-    // (max, sum) per head over the block
+    // (max, sum) per head: over the 16 token lanes of each lane group, then waves
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int s = 1; s < 64; s <<= 1) {
-            const float om = __shfl_xor(m[g], s), ol = __shfl_xor(l[g], s);
-            const float nm = fmaxf(m[g], om);
+        for (int s = 1; s < 16; s <<= 1) {
+            const float om = __shfl_xor(m[j], s), ol = __shfl_xor(l[j], s);
+            const float nm = fmaxf(m[j], om);
             float nl = 0.0f;
-            if (nm != -INFINITY) nl = l[g] * exp2f((m[g] - nm) * kLog2e) + ol * exp2f((om - nm) * kLog2e);
-            m[g] = nm;
-            l[g] = nl;
+            if (nm != -INFINITY) nl = l[j] * exp2f((m[j] - nm) * kLog2e) + ol * exp2f((om - nm) * kLog2e);
+            m[j] = nm;
+            l[j] = nl;
         }
-        if (lane == 0) { s_red[wave][g][0] = m[g]; s_red[wave][g][1] = l[g]; }
+        if (t == 0) {
+            s_red[wave][4 * kq + j][0] = m[j];
+            s_red[wave][4 * kq + j][1] = l[j];
+        }
     }
     __syncthreads();
     if (tid < G) {
@@ -273,7 +298,6 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
     __shared__ int s_tok[256];
     __shared__ int s_wcount[4];
     __shared__ float s_acc[4][G][128];
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk_id = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
@@ -406,51 +430,48 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
         const float s = s_acc[0][g][c] + s_acc[1][g][c] + s_acc[2][g][c] + s_acc[3][g][c];
         a.part[((head0 + g) * a.n_chunks + chunk_id) * 128 + c] = s;
     }
-    // the last block of this (batch, kv head) merges the chunk partials
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(a.cnt + row, 1u);
-        s_last = (prev == uint32_t(a.n_chunks - 1)) ? 1 : 0;
+}
+
+// ------------------------------------------------------------------- merge
+// One wave per (batch, q head): sum the chunk partials and rotate back,
+// out = R^T acc = D H acc / sqrt(d) (rotated V codecs only).
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+    const int head = blockIdx.x;  // b * Hq + h
+    const int lane = threadIdx.x;
+    float v0 = 0.0f, v1 = 0.0f;
+    const float *pp = a.part + int64_t(head) * a.n_chunks * 128;
+#pragma unroll 8
+    for (int c = 0; c < a.n_chunks; ++c) {
+        v0 += pp[c * 128 + lane];
+        v1 += pp[c * 128 + lane + 64];
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int g = wave; g < G; g += 4) {
-        float v0 = 0.0f, v1 = 0.0f;
-        const volatile float *pp = a.part + (head0 + g) * a.n_chunks * 128;
-        for (int c = 0; c < a.n_chunks; ++c) {
-            v0 += pp[c * 128 + lane];
-            v1 += pp[c * 128 + lane + 64];
-        }
-        if (a.v_rotated) {
-            // out = R^T acc = D H acc / sqrt(d)
-            const float s0 = v0 + v1, s1 = v0 - v1;
-            v0 = s0;
-            v1 = s1;
+    if (a.v_rotated) {
+        const float s0 = v0 + v1, s1 = v0 - v1;
+        v0 = s0;
+        v1 = s1;
 #pragma unroll
-            for (int s = 1; s < 64; s <<= 1) {
-                const float sg = (lane & s) ? -1.0f : 1.0f;
-                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-                v0 = fmaf(sg, v0, p0);
-                v1 = fmaf(sg, v1, p1);
-            }
-            v0 *= a.tab->signs[lane] * kRsqrtD;
-            v1 *= a.tab->signs[lane + 64] * kRsqrtD;
+        for (int s = 1; s < 64; s <<= 1) {
+            const float sg = (lane & s) ? -1.0f : 1.0f;
+            const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+            v0 = fmaf(sg, v0, p0);
+            v1 = fmaf(sg, v1, p1);
         }
-        a.out[(head0 + g) * 128 + lane] = v0;
-        a.out[(head0 + g) * 128 + lane + 64] = v1;
+        v0 *= a.tab->signs[lane] * kRsqrtD;
+        v1 *= a.tab->signs[lane + 64] * kRsqrtD;
     }
-    if (tid == 0) a.cnt[row] = 0u;
+    a.out[int64_t(head) * 128 + lane] = v0;
+    a.out[int64_t(head) * 128 + lane + 64] = v1;
 }
 
 template <int G, int KK, int KB, int VK, int VB>
 static int launch_pair(const AttnArgs &a, hipStream_t s) {
     dim3 grid(unsigned(a.n_chunks), unsigned(a.B * a.Hkv));
     hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, a, a.qr, a.qp, a.kidx,
-                       a.scores);
+                       a.ksign, a.knorm, a.scores);
     if (hipGetLastError() != hipSuccess) return 1;
     hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return 1;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(a.B * a.Hq)), dim3(64), 0, s, a);
     return int(hipGetLastError());
 }
 
@@ -504,11 +525,9 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.seq_lens = seq_lens;
     a.qr = reinterpret_cast<float *>(w + plan.off_qr);
     a.qp = reinterpret_cast<float *>(w + plan.off_qp);
-    a.qsum = reinterpret_cast<float *>(w + plan.off_qsum);
     a.scores = reinterpret_cast<float *>(w + plan.off_scores);
     a.stats = reinterpret_cast<float *>(w + plan.off_stats);
     a.part = reinterpret_cast<float *>(w + plan.off_part);
-    a.cnt = reinterpret_cast<uint32_t *>(w + plan.off_cnt);
     a.out = out;
     a.tau = tau;
     a.B = B;

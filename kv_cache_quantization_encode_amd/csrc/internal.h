@@ -17,6 +17,7 @@ struct DevTables {
     uint32_t sign_pair_xor[4][16];   // fp16-pair sign flips of D per lane quarter
     float signs[kHeadDim];           // D
     uint16_t S[kHeadDim * kHeadDim]; // QJL matrix, fp16 bits, row-major [m][d]
+    uint16_t ST[kHeadDim * kHeadDim];// its transpose [d][m]
     uint16_t S_enc[32 * 64 * 8];     // S as encode MFMA A-fragments
     uint16_t St_dec[32 * 64 * 8];    // S^T as dequant MFMA A-fragments
 };
@@ -35,7 +36,7 @@ bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out);
 struct AttnPlan {
     int n_chunks;    // token chunks per (batch, kv head)
     int chunk;       // tokens per chunk (multiple of 256)
-    size_t off_qr, off_qp, off_qsum, off_scores, off_stats, off_part, off_cnt, total;
+    size_t off_qr, off_qp, off_scores, off_stats, off_part, total;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
 

@@ -134,6 +134,8 @@ void build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
         for (int k = (1 << b) - 1; k < 16; ++k) t->bounds[b - 1][k] = INFINITY;
     }
     random_tables(d, m, seed, t->signs, t->S);
+    for (int r = 0; r < m; ++r)
+        for (int c = 0; c < d; ++c) t->ST[c * m + r] = t->S[r * d + c];
     // xor masks that flip the sign bits of packed fp16 pairs: lane quarter q
     // holds coordinates 32q..32q+31, pair p covers 32q+2p and 32q+2p+1
     for (int q = 0; q < 4; ++q)
