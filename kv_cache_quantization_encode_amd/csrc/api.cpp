@@ -60,7 +60,7 @@ bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out) {
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     AttnPlan p{};
     const int64_t rows = int64_t(B) * Hkv;
-    int64_t want = (2048 + rows - 1) / rows;  // aim for ~2048 blocks per pass
+    int64_t want = (512 + rows - 1) / rows;  // aim for ~512 blocks per pass
     int64_t maxc = (int64_t(T) + 255) / 256;
     int64_t nc = want < maxc ? want : maxc;
     if (nc < 1) nc = 1;
@@ -72,8 +72,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     p.chunk = int(chunk);
     const int64_t heads = int64_t(B) * Hq;
     int64_t off = 0;
-    p.off_qr = size_t(off); off = align256(off + heads * kHeadDim * 4);
-    p.off_qp = size_t(off); off = align256(off + heads * kHeadDim * 4);
+    p.off_qfrag = size_t(off); off = align256(off + rows * 16 * 64 * 16);
     p.off_scores = size_t(off); off = align256(off + heads * int64_t(T) * 4);
     p.off_stats = size_t(off); off = align256(off + heads * nc * 2 * 4);
     p.off_part = size_t(off); off = align256(off + heads * nc * kHeadDim * 4);
@@ -140,7 +139,7 @@ tq_status tq_codebook_init(tq_ctx **ctx, int head_dim, int qjl_dim, uint64_t see
     DevTables *host = new (std::nothrow) DevTables;
     tq_ctx *c = new (std::nothrow) tq_ctx;
     if (!host || !c) { delete host; delete c; return TQ_ERR_ALLOC; }
-    build_device_tables(head_dim, qjl_dim, seed, host);
+    if (!build_device_tables(head_dim, qjl_dim, seed, host)) { delete host; delete c; return TQ_ERR_UNSUPPORTED; }
     int dev = 0;
     hipDeviceProp_t prop;
     if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -174,6 +173,7 @@ tq_status tq_ctx_destroy(tq_ctx *ctx) {
 tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, int64_t n_vec,
                        tq_format kf, tq_format vf, void *k_packed, void *v_packed, void *stream) {
     if (!ctx || n_vec < 0) return TQ_ERR_INVALID_ARG;
+    if (n_vec > kMaxRows) return TQ_ERR_UNSUPPORTED;
     if (!k_f16 && !v_f16) return TQ_ERR_INVALID_ARG;
     tq_planes_desc kl{}, vl{};
     if (k_f16) {
@@ -193,6 +193,7 @@ tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, 
 tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64_t n_vec,
                        void *out_f16, void *stream) {
     if (!ctx || !packed || !out_f16 || n_vec < 0) return TQ_ERR_INVALID_ARG;
+    if (n_vec > kMaxRows) return TQ_ERR_UNSUPPORTED;
     if (!aligned(packed, 256) || !aligned(out_f16, 16)) return TQ_ERR_INVALID_ARG;
     tq_planes_desc l{};
     if (!plane_layout(f, ctx->head_dim, n_vec, &l)) return TQ_ERR_INVALID_ARG;
@@ -221,7 +222,7 @@ tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_pac
     if (vf.kind == TQ_KIND_PROD) return TQ_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
     if (g != 1 && g != 2 && g != 4 && g != 8) return TQ_ERR_UNSUPPORTED;
-    if (int64_t(B) * Hkv * T > (int64_t(1) << 36)) return TQ_ERR_UNSUPPORTED;
+    if (int64_t(B) * Hkv * T > kMaxRows || int64_t(T) * 128 >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
     const int64_t n_vec = int64_t(B) * Hkv * T;
     tq_planes_desc kl{}, vl{};
     if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))

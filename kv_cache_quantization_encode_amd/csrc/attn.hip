@@ -14,7 +14,8 @@
 // accumulated in the rotated domain and rotated back once per head.
 //
 // Passes (one stream, no host synchronisation):
-//   1. prologue   one wave per (batch, q head): q_rot and q_proj.
+//   1. prologue   one block per (batch, kv head): q_rot and q_proj of its query
+//                 heads, written as pre-split MFMA operands.
 //   2. scores     grid (chunk, batch*kv head); MFMA over 16-token tiles with
 //                 the g query heads of the kv head as rows; scores go to the
 //                 workspace with per-chunk (max, sum exp) per head.
@@ -40,11 +41,13 @@ struct AttnArgs {
     const uint8_t *kidx, *ksign, *knorm;  // K planes
     const uint8_t *vidx, *vnorm;          // V planes
     const int32_t *seq_lens;
-    float *qr, *qp, *scores, *stats, *part;
+    half8 *qfrag;
+    float *scores, *stats, *part;
     float *out;
     float tau;
     int B, Hq, Hkv, T, chunk, n_chunks;
     int k_rotated;  // K codec works in the rotated domain
+    int want_proj;  // K carries QJL sign bits
     int v_rotated;  // V codec works in the rotated domain
 };
 
@@ -55,47 +58,98 @@ __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
 }
 
 // ---------------------------------------------------------------- prologue
-// q_rot = R q = H D q / sqrt(d) for rotated keys (q itself for q8 keys) and
-// q_proj = S q_rot, both unscaled fp32; the score scales are applied per token.
-__global__ __launch_bounds__(64) void attn_prologue_kernel(AttnArgs a, int want_proj) {
-    __shared__ float s_q[128];
-    const int head = blockIdx.x;  // b * Hq + h
-    const int lane = threadIdx.x;
-    const uint16_t *q = a.q + int64_t(head) * 128;
-    float v0 = h2f(q[lane]), v1 = h2f(q[lane + 64]);
-    if (a.k_rotated) {
-        v0 *= a.tab->signs[lane];
-        v1 *= a.tab->signs[lane + 64];
-        // H over coordinate bit 6 in-lane, bits 0..5 across lanes
-        const float s0 = v0 + v1, s1 = v0 - v1;
-        v0 = s0;
-        v1 = s1;
+// One block per (batch, kv head).  For each of its g query heads:
+// q_rot = R q = H D q / sqrt(d) (q itself for q8 keys) and q_proj = S q_rot,
+// unscaled fp32 (the score scales are applied per token).  The block then
+// writes them as the A operands of the scores MFMAs: 16 fragments (k-step s,
+// kind rot-hi/rot-lo/proj-hi/proj-lo) x 64 lanes x 8 fp16, lane (h, kq)
+// holding head h (zero for h >= g) at coordinates c0 + [0,8) with
+// c0 = 32 kq + 8 s (rotated keys) or 32 s + 8 kq (q8 keys).
+template <int G>
+__global__ __launch_bounds__(256) void attn_prologue_kernel(AttnArgs a, int want_proj) {
+    __shared__ float s_q[G][128];
+    __shared__ float s_p[G][128];
+    const int row = blockIdx.x;  // b * Hkv + kvh
+    const int b = row / a.Hkv, kvh = row - b * a.Hkv;
+    const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int g = wave; g < G; g += 4) {
+        const uint16_t *q = a.q + (head0 + g) * 128;
+        float v0 = h2f(q[lane]), v1 = h2f(q[lane + 64]);
+        if (a.k_rotated) {
+            v0 *= a.tab->signs[lane];
+            v1 *= a.tab->signs[lane + 64];
+            // H over coordinate bit 6 in-lane, bits 0..5 across lanes
+            const float s0 = v0 + v1, s1 = v0 - v1;
+            v0 = s0;
+            v1 = s1;
 #pragma unroll
-        for (int s = 1; s < 64; s <<= 1) {
-            const float sg = (lane & s) ? -1.0f : 1.0f;
-            const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-            v0 = fmaf(sg, v0, p0);
-            v1 = fmaf(sg, v1, p1);
+            for (int s = 1; s < 64; s <<= 1) {
+                const float sg = (lane & s) ? -1.0f : 1.0f;
+                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+                v0 = fmaf(sg, v0, p0);
+                v1 = fmaf(sg, v1, p1);
+            }
+            v0 *= kRsqrtD;
+            v1 *= kRsqrtD;
         }
-        v0 *= kRsqrtD;
-        v1 *= kRsqrtD;
+        s_q[g][lane] = v0;
+        s_q[g][lane + 64] = v1;
     }
-    a.qr[int64_t(head) * 128 + lane] = v0;
-    a.qr[int64_t(head) * 128 + lane + 64] = v1;
+    __syncthreads();
     if (want_proj) {
-        s_q[lane] = v0;
-        s_q[lane + 64] = v1;
-        __syncthreads();
-        const uint16_t *ST = a.tab->ST;  // S^T: lanes read consecutive projections
-        float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll 8
-        for (int i = 0; i < 128; ++i) {
-            const float qi = s_q[i];
-            p0 = fmaf(h2f(ST[i * 128 + lane]), qi, p0);
-            p1 = fmaf(h2f(ST[i * 128 + lane + 64]), qi, p1);
+        // q_proj = S q_rot on the MFMA units: rows = 128 projections (wave w
+        // takes row blocks 2w, 2w+1), columns = the g heads (zero-padded to
+        // 16), k = coordinates 32 kq + 8 s + j; q_rot split into fp16 hi + lo
+        const int h = lane & 15, kq = lane >> 4;
+        half8 bh[4], bl[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = h < G ? s_q[h][32 * kq + 8 * st + j] : 0.0f;
+                const _Float16 hi = _Float16(v);
+                bh[st][j] = hi;
+                bl[st][j] = _Float16(v - float(hi));
+            }
         }
-        a.qp[int64_t(head) * 128 + lane] = p0;
-        a.qp[int64_t(head) * 128 + lane + 64] = p1;
+        const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);  // row-major [128][128]
+#pragma unroll
+        for (int rb2 = 0; rb2 < 2; ++rb2) {
+            const int rb = 2 * wave + rb2;
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const half8 af = S8[(16 * rb + h) * 16 + 4 * kq + st];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bh[st], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl[st], acc, 0, 0, 0);
+            }
+            // lane (h, kq) holds projections 16 rb + 4 kq + j of head h
+            if (h < G) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_p[h][16 * rb + 4 * kq + j] = acc[j];
+            }
+        }
+        __syncthreads();
+    }
+    half8 *frag = a.qfrag + int64_t(row) * 16 * 64;
+    for (int e = tid; e < 16 * 64; e += 256) {
+        const int f = e >> 6, l = e & 63;
+        const int kind = f >> 2, s = f & 3;
+        const int h = l & 15, kq = l >> 4;
+        const int c0 = a.k_rotated ? 32 * kq + 8 * s : 32 * s + 8 * kq;
+        half8 out;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = 0.0f;
+            if (h < G) {
+                if (kind < 2) v = s_q[h][c0 + j];
+                else if (want_proj) v = s_p[h][c0 + j];
+            }
+            const _Float16 hi = _Float16(v);
+            out[j] = (kind & 1) ? _Float16(v - float(hi)) : hi;
+        }
+        frag[e] = out;
     }
 }
 
@@ -108,6 +162,23 @@ __global__ __launch_bounds__(64) void attn_prologue_kernel(AttnArgs a, int want_
 // the query is split into hi + lo fp16 halves and every codebook level into
 // hi + lo halves (three products, dropping lo*lo); the QJL operand is +-1,
 // exact in fp16.  q8 keys use k-steps = the four 32-element scale blocks.
+// 2^x on the transcendental unit (v_exp_f32); only used for softmax weights
+// of arguments <= 0, where its flush of results below 2^-126 is immaterial.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Eight fp16 +-1 values from bits 8s..8s+7 of w (bit set -> +1): per pair of
+// bits, x * (2^15 + 2^30) places the inverted bits at the two sign positions.
+__device__ __forceinline__ half8 pm_one8(uint32_t w, int s) {
+    const uint32_t nb = ~w >> (8 * s);
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t x = (nb >> (2 * p)) & 3u;
+        d[p] = ((x * 0x40008000u) & 0x80008000u) | 0x3C003C00u;
+    }
+    return __builtin_bit_cast(half8, d);
+}
+
 __device__ __forceinline__ void split_half8(const float *src, half8 &hi, half8 &lo) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -118,13 +189,13 @@ __device__ __forceinline__ void split_half8(const float *src, half8 &hi, half8 &
 }
 
 template <int G, int KIND, int BITS>
-__global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const float *__restrict__ qr_all,
-                                                          const float *__restrict__ qp_all,
-                                                          const uint8_t *__restrict__ kidx,
+__global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
                                                           const uint8_t *__restrict__ ksign,
                                                           const uint8_t *__restrict__ knorm,
                                                           float *__restrict__ scores) {
     static_assert(G <= 16, "at most 16 query heads per kv head");
+    constexpr int NT = 4;                   // tiles of 16 tokens per wave per 256-token slice
+    constexpr int W = KIND == TQ_KIND_Q8 ? 8 : BITS;  // code dwords per lane and tile
     __shared__ uint32_t s_lut[16];          // level k as fp16 hi | fp16 lo << 16
     __shared__ float s_red[4][16][2];       // per wave, per head: (max, sum)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -141,125 +212,156 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const floa
                          (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
         }
     }
-    // A operands: lane (h = l&15, kq) holds 8 query values per k-step
+    const int L = seq_len_of(a, b);
+    const int t0 = chunk_id * a.chunk;
+    const int t1 = min(t0 + a.chunk, L);
+    // per-(batch, kv head) bases of the planes; offsets below are 32-bit
+    // (T * 128 < 2^31 is checked on the host)
+    const uint8_t *kid = kidx + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 128 : 16 * BITS);
+    const uint8_t *ksg = ksign + int64_t(row) * a.T * 16;
+    const uint8_t *knm = knorm + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 8 : (KIND == TQ_KIND_PROD ? 4 : 2));
+
+    // raw packed data of this wave's NT tiles in the current slice; the loads
+    // for all NT tiles are issued before any is used (bytes in flight)
+    uint32_t wk[NT][W], sw[NT], nn[NT];
+    uint2 q8s[NT];
+    auto load_slice = [&](int base) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int tok = base + wave * 16 + 64 * i + t;
+            if (tok < t1) {
+                if constexpr (KIND == TQ_KIND_Q8) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
+                        wk[i][2 * s] = u.x;
+                        wk[i][2 * s + 1] = u.y;
+                    }
+                    q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
+                } else {
+                    const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
+#pragma unroll
+                    for (int w = 0; w < W; ++w) wk[i][w] = src[w];
+                    if constexpr (KIND == TQ_KIND_PROD) {
+                        sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
+                        nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
+                    } else {
+                        nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < W; ++w) wk[i][w] = 0;
+                sw[i] = 0;
+                nn[i] = 0;
+                q8s[i] = uint2{0u, 0u};
+            }
+        }
+    };
+    if (t0 < t1) load_slice(t0);
+
+    // A operands, pre-split by the prologue: fragments rot-hi, rot-lo,
+    // proj-hi, proj-lo for k-steps 0..3
     half8 arh[4], arl[4], aph[4], apl[4];
     {
-        const int h = lane & 15;
-        float buf[8];
+        const half8 *frag = a.qfrag + int64_t(row) * 16 * 64 + lane;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int c0 = (KIND == TQ_KIND_Q8) ? 32 * s + 8 * kq : 32 * kq + 8 * s;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) buf[j] = h < G ? qr_all[(head0 + h) * 128 + c0 + j] : 0.0f;
-            split_half8(buf, arh[s], arl[s]);
+            arh[s] = frag[(0 * 4 + s) * 64];
+            arl[s] = frag[(1 * 4 + s) * 64];
             if constexpr (KIND == TQ_KIND_PROD) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) buf[j] = h < G ? qp_all[(head0 + h) * 128 + c0 + j] : 0.0f;
-                split_half8(buf, aph[s], apl[s]);
+                aph[s] = frag[(2 * 4 + s) * 64];
+                apl[s] = frag[(3 * 4 + s) * 64];
             }
         }
     }
     __syncthreads();
-    const int L = seq_len_of(a, b);
-    const int t0 = chunk_id * a.chunk;
-    const int t1 = min(t0 + a.chunk, L);
     float m[4], l[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
-    const _Float16 one = _Float16(1.0f), mone = _Float16(-1.0f);
 
-    for (int tb = t0 + wave * 16; tb < t1; tb += 64) {
-        const int tok = tb + t;
-        const bool valid = tok < t1;
-        const int64_t vec = int64_t(row) * a.T + tok;
-        floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-        float sc[4];
-        if constexpr (KIND == TQ_KIND_Q8) {
-            uint2 raw[4] = {};
-            uint2 scl = {};
-            if (valid) {
+    for (int base = t0; base < t1; base += 256) {
+        float scv[NT][4];  // this lane's scores of the slice, -inf where absent
 #pragma unroll
-                for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const uint2 *>(kidx + vec * 128 + 32 * s + 8 * kq);
-                scl = *reinterpret_cast<const uint2 *>(knorm + vec * 8);
-            }
-            const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < NT; ++i) {
+            const int tok = base + wave * 16 + 64 * i + t;
+            const bool valid = tok < t1;
+            float sc[4];
+            if constexpr (KIND == TQ_KIND_Q8) {
+                const uint2 scl = q8s[i];
+                const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8 bv;
+                for (int s = 0; s < 4; ++s) {
+                    half8 bv;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t w = j < 4 ? raw[s].x : raw[s].y;
-                    bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t w = wk[i][2 * s + (j >> 2)];
+                        bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
+                    }
+                    floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
+                    ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bv, ds, 0, 0, 0);
+                    ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bv, ds, 0, 0, 0);
+                    // lane (t, kq) holds heads 4kq + j of token t; scale of block s of token t
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = fmaf(bs[s], ds[j], acc[j]);
                 }
-                floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
-                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bv, ds, 0, 0, 0);
-                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bv, ds, 0, 0, 0);
-                // lane (t, kq) holds heads 4kq + j of token t; scale of block s for token t
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = fmaf(bs[s], ds[j], acc[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = acc[j] * kRsqrtD;
-        } else {
-            uint32_t w[BITS];
-            uint32_t sw = 0, nn = 0;
-            if (valid) {
-                const uint32_t *src = reinterpret_cast<const uint32_t *>(kidx + vec * (16 * BITS) + 4 * BITS * kq);
-#pragma unroll
-                for (int i = 0; i < BITS; ++i) w[i] = src[i];
-                if constexpr (KIND == TQ_KIND_PROD) {
-                    sw = reinterpret_cast<const uint32_t *>(ksign + vec * 16)[kq];
-                    nn = reinterpret_cast<const uint32_t *>(knorm)[vec];
-                } else {
-                    nn = reinterpret_cast<const uint16_t *>(knorm)[vec];
-                }
+                for (int j = 0; j < 4; ++j) sc[j] = acc[j] * kRsqrtD;
             } else {
-#pragma unroll
-                for (int i = 0; i < BITS; ++i) w[i] = 0;
-            }
-            Unroll<4>::run([&](auto S) {
-                constexpr int s = decltype(S)::value;
-                half8 bh, bl;
-                Unroll<8>::run([&](auto J) {
-                    constexpr int j = decltype(J)::value;
-                    const uint32_t e = s_lut[code_at<BITS, 8 * s + j>(w)];
-                    bh[j] = __builtin_bit_cast(_Float16, uint16_t(e & 0xFFFFu));
-                    bl[j] = __builtin_bit_cast(_Float16, uint16_t(e >> 16));
+                floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+                Unroll<4>::run([&](auto S) {
+                    constexpr int s = decltype(S)::value;
+                    half8 bh, bl;
+                    Unroll<8>::run([&](auto J) {
+                        constexpr int j = decltype(J)::value;
+                        const uint32_t e = s_lut[code_at<BITS, 8 * s + j>(wk[i])];
+                        bh[j] = __builtin_bit_cast(_Float16, uint16_t(e & 0xFFFFu));
+                        bl[j] = __builtin_bit_cast(_Float16, uint16_t(e >> 16));
+                    });
+                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bh, d0, 0, 0, 0);
+                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bl, d0, 0, 0, 0);
+                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bh, d0, 0, 0, 0);
+                    if constexpr (KIND == TQ_KIND_PROD) {
+                        const half8 sg = pm_one8(sw[i], s);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aph[s], sg, d1, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[s], sg, d1, 0, 0, 0);
+                    }
                 });
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bh, d0, 0, 0, 0);
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bl, d0, 0, 0, 0);
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bh, d0, 0, 0, 0);
-                if constexpr (KIND == TQ_KIND_PROD) {
-                    half8 sg;
+                // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
+                const float n = h2f(nn[i] & 0xFFFFu) * (1.0f / 128.0f);
+                const float gq = h2f(nn[i] >> 16) * kQjlOverSqrtD;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) sg[j] = ((sw >> (8 * s + j)) & 1u) ? one : mone;
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aph[s], sg, d1, 0, 0, 0);
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[s], sg, d1, 0, 0, 0);
-                }
-            });
-            // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
-            const float n = h2f(nn & 0xFFFFu) * (1.0f / 128.0f);
-            const float gq = h2f(nn >> 16) * kQjlOverSqrtD;
+                for (int j = 0; j < 4; ++j) sc[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
+            }
+            // lane (t, kq) holds heads 4kq + j of token tok
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * kq + j;
+                const bool live = h < G && valid;
+                if (live) scores[(head0 + h) * a.T + tok] = sc[j];
+                scv[i][j] = live ? sc[j] * kLog2e : -INFINITY;
+            }
         }
-        // lane (t, kq) holds heads 4kq + j of token tok
+        // running (max, sum) per lane and head, once per slice, in log2 units
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int h = 4 * kq + j;
-            if (h < G && valid) {
-                scores[(head0 + h) * a.T + tok] = sc[j];
-                if (sc[j] > m[j]) {
-                    l[j] = l[j] * exp2f((m[j] - sc[j]) * kLog2e) + 1.0f;
-                    m[j] = sc[j];
-                } else {
-                    l[j] += exp2f((sc[j] - m[j]) * kLog2e);
-                }
+            float mx = scv[0][j];
+#pragma unroll
+            for (int i = 1; i < NT; ++i) mx = fmaxf(mx, scv[i][j]);
+            const float nm = fmaxf(m[j], mx);
+            if (nm != -INFINITY) {
+                float acc = l[j] * fast_exp2(m[j] - nm);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) acc += fast_exp2(scv[i][j] - nm);
+                l[j] = acc;
+                m[j] = nm;
             }
         }
+        if (base + 256 < t1) load_slice(base + 256);
     }
-    // (max, sum) per head: over the 16 token lanes of each lane group, then waves
+    // (max, sum) per head: over the 16 token lanes of each lane group, then
+    // over the waves; m is kept in log2 units and stored in natural units
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -267,7 +369,7 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const floa
             const float om = __shfl_xor(m[j], s), ol = __shfl_xor(l[j], s);
             const float nm = fmaxf(m[j], om);
             float nl = 0.0f;
-            if (nm != -INFINITY) nl = l[j] * exp2f((m[j] - nm) * kLog2e) + ol * exp2f((om - nm) * kLog2e);
+            if (nm != -INFINITY) nl = l[j] * fast_exp2(m[j] - nm) + ol * fast_exp2(om - nm);
             m[j] = nm;
             l[j] = nl;
         }
@@ -282,9 +384,9 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const floa
         for (int w = 0; w < 4; ++w) mm = fmaxf(mm, s_red[w][tid][0]);
         float ll = 0.0f;
         if (mm != -INFINITY)
-            for (int w = 0; w < 4; ++w) ll += s_red[w][tid][1] * exp2f((s_red[w][tid][0] - mm) * kLog2e);
+            for (int w = 0; w < 4; ++w) ll += s_red[w][tid][1] * fast_exp2(s_red[w][tid][0] - mm);
         float *st = a.stats + ((head0 + tid) * a.n_chunks + chunk_id) * 2;
-        st[0] = mm;
+        st[0] = mm == -INFINITY ? mm : mm / kLog2e;
         st[1] = ll;
     }
 }
@@ -370,44 +472,67 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
             for (int g = 0; g < G; ++g) s_w[g][slot] = wgt[g];
         }
         __syncthreads();
-        // 3) accumulate kept rows: 16 tokens per pass (4 per wave), 8 coordinates per lane
-        for (int k0 = 0; k0 < total; k0 += 16) {
-            const int slot = k0 + wave * 4 + tk;
-            if (slot < total) {
-                const int64_t vec = int64_t(row) * a.T + s_tok[slot];
-                float val[8];
-                if constexpr (KIND == TQ_KIND_Q8) {
-                    const uint2 u = *reinterpret_cast<const uint2 *>(a.vidx + vec * 128 + 8 * cg);
-                    const float bsc = h2f(reinterpret_cast<const uint16_t *>(a.vnorm)[vec * 4 + (cg >> 2)]);
+        // 3) accumulate kept rows: 16 tokens per pass (4 per wave), 8 coordinates
+        //    per lane; the loads of 4 passes are issued before any is used
+        constexpr int PASSES = 4;
+        for (int k0 = 0; k0 < total; k0 += 16 * PASSES) {
+            uint32_t raw[PASSES][2];
+            float bsc[PASSES];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        val[j] = float(int8_t((u.x >> (8 * j)) & 0xFFu)) * bsc;
-                        val[4 + j] = float(int8_t((u.y >> (8 * j)) & 0xFFu)) * bsc;
+            for (int ps = 0; ps < PASSES; ++ps) {
+                const int slot = k0 + 16 * ps + wave * 4 + tk;
+                raw[ps][0] = raw[ps][1] = 0u;
+                bsc[ps] = 0.0f;
+                if (slot < total) {
+                    const int64_t vec = int64_t(row) * a.T + s_tok[slot];
+                    if constexpr (KIND == TQ_KIND_Q8) {
+                        const uint2 u = *reinterpret_cast<const uint2 *>(a.vidx + vec * 128 + 8 * cg);
+                        raw[ps][0] = u.x;
+                        raw[ps][1] = u.y;
+                        bsc[ps] = h2f(reinterpret_cast<const uint16_t *>(a.vnorm)[vec * 4 + (cg >> 2)]);
+                    } else {
+                        const uint8_t *rowp = a.vidx + vec * (16 * BITS);
+                        if constexpr (BITS == 4) {
+                            raw[ps][0] = reinterpret_cast<const uint32_t *>(rowp)[cg];
+                        } else if constexpr (BITS == 2) {
+                            raw[ps][0] = reinterpret_cast<const uint16_t *>(rowp)[cg];
+                        } else if constexpr (BITS == 1) {
+                            raw[ps][0] = rowp[cg];
+                        } else {  // 3 bits: 24 bits starting at byte 3*cg
+                            const uint32_t *wp = reinterpret_cast<const uint32_t *>(rowp);
+                            const int byte = 3 * cg;
+                            raw[ps][0] = wp[byte >> 2];
+                            raw[ps][1] = wp[(byte + 2) >> 2];
+                        }
                     }
-                } else {
-                    const uint8_t *rowp = a.vidx + vec * (16 * BITS);
-                    uint32_t bitsw;
-                    if constexpr (BITS == 4) {
-                        bitsw = reinterpret_cast<const uint32_t *>(rowp)[cg];
-                    } else if constexpr (BITS == 2) {
-                        bitsw = reinterpret_cast<const uint16_t *>(rowp)[cg];
-                    } else if constexpr (BITS == 1) {
-                        bitsw = rowp[cg];
-                    } else {  // 3 bits: 24 bits starting at byte 3*cg
-                        const uint32_t *wp = reinterpret_cast<const uint32_t *>(rowp);
-                        const int byte = 3 * cg;
-                        const uint32_t lo = wp[byte >> 2], hi = wp[(byte + 2) >> 2];
-                        const uint64_t both = (uint64_t(hi) << 32) | lo;
-                        bitsw = uint32_t(both >> (8 * (byte & 3)));
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) val[j] = s_levels[(bitsw >> (BITS * j)) & ((1u << BITS) - 1u)];
                 }
+            }
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float wg = s_w[g][slot];
+            for (int ps = 0; ps < PASSES; ++ps) {
+                const int slot = k0 + 16 * ps + wave * 4 + tk;
+                if (slot < total) {
+                    float val[8];
+                    if constexpr (KIND == TQ_KIND_Q8) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
+                        for (int j = 0; j < 4; ++j) {
+                            val[j] = float(int8_t((raw[ps][0] >> (8 * j)) & 0xFFu)) * bsc[ps];
+                            val[4 + j] = float(int8_t((raw[ps][1] >> (8 * j)) & 0xFFu)) * bsc[ps];
+                        }
+                    } else {
+                        uint32_t bitsw = raw[ps][0];
+                        if constexpr (BITS == 3) {
+                            const uint64_t both = (uint64_t(raw[ps][1]) << 32) | raw[ps][0];
+                            bitsw = uint32_t(both >> (8 * ((3 * cg) & 3)));
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) val[j] = s_levels[(bitsw >> (BITS * j)) & ((1u << BITS) - 1u)];
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float wg = s_w[g][slot];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
+                    }
                 }
             }
         }
@@ -433,18 +558,26 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------- merge
-// One wave per (batch, q head): sum the chunk partials and rotate back,
-// out = R^T acc = D H acc / sqrt(d) (rotated V codecs only).
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+// One block per (batch, q head): the 4 waves each sum a quarter of the chunk
+// partials, then wave 0 rotates back, out = R^T acc = D H acc / sqrt(d)
+// (rotated V codecs only).
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    __shared__ float s_sum[4][128];
     const int head = blockIdx.x;  // b * Hq + h
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float v0 = 0.0f, v1 = 0.0f;
     const float *pp = a.part + int64_t(head) * a.n_chunks * 128;
 #pragma unroll 8
-    for (int c = 0; c < a.n_chunks; ++c) {
+    for (int c = wave; c < a.n_chunks; c += 4) {
         v0 += pp[c * 128 + lane];
         v1 += pp[c * 128 + lane + 64];
     }
+    s_sum[wave][lane] = v0;
+    s_sum[wave][lane + 64] = v1;
+    __syncthreads();
+    if (wave != 0) return;
+    v0 = s_sum[0][lane] + s_sum[1][lane] + s_sum[2][lane] + s_sum[3][lane];
+    v1 = s_sum[0][lane + 64] + s_sum[1][lane + 64] + s_sum[2][lane + 64] + s_sum[3][lane + 64];
     if (a.v_rotated) {
         const float s0 = v0 + v1, s1 = v0 - v1;
         v0 = s0;
@@ -466,12 +599,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 template <int G, int KK, int KB, int VK, int VB>
 static int launch_pair(const AttnArgs &a, hipStream_t s) {
     dim3 grid(unsigned(a.n_chunks), unsigned(a.B * a.Hkv));
-    hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, a, a.qr, a.qp, a.kidx,
-                       a.ksign, a.knorm, a.scores);
+    hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, a, a.kidx, a.ksign, a.knorm,
+                       a.scores);
     if (hipGetLastError() != hipSuccess) return 1;
     hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return 1;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(a.B * a.Hq)), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(a.B * a.Hq)), dim3(256), 0, s, a);
     return int(hipGetLastError());
 }
 
@@ -489,6 +622,8 @@ static int dispatch_v(const AttnArgs &a, tq_format vf, hipStream_t s) {
 
 template <int G>
 static int dispatch_k(const AttnArgs &a, tq_format kf, tq_format vf, hipStream_t s) {
+    hipLaunchKernelGGL((attn_prologue_kernel<G>), dim3(unsigned(a.B * a.Hkv)), dim3(256), 0, s, a, a.want_proj);
+    if (hipGetLastError() != hipSuccess) return 1;
     if (kf.kind == TQ_KIND_Q8) return dispatch_v<G, TQ_KIND_Q8, 8>(a, vf, s);
     if (kf.kind == TQ_KIND_PROD) {
         switch (kf.bits) {
@@ -523,8 +658,7 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.vidx = vb + vlay.idx_offset;
     a.vnorm = vb + vlay.norm_offset;
     a.seq_lens = seq_lens;
-    a.qr = reinterpret_cast<float *>(w + plan.off_qr);
-    a.qp = reinterpret_cast<float *>(w + plan.off_qp);
+    a.qfrag = reinterpret_cast<half8 *>(w + plan.off_qfrag);
     a.scores = reinterpret_cast<float *>(w + plan.off_scores);
     a.stats = reinterpret_cast<float *>(w + plan.off_stats);
     a.part = reinterpret_cast<float *>(w + plan.off_part);
@@ -538,9 +672,7 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.n_chunks = plan.n_chunks;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
-    hipLaunchKernelGGL(attn_prologue_kernel, dim3(unsigned(B * Hq)), dim3(64), 0, s, a,
-                       kf.kind == TQ_KIND_PROD ? 1 : 0);
-    if (hipGetLastError() != hipSuccess) return 1;
+    a.want_proj = kf.kind == TQ_KIND_PROD ? 1 : 0;
     switch (Hq / Hkv) {
         case 1: return dispatch_k<1>(a, kf, vf, s);
         case 2: return dispatch_k<2>(a, kf, vf, s);

@@ -6,7 +6,8 @@
 // <q, k_hat> unbiased for Gaussian S).  q8 blocks: int8 * fp16 block scale.
 //
 // Lane layout as in the encoder: 16 tokens per wavefront, lane l owns token
-// l&15 and coordinates 32*(l>>4)+[0,32).  The QJL term S^T (2b - 1) for the
+// l&15 and, in the rotated domain, coordinates 32*(l>>4)+[0,32); the inverse
+// transform leaves it holding 8*(l>>4) + [0,8) + 32k of the output row.  The QJL term S^T (2b - 1) for the
 // 16 tokens of a wave is one [128 x 128] x [128 x 16] fp16 MFMA product
 // (entries of S and +-1 are exact in fp16; fp32 accumulation).
 #include <type_traits>
@@ -35,9 +36,11 @@ __global__ __launch_bounds__(256) void decode_tq_kernel(const DevTables *__restr
     }
     __syncthreads();
     const int t = lane & 15, q = lane >> 4;
+    // D/sqrt(d) for the coordinates this lane holds after the transform
+    // (layout A: register r holds coordinate 8q + (r&7) + 32(r>>3))
     float dsg[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) dsg[j] = tab->signs[32 * q + j] * kRsqrtD;
+    for (int r = 0; r < 32; ++r) dsg[r] = tab->signs[layoutA_coord(q, r)] * kRsqrtD;
 
     for (int64_t tile = int64_t(blockIdx.x) * 4 + wave; tile < n_tiles; tile += int64_t(gridDim.x) * 4) {
         const int64_t tok = tile * 16 + t;
@@ -87,16 +90,16 @@ __global__ __launch_bounds__(256) void decode_tq_kernel(const DevTables *__restr
                 for (int j = 0; j < 4; ++j) v[4 * cb + j] = fmaf(gs, acc[j], v[4 * cb + j]);
             }
         }
-        // x_hat = R^T v = D H v / sqrt(d)
-        fwht_inlane32(v);
-        fwht_crosslane(v, lane);
+        // x_hat = R^T v = D H v / sqrt(d); the transform leaves layout A
+        fwht128_swap(v);
         if (valid) {
             uint32_t o[16];
 #pragma unroll
             for (int p = 0; p < 16; ++p) o[p] = f2h(v[2 * p] * dsg[2 * p]) | (f2h(v[2 * p + 1] * dsg[2 * p + 1]) << 16);
-            uint4 *dst = reinterpret_cast<uint4 *>(out + tok * kHeadDim + 32 * q);
+            uint16_t *row = out + tok * kHeadDim + 8 * q;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dst[c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint4 *>(row + 32 * k) = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
         }
     }
 }

@@ -37,25 +37,51 @@ __device__ __forceinline__ void fwht_inlane32(float (&v)[32]) {
     }
 }
 
-// Butterflies over coordinate bits 5 and 6 (partner lanes l^16 and l^32):
-// the lower lane keeps a + b, the upper lane b' - a' = (partner) - (own).
-__device__ __forceinline__ void fwht_crosslane(float (&v)[32], int lane) {
-#pragma unroll
-    for (int s = 16; s <= 32; s <<= 1) {
-        const float sg = (lane & s) ? -1.0f : 1.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float p = __shfl_xor(v[i], s);
-            v[i] = fmaf(sg, v[i], p);
-        }
-    }
+// The two cross-lane butterfly stages as register swaps (gfx950
+// v_permlane32_swap / v_permlane16_swap).  permlane32_swap(a, b) leaves lanes
+// 0..31 holding both halves (lanes l and l+32) of element a and lanes 32..63
+// both halves of element b; the butterfly then runs in-lane.  Each stage
+// therefore trades one lane bit for one register bit:
+//   stage 1: lane bit 5 <-> register bit 4 (pairs r, r+16),
+//   stage 2: lane bit 4 <-> register bit 3 (pairs r, r+8).
+// Applied after the five in-lane stages, the whole sequence is the full
+// 128-point transform and maps
+//   layout A: lane bits (4,5) = coord bits (3,4), register bits = (0,1,2,5,6)
+//   layout N: lane bits (4,5) = coord bits (5,6), register bits = (0,1,2,3,4)
+// onto each other in either direction (N is the natural "32 consecutive
+// coordinates per lane" layout).
+__device__ __forceinline__ void swap_butterfly32(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+    a = x + y;
+    b = x - y;
+}
+__device__ __forceinline__ void swap_butterfly16(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+    a = x + y;
+    b = x - y;
 }
 
-__device__ __forceinline__ float quad_sum(float x) {  // sum over lanes l, l^16, l^32, l^48
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+__device__ __forceinline__ void fwht128_swap(float (&v)[32]) {
+    fwht_inlane32(v);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) swap_butterfly32(v[r], v[r + 16]);
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+        if ((r & 8) == 0) swap_butterfly16(v[r], v[r + 8]);
 }
+
+// Sum over lanes l, l^16, l^32, l^48 (result in every lane).
+__device__ __forceinline__ float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Coordinate held in register r by lane quarter q in layout A.
+__host__ __device__ constexpr int layoutA_coord(int q, int r) { return 8 * q + (r & 7) + 32 * (r >> 3); }
 
 // Code i (compile-time) of width B from an LSB-first bitstream held in dwords.
 template <int B, int I>

@@ -9,12 +9,23 @@
 namespace tq {
 
 constexpr int kHeadDim = 128;  // head_dim (= QJL dimension m) of this build
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 16;  // rows per packed tensor (32-bit row indices)
+
+// One bucket of the quantiser lookup: z in bucket j gets index
+// base + (z >= thr) and level (z >= thr ? c_hi : c_lo).
+struct QBucket {
+    float thr;
+    uint32_t base;
+    float c_lo, c_hi;
+};
+constexpr int kBuckets = 26;  // bucket j = clamp(floor(4 z + 12.5), 0, 25)
 
 // Tables uploaded once per ctx.  Plain data, identical on host and device.
 struct DevTables {
     float levels[4][16];             // row b-1: 2^b ascending N(0,1) Lloyd-Max levels
     float bounds[4][16];             // row b-1: 2^b-1 midpoints, then +inf padding
-    uint32_t sign_pair_xor[4][16];   // fp16-pair sign flips of D per lane quarter
+    uint32_t sign_pair_xor[4][16];   // fp16-pair sign flips of D per lane quarter (load layout A)
+    QBucket qlut[4][32];             // row b-1: quantiser buckets of the b-bit codebook
     float signs[kHeadDim];           // D
     uint16_t S[kHeadDim * kHeadDim]; // QJL matrix, fp16 bits, row-major [m][d]
     uint16_t ST[kHeadDim * kHeadDim];// its transpose [d][m]
@@ -27,7 +38,7 @@ uint16_t double_to_half_rne(double v);
 double half_to_double(uint16_t h);
 void lloyd_max_gaussian(int bits, double *levels, double *bounds);
 void random_tables(int d, int m, uint64_t seed, float *signs, uint16_t *S);
-void build_device_tables(int d, int m, uint64_t seed, DevTables *t);
+bool build_device_tables(int d, int m, uint64_t seed, DevTables *t);
 
 // Plane layout (api.cpp); returns false for an invalid format/size.
 bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out);
@@ -36,7 +47,7 @@ bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out);
 struct AttnPlan {
     int n_chunks;    // token chunks per (batch, kv head)
     int chunk;       // tokens per chunk (multiple of 256)
-    size_t off_qr, off_qp, off_scores, off_stats, off_part, total;
+    size_t off_qfrag, off_scores, off_stats, off_part, total;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
 

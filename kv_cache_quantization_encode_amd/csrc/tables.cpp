@@ -124,7 +124,7 @@ void random_tables(int d, int m, uint64_t seed, float *signs, uint16_t *S) {
     }
 }
 
-void build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
+bool build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
     std::memset(t, 0, sizeof(DevTables));
     for (int b = 1; b <= 4; ++b) {
         double lv[16], bd[15];
@@ -136,15 +136,46 @@ void build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
     random_tables(d, m, seed, t->signs, t->S);
     for (int r = 0; r < m; ++r)
         for (int c = 0; c < d; ++c) t->ST[c * m + r] = t->S[r * d + c];
-    // xor masks that flip the sign bits of packed fp16 pairs: lane quarter q
-    // holds coordinates 32q..32q+31, pair p covers 32q+2p and 32q+2p+1
+    // xor masks that flip the sign bits of packed fp16 pairs in the encoder's
+    // load layout: lane quarter q holds coordinates 8q + (r&7) + 32(r>>3) in
+    // register r, pair p = registers 2p, 2p+1
     for (int q = 0; q < 4; ++q)
         for (int p = 0; p < 16; ++p) {
+            const int c0 = 8 * q + ((2 * p) & 7) + 32 * ((2 * p) >> 3);
             uint32_t msk = 0;
-            if (t->signs[32 * q + 2 * p] < 0) msk |= 0x8000u;
-            if (t->signs[32 * q + 2 * p + 1] < 0) msk |= 0x80000000u;
+            if (t->signs[c0] < 0) msk |= 0x8000u;
+            if (t->signs[c0 + 1] < 0) msk |= 0x80000000u;
             t->sign_pair_xor[q][p] = msk;
         }
+    // Quantiser buckets: edges e_j = -3.125 + 0.25 j (j = 1..25), bucket 0 below
+    // e_1, bucket 25 above e_25.  Every Lloyd-Max boundary of 1..4 bits lies at
+    // least 0.02 from an edge and no bucket holds two boundaries, so
+    // idx = #{t_k <= z} = base_j + (z >= thr_j) even when rounding moves a z
+    // next to an edge into the neighbouring bucket.
+    for (int b = 1; b <= 4; ++b) {
+        double lv[16], bd[15];
+        lloyd_max_gaussian(b, lv, bd);
+        const int L = 1 << b;
+        for (int j = 0; j < 32; ++j) {
+            QBucket qb{INFINITY, 0u, 0.0f, 0.0f};
+            if (j < kBuckets) {
+                const double lo = j == 0 ? -INFINITY : -3.125 + 0.25 * j;
+                const double hi = j == kBuckets - 1 ? INFINITY : -3.125 + 0.25 * (j + 1);
+                int base = 0, inside = 0;
+                double thr = INFINITY;
+                for (int k = 0; k + 1 < L; ++k) {
+                    if (bd[k] < lo) ++base;
+                    else if (bd[k] < hi) { ++inside; thr = bd[k]; }
+                }
+                if (inside > 1) return false;  // cannot happen for these codebooks
+                qb.thr = float(thr);
+                qb.base = uint32_t(base);
+                qb.c_lo = float(lv[base]);
+                qb.c_hi = float(lv[base + 1 < L ? base + 1 : base]);
+            }
+            t->qlut[b - 1][j] = qb;
+        }
+    }
     // Encode QJL fragments (A operand of a 16x16x32 MFMA, rows = projections).
     // Fragment f = mb*4 + s; lane l = 16*q + i supplies the eight fp16 values
     //   S[32*(i/4) + 4*mb + i%4][32*q + 8*s + j],  j = 0..7,
@@ -167,6 +198,7 @@ void build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
                 for (int j = 0; j < 8; ++j)
                     t->St_dec[((cb * 4 + s) * 64 + l) * 8 + j] = t->S[(32 * q + 8 * s + j) * d + col];
             }
+    return true;
 }
 
 }  // namespace tq
