@@ -14,26 +14,30 @@
 // accumulated in the rotated domain and rotated back once per head.
 //
 // Passes (one stream, no host synchronisation):
-//   1. prologue   one block per (batch, kv head): q_rot and q_proj of its query
-//                 heads, written as pre-split MFMA operands.
-//   2. scores     grid (chunk, batch*kv head); MFMA over 16-token tiles with
-//                 the g query heads of the kv head as rows; scores go to the
-//                 workspace with per-chunk (max, sum exp) per head.
-//   3. values     same grid; combines the chunk statistics into the exact
-//                 softmax normaliser, keeps tokens with some weight >= tau,
-//                 compacts them, accumulates weight * level over 8 coordinates
-//                 per lane, writes the chunk's partial sum.
-//   4. merge      one wave per (batch, q head): sum of the partials, then R^T.
+//   1. scores   grid (chunk, batch*kv head).  Each block first forms q_rot and
+//               q_proj of the g query heads of its kv head (q_proj on MFMA)
+//               while its first K tiles are being fetched, then scores 16-token
+//               tiles with v_mfma_f32_16x16x32_f16 (rows = query heads), two
+//               256-token slices in flight.  Scores go to the workspace with
+//               per-chunk (max, sum exp) per head.
+//   2. values   same grid; combines the chunk statistics into the exact softmax
+//               normaliser, keeps tokens with some weight >= tau, compacts them
+//               (up to 1024 tokens at a time, all loads issued together),
+//               accumulates weight * level over 8 coordinates per lane and
+//               writes the chunk's partial sum.
+//   3. merge    one block per (batch, q head): sum of the partials, then R^T.
+// Exact sparse V needs the global softmax statistics before any V row is
+// skipped, hence the kernel boundary between passes 1 and 2.
 #include <type_traits>
 
 #include "device_common.h"
 
 namespace tq {
 
-constexpr float kRsqrtD = 0.08838834764831845f;            // 1/sqrt(128)
+constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 constexpr float kQjlOverSqrtD = 1.2533141373155003f / 128.0f * 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
-
+constexpr int kSuper = 1024;  // tokens compacted together in the values pass
 
 struct AttnArgs {
     const DevTables *tab;
@@ -41,13 +45,11 @@ struct AttnArgs {
     const uint8_t *kidx, *ksign, *knorm;  // K planes
     const uint8_t *vidx, *vnorm;          // V planes
     const int32_t *seq_lens;
-    half8 *qfrag;
     float *scores, *stats, *part;
     float *out;
     float tau;
     int B, Hq, Hkv, T, chunk, n_chunks;
     int k_rotated;  // K codec works in the rotated domain
-    int want_proj;  // K carries QJL sign bits
     int v_rotated;  // V codec works in the rotated domain
 };
 
@@ -57,111 +59,6 @@ __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
     return L < 0 ? 0 : (L > a.T ? a.T : L);
 }
 
-// ---------------------------------------------------------------- prologue
-// One block per (batch, kv head).  For each of its g query heads:
-// q_rot = R q = H D q / sqrt(d) (q itself for q8 keys) and q_proj = S q_rot,
-// unscaled fp32 (the score scales are applied per token).  The block then
-// writes them as the A operands of the scores MFMAs: 16 fragments (k-step s,
-// kind rot-hi/rot-lo/proj-hi/proj-lo) x 64 lanes x 8 fp16, lane (h, kq)
-// holding head h (zero for h >= g) at coordinates c0 + [0,8) with
-// c0 = 32 kq + 8 s (rotated keys) or 32 s + 8 kq (q8 keys).
-template <int G>
-__global__ __launch_bounds__(256) void attn_prologue_kernel(AttnArgs a, int want_proj) {
-    __shared__ float s_q[G][128];
-    __shared__ float s_p[G][128];
-    const int row = blockIdx.x;  // b * Hkv + kvh
-    const int b = row / a.Hkv, kvh = row - b * a.Hkv;
-    const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int g = wave; g < G; g += 4) {
-        const uint16_t *q = a.q + (head0 + g) * 128;
-        float v0 = h2f(q[lane]), v1 = h2f(q[lane + 64]);
-        if (a.k_rotated) {
-            v0 *= a.tab->signs[lane];
-            v1 *= a.tab->signs[lane + 64];
-            // H over coordinate bit 6 in-lane, bits 0..5 across lanes
-            const float s0 = v0 + v1, s1 = v0 - v1;
-            v0 = s0;
-            v1 = s1;
-#pragma unroll
-            for (int s = 1; s < 64; s <<= 1) {
-                const float sg = (lane & s) ? -1.0f : 1.0f;
-                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-                v0 = fmaf(sg, v0, p0);
-                v1 = fmaf(sg, v1, p1);
-            }
-            v0 *= kRsqrtD;
-            v1 *= kRsqrtD;
-        }
-        s_q[g][lane] = v0;
-        s_q[g][lane + 64] = v1;
-    }
-    __syncthreads();
-    if (want_proj) {
-        // q_proj = S q_rot on the MFMA units: rows = 128 projections (wave w
-        // takes row blocks 2w, 2w+1), columns = the g heads (zero-padded to
-        // 16), k = coordinates 32 kq + 8 s + j; q_rot split into fp16 hi + lo
-        const int h = lane & 15, kq = lane >> 4;
-        half8 bh[4], bl[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float v = h < G ? s_q[h][32 * kq + 8 * st + j] : 0.0f;
-                const _Float16 hi = _Float16(v);
-                bh[st][j] = hi;
-                bl[st][j] = _Float16(v - float(hi));
-            }
-        }
-        const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);  // row-major [128][128]
-#pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2) {
-            const int rb = 2 * wave + rb2;
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const half8 af = S8[(16 * rb + h) * 16 + 4 * kq + st];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bh[st], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl[st], acc, 0, 0, 0);
-            }
-            // lane (h, kq) holds projections 16 rb + 4 kq + j of head h
-            if (h < G) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s_p[h][16 * rb + 4 * kq + j] = acc[j];
-            }
-        }
-        __syncthreads();
-    }
-    half8 *frag = a.qfrag + int64_t(row) * 16 * 64;
-    for (int e = tid; e < 16 * 64; e += 256) {
-        const int f = e >> 6, l = e & 63;
-        const int kind = f >> 2, s = f & 3;
-        const int h = l & 15, kq = l >> 4;
-        const int c0 = a.k_rotated ? 32 * kq + 8 * s : 32 * s + 8 * kq;
-        half8 out;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float v = 0.0f;
-            if (h < G) {
-                if (kind < 2) v = s_q[h][c0 + j];
-                else if (want_proj) v = s_p[h][c0 + j];
-            }
-            const _Float16 hi = _Float16(v);
-            out[j] = (kind & 1) ? _Float16(v - float(hi)) : hi;
-        }
-        frag[e] = out;
-    }
-}
-
-// ------------------------------------------------------------------ scores
-// One wavefront scores 16 tokens of one kv head at a time with
-// v_mfma_f32_16x16x32_f16: rows = query heads of the group (zero-padded to
-// 16), columns = tokens, k = coordinates.  Lane l supplies token l&15 and the
-// 32 coordinates 32*(l>>4)+[0,32) of its packed row (8 per MFMA k-step), so a
-// lane unpacks exactly the b dwords it loaded.  fp32 accuracy from fp16 MFMA:
-// the query is split into hi + lo fp16 halves and every codebook level into
-// hi + lo halves (three products, dropping lo*lo); the QJL operand is +-1,
-// exact in fp16.  q8 keys use k-steps = the four 32-element scale blocks.
 // 2^x on the transcendental unit (v_exp_f32); only used for softmax weights
 // of arguments <= 0, where its flush of results below 2^-126 is immaterial.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -188,16 +85,220 @@ __device__ __forceinline__ void split_half8(const float *src, half8 &hi, half8 &
     }
 }
 
+// ------------------------------------------------------------ query operands
+// q_rot = H D q / sqrt(d) for rotated keys (q itself for q8 keys) and
+// q_proj = S q_rot (unscaled fp32; the score scales are applied per token) of
+// the G query heads starting at head0, left in s_q / s_p.  q_proj runs on the
+// MFMA units: rows = 128 projections (wave w takes row blocks 2w, 2w+1),
+// columns = the G heads (zero-padded to 16), k = coordinates, q_rot split into
+// fp16 hi + lo against the fp16-exact S.
+template <int G>
+__device__ __forceinline__ void query_vectors(const AttnArgs &a, int64_t head0, bool want_proj,
+                                              float (*s_q)[128], float (*s_p)[128]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int g = wave; g < G; g += 4) {
+        const uint16_t *q = a.q + (head0 + g) * 128;
+        float v0 = h2f(q[lane]), v1 = h2f(q[lane + 64]);
+        if (a.k_rotated) {
+            v0 *= a.tab->signs[lane];
+            v1 *= a.tab->signs[lane + 64];
+            // H over coordinate bit 6 in-lane, bits 0..5 across lanes
+            const float s0 = v0 + v1, s1 = v0 - v1;
+            v0 = s0;
+            v1 = s1;
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                const float sg = (lane & s) ? -1.0f : 1.0f;
+                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+                v0 = fmaf(sg, v0, p0);
+                v1 = fmaf(sg, v1, p1);
+            }
+            v0 *= kRsqrtD;
+            v1 *= kRsqrtD;
+        }
+        s_q[g][lane] = v0;
+        s_q[g][lane + 64] = v1;
+    }
+    __syncthreads();
+    if (!want_proj) return;
+    const int h = lane & 15, kq = lane >> 4;
+    half8 bh[4], bl[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        float buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) buf[j] = h < G ? s_q[h][32 * kq + 8 * st + j] : 0.0f;
+        split_half8(buf, bh[st], bl[st]);
+    }
+    const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);  // row-major [128][128]
+#pragma unroll
+    for (int rb2 = 0; rb2 < 2; ++rb2) {
+        const int rb = 2 * wave + rb2;
+        floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const half8 af = S8[(16 * rb + h) * 16 + 4 * kq + st];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bh[st], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl[st], acc, 0, 0, 0);
+        }
+        // lane (h, kq) holds projections 16 rb + 4 kq + j of head h
+        if (h < G) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_p[h][16 * rb + 4 * kq + j] = acc[j];
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ scores
+// One wavefront scores 16 tokens of one kv head at a time with
+// v_mfma_f32_16x16x32_f16: rows = query heads of the group (zero-padded to
+// 16), columns = tokens, k = coordinates.  Lane l supplies token l&15 and the
+// 32 coordinates 32*(l>>4)+[0,32) of its packed row (8 per MFMA k-step), so a
+// lane unpacks exactly the b dwords it loaded.  fp32 accuracy from fp16 MFMA:
+// the query is split into hi + lo fp16 halves and every codebook level into
+// hi + lo halves (three products, dropping lo*lo); the QJL operand is +-1,
+// exact in fp16.  q8 keys use k-steps = the four 32-element scale blocks.
+template <int KIND, int BITS>
+struct KTiles {
+    static constexpr int NT = 4;  // tiles of 16 tokens per wave per 256-token slice
+    static constexpr int W = KIND == TQ_KIND_Q8 ? 8 : BITS;
+    uint32_t wk[NT][W], sw[NT], nn[NT];
+    uint2 q8s[NT];
+};
+
+template <int KIND, int BITS>
+__device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int t1, int wave, int t, int kq,
+                                            const uint8_t *kid, const uint8_t *ksg, const uint8_t *knm) {
+    using KT = KTiles<KIND, BITS>;
+#pragma unroll
+    for (int i = 0; i < KT::NT; ++i) {
+        const int tok = base + wave * 16 + 64 * i + t;
+        if (tok < t1) {
+            if constexpr (KIND == TQ_KIND_Q8) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
+                    d.wk[i][2 * s] = u.x;
+                    d.wk[i][2 * s + 1] = u.y;
+                }
+                d.q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
+            } else {
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
+#pragma unroll
+                for (int w = 0; w < KT::W; ++w) d.wk[i][w] = src[w];
+                if constexpr (KIND == TQ_KIND_PROD) {
+                    d.sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
+                    d.nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
+                } else {
+                    d.nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < KT::W; ++w) d.wk[i][w] = 0;
+            d.sw[i] = 0;
+            d.nn[i] = 0;
+            d.q8s[i] = uint2{0u, 0u};
+        }
+    }
+}
+
+template <int G, int KIND, int BITS>
+__device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
+                                             int kq, const uint32_t *s_lut, const half8 (&arh)[4],
+                                             const half8 (&arl)[4], const half8 (&aph)[4], const half8 (&apl)[4],
+                                             float *__restrict__ scores, int64_t head0, int T, float (&m)[4],
+                                             float (&l)[4]) {
+    using KT = KTiles<KIND, BITS>;
+    float scv[KT::NT][4];  // this lane's scores of the slice in log2 units, -inf where absent
+#pragma unroll
+    for (int i = 0; i < KT::NT; ++i) {
+        const int tok = base + wave * 16 + 64 * i + t;
+        const bool valid = tok < t1;
+        float sc[4];
+        if constexpr (KIND == TQ_KIND_Q8) {
+            const uint2 scl = d.q8s[i];
+            const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                half8 bv;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t w = d.wk[i][2 * s + (j >> 2)];
+                    bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
+                }
+                floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
+                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bv, ds, 0, 0, 0);
+                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bv, ds, 0, 0, 0);
+                // lane (t, kq) holds heads 4kq + j of token t; scale of block s of token t
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = fmaf(bs[s], ds[j], acc[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = acc[j] * kRsqrtD;
+        } else {
+            floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+            Unroll<4>::run([&](auto S) {
+                constexpr int s = decltype(S)::value;
+                half8 bh, bl;
+                Unroll<8>::run([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    const uint32_t e = s_lut[code_at<BITS, 8 * s + j>(d.wk[i])];
+                    bh[j] = __builtin_bit_cast(_Float16, uint16_t(e & 0xFFFFu));
+                    bl[j] = __builtin_bit_cast(_Float16, uint16_t(e >> 16));
+                });
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bh, d0, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bl, d0, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bh, d0, 0, 0, 0);
+                if constexpr (KIND == TQ_KIND_PROD) {
+                    const half8 sg = pm_one8(d.sw[i], s);
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aph[s], sg, d1, 0, 0, 0);
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[s], sg, d1, 0, 0, 0);
+                }
+            });
+            // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
+            const float n = h2f(d.nn[i] & 0xFFFFu) * (1.0f / 128.0f);
+            const float gq = h2f(d.nn[i] >> 16) * kQjlOverSqrtD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
+        }
+        // lane (t, kq) holds heads 4kq + j of token tok
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int h = 4 * kq + j;
+            const bool live = h < G && valid;
+            if (live) scores[(head0 + h) * T + tok] = sc[j];
+            scv[i][j] = live ? sc[j] * kLog2e : -INFINITY;
+        }
+    }
+    // running (max, sum) per lane and head, once per slice, in log2 units
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float mx = scv[0][j];
+#pragma unroll
+        for (int i = 1; i < KT::NT; ++i) mx = fmaxf(mx, scv[i][j]);
+        const float nm = fmaxf(m[j], mx);
+        if (nm != -INFINITY) {
+            float acc = l[j] * fast_exp2(m[j] - nm);
+#pragma unroll
+            for (int i = 0; i < KT::NT; ++i) acc += fast_exp2(scv[i][j] - nm);
+            l[j] = acc;
+            m[j] = nm;
+        }
+    }
+}
+
 template <int G, int KIND, int BITS>
 __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
                                                           const uint8_t *__restrict__ ksign,
                                                           const uint8_t *__restrict__ knorm,
                                                           float *__restrict__ scores) {
     static_assert(G <= 16, "at most 16 query heads per kv head");
-    constexpr int NT = 4;                   // tiles of 16 tokens per wave per 256-token slice
-    constexpr int W = KIND == TQ_KIND_Q8 ? 8 : BITS;  // code dwords per lane and tile
     __shared__ uint32_t s_lut[16];          // level k as fp16 hi | fp16 lo << 16
     __shared__ float s_red[4][16][2];       // per wave, per head: (max, sum)
+    __shared__ float s_q[G][128], s_p[G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = lane & 15, kq = lane >> 4;
     const int chunk_id = blockIdx.x, row = blockIdx.y;  // row = b*Hkv + kvh
@@ -215,150 +316,47 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     const int L = seq_len_of(a, b);
     const int t0 = chunk_id * a.chunk;
     const int t1 = min(t0 + a.chunk, L);
-    // per-(batch, kv head) bases of the planes; offsets below are 32-bit
+    // per-(batch, kv head) bases of the planes; token offsets below are 32-bit
     // (T * 128 < 2^31 is checked on the host)
     const uint8_t *kid = kidx + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 128 : 16 * BITS);
     const uint8_t *ksg = ksign + int64_t(row) * a.T * 16;
     const uint8_t *knm = knorm + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 8 : (KIND == TQ_KIND_PROD ? 4 : 2));
 
-    // raw packed data of this wave's NT tiles in the current slice; the loads
-    // for all NT tiles are issued before any is used (bytes in flight)
-    uint32_t wk[NT][W], sw[NT], nn[NT];
-    uint2 q8s[NT];
-    auto load_slice = [&](int base) {
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int tok = base + wave * 16 + 64 * i + t;
-            if (tok < t1) {
-                if constexpr (KIND == TQ_KIND_Q8) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
-                        wk[i][2 * s] = u.x;
-                        wk[i][2 * s + 1] = u.y;
-                    }
-                    q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
-                } else {
-                    const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
-#pragma unroll
-                    for (int w = 0; w < W; ++w) wk[i][w] = src[w];
-                    if constexpr (KIND == TQ_KIND_PROD) {
-                        sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
-                        nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
-                    } else {
-                        nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int w = 0; w < W; ++w) wk[i][w] = 0;
-                sw[i] = 0;
-                nn[i] = 0;
-                q8s[i] = uint2{0u, 0u};
-            }
-        }
-    };
-    if (t0 < t1) load_slice(t0);
+    // first slice's K tiles in flight while the query operands are formed
+    KTiles<KIND, BITS> ta, tb;
+    if (t0 < t1) load_ktiles(ta, t0, t1, wave, t, kq, kid, ksg, knm);
 
-    // A operands, pre-split by the prologue: fragments rot-hi, rot-lo,
-    // proj-hi, proj-lo for k-steps 0..3
+    query_vectors<G>(a, head0, KIND == TQ_KIND_PROD, s_q, s_p);
+    // A operands: lane (h = l&15, kq) holds 8 query values per k-step at
+    // c0 = 32 kq + 8 s (rotated keys) or 32 s + 8 kq (q8 keys)
     half8 arh[4], arl[4], aph[4], apl[4];
     {
-        const half8 *frag = a.qfrag + int64_t(row) * 16 * 64 + lane;
+        const int h = lane & 15;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            arh[s] = frag[(0 * 4 + s) * 64];
-            arl[s] = frag[(1 * 4 + s) * 64];
+            const int c0 = (KIND == TQ_KIND_Q8) ? 32 * s + 8 * kq : 32 * kq + 8 * s;
+            float buf[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) buf[j] = h < G ? s_q[h][c0 + j] : 0.0f;
+            split_half8(buf, arh[s], arl[s]);
             if constexpr (KIND == TQ_KIND_PROD) {
-                aph[s] = frag[(2 * 4 + s) * 64];
-                apl[s] = frag[(3 * 4 + s) * 64];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) buf[j] = h < G ? s_p[h][c0 + j] : 0.0f;
+                split_half8(buf, aph[s], apl[s]);
             }
         }
     }
-    __syncthreads();
     float m[4], l[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
 
-    for (int base = t0; base < t1; base += 256) {
-        float scv[NT][4];  // this lane's scores of the slice, -inf where absent
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int tok = base + wave * 16 + 64 * i + t;
-            const bool valid = tok < t1;
-            float sc[4];
-            if constexpr (KIND == TQ_KIND_Q8) {
-                const uint2 scl = q8s[i];
-                const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
-                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    half8 bv;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t w = wk[i][2 * s + (j >> 2)];
-                        bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
-                    }
-                    floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
-                    ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bv, ds, 0, 0, 0);
-                    ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bv, ds, 0, 0, 0);
-                    // lane (t, kq) holds heads 4kq + j of token t; scale of block s of token t
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = fmaf(bs[s], ds[j], acc[j]);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sc[j] = acc[j] * kRsqrtD;
-            } else {
-                floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-                Unroll<4>::run([&](auto S) {
-                    constexpr int s = decltype(S)::value;
-                    half8 bh, bl;
-                    Unroll<8>::run([&](auto J) {
-                        constexpr int j = decltype(J)::value;
-                        const uint32_t e = s_lut[code_at<BITS, 8 * s + j>(wk[i])];
-                        bh[j] = __builtin_bit_cast(_Float16, uint16_t(e & 0xFFFFu));
-                        bl[j] = __builtin_bit_cast(_Float16, uint16_t(e >> 16));
-                    });
-                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bh, d0, 0, 0, 0);
-                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bl, d0, 0, 0, 0);
-                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bh, d0, 0, 0, 0);
-                    if constexpr (KIND == TQ_KIND_PROD) {
-                        const half8 sg = pm_one8(sw[i], s);
-                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aph[s], sg, d1, 0, 0, 0);
-                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[s], sg, d1, 0, 0, 0);
-                    }
-                });
-                // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
-                const float n = h2f(nn[i] & 0xFFFFu) * (1.0f / 128.0f);
-                const float gq = h2f(nn[i] >> 16) * kQjlOverSqrtD;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sc[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
-            }
-            // lane (t, kq) holds heads 4kq + j of token tok
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int h = 4 * kq + j;
-                const bool live = h < G && valid;
-                if (live) scores[(head0 + h) * a.T + tok] = sc[j];
-                scv[i][j] = live ? sc[j] * kLog2e : -INFINITY;
-            }
-        }
-        // running (max, sum) per lane and head, once per slice, in log2 units
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float mx = scv[0][j];
-#pragma unroll
-            for (int i = 1; i < NT; ++i) mx = fmaxf(mx, scv[i][j]);
-            const float nm = fmaxf(m[j], mx);
-            if (nm != -INFINITY) {
-                float acc = l[j] * fast_exp2(m[j] - nm);
-#pragma unroll
-                for (int i = 0; i < NT; ++i) acc += fast_exp2(scv[i][j] - nm);
-                l[j] = acc;
-                m[j] = nm;
-            }
-        }
-        if (base + 256 < t1) load_slice(base + 256);
+    // two 256-token slices in flight: while one is scored the next is fetched
+    for (int base = t0; base < t1; base += 512) {
+        if (base + 256 < t1) load_ktiles(tb, base + 256, t1, wave, t, kq, kid, ksg, knm);
+        score_ktiles<G>(ta, base, t1, wave, t, kq, s_lut, arh, arl, aph, apl, scores, head0, a.T, m, l);
+        if (base + 512 < t1) load_ktiles(ta, base + 512, t1, wave, t, kq, kid, ksg, knm);
+        if (base + 256 < t1)
+            score_ktiles<G>(tb, base + 256, t1, wave, t, kq, s_lut, arh, arl, aph, apl, scores, head0, a.T, m, l);
     }
     // (max, sum) per head: over the 16 token lanes of each lane group, then
     // over the waves; m is kept in log2 units and stored in natural units
@@ -394,20 +392,41 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
 // ------------------------------------------------------------------ values
 template <int G, int KIND, int BITS>
 __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
+    constexpr int R = kSuper / 256;  // tokens per thread per super-slice
     __shared__ float s_levels[16];
     __shared__ float s_M[G], s_invL[G];
-    __shared__ float s_w[G][256];
-    __shared__ int s_tok[256];
-    __shared__ int s_wcount[4];
+    __shared__ float s_w[G][kSuper];
+    __shared__ int s_tok[kSuper];
+    __shared__ int s_wcount[R][4];
     __shared__ float s_acc[4][G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk_id = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
-    const int hq0 = kvh * G;
-    const int64_t head0 = int64_t(b) * a.Hq + hq0;
+    const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
     if constexpr (KIND != TQ_KIND_Q8) {
         if (tid < 16) s_levels[tid] = a.tab->levels[BITS - 1][tid];
     }
+    const int L = seq_len_of(a, b);
+    const int t0 = chunk_id * a.chunk;
+    const int t1 = min(t0 + a.chunk, L);
+    const float *sc_base = a.scores + head0 * a.T;
+    const uint16_t *vn_base = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
+
+    // scores (and V norms) of the first super-slice: in flight with the stats
+    float sv[R][G], vs[R];
+    auto load_super = [&](int base) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int tt = base + 256 * r + tid;
+            const bool ok = tt < t1;
+#pragma unroll
+            for (int g = 0; g < G; ++g) sv[r][g] = ok ? sc_base[int64_t(g) * a.T + tt] : -INFINITY;
+            if constexpr (KIND != TQ_KIND_Q8) vs[r] = ok ? h2f(vn_base[tt]) * kRsqrtD : 0.0f;
+            else vs[r] = 1.0f;
+        }
+    };
+    if (t0 < t1) load_super(t0);
+
     // exact softmax statistics from all chunks of this (batch, kv head)
     for (int g = wave; g < G; g += 4) {
         const float *st = a.stats + (head0 + g) * a.n_chunks * 2;
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
         for (int s = 1; s < 64; s <<= 1) mm = fmaxf(mm, __shfl_xor(mm, s));
         float ll = 0.0f;
         if (mm != -INFINITY)
-            for (int c = lane; c < a.n_chunks; c += 64) ll += st[2 * c + 1] * exp2f((st[2 * c] - mm) * kLog2e);
+            for (int c = lane; c < a.n_chunks; c += 64) ll += st[2 * c + 1] * fast_exp2((st[2 * c] - mm) * kLog2e);
 #pragma unroll
         for (int s = 1; s < 64; s <<= 1) ll += __shfl_xor(ll, s);
         if (lane == 0) {
@@ -426,9 +445,6 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    const int L = seq_len_of(a, b);
-    const int t0 = chunk_id * a.chunk;
-    const int t1 = min(t0 + a.chunk, L);
     const int tk = lane >> 4, cg = lane & 15;  // token slot within the wave, coordinate group
     float acc[G][8];
 #pragma unroll
@@ -436,42 +452,44 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
 
-    for (int base = t0; base < t1; base += 256) {
-        // 1) weights and the keep decision, one token per thread
-        const int t = base + tid;
-        float wgt[G];
-        bool keep = false;
-        if (t < t1) {
-            float vscale = 1.0f;
-            if constexpr (KIND != TQ_KIND_Q8)
-                vscale = h2f(reinterpret_cast<const uint16_t *>(a.vnorm)[int64_t(row) * a.T + t]) * kRsqrtD;
+    for (int base = t0; base < t1; base += kSuper) {
+        // 1) weights and the keep decision, R tokens per thread
+        bool keep[R];
+        uint64_t bal[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            keep[r] = false;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float s = a.scores[(head0 + g) * a.T + t];
-                const float p = exp2f((s - s_M[g]) * kLog2e) * s_invL[g];
-                const bool k = p >= a.tau;
-                keep |= k;
-                wgt[g] = k ? p * vscale : 0.0f;
+                const float p = fast_exp2((sv[r][g] - s_M[g]) * kLog2e) * s_invL[g];
+                const bool k = p >= a.tau && sv[r][g] != -INFINITY;
+                keep[r] |= k;
+                sv[r][g] = k ? p * vs[r] : 0.0f;  // reuse as the weight
+            }
+            bal[r] = __ballot(keep[r]);
+            if (lane == 0) s_wcount[r][wave] = __popcll(bal[r]);
+        }
+        __syncthreads();
+        // 2) compaction in token order
+        int total = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int off = total;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int c = s_wcount[r][w];
+                off += (w < wave) ? c : 0;
+                total += c;
+            }
+            if (keep[r]) {
+                const int slot = off + __popcll(bal[r] & ((uint64_t(1) << lane) - 1));
+                s_tok[slot] = base + 256 * r + tid;
+#pragma unroll
+                for (int g = 0; g < G; ++g) s_w[g][slot] = sv[r][g];
             }
         }
-        // 2) compact the kept tokens of this 256-token slice
-        const uint64_t bal = __ballot(keep);
-        if (lane == 0) s_wcount[wave] = __popcll(bal);
         __syncthreads();
-        int off = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int c = s_wcount[w];
-            off += (w < wave) ? c : 0;
-            total += c;
-        }
-        if (keep) {
-            const int slot = off + __popcll(bal & ((uint64_t(1) << lane) - 1));
-            s_tok[slot] = t;
-#pragma unroll
-            for (int g = 0; g < G; ++g) s_w[g][slot] = wgt[g];
-        }
-        __syncthreads();
+        if (base + kSuper < t1) load_super(base + kSuper);  // next super-slice in flight
         // 3) accumulate kept rows: 16 tokens per pass (4 per wave), 8 coordinates
         //    per lane; the loads of 4 passes are issued before any is used
         constexpr int PASSES = 4;
@@ -596,8 +614,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     a.out[int64_t(head) * 128 + lane + 64] = v1;
 }
 
+// ------------------------------------------------------------------ launch
 template <int G, int KK, int KB, int VK, int VB>
-static int launch_pair(const AttnArgs &a, hipStream_t s) {
+static int launch_passes(const AttnArgs &a, hipStream_t s) {
     dim3 grid(unsigned(a.n_chunks), unsigned(a.B * a.Hkv));
     hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, a, a.kidx, a.ksign, a.knorm,
                        a.scores);
@@ -610,20 +629,18 @@ static int launch_pair(const AttnArgs &a, hipStream_t s) {
 
 template <int G, int KK, int KB>
 static int dispatch_v(const AttnArgs &a, tq_format vf, hipStream_t s) {
-    if (vf.kind == TQ_KIND_Q8) return launch_pair<G, KK, KB, TQ_KIND_Q8, 8>(a, s);
+    if (vf.kind == TQ_KIND_Q8) return launch_passes<G, KK, KB, TQ_KIND_Q8, 8>(a, s);
     switch (vf.bits) {
-        case 1: return launch_pair<G, KK, KB, TQ_KIND_MSE, 1>(a, s);
-        case 2: return launch_pair<G, KK, KB, TQ_KIND_MSE, 2>(a, s);
-        case 3: return launch_pair<G, KK, KB, TQ_KIND_MSE, 3>(a, s);
-        case 4: return launch_pair<G, KK, KB, TQ_KIND_MSE, 4>(a, s);
+        case 1: return launch_passes<G, KK, KB, TQ_KIND_MSE, 1>(a, s);
+        case 2: return launch_passes<G, KK, KB, TQ_KIND_MSE, 2>(a, s);
+        case 3: return launch_passes<G, KK, KB, TQ_KIND_MSE, 3>(a, s);
+        case 4: return launch_passes<G, KK, KB, TQ_KIND_MSE, 4>(a, s);
     }
     return int(hipErrorInvalidValue);
 }
 
 template <int G>
 static int dispatch_k(const AttnArgs &a, tq_format kf, tq_format vf, hipStream_t s) {
-    hipLaunchKernelGGL((attn_prologue_kernel<G>), dim3(unsigned(a.B * a.Hkv)), dim3(256), 0, s, a, a.want_proj);
-    if (hipGetLastError() != hipSuccess) return 1;
     if (kf.kind == TQ_KIND_Q8) return dispatch_v<G, TQ_KIND_Q8, 8>(a, vf, s);
     if (kf.kind == TQ_KIND_PROD) {
         switch (kf.bits) {
@@ -658,7 +675,6 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.vidx = vb + vlay.idx_offset;
     a.vnorm = vb + vlay.norm_offset;
     a.seq_lens = seq_lens;
-    a.qfrag = reinterpret_cast<half8 *>(w + plan.off_qfrag);
     a.scores = reinterpret_cast<float *>(w + plan.off_scores);
     a.stats = reinterpret_cast<float *>(w + plan.off_stats);
     a.part = reinterpret_cast<float *>(w + plan.off_part);
@@ -672,7 +688,6 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.n_chunks = plan.n_chunks;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
-    a.want_proj = kf.kind == TQ_KIND_PROD ? 1 : 0;
     switch (Hq / Hkv) {
         case 1: return dispatch_k<1>(a, kf, vf, s);
         case 2: return dispatch_k<2>(a, kf, vf, s);
