@@ -130,7 +130,9 @@ tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64
  * out_f32: device [B, Hq, d].  workspace: device, at least
  * tq_attn_workspace_bytes(...) bytes, 256-byte aligned; its contents need no
  * initialisation and are clobbered.  K: MSE, PROD or Q8; V: MSE or Q8.
- * Calls that share one workspace must be ordered on one stream. */
+ * out_f32 is written as a sum of per-chunk shares added with fp32 atomics,
+ * so repeated calls may differ in the last bits.  Calls that share one
+ * workspace or one output must be ordered on one stream. */
 tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
                          const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
                          int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,

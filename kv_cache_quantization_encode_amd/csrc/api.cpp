@@ -74,7 +74,6 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     int64_t off = 0;
     p.off_scores = size_t(off); off = align256(off + heads * int64_t(T) * 4);
     p.off_stats = size_t(off); off = align256(off + heads * nc * 2 * 4);
-    p.off_part = size_t(off); off = align256(off + heads * nc * kHeadDim * 4);
     p.total = size_t(off);
     return p;
 }

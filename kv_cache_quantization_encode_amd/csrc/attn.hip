@@ -45,7 +45,7 @@ struct AttnArgs {
     const uint8_t *kidx, *ksign, *knorm;  // K planes
     const uint8_t *vidx, *vnorm;          // V planes
     const int32_t *seq_lens;
-    float *scores, *stats, *part;
+    float *scores, *stats;
     float *out;
     float tau;
     int B, Hq, Hkv, T, chunk, n_chunks;
@@ -63,45 +63,66 @@ __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
 // of arguments <= 0, where its flush of results below 2^-126 is immaterial.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Eight fp16 +-1 values from bits 8s..8s+7 of w (bit set -> +1): per pair of
-// bits, x * (2^15 + 2^30) places the inverted bits at the two sign positions.
-__device__ __forceinline__ half8 pm_one8(uint32_t w, int s) {
-    const uint32_t nb = ~w >> (8 * s);
-    uint32_t d[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t x = (nb >> (2 * p)) & 3u;
-        d[p] = ((x * 0x40008000u) & 0x80008000u) | 0x3C003C00u;
-    }
-    return __builtin_bit_cast(half8, d);
-}
-
-__device__ __forceinline__ void split_half8(const float *src, half8 &hi, half8 &lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const _Float16 h = _Float16(src[j]);
-        hi[j] = h;
-        lo[j] = _Float16(src[j] - float(h));
-    }
-}
-
 // ------------------------------------------------------------ query operands
-// q_rot = H D q / sqrt(d) for rotated keys (q itself for q8 keys) and
-// q_proj = S q_rot (unscaled fp32; the score scales are applied per token) of
-// the G query heads starting at head0, left in s_q / s_p.  q_proj runs on the
-// MFMA units: rows = 128 projections (wave w takes row blocks 2w, 2w+1),
-// columns = the G heads (zero-padded to 16), k = coordinates, q_rot split into
-// fp16 hi + lo against the fp16-exact S.
-template <int G>
-__device__ __forceinline__ void query_vectors(const AttnArgs &a, int64_t head0, bool want_proj,
-                                              float (*s_q)[128], float (*s_p)[128]) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int g = wave; g < G; g += 4) {
-        const uint16_t *q = a.q + (head0 + g) * 128;
-        float v0 = h2f(q[lane]), v1 = h2f(q[lane + 64]);
+// The MFMA A operands of the scores pass hold each query twice: row h < G is
+// the fp16 hi half and row G + h the fp16 lo half of head h (rows >= 2G are
+// zero), so that the two rows together carry the fp32 value to about 2^-22.
+//   s_a:  q_rot = H D q / sqrt(d) for rotated keys, q itself for q8 keys;
+//   s_ap: q_proj = S q_rot (unscaled; the score scales are applied per token).
+// q_proj runs on the MFMA units: rows = 128 projections (wave w takes row
+// blocks 2w, 2w+1), columns = heads (hi rows, then lo rows), k = coordinates;
+// S is exact in fp16.  All global reads of this setup are issued at kernel
+// entry (QueryLoads) and consumed after the lookup tables are built.
+template <int G, bool PROJ>
+struct QueryLoads {
+    static constexpr int NH = (G + 3) / 4;  // heads per wave
+    uint32_t q0[NH], q1[NH];                // fp16 bits of coordinates lane, lane + 64
+    float sg0, sg1;                         // D entries of those coordinates
+    half8 sf[PROJ ? 8 : 1];                 // S fragments (row block, k-step)
+};
+
+template <int G, bool PROJ>
+__device__ __forceinline__ void load_query(QueryLoads<G, PROJ> &ql, const AttnArgs &a, int64_t head0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < ql.NH; ++i) {
+        const int g = wave + 4 * i;
+        const uint16_t *q = a.q + (head0 + (g < G ? g : 0)) * 128;
+        ql.q0[i] = q[lane];
+        ql.q1[i] = q[lane + 64];
+    }
+    ql.sg0 = a.tab->signs[lane];
+    ql.sg1 = a.tab->signs[lane + 64];
+    if constexpr (PROJ) {
+        const int h = lane & 15, kq = lane >> 4;
+        const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);  // row-major [128][128]
+#pragma unroll
+        for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) ql.sf[4 * rb2 + st] = S8[(16 * (2 * wave + rb2) + h) * 16 + 4 * kq + st];
+    }
+}
+
+__device__ __forceinline__ void put_hi_lo(_Float16 *hi, _Float16 *lo, float x) {
+    const _Float16 h = _Float16(x);
+    *hi = h;
+    *lo = _Float16(x - float(h));
+}
+
+// Fills s_a (and s_ap) rows 0 .. 2G-1; rows 2G .. 15 must already be zero.
+// Ends with a barrier.
+template <int G, bool PROJ>
+__device__ __forceinline__ void build_query_rows(const QueryLoads<G, PROJ> &ql, const AttnArgs &a,
+                                                 _Float16 (*s_a)[128], _Float16 (*s_ap)[128]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < ql.NH; ++i) {
+        const int g = wave + 4 * i;
+        if (g >= G) break;
+        float v0 = h2f(ql.q0[i]), v1 = h2f(ql.q1[i]);
         if (a.k_rotated) {
-            v0 *= a.tab->signs[lane];
-            v1 *= a.tab->signs[lane + 64];
+            v0 *= ql.sg0;
+            v1 *= ql.sg1;
             // H over coordinate bit 6 in-lane, bits 0..5 across lanes
             const float s0 = v0 + v1, s1 = v0 - v1;
             v0 = s0;
@@ -116,49 +137,47 @@ __device__ __forceinline__ void query_vectors(const AttnArgs &a, int64_t head0, 
             v0 *= kRsqrtD;
             v1 *= kRsqrtD;
         }
-        s_q[g][lane] = v0;
-        s_q[g][lane + 64] = v1;
+        put_hi_lo(&s_a[g][lane], &s_a[G + g][lane], v0);
+        put_hi_lo(&s_a[g][lane + 64], &s_a[G + g][lane + 64], v1);
     }
     __syncthreads();
-    if (!want_proj) return;
-    const int h = lane & 15, kq = lane >> 4;
-    half8 bh[4], bl[4];
+    if constexpr (PROJ) {
+        const int c = lane & 15, kq = lane >> 4;
+        // B operand: column c = hi row c of s_a for c < G, lo row c - G + G
+        // (= row c) for G <= c < 2G, zero above; i.e. simply row c of s_a
+        half8 bq[4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        float buf[8];
+        for (int st = 0; st < 4; ++st) bq[st] = *reinterpret_cast<const half8 *>(&s_a[c][32 * kq + 8 * st]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) buf[j] = h < G ? s_q[h][32 * kq + 8 * st + j] : 0.0f;
-        split_half8(buf, bh[st], bl[st]);
-    }
-    const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);  // row-major [128][128]
+        for (int rb2 = 0; rb2 < 2; ++rb2) {
+            const int rb = 2 * wave + rb2;
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int rb2 = 0; rb2 < 2; ++rb2) {
-        const int rb = 2 * wave + rb2;
-        floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int st = 0; st < 4; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql.sf[4 * rb2 + st], bq[st], acc, 0, 0, 0);
+            // lane (c, kq) holds projections 16 rb + 4 kq + j of column c;
+            // q_proj of head h = column h + column G + h (lanes c and c + G)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const half8 af = S8[(16 * rb + h) * 16 + 4 * kq + st];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bh[st], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl[st], acc, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const float other = __shfl_down(acc[j], G, 16);
+                if (c < G) put_hi_lo(&s_ap[c][16 * rb + 4 * kq + j], &s_ap[G + c][16 * rb + 4 * kq + j],
+                                     acc[j] + other);
+            }
         }
-        // lane (h, kq) holds projections 16 rb + 4 kq + j of head h
-        if (h < G) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s_p[h][16 * rb + 4 * kq + j] = acc[j];
-        }
+        __syncthreads();
     }
-    __syncthreads();
 }
 
 // ------------------------------------------------------------------ scores
 // One wavefront scores 16 tokens of one kv head at a time with
-// v_mfma_f32_16x16x32_f16: rows = query heads of the group (zero-padded to
-// 16), columns = tokens, k = coordinates.  Lane l supplies token l&15 and the
-// 32 coordinates 32*(l>>4)+[0,32) of its packed row (8 per MFMA k-step), so a
-// lane unpacks exactly the b dwords it loaded.  fp32 accuracy from fp16 MFMA:
-// the query is split into hi + lo fp16 halves and every codebook level into
-// hi + lo halves (three products, dropping lo*lo); the QJL operand is +-1,
-// exact in fp16.  q8 keys use k-steps = the four 32-element scale blocks.
+// v_mfma_f32_16x16x32_f16: columns = tokens, k = coordinates, and the 16 rows
+// carry the query of the G heads twice, as fp16 hi halves (rows h) and fp16
+// lo halves (rows G + h), so that row h plus row G + h is the fp32 query to
+// about 2^-22.  Lane l supplies token l&15 and the 32 coordinates
+// 32*(l>>4)+[0,32) of its packed row (8 per MFMA k-step), so a lane unpacks
+// exactly the b dwords it loaded.  Codebook levels enter as fp16 hi + lo
+// halves (two MFMAs into one accumulator); the QJL operand is +-1, exact in
+// fp16.  q8 keys use k-steps = the four 32-element scale blocks.
 template <int KIND, int BITS>
 struct KTiles {
     static constexpr int NT = 4;  // tiles of 16 tokens per wave per 256-token slice
@@ -167,14 +186,14 @@ struct KTiles {
     uint2 q8s[NT];
 };
 
-template <int KIND, int BITS>
+template <bool FULL, int KIND, int BITS>
 __device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int t1, int wave, int t, int kq,
                                             const uint8_t *kid, const uint8_t *ksg, const uint8_t *knm) {
     using KT = KTiles<KIND, BITS>;
 #pragma unroll
     for (int i = 0; i < KT::NT; ++i) {
         const int tok = base + wave * 16 + 64 * i + t;
-        if (tok < t1) {
+        if (FULL || tok < t1) {
             if constexpr (KIND == TQ_KIND_Q8) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -204,10 +223,37 @@ __device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int
     }
 }
 
-template <int G, int KIND, int BITS>
+// Adds row G + h of the MFMA result to row h: lane (t, kq) holds rows
+// 4 kq + j, so for G <= 2 both rows are in the lane, for G = 4 in lanes l and
+// l ^ 16, for G = 8 in lanes l and l ^ 32.
+template <int G>
+__device__ __forceinline__ void fold_rows(float (&e)[4]) {
+    if constexpr (G == 1) {
+        e[0] += e[1];
+    } else if constexpr (G == 2) {
+        e[0] += e[2];
+        e[1] += e[3];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t x = __float_as_uint(e[j]);
+            const auto r = G == 4 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+            e[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    }
+}
+
+// Whether lane group kq, register j holds the score of head 4 kq + j.
+template <int G>
+__device__ __forceinline__ bool holds_head(int kq, int j) {
+    return G >= 4 ? kq < G / 4 : (kq == 0 && j < G);
+}
+
+template <bool FULL, int G, int KIND, int BITS>
 __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
-                                             int kq, const uint32_t *s_lut, const half8 (&arh)[4],
-                                             const half8 (&arl)[4], const half8 (&aph)[4], const half8 (&apl)[4],
+                                             int kq, const uint2 *s_pair, const half8 *s_sgn,
+                                             const half8 (&aq)[8], const half8 (&ap)[4],
                                              float *__restrict__ scores, int64_t head0, int T, float (&m)[4],
                                              float (&l)[4]) {
     using KT = KTiles<KIND, BITS>;
@@ -215,12 +261,13 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
 #pragma unroll
     for (int i = 0; i < KT::NT; ++i) {
         const int tok = base + wave * 16 + 64 * i + t;
-        const bool valid = tok < t1;
-        float sc[4];
+        const bool valid = FULL || tok < t1;
+        float e[4];
         if constexpr (KIND == TQ_KIND_Q8) {
             const uint2 scl = d.q8s[i];
             const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 half8 bv;
@@ -230,48 +277,54 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
                     bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
                 }
                 floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
-                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bv, ds, 0, 0, 0);
-                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bv, ds, 0, 0, 0);
-                // lane (t, kq) holds heads 4kq + j of token t; scale of block s of token t
+                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bv, ds, 0, 0, 0);  // aq[0..3] only
+                // scale of block s of token t
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = fmaf(bs[s], ds[j], acc[j]);
+                for (int j = 0; j < 4; ++j) e[j] = fmaf(bs[s], ds[j], e[j]);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = acc[j] * kRsqrtD;
+            for (int j = 0; j < 4; ++j) e[j] *= kRsqrtD;
         } else {
-            floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-            Unroll<4>::run([&](auto S) {
-                constexpr int s = decltype(S)::value;
-                half8 bh, bl;
-                Unroll<8>::run([&](auto J) {
-                    constexpr int j = decltype(J)::value;
-                    const uint32_t e = s_lut[code_at<BITS, 8 * s + j>(d.wk[i])];
-                    bh[j] = __builtin_bit_cast(_Float16, uint16_t(e & 0xFFFFu));
-                    bl[j] = __builtin_bit_cast(_Float16, uint16_t(e >> 16));
-                });
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bh, d0, 0, 0, 0);
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arh[s], bl, d0, 0, 0, 0);
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(arl[s], bh, d0, 0, 0, 0);
-                if constexpr (KIND == TQ_KIND_PROD) {
-                    const half8 sg = pm_one8(d.sw[i], s);
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aph[s], sg, d1, 0, 0, 0);
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[s], sg, d1, 0, 0, 0);
-                }
+            // all table reads of the tile first.  Field f (codes 2f, 2f+1 of
+            // the lane) gives (hi(c0) hi(c1) | lo(c0) lo(c1)); fields 2u and
+            // 2u+1 side by side are the B operand of k-step u, whose A operand
+            // repeats each query value against its level's hi and lo half.
+            uint2 ef[16];
+            half8 sg[4];
+            Unroll<16>::run([&](auto P) {
+                constexpr int pr = decltype(P)::value;
+                ef[pr] = s_pair[code_at<2 * BITS, pr>(d.wk[i])];
             });
+            if constexpr (KIND == TQ_KIND_PROD) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) sg[s] = s_sgn[(d.sw[i] >> (8 * s)) & 0xFFu];
+            }
+            floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint4 bv = make_uint4(ef[2 * u].x, ef[2 * u].y, ef[2 * u + 1].x, ef[2 * u + 1].y);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[u], __builtin_bit_cast(half8, bv), d0, 0, 0, 0);
+            }
+            if constexpr (KIND == TQ_KIND_PROD) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[s], sg[s], d1, 0, 0, 0);
+            }
             // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
             const float n = h2f(d.nn[i] & 0xFFFFu) * (1.0f / 128.0f);
             const float gq = h2f(d.nn[i] >> 16) * kQjlOverSqrtD;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
+            for (int j = 0; j < 4; ++j) e[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
         }
-        // lane (t, kq) holds heads 4kq + j of token tok
+        fold_rows<G>(e);
+        // lane (t, kq) now holds heads 4 kq + j of token tok where holds_head
+        if (valid && holds_head<G>(kq, 0)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int h = 4 * kq + j;
-            const bool live = h < G && valid;
-            if (live) scores[(head0 + h) * T + tok] = sc[j];
-            scv[i][j] = live ? sc[j] * kLog2e : -INFINITY;
+            for (int j = 0; j < 4; ++j)
+                if (holds_head<G>(kq, j)) scores[(head0 + 4 * kq + j) * T + tok] = e[j];
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) scv[i][j] = (valid && holds_head<G>(kq, j)) ? e[j] * kLog2e : -INFINITY;
     }
     // running (max, sum) per lane and head, once per slice, in log2 units
 #pragma unroll
@@ -295,24 +348,20 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
                                                           const uint8_t *__restrict__ ksign,
                                                           const uint8_t *__restrict__ knorm,
                                                           float *__restrict__ scores) {
-    static_assert(G <= 16, "at most 16 query heads per kv head");
-    __shared__ uint32_t s_lut[16];          // level k as fp16 hi | fp16 lo << 16
-    __shared__ float s_red[4][16][2];       // per wave, per head: (max, sum)
-    __shared__ float s_q[G][128], s_p[G][128];
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "1, 2, 4 or 8 query heads per kv head");
+    // s_pair[f]: fp16 hi halves and fp16 lo halves of the two levels of a
+    // 2-code field f = c0 | c1 << BITS; s_sgn[byte]: eight fp16 +-1 (bit set -> +1)
+    constexpr int kPairs = KIND == TQ_KIND_Q8 ? 1 : 1 << (2 * BITS);
+    __shared__ uint2 s_pair[kPairs];
+    __shared__ half8 s_sgn[KIND == TQ_KIND_PROD ? 256 : 1];
+    __shared__ float s_red[4][16][2];  // per wave, per head: (max, sum)
+    __shared__ __attribute__((aligned(16))) _Float16 s_a[16][128];
+    __shared__ __attribute__((aligned(16))) _Float16 s_ap[KIND == TQ_KIND_PROD ? 16 : 1][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = lane & 15, kq = lane >> 4;
     const int chunk_id = blockIdx.x, row = blockIdx.y;  // row = b*Hkv + kvh
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
     const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
-    if constexpr (KIND != TQ_KIND_Q8) {
-        if (tid < 16) {
-            const float c = a.tab->levels[BITS - 1][tid];
-            const _Float16 hi = _Float16(c);
-            const _Float16 lo = _Float16(c - float(hi));
-            s_lut[tid] = uint32_t(__builtin_bit_cast(uint16_t, hi)) |
-                         (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
-        }
-    }
     const int L = seq_len_of(a, b);
     const int t0 = chunk_id * a.chunk;
     const int t1 = min(t0 + a.chunk, L);
@@ -322,28 +371,83 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     const uint8_t *ksg = ksign + int64_t(row) * a.T * 16;
     const uint8_t *knm = knorm + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 8 : (KIND == TQ_KIND_PROD ? 4 : 2));
 
-    // first slice's K tiles in flight while the query operands are formed
+    // global reads first: query, D, S fragments, levels and the first slice's
+    // K tiles are all in flight while the tables are built.  A chunk whose
+    // length is a multiple of 512 has only whole slices and takes the path
+    // without per-token bounds checks.
+    QueryLoads<G, KIND == TQ_KIND_PROD> ql;
+    load_query(ql, a, head0);
+    float lv[2] = {0.0f, 0.0f};
+    if constexpr (KIND != TQ_KIND_Q8) {
+        if (tid < kPairs) {
+            lv[0] = a.tab->levels[BITS - 1][tid & ((1 << BITS) - 1)];
+            lv[1] = a.tab->levels[BITS - 1][tid >> BITS];
+        }
+    }
+    const int n_tok = max(t1 - t0, 0);
+    const bool whole = (n_tok & 511) == 0;
     KTiles<KIND, BITS> ta, tb;
-    if (t0 < t1) load_ktiles(ta, t0, t1, wave, t, kq, kid, ksg, knm);
+    if (whole) {
+        if (n_tok > 0) load_ktiles<true>(ta, t0, t1, wave, t, kq, kid, ksg, knm);
+    } else {
+        load_ktiles<false>(ta, t0, t1, wave, t, kq, kid, ksg, knm);
+    }
 
-    query_vectors<G>(a, head0, KIND == TQ_KIND_PROD, s_q, s_p);
-    // A operands: lane (h = l&15, kq) holds 8 query values per k-step at
-    // c0 = 32 kq + 8 s (rotated keys) or 32 s + 8 kq (q8 keys)
-    half8 arh[4], arl[4], aph[4], apl[4];
-    {
-        const int h = lane & 15;
+    // the output rows of this kv head start at zero; the values pass adds
+    // every chunk's share into them
+    if (chunk_id == 0) {
+        for (int i = tid; i < G * 128; i += 256) a.out[head0 * 128 + i] = 0.0f;
+    }
+    // zero stacked rows 2G .. 15
+    for (int i = tid; i < (16 - 2 * G) * 32; i += 256) {
+        reinterpret_cast<uint2 *>(&s_a[2 * G][0])[i] = uint2{0u, 0u};
+        if constexpr (KIND == TQ_KIND_PROD) reinterpret_cast<uint2 *>(&s_ap[2 * G][0])[i] = uint2{0u, 0u};
+    }
+    if constexpr (KIND == TQ_KIND_PROD) {
+        half8 v;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c0 = (KIND == TQ_KIND_Q8) ? 32 * s + 8 * kq : 32 * kq + 8 * s;
-            float buf[8];
+        for (int j = 0; j < 8; ++j) v[j] = ((tid >> j) & 1) ? _Float16(1.0f) : _Float16(-1.0f);
+        s_sgn[tid] = v;
+    }
+    if constexpr (KIND != TQ_KIND_Q8) {
+        if (tid < kPairs) {
+            uint32_t hp = 0, lp = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) buf[j] = h < G ? s_q[h][c0 + j] : 0.0f;
-            split_half8(buf, arh[s], arl[s]);
-            if constexpr (KIND == TQ_KIND_PROD) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) buf[j] = h < G ? s_p[h][c0 + j] : 0.0f;
-                split_half8(buf, aph[s], apl[s]);
+            for (int u = 0; u < 2; ++u) {
+                const _Float16 hi = _Float16(lv[u]);
+                const _Float16 lo = _Float16(lv[u] - float(hi));
+                hp |= uint32_t(__builtin_bit_cast(uint16_t, hi)) << (16 * u);
+                lp |= uint32_t(__builtin_bit_cast(uint16_t, lo)) << (16 * u);
             }
+            s_pair[tid] = uint2{hp, lp};
+        }
+    }
+    build_query_rows<G>(ql, a, s_a, s_ap);
+
+    // A operands, row r = l&15 of the stacked rows.  Rotated keys: k-step
+    // u of lane group kq covers coordinates c0 = 32 kq + 4u .. c0+3 as
+    // (q0 q1 q0 q1 q2 q3 q2 q3) against (hi hi lo lo hi hi lo lo) of the
+    // levels; the QJL k-step s covers 32 kq + 8s .. +7.  q8 keys: k-step s
+    // covers 32 s + 8 kq .. +7.
+    half8 aq[8], ap[4];
+    {
+        const _Float16 *ra = s_a[lane & 15];
+        if constexpr (KIND == TQ_KIND_Q8) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) aq[s] = *reinterpret_cast<const half8 *>(ra + 32 * s + 8 * kq);
+#pragma unroll
+            for (int s = 4; s < 8; ++s) aq[s] = half8{};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(ra + 32 * kq + 4 * u);
+                aq[u] = __builtin_bit_cast(half8, make_uint4(v.x, v.x, v.y, v.y));
+            }
+        }
+        if constexpr (KIND == TQ_KIND_PROD) {
+            const _Float16 *rp = s_ap[lane & 15];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ap[s] = *reinterpret_cast<const half8 *>(rp + 32 * kq + 8 * s);
         }
     }
     float m[4], l[4];
@@ -351,13 +455,19 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     for (int j = 0; j < 4; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
 
     // two 256-token slices in flight: while one is scored the next is fetched
-    for (int base = t0; base < t1; base += 512) {
-        if (base + 256 < t1) load_ktiles(tb, base + 256, t1, wave, t, kq, kid, ksg, knm);
-        score_ktiles<G>(ta, base, t1, wave, t, kq, s_lut, arh, arl, aph, apl, scores, head0, a.T, m, l);
-        if (base + 512 < t1) load_ktiles(ta, base + 512, t1, wave, t, kq, kid, ksg, knm);
-        if (base + 256 < t1)
-            score_ktiles<G>(tb, base + 256, t1, wave, t, kq, s_lut, arh, arl, aph, apl, scores, head0, a.T, m, l);
-    }
+    auto scan = [&](auto full_c) {
+        constexpr bool F = decltype(full_c)::value;
+        for (int base = t0; base < t1; base += 512) {
+            if (base + 256 < t1) load_ktiles<F>(tb, base + 256, t1, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            if (base + 512 < t1) load_ktiles<F>(ta, base + 512, t1, wave, t, kq, kid, ksg, knm);
+            if (base + 256 < t1)
+                score_ktiles<F, G>(tb, base + 256, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0,
+                                   a.T, m, l);
+        }
+    };
+    if (whole) scan(std::true_type{});
+    else scan(std::false_type{});
     // (max, sum) per head: over the 16 token lanes of each lane group, then
     // over the waves; m is kept in log2 units and stored in natural units
 #pragma unroll
@@ -452,6 +562,7 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
 
+    bool kept_any = false;  // uniform over the block
     for (int base = t0; base < t1; base += kSuper) {
         // 1) weights and the keep decision, R tokens per thread
         bool keep[R];
@@ -459,12 +570,14 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             keep[r] = false;
+            if (base + 256 * r < t1) {  // uniform
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float p = fast_exp2((sv[r][g] - s_M[g]) * kLog2e) * s_invL[g];
-                const bool k = p >= a.tau && sv[r][g] != -INFINITY;
-                keep[r] |= k;
-                sv[r][g] = k ? p * vs[r] : 0.0f;  // reuse as the weight
+                for (int g = 0; g < G; ++g) {
+                    const float p = fast_exp2((sv[r][g] - s_M[g]) * kLog2e) * s_invL[g];
+                    const bool k = p >= a.tau && sv[r][g] != -INFINITY;
+                    keep[r] |= k;
+                    sv[r][g] = k ? p * vs[r] : 0.0f;  // reuse as the weight
+                }
             }
             bal[r] = __ballot(keep[r]);
             if (lane == 0) s_wcount[r][wave] = __popcll(bal[r]);
@@ -488,11 +601,12 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
                 for (int g = 0; g < G; ++g) s_w[g][slot] = sv[r][g];
             }
         }
+        kept_any |= total > 0;
         __syncthreads();
         if (base + kSuper < t1) load_super(base + kSuper);  // next super-slice in flight
         // 3) accumulate kept rows: 16 tokens per pass (4 per wave), 8 coordinates
         //    per lane; the loads of 4 passes are issued before any is used
-        constexpr int PASSES = 4;
+        constexpr int PASSES = 16;
         for (int k0 = 0; k0 < total; k0 += 16 * PASSES) {
             uint32_t raw[PASSES][2];
             float bsc[PASSES];
@@ -568,50 +682,34 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
             for (int j = 0; j < 8; ++j) s_acc[wave][g][8 * cg + j] = acc[g][j];
     }
     __syncthreads();
-    for (int i = tid; i < G * 128; i += 256) {
-        const int g = i >> 7, c = i & 127;
-        const float s = s_acc[0][g][c] + s_acc[1][g][c] + s_acc[2][g][c] + s_acc[3][g][c];
-        a.part[((head0 + g) * a.n_chunks + chunk_id) * 128 + c] = s;
-    }
-}
-
-// ------------------------------------------------------------------- merge
-// One block per (batch, q head): the 4 waves each sum a quarter of the chunk
-// partials, then wave 0 rotates back, out = R^T acc = D H acc / sqrt(d)
-// (rotated V codecs only).
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-    __shared__ float s_sum[4][128];
-    const int head = blockIdx.x;  // b * Hq + h
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float v0 = 0.0f, v1 = 0.0f;
-    const float *pp = a.part + int64_t(head) * a.n_chunks * 128;
-#pragma unroll 8
-    for (int c = wave; c < a.n_chunks; c += 4) {
-        v0 += pp[c * 128 + lane];
-        v1 += pp[c * 128 + lane + 64];
-    }
-    s_sum[wave][lane] = v0;
-    s_sum[wave][lane + 64] = v1;
-    __syncthreads();
-    if (wave != 0) return;
-    v0 = s_sum[0][lane] + s_sum[1][lane] + s_sum[2][lane] + s_sum[3][lane];
-    v1 = s_sum[0][lane + 64] + s_sum[1][lane + 64] + s_sum[2][lane + 64] + s_sum[3][lane + 64];
-    if (a.v_rotated) {
-        const float s0 = v0 + v1, s1 = v0 - v1;
-        v0 = s0;
-        v1 = s1;
+    // the chunk's share of each head, rotated back (out = R^T acc = D H acc /
+    // sqrt(d) for rotated V codecs; R^T is linear, so shares rotate one by
+    // one) and added into the output, which the scores pass zeroed.  A chunk
+    // that kept no row adds nothing.
+    if (kept_any) {
+        for (int g = wave; g < G; g += 4) {
+            float v0 = s_acc[0][g][lane] + s_acc[1][g][lane] + s_acc[2][g][lane] + s_acc[3][g][lane];
+            float v1 = s_acc[0][g][lane + 64] + s_acc[1][g][lane + 64] + s_acc[2][g][lane + 64] +
+                       s_acc[3][g][lane + 64];
+            if (a.v_rotated) {
+                const float s0 = v0 + v1, s1 = v0 - v1;
+                v0 = s0;
+                v1 = s1;
 #pragma unroll
-        for (int s = 1; s < 64; s <<= 1) {
-            const float sg = (lane & s) ? -1.0f : 1.0f;
-            const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-            v0 = fmaf(sg, v0, p0);
-            v1 = fmaf(sg, v1, p1);
+                for (int s = 1; s < 64; s <<= 1) {
+                    const float sg = (lane & s) ? -1.0f : 1.0f;
+                    const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+                    v0 = fmaf(sg, v0, p0);
+                    v1 = fmaf(sg, v1, p1);
+                }
+                v0 *= a.tab->signs[lane] * kRsqrtD;
+                v1 *= a.tab->signs[lane + 64] * kRsqrtD;
+            }
+            float *o = a.out + (head0 + g) * 128;
+            __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        v0 *= a.tab->signs[lane] * kRsqrtD;
-        v1 *= a.tab->signs[lane + 64] * kRsqrtD;
     }
-    a.out[int64_t(head) * 128 + lane] = v0;
-    a.out[int64_t(head) * 128 + lane + 64] = v1;
 }
 
 // ------------------------------------------------------------------ launch
@@ -620,10 +718,9 @@ static int launch_passes(const AttnArgs &a, hipStream_t s) {
     dim3 grid(unsigned(a.n_chunks), unsigned(a.B * a.Hkv));
     hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, a, a.kidx, a.ksign, a.knorm,
                        a.scores);
-    if (hipGetLastError() != hipSuccess) return 1;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return int(e);
     hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(256), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return 1;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(a.B * a.Hq)), dim3(256), 0, s, a);
     return int(hipGetLastError());
 }
 
@@ -677,7 +774,6 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.seq_lens = seq_lens;
     a.scores = reinterpret_cast<float *>(w + plan.off_scores);
     a.stats = reinterpret_cast<float *>(w + plan.off_stats);
-    a.part = reinterpret_cast<float *>(w + plan.off_part);
     a.out = out;
     a.tau = tau;
     a.B = B;
