@@ -37,7 +37,9 @@ namespace tq {
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 constexpr float kQjlOverSqrtD = 1.2533141373155003f / 128.0f * 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSuper = 1024;  // tokens compacted together in the values pass
+constexpr int kSuper = 1024;   // tokens compacted together in the values pass
+constexpr int kVThreads = 512;  // threads per values block
+constexpr int kVWaves = kVThreads / 64;
 
 struct AttnArgs {
     const DevTables *tab;
@@ -62,6 +64,32 @@ __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
 // 2^x on the transcendental unit (v_exp_f32); only used for softmax weights
 // of arguments <= 0, where its flush of results below 2^-126 is immaterial.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the 16 lanes of a DPP row: quad_perm xor 1, quad_perm
+// xor 2, row_half_mirror, row_mirror; every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));
+    x = fmaxf(x, dpp_mov<0x4E>(x));
+    x = fmaxf(x, dpp_mov<0x141>(x));
+    return fmaxf(x, dpp_mov<0x140>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x141>(x);
+    return x + dpp_mov<0x140>(x);
+}
+// Max over lanes l, l^16, l^32, l^48 (result in every lane).
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // ------------------------------------------------------------ query operands
 // The MFMA A operands of the scores pass hold each query twice: row h < G is
@@ -186,39 +214,34 @@ struct KTiles {
     uint2 q8s[NT];
 };
 
-template <bool FULL, int KIND, int BITS>
-__device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int t1, int wave, int t, int kq,
+// Loads the K tiles of one 256-token slice.  Tokens at or past t1 read row
+// tmax instead (any valid row: the scores of such tokens are discarded), so
+// every call issues the same loads and the waits before scoring stay exact.
+template <int KIND, int BITS>
+__device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int tmax, int wave, int t, int kq,
                                             const uint8_t *kid, const uint8_t *ksg, const uint8_t *knm) {
     using KT = KTiles<KIND, BITS>;
 #pragma unroll
     for (int i = 0; i < KT::NT; ++i) {
-        const int tok = base + wave * 16 + 64 * i + t;
-        if (FULL || tok < t1) {
-            if constexpr (KIND == TQ_KIND_Q8) {
+        const int tok = min(base + wave * 16 + 64 * i + t, tmax);
+        if constexpr (KIND == TQ_KIND_Q8) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
-                    d.wk[i][2 * s] = u.x;
-                    d.wk[i][2 * s + 1] = u.y;
-                }
-                d.q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
-            } else {
-                const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
-#pragma unroll
-                for (int w = 0; w < KT::W; ++w) d.wk[i][w] = src[w];
-                if constexpr (KIND == TQ_KIND_PROD) {
-                    d.sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
-                    d.nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
-                } else {
-                    d.nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
-                }
+            for (int s = 0; s < 4; ++s) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
+                d.wk[i][2 * s] = u.x;
+                d.wk[i][2 * s + 1] = u.y;
             }
+            d.q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
         } else {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
 #pragma unroll
-            for (int w = 0; w < KT::W; ++w) d.wk[i][w] = 0;
-            d.sw[i] = 0;
-            d.nn[i] = 0;
-            d.q8s[i] = uint2{0u, 0u};
+            for (int w = 0; w < KT::W; ++w) d.wk[i][w] = src[w];
+            if constexpr (KIND == TQ_KIND_PROD) {
+                d.sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
+                d.nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
+            } else {
+                d.nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
+            }
         }
     }
 }
@@ -258,8 +281,29 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
                                              float (&l)[4]) {
     using KT = KTiles<KIND, BITS>;
     float scv[KT::NT][4];  // this lane's scores of the slice in log2 units, -inf where absent
+    // B operands of the rotated-key path.  Field f (codes 2f, 2f+1 of the
+    // lane) gives (hi(c0) hi(c1) | lo(c0) lo(c1)); fields 2u and 2u+1 side by
+    // side are the B operand of k-step u, whose A operand repeats each query
+    // value against its level's hi and lo half.  The table reads of tile i+1
+    // are issued before the MFMAs of tile i, so LDS latency overlaps them.
+    struct Ops {
+        uint2 ef[16];
+        half8 sg[4];
+    };
+    Ops ops[2];
+    auto fetch = [&](int i, Ops &o) {
+        Unroll<16>::run([&](auto P) {
+            constexpr int pr = decltype(P)::value;
+            o.ef[pr] = s_pair[code_at<2 * BITS, pr>(d.wk[i])];
+        });
+        if constexpr (KIND == TQ_KIND_PROD) {
 #pragma unroll
-    for (int i = 0; i < KT::NT; ++i) {
+            for (int s = 0; s < 4; ++s) o.sg[s] = s_sgn[(d.sw[i] >> (8 * s)) & 0xFFu];
+        }
+    };
+    if constexpr (KIND != TQ_KIND_Q8) fetch(0, ops[0]);
+    Unroll<KT::NT>::run([&](auto I) {
+        constexpr int i = decltype(I)::value;
         const int tok = base + wave * 16 + 64 * i + t;
         const bool valid = FULL || tok < t1;
         float e[4];
@@ -285,30 +329,19 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
 #pragma unroll
             for (int j = 0; j < 4; ++j) e[j] *= kRsqrtD;
         } else {
-            // all table reads of the tile first.  Field f (codes 2f, 2f+1 of
-            // the lane) gives (hi(c0) hi(c1) | lo(c0) lo(c1)); fields 2u and
-            // 2u+1 side by side are the B operand of k-step u, whose A operand
-            // repeats each query value against its level's hi and lo half.
-            uint2 ef[16];
-            half8 sg[4];
-            Unroll<16>::run([&](auto P) {
-                constexpr int pr = decltype(P)::value;
-                ef[pr] = s_pair[code_at<2 * BITS, pr>(d.wk[i])];
-            });
-            if constexpr (KIND == TQ_KIND_PROD) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) sg[s] = s_sgn[(d.sw[i] >> (8 * s)) & 0xFFu];
-            }
+            if constexpr (i + 1 < KT::NT) fetch(i + 1, ops[(i + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const Ops &o = ops[i & 1];
             floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const uint4 bv = make_uint4(ef[2 * u].x, ef[2 * u].y, ef[2 * u + 1].x, ef[2 * u + 1].y);
+                const uint4 bv = make_uint4(o.ef[2 * u].x, o.ef[2 * u].y, o.ef[2 * u + 1].x, o.ef[2 * u + 1].y);
                 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[u], __builtin_bit_cast(half8, bv), d0, 0, 0, 0);
             }
             if constexpr (KIND == TQ_KIND_PROD) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[s], sg[s], d1, 0, 0, 0);
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[s], o.sg[s], d1, 0, 0, 0);
             }
             // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
             const float n = h2f(d.nn[i] & 0xFFFFu) * (1.0f / 128.0f);
@@ -325,7 +358,7 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) scv[i][j] = (valid && holds_head<G>(kq, j)) ? e[j] * kLog2e : -INFINITY;
-    }
+    });
     // running (max, sum) per lane and head, once per slice, in log2 units
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -384,14 +417,15 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
             lv[1] = a.tab->levels[BITS - 1][tid >> BITS];
         }
     }
+    // keep these small loads ahead of the K tiles in the memory queue, so
+    // the query setup below does not wait for the (slower) K tiles
+    asm volatile("" ::: "memory");
+    // rows past the sequence (or of an empty chunk) read row tmax instead
     const int n_tok = max(t1 - t0, 0);
     const bool whole = (n_tok & 511) == 0;
+    const int tmax = max(t1 - 1, 0);
     KTiles<KIND, BITS> ta, tb;
-    if (whole) {
-        if (n_tok > 0) load_ktiles<true>(ta, t0, t1, wave, t, kq, kid, ksg, knm);
-    } else {
-        load_ktiles<false>(ta, t0, t1, wave, t, kq, kid, ksg, knm);
-    }
+    load_ktiles(ta, t0, tmax, wave, t, kq, kid, ksg, knm);
 
     // the output rows of this kv head start at zero; the values pass adds
     // every chunk's share into them
@@ -457,13 +491,18 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     // two 256-token slices in flight: while one is scored the next is fetched
     auto scan = [&](auto full_c) {
         constexpr bool F = decltype(full_c)::value;
-        for (int base = t0; base < t1; base += 512) {
-            if (base + 256 < t1) load_ktiles<F>(tb, base + 256, t1, wave, t, kq, kid, ksg, knm);
+        if (t0 >= t1) return;
+        for (int base = t0;; base += 512) {
+            load_ktiles(tb, base + 256, tmax, wave, t, kq, kid, ksg, knm);
             score_ktiles<F, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
-            if (base + 512 < t1) load_ktiles<F>(ta, base + 512, t1, wave, t, kq, kid, ksg, knm);
-            if (base + 256 < t1)
-                score_ktiles<F, G>(tb, base + 256, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0,
-                                   a.T, m, l);
+            if (base + 512 >= t1) {
+                if (F || base + 256 < t1)
+                    score_ktiles<F, G>(tb, base + 256, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0,
+                                       a.T, m, l);
+                break;
+            }
+            load_ktiles(ta, base + 512, tmax, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, G>(tb, base + 256, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
         }
     };
     if (whole) scan(std::true_type{});
@@ -472,15 +511,9 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     // over the waves; m is kept in log2 units and stored in natural units
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int s = 1; s < 16; s <<= 1) {
-            const float om = __shfl_xor(m[j], s), ol = __shfl_xor(l[j], s);
-            const float nm = fmaxf(m[j], om);
-            float nl = 0.0f;
-            if (nm != -INFINITY) nl = l[j] * fast_exp2(m[j] - nm) + ol * fast_exp2(om - nm);
-            m[j] = nm;
-            l[j] = nl;
-        }
+        const float mx = row16_max(m[j]);
+        l[j] = row16_sum(m[j] == -INFINITY ? 0.0f : l[j] * fast_exp2(m[j] - mx));
+        m[j] = mx;
         if (t == 0) {
             s_red[wave][4 * kq + j][0] = m[j];
             s_red[wave][4 * kq + j][1] = l[j];
@@ -501,57 +534,70 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
 
 // ------------------------------------------------------------------ values
 template <int G, int KIND, int BITS>
-__global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
-    constexpr int R = kSuper / 256;  // tokens per thread per super-slice
-    __shared__ float s_levels[16];
+__global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
+    constexpr int R = kSuper / kVThreads;  // tokens per thread per super-slice
+    // s_vpair[f]: the two levels of a 2-code field f = c0 | c1 << BITS
+    constexpr int kVPairs = KIND == TQ_KIND_Q8 ? 1 : 1 << (2 * BITS);
+    __shared__ float2 s_vpair[kVPairs];
     __shared__ float s_M[G], s_invL[G];
     __shared__ float s_w[G][kSuper];
     __shared__ int s_tok[kSuper];
-    __shared__ int s_wcount[R][4];
-    __shared__ float s_acc[4][G][128];
+    __shared__ int s_wcount[R][kVWaves];
+    __shared__ float s_acc[kVWaves][G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk_id = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
     const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
-    if constexpr (KIND != TQ_KIND_Q8) {
-        if (tid < 16) s_levels[tid] = a.tab->levels[BITS - 1][tid];
-    }
     const int L = seq_len_of(a, b);
     const int t0 = chunk_id * a.chunk;
     const int t1 = min(t0 + a.chunk, L);
+    if (t0 >= t1) return;  // an empty chunk adds nothing (uniform over the block)
+    const int tmax = t1 - 1;
     const float *sc_base = a.scores + head0 * a.T;
     const uint16_t *vn_base = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
 
-    // scores (and V norms) of the first super-slice: in flight with the stats
-    float sv[R][G], vs[R];
+    // every global read of the prologue is issued before any is used: the
+    // levels, the chunk statistics of head `wave`, and the scores and V norms
+    // of the first super-slice (tokens past the chunk read row tmax and are
+    // masked out later)
+    float2 lv = make_float2(0.0f, 0.0f);
+    if constexpr (KIND != TQ_KIND_Q8) {
+        const int f = tid & (kVPairs - 1);
+        lv = make_float2(a.tab->levels[BITS - 1][f & ((1 << BITS) - 1)], a.tab->levels[BITS - 1][f >> BITS]);
+    }
+    const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
+    const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
+    float sv[R][G];
+    uint32_t vraw[R];
     auto load_super = [&](int base) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int tt = base + 256 * r + tid;
-            const bool ok = tt < t1;
+            const int tt = min(base + kVThreads * r + tid, tmax);
 #pragma unroll
-            for (int g = 0; g < G; ++g) sv[r][g] = ok ? sc_base[int64_t(g) * a.T + tt] : -INFINITY;
-            if constexpr (KIND != TQ_KIND_Q8) vs[r] = ok ? h2f(vn_base[tt]) * kRsqrtD : 0.0f;
-            else vs[r] = 1.0f;
+            for (int g = 0; g < G; ++g) sv[r][g] = sc_base[int64_t(g) * a.T + tt];
+            if constexpr (KIND != TQ_KIND_Q8) vraw[r] = vn_base[tt];
         }
     };
-    if (t0 < t1) load_super(t0);
+    load_super(t0);
+    asm volatile("" ::: "memory");
 
+    if constexpr (KIND != TQ_KIND_Q8) {
+        if (tid < kVPairs) s_vpair[tid] = lv;
+    }
     // exact softmax statistics from all chunks of this (batch, kv head)
-    for (int g = wave; g < G; g += 4) {
-        const float *st = a.stats + (head0 + g) * a.n_chunks * 2;
-        float mm = -INFINITY;
-        for (int c = lane; c < a.n_chunks; c += 64) mm = fmaxf(mm, st[2 * c]);
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) mm = fmaxf(mm, __shfl_xor(mm, s));
+    if (wave < G) {
+        float mm = lane < a.n_chunks ? st0.x : -INFINITY;
+        for (int c = lane + 64; c < a.n_chunks; c += 64) mm = fmaxf(mm, st[2 * c]);
+        mm = quad_max(row16_max(mm));
         float ll = 0.0f;
-        if (mm != -INFINITY)
-            for (int c = lane; c < a.n_chunks; c += 64) ll += st[2 * c + 1] * fast_exp2((st[2 * c] - mm) * kLog2e);
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) ll += __shfl_xor(ll, s);
+        if (mm != -INFINITY) {
+            if (lane < a.n_chunks) ll = st0.y * fast_exp2((st0.x - mm) * kLog2e);
+            for (int c = lane + 64; c < a.n_chunks; c += 64) ll += st[2 * c + 1] * fast_exp2((st[2 * c] - mm) * kLog2e);
+        }
+        ll = quad_sum(row16_sum(ll));
         if (lane == 0) {
-            s_M[g] = mm;
-            s_invL[g] = ll > 0.0f ? 1.0f / ll : 0.0f;
+            s_M[wave] = mm;
+            s_invL[wave] = ll > 0.0f ? 1.0f / ll : 0.0f;
         }
     }
     __syncthreads();
@@ -570,13 +616,15 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             keep[r] = false;
-            if (base + 256 * r < t1) {  // uniform
+            if (base + kVThreads * r < t1) {  // uniform
+                const bool ok = base + kVThreads * r + tid < t1;
+                const float vsc = KIND == TQ_KIND_Q8 ? 1.0f : h2f(vraw[r]) * kRsqrtD;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const float p = fast_exp2((sv[r][g] - s_M[g]) * kLog2e) * s_invL[g];
-                    const bool k = p >= a.tau && sv[r][g] != -INFINITY;
+                    const bool k = ok && p >= a.tau;
                     keep[r] |= k;
-                    sv[r][g] = k ? p * vs[r] : 0.0f;  // reuse as the weight
+                    sv[r][g] = k ? p * vsc : 0.0f;  // reuse as the weight
                 }
             }
             bal[r] = __ballot(keep[r]);
@@ -589,14 +637,14 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
         for (int r = 0; r < R; ++r) {
             int off = total;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < kVWaves; ++w) {
                 const int c = s_wcount[r][w];
                 off += (w < wave) ? c : 0;
                 total += c;
             }
             if (keep[r]) {
                 const int slot = off + __popcll(bal[r] & ((uint64_t(1) << lane) - 1));
-                s_tok[slot] = base + 256 * r + tid;
+                s_tok[slot] = base + kVThreads * r + tid;
 #pragma unroll
                 for (int g = 0; g < G; ++g) s_w[g][slot] = sv[r][g];
             }
@@ -604,19 +652,22 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
         kept_any |= total > 0;
         __syncthreads();
         if (base + kSuper < t1) load_super(base + kSuper);  // next super-slice in flight
-        // 3) accumulate kept rows: 16 tokens per pass (4 per wave), 8 coordinates
-        //    per lane; the loads of 4 passes are issued before any is used
-        constexpr int PASSES = 16;
-        for (int k0 = 0; k0 < total; k0 += 16 * PASSES) {
+        // 3) accumulate kept rows: 4 tokens per wave and pass, 8
+        //    coordinates per lane.  All row loads of a batch are issued before
+        //    any is used (a slot past `total` reads a kept row), and passes run
+        //    four at a time without branches (such slots carry weight 0); the
+        //    number of groups of four is uniform over the block.
+        constexpr int PASSES = 8, PER_PASS = 4 * kVWaves;
+        for (int k0 = 0; k0 < total; k0 += PER_PASS * PASSES) {
+            const int npass = min((total - k0 + PER_PASS - 1) / PER_PASS, PASSES);
             uint32_t raw[PASSES][2];
             float bsc[PASSES];
-#pragma unroll
-            for (int ps = 0; ps < PASSES; ++ps) {
-                const int slot = k0 + 16 * ps + wave * 4 + tk;
-                raw[ps][0] = raw[ps][1] = 0u;
-                bsc[ps] = 0.0f;
-                if (slot < total) {
+            Unroll<PASSES>::run([&](auto P) {
+                constexpr int ps = decltype(P)::value;
+                {
+                    const int slot = min(k0 + PER_PASS * ps + wave * 4 + tk, total - 1);
                     const int64_t vec = int64_t(row) * a.T + s_tok[slot];
+                    raw[ps][1] = 0u;
                     if constexpr (KIND == TQ_KIND_Q8) {
                         const uint2 u = *reinterpret_cast<const uint2 *>(a.vidx + vec * 128 + 8 * cg);
                         raw[ps][0] = u.x;
@@ -638,39 +689,51 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
                         }
                     }
                 }
-            }
+            });
+            // every row load above is issued before the first use below
+            asm volatile("" ::: "memory");
+            Unroll<PASSES / 4>::run([&](auto Q) {
+                constexpr int q4 = decltype(Q)::value;
+                if (4 * q4 < npass) {
 #pragma unroll
-            for (int ps = 0; ps < PASSES; ++ps) {
-                const int slot = k0 + 16 * ps + wave * 4 + tk;
-                if (slot < total) {
-                    float val[8];
-                    if constexpr (KIND == TQ_KIND_Q8) {
+                    for (int u = 0; u < 4; ++u) {
+                        const int ps = 4 * q4 + u;
+                        const int slot = k0 + PER_PASS * ps + wave * 4 + tk;
+                        const bool live = slot < total;
+                        float val[8];
+                        if constexpr (KIND == TQ_KIND_Q8) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            val[j] = float(int8_t((raw[ps][0] >> (8 * j)) & 0xFFu)) * bsc[ps];
-                            val[4 + j] = float(int8_t((raw[ps][1] >> (8 * j)) & 0xFFu)) * bsc[ps];
+                            for (int j = 0; j < 4; ++j) {
+                                val[j] = float(int8_t((raw[ps][0] >> (8 * j)) & 0xFFu)) * bsc[ps];
+                                val[4 + j] = float(int8_t((raw[ps][1] >> (8 * j)) & 0xFFu)) * bsc[ps];
+                            }
+                        } else {
+                            uint32_t bitsw = raw[ps][0];
+                            if constexpr (BITS == 3) {
+                                const uint64_t both = (uint64_t(raw[ps][1]) << 32) | raw[ps][0];
+                                bitsw = uint32_t(both >> (8 * ((3 * cg) & 3)));
+                            }
+                            // 2-code fields: one table read gives two levels
+#pragma unroll
+                            for (int f = 0; f < 4; ++f) {
+                                const float2 lv = s_vpair[(bitsw >> (2 * BITS * f)) & ((1u << (2 * BITS)) - 1u)];
+                                val[2 * f] = lv.x;
+                                val[2 * f + 1] = lv.y;
+                            }
                         }
-                    } else {
-                        uint32_t bitsw = raw[ps][0];
-                        if constexpr (BITS == 3) {
-                            const uint64_t both = (uint64_t(raw[ps][1]) << 32) | raw[ps][0];
-                            bitsw = uint32_t(both >> (8 * ((3 * cg) & 3)));
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            const float wg = live ? s_w[g][slot] : 0.0f;
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
                         }
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) val[j] = s_levels[(bitsw >> (BITS * j)) & ((1u << BITS) - 1u)];
-                    }
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float wg = s_w[g][slot];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
                     }
                 }
-            }
+            });
         }
         __syncthreads();
     }
-    // reduce over the 4 token slots of each wave, then over the 4 waves
+    // reduce over the 4 token slots of each wave, then over the waves
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -687,10 +750,13 @@ __global__ __launch_bounds__(256) void attn_values_kernel(AttnArgs a) {
     // one) and added into the output, which the scores pass zeroed.  A chunk
     // that kept no row adds nothing.
     if (kept_any) {
-        for (int g = wave; g < G; g += 4) {
-            float v0 = s_acc[0][g][lane] + s_acc[1][g][lane] + s_acc[2][g][lane] + s_acc[3][g][lane];
-            float v1 = s_acc[0][g][lane + 64] + s_acc[1][g][lane + 64] + s_acc[2][g][lane + 64] +
-                       s_acc[3][g][lane + 64];
+        for (int g = wave; g < G; g += kVWaves) {
+            float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kVWaves; ++w) {
+                v0 += s_acc[w][g][lane];
+                v1 += s_acc[w][g][lane + 64];
+            }
             if (a.v_rotated) {
                 const float s0 = v0 + v1, s1 = v0 - v1;
                 v0 = s0;
@@ -720,7 +786,7 @@ static int launch_passes(const AttnArgs &a, hipStream_t s) {
                        a.scores);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return int(e);
-    hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(kVThreads), 0, s, a);
     return int(hipGetLastError());
 }
 
