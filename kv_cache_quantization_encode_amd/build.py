@@ -21,8 +21,11 @@ SOURCES = ["tables.cpp", "api.cpp", "encode.hip", "dequant.hip", "attn.hip", "mi
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 (v_pk_*_f32)
 # instructions; hipcc's host pass reports the feature as unknown, harmlessly.
+# -amdgpu-mfma-vgpr-form lets MFMA results land in ordinary VGPRs (no
+# accumulator-register copies before the VALU uses them).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-I" + os.path.join(HERE, "..", "include")]
 
 

@@ -112,6 +112,42 @@ struct Unroll {
     }
 };
 
+// Blocks of `kernel` that can be resident at once on the current device (the
+// occupancy calculator's per-CU count times the CU count), cached per device
+// in `cache` (kMaxDevices entries, zero-initialised).  Persistent kernels size
+// their grids with it so that no block waits for a second round.
+constexpr int kMaxDevices = 64;
+template <typename Kernel>
+inline int resident_blocks(Kernel kernel, int threads, int *cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+    if (dev >= 0) {
+        const int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+        if (v > 0) return v;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel), threads, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
+        cus < 1)
+        cus = 1;
+    const int v = per_cu * cus;
+    if (dev >= 0) __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    return v;
+}
+
+// Grid of a persistent kernel whose waves (4 per block) stride over n_items
+// tiles: as few rounds as the resident capacity allows, with the tiles spread
+// evenly over the blocks of the last round count.
+inline int64_t persistent_grid(int64_t n_items, int resident) {
+    const int64_t per_round = int64_t(resident) * 4;
+    const int64_t rounds = (n_items + per_round - 1) / per_round;
+    if (rounds < 1) return 1;
+    return (n_items + 4 * rounds - 1) / (4 * rounds);
+}
+
 // binary64 -> binary16 with one rounding (nearest, ties to even), from the
 // bit pattern; used for per-group scales that must match an exact reference.
 __device__ __forceinline__ uint32_t double_to_half_bits(double v) {

@@ -7,16 +7,16 @@
 // yeyulingfeng.com TurboQuant+ introduction, core item 3: boundary layers
 // kept at q8_0 (symmetric absmax int8 per block of 32 here).
 //
-// Work split: one wavefront = 16 tokens, lane l owns token l&15.  A lane
-// loads the 32 coordinates 8*(l>>4) + [0,8) + 32k (k = 0..3), runs the five
-// in-register butterfly stages, then two permlane-swap stages that finish the
-// 128-point transform and leave it holding coordinates 32*(l>>4) + [0,32).
-// The standardised coordinates z = H (D x) / n are quantised against the fp32
-// Lloyd-Max boundaries (bucket lookup for 3-4 bits).  For K the rotated
-// residual e = z - c[idx] is projected on the MFMA units: P = S e for the 16
-// tokens of the wave as a [128 x 128] x [128 x 16] fp16 product with fp32
-// accumulation, e split into hi + lo fp16 halves (scaled by 2^8 first so the
-// lo half stays normal) so that the product keeps ~22 mantissa bits.
+// Work split: one wavefront = 16 tokens.  Both dense products run on the
+// MFMA units (v_mfma_f32_16x16x32_f16, columns = the 16 tokens):
+//   y = H diag(D) x  with the +-1 matrix as A operand (exact in fp16) and the
+//   fp16 input rows as B operand, so no conversion or butterfly is spent on
+//   the rotation; lane (t, q) receives coordinates 32q + [0,32) of token t;
+//   P = S e  (K only) with the rotated residual e split into hi + lo fp16
+//   halves (scaled by 2^8 first so the lo half stays normal), ~22 mantissa bits.
+// The norm is a packed fp16 dot product of the row with itself (fp32
+// accumulation); z = y / n is quantised against the fp32 Lloyd-Max
+// boundaries (bucket lookup for 3-4 bits).
 #include <type_traits>
 
 #include "device_common.h"
@@ -41,26 +41,40 @@ __device__ __forceinline__ uint32_t quantise(float z, const float *bnd, const fl
     } else {
         int j = int(fmaf(z, 4.0f, 12.5f));
         j = j < 0 ? 0 : (j > kBuckets - 1 ? kBuckets - 1 : j);
-        const QBucket qb = s_lut[j];
-        const bool up = z >= qb.thr;
-        zhat = up ? qb.c_hi : qb.c_lo;
-        return qb.base + (up ? 1u : 0u);
+        const uint4 qb = reinterpret_cast<const uint4 *>(s_lut)[j];  // {thr, base, c_lo, c_hi}
+        const bool up = z >= __uint_as_float(qb.x);
+        zhat = __uint_as_float(up ? qb.w : qb.z);
+        return qb.y + (up ? 1u : 0u);
     }
 }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
 template <int BITS, bool PROD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
-void encode_tq_kernel(const DevTables *__restrict__ tab, const uint16_t *__restrict__ x, int64_t n_vec,
-                      uint8_t *__restrict__ idx_plane, uint8_t *__restrict__ sign_plane,
-                      uint8_t *__restrict__ norm_plane, int64_t n_tiles) {
+__global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restrict__ tab,
+                                                        const uint16_t *__restrict__ x, int64_t n_vec,
+                                                        uint8_t *__restrict__ idx_plane,
+                                                        uint8_t *__restrict__ sign_plane,
+                                                        uint8_t *__restrict__ norm_plane, int64_t n_tiles) {
     __shared__ float s_levels[16];
-    __shared__ QBucket s_lut[kBuckets];
+    __shared__ __attribute__((aligned(16))) QBucket s_lut[kBuckets];
+    __shared__ half8 s_rot[32 * 64];
     __shared__ half8 s_frag[PROD ? 32 * 64 : 1];
-    __shared__ uint4 s_sx[4][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < 16) s_levels[tid] = tab->levels[BITS - 1][tid];
-    if (tid < kBuckets) s_lut[tid] = tab->qlut[BITS - 1][tid];
-    if (tid < 16) s_sx[tid >> 2][tid & 3] = reinterpret_cast<const uint4 *>(tab->sign_pair_xor)[tid];
+    // K works with 2^8-scaled levels (the residual is formed scaled)
+    const float lscale = PROD ? 256.0f : 1.0f;
+    if (tid < 16) s_levels[tid] = tab->levels[BITS - 1][tid] * lscale;
+    if (tid < kBuckets) {
+        QBucket qb = tab->qlut[BITS - 1][tid];
+        qb.c_lo *= lscale;
+        qb.c_hi *= lscale;
+        s_lut[tid] = qb;
+    }
+    {
+        const half8 *src = reinterpret_cast<const half8 *>(tab->R_enc);
+        for (int i = tid; i < 32 * 64; i += 256) s_rot[i] = src[i];
+    }
     if constexpr (PROD) {
         const half8 *src = reinterpret_cast<const half8 *>(tab->S_enc);
         for (int i = tid; i < 32 * 64; i += 256) s_frag[i] = src[i];
@@ -72,70 +86,90 @@ void encode_tq_kernel(const DevTables *__restrict__ tab, const uint16_t *__restr
 #pragma unroll
     for (int k = 0; k < 3; ++k) bnd[k] = tab->bounds[BITS - 1][k];
 
-    // row counts are below 2^31 (checked on the host), so 32-bit indices
+    // row counts are below 2^31 (checked on the host), so 32-bit indices.
+    // B operand of k-step s: input coordinates 32s + 8q + [0,8) of token t.
+    // The next tile's rows are loaded while this one is processed; rows past
+    // the end (and the prefetch after the last tile) read row nv - 1, whose
+    // results are not stored.
     const int ntl = int(n_tiles), nv = int(n_vec);
-    for (int tile = int(blockIdx.x) * 4 + wave; tile < ntl; tile += int(gridDim.x) * 4) {
+    const int stride = int(gridDim.x) * 4;
+    auto load_rows = [&](int tl, half8 (&xr)[4]) {
+        const int tk = min(tl * 16 + t, nv - 1);
+        const uint16_t *row = x + size_t(tk) * kHeadDim + 8 * q;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xr[s] = *reinterpret_cast<const half8 *>(row + 32 * s);
+    };
+    half8 xb[4], xn[4];
+    load_rows(min(int(blockIdx.x) * 4 + wave, ntl - 1), xb);
+    for (int tile = int(blockIdx.x) * 4 + wave; tile < ntl; tile += stride) {
         const int tok = tile * 16 + t;
         const bool valid = tok < nv;
-        // load layout A: register r holds coordinate 8q + (r&7) + 32(r>>3)
-        uint32_t w[16];
-        if (valid) {
-            const uint16_t *row = x + size_t(tok) * kHeadDim + 8 * q;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(row + 32 * k);
-                w[4 * k + 0] = u.x; w[4 * k + 1] = u.y; w[4 * k + 2] = u.z; w[4 * k + 3] = u.w;
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < 16; ++p) w[p] = 0;
-        }
-        uint32_t sx[16];  // sign flips of D for this lane's coordinates (LDS, per tile)
-        {
-            int qq = q;
-            asm volatile("" : "+v"(qq));
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint4 u = s_sx[qq][k];
-                sx[4 * k] = u.x; sx[4 * k + 1] = u.y; sx[4 * k + 2] = u.z; sx[4 * k + 3] = u.w;
-            }
-        }
-        float v[32];
+        load_rows(min(tile + stride, ntl - 1), xn);
+        // n^2: packed fp16 products, fp32 accumulation, then over the 4 lanes
         float ss = 0.0f;
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const uint32_t sgn = w[p] ^ sx[p];  // D x on the packed fp16 pair
-            v[2 * p] = h2f(sgn & 0xFFFFu);
-            v[2 * p + 1] = h2f(sgn >> 16);
-            ss = fmaf(v[2 * p], v[2 * p], ss);
-            ss = fmaf(v[2 * p + 1], v[2 * p + 1], ss);
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const half2v h = half2v{xb[s][2 * p], xb[s][2 * p + 1]};
+                ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+            }
         ss = quad_sum(ss);
         const float n = sqrtf(ss);
-        fwht128_swap(v);  // now lane q holds coordinates 32q + r
         const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+        // y = H D x; lane (t, q) ends with coordinates 32q + 4rb + j in yb[rb][j].
+        // The fragments are read at their use (opaque index: not hoisted).
+        floatx4 yb[8];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) yb[rb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            int fl = lane;
+            asm volatile("" : "+v"(fl));
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int rb = 0; rb < 8; ++rb)
+                    yb[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_rot[(rb * 4 + s) * 64 + fl], xb[s], yb[rb], 0,
+                                                                    0, 0);
+        }
         uint32_t packed[BITS];
 #pragma unroll
         for (int i = 0; i < BITS; ++i) packed[i] = 0;
         // K: residual e = z - c[idx], scaled by 2^8 so that its fp16 lo half
-        // stays normal, split into the hi/lo MFMA operands as it is produced
-        half8 bhi[PROD ? 4 : 1], blo[PROD ? 4 : 1];
-        float se = 0.0f;
+        // stays normal (levels in s_levels / s_lut are pre-scaled by 2^8 for
+        // K), split into the hi/lo MFMA operands a pair at a time
+        uint32_t bhi[PROD ? 16 : 1], blo[PROD ? 16 : 1];
+        float se = 0.0f;  // sum of (2^8 e)^2
+        float es_prev = 0.0f;
         Unroll<32>::run([&](auto J) {
             constexpr int j = decltype(J)::value;
-            const float z = v[j] * inv;  // z = H(Dx)/n = sqrt(d) R x / n
+            const float z = yb[j >> 2][j & 3] * inv;  // z = H(Dx)/n = sqrt(d) R x / n
             float zhat;
             const uint32_t c = quantise<BITS>(z, bnd, s_levels, s_lut, zhat);
             put_code<BITS, j>(packed, c);
             if constexpr (PROD) {
-                const float e = z - zhat;
-                se = fmaf(e, e, se);
-                const float es = e * 256.0f;
-                const _Float16 hi = _Float16(es);
-                bhi[j >> 3][j & 7] = hi;
-                blo[j >> 3][j & 7] = _Float16(es - float(hi));
+                const float es = fmaf(z, 256.0f, -zhat);
+                se = fmaf(es, es, se);
+                if constexpr (j & 1) {
+                    const half2v hi = __builtin_convertvector(float2v{es_prev, es}, half2v);
+                    const half2v lo = __builtin_convertvector(
+                        float2v{es_prev - float(hi[0]), es - float(hi[1])}, half2v);
+                    bhi[j >> 1] = __builtin_bit_cast(uint32_t, hi);
+                    blo[j >> 1] = __builtin_bit_cast(uint32_t, lo);
+                } else {
+                    es_prev = es;
+                }
             }
         });
+        // the prefetched rows become the next tile's operands here, before any
+        // store of this tile: loads and stores share one completion counter,
+        // so waiting for them after a (possibly skipped) store would wait for
+        // the stores as well
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            xb[s] = xn[s];
+            asm volatile("" : "+v"(xb[s]));
+        }
         if (valid) {
             uint32_t *dst = reinterpret_cast<uint32_t *>(idx_plane + size_t(tok) * (16 * BITS) + q * (4 * BITS));
 #pragma unroll
@@ -146,29 +180,35 @@ void encode_tq_kernel(const DevTables *__restrict__ tab, const uint16_t *__restr
                 reinterpret_cast<uint16_t *>(norm_plane)[tok] = uint16_t(f2h(n));
         } else {
             se = quad_sum(se);
-            const float gamma = n * sqrtf(se) * kInvSqrtD;
+            const float gamma = n * sqrtf(se) * (kInvSqrtD / 256.0f);
             floatx4 acc[8];
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) acc[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            // read the S fragments from LDS at their use: an opaque index keeps
-            // the compiler from hoisting all 32 of them out of the tile loop
             int fl = lane;
             asm volatile("" : "+v"(fl));
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
+                const half8 bh = __builtin_bit_cast(half8, make_uint4(bhi[4 * s], bhi[4 * s + 1], bhi[4 * s + 2],
+                                                                      bhi[4 * s + 3]));
+                const half8 bl = __builtin_bit_cast(half8, make_uint4(blo[4 * s], blo[4 * s + 1], blo[4 * s + 2],
+                                                                      blo[4 * s + 3]));
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) {
                     const half8 a = s_frag[(mb * 4 + s) * 64 + fl];
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bhi[s], acc[mb], 0, 0, 0);
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, blo[s], acc[mb], 0, 0, 0);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, acc[mb], 0, 0, 0);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[mb], 0, 0, 0);
                 }
             }
-            // lane (t, q) now holds projections 32q + 4mb + j of token t
-            uint32_t bits = 0;
+            // lane (t, q) now holds projections 32q + 4mb + j of token t.  Bit
+            // (4mb + j) = [P > 0]: shift the sign bits in from the top, from
+            // projection 31 down to 0, then invert; a zero residual (all P = 0)
+            // gives no set bit.
+            uint32_t neg = 0;
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
+            for (int mb = 7; mb >= 0; --mb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bits |= (acc[mb][j] > 0.0f ? 1u : 0u) << (4 * mb + j);
+                for (int j = 3; j >= 0; --j) neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(acc[mb][j]), 31);
+            const uint32_t bits = se > 0.0f ? ~neg : 0u;
             if (valid) {
                 reinterpret_cast<uint32_t *>(sign_plane + size_t(tok) * 16)[q] = bits;
                 if (q == 0)
@@ -223,9 +263,10 @@ template <int BITS, bool PROD>
 static int launch_tq(const DevTables *tab, const uint16_t *x, int64_t n_vec, uint8_t *base,
                      const tq_planes_desc &lay, hipStream_t s) {
     const int64_t n_tiles = (n_vec + 15) / 16;
-    int64_t blocks = (n_tiles + 3) / 4;
-    if (PROD && blocks > 1024) blocks = 1024;  // amortise the 32 KB fragment load
-    if (blocks > (int64_t(1) << 30)) blocks = int64_t(1) << 30;
+    // persistent blocks amortise the 32 KB (64 KB with S) of LDS fragments:
+    // as many as are resident at once, each wave striding over the tiles
+    static int cache[kMaxDevices];
+    const int64_t blocks = persistent_grid(n_tiles, resident_blocks(encode_tq_kernel<BITS, PROD>, 256, cache));
     hipLaunchKernelGGL((encode_tq_kernel<BITS, PROD>), dim3(unsigned(blocks)), dim3(256), 0, s, tab, x,
                        n_vec, base + lay.idx_offset, PROD ? base + lay.sign_offset : nullptr,
                        base + lay.norm_offset, n_tiles);
