@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 70B-like full-cache step and the batched needle decode")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
     return ap.parse_args()
@@ -123,6 +125,171 @@ def cpu_baseline(tokens: int):
         "encode_mtok_s": tokens / (t1 - t0) / 1e6,
         "host_cpus": os.cpu_count(),
     }
+
+
+def kept_v_rows(TK, ctx, q, kbuf, kf, B, Hq, Hkv, T, tau, dev):
+    """Number of V rows the exact sparse-V rule keeps (some query head of the
+    group has weight >= tau), from the library's own dequantisation of the
+    packed K and a float32 softmax on the GPU.  Byte accounting only; it runs
+    outside every timed region."""
+    import torch
+    n_vec = B * Hkv * T
+    khat = torch.empty((n_vec, 128), dtype=torch.float16, device=dev)
+    TK.tq_decode_kv(ctx, kbuf, kf, n_vec, khat)
+    g = Hq // Hkv
+    kh = khat.view(B * Hkv, T, 128).float()
+    qq = q.view(B * Hkv, g, 128).float().transpose(1, 2).contiguous()
+    scores = torch.bmm(kh, qq) / math.sqrt(128)  # [B*Hkv, T, g]
+    p = torch.softmax(scores, dim=1)
+    kept = int((p >= tau).any(dim=2).sum().item())
+    del khat, kh, scores, p
+    return kept
+
+
+def v_bytes_read(TK, vf, n_vec, kept):
+    """V bytes the decode reads: index rows of kept tokens only, plus every
+    fp16 norm (codebook V: the norm scales each candidate's weight) or the
+    block scales of kept rows (q8 V)."""
+    if vf.kind == TK.KIND_Q8:
+        return kept * (128 + 8)
+    return kept * 16 * vf.bits + n_vec * 2
+
+
+def outlier_normal_gpu(gen, shape, n_out, dev, scale=20.0):
+    """N(0,1) fp16 tensor [..., T, 128] with n_out channels per leading index
+    scaled by `scale` (the tiny/70B-like recipe), drawn on the GPU."""
+    import torch
+    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    lead = x.view(-1, shape[-2], shape[-1])
+    for i in range(lead.shape[0]):
+        ch = torch.randperm(shape[-1], generator=gen, device=dev)[:n_out]
+        lead[i][:, ch] *= scale
+    return x.half()
+
+
+def graph_time(fn, reps, warm, stream):
+    """Mean time of one replay of a HIP graph that holds fn(), by HIP events
+    on the replay stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager run before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    cur = torch.cuda.current_stream()
+    for a, b in ev:
+        a.record(cur)
+        g.replay()
+        b.record(cur)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+
+def bench_70b(TK, ctx, dev, reps=10, warm=3):
+    """70B-like full cache on one GPU: 80 layers x 8 KV heads x 131072 tokens,
+    64 query heads; turbo3 K (2-bit codebook + QJL) + 2-bit V, layers 0, 1,
+    78, 79 at q8 for K and V.  K/V of each layer are N(0,1) with 4 channels
+    x20 (seed 404 + layer, drawn on the GPU), encoded once; one decode step =
+    the 80 per-layer attention calls, replayed as one HIP graph."""
+    import torch
+    L, Hkv, Hq, T, B = 80, 8, 64, 131072, 1
+    n_vec = B * Hkv * T
+    tau = 1e-6
+    boundary = (0, 1, 78, 79)
+    layers = []
+    moved = logical = 0
+    for l in range(L):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(404 + l)
+        if l in boundary:
+            kf, vf = TK.Q8, TK.Q8
+        else:
+            kf, vf = TK.turbo_k(3), TK.mse(2)
+        k = outlier_normal_gpu(gen, (Hkv, T, 128), 4, dev).view(-1, 128)
+        v = outlier_normal_gpu(gen, (Hkv, T, 128), 4, dev).view(-1, 128)
+        q = torch.randn((B, Hq, 128), generator=gen, device=dev).half()
+        kp, vp = TK.alloc_packed(kf, n_vec), TK.alloc_packed(vf, n_vec)
+        TK.tq_encode_kv(ctx, k, v, n_vec, kf, vf, kp.buf, vp.buf)
+        del k, v
+        kept = kept_v_rows(TK, ctx, q, kp.buf, kf, B, Hq, Hkv, T, tau, dev)
+        kb = int(kp.layout.total_bytes)
+        moved += kb + v_bytes_read(TK, vf, n_vec, kept) + B * Hq * 128 * (2 + 4)
+        logical += kb + int(vp.layout.total_bytes) + B * Hq * 128 * (2 + 4)
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        layers.append((q, kp, vp, kf, vf, out))
+    ws, wsb = TK.alloc_workspace(B, Hq, Hkv, T, TK.turbo_k(3), TK.mse(2))
+
+    def step():
+        for q, kp, vp, kf, vf, out in layers:
+            TK.tq_attn_decode(ctx, q, kp.buf, vp.buf, kf, vf, B, Hq, Hkv, T, None, tau, out, ws, wsb)
+
+    t = graph_time(step, reps, warm, None)
+    res = {"workload": "70B-like decode step: 80 layers x 8 KV / 64 q heads x 131072 tokens, batch 1; "
+                       "turbo3 K + 2-bit V, layers 0,1,78,79 q8; one HIP graph of 80 calls",
+           "step_ms": round(t * 1e3, 4), "moved_gb": round(moved / 1e9, 4), "logical_gb": round(logical / 1e9, 4),
+           "moved_gbs": round(moved / t / 1e9, 1), "frac_hbm": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
+           "logical_gbs": round(logical / t / 1e9, 1)}
+    del layers, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_needle(TK, ctx, dev, reps=20, warm=5):
+    """Batched needle decode: 64 sequences x 8192 tokens, 32 q / 8 KV heads;
+    K N(0,1) with 8 channels x20 per KV head, V N(0,1); each query head points
+    at one of 16 needle keys of its sequence (outlier channels removed, norm
+    3 sqrt(128)), so each head's softmax is dominated by one token.  turbo4 K
+    + 2-bit V, tau 1e-6.  Drawn on the GPU (seed 505)."""
+    import torch
+    B, T, Hq, Hkv = 64, 8192, 32, 8
+    n_vec = B * Hkv * T
+    tau = 1e-6
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(505)
+    k = torch.randn((B, Hkv, T, 128), generator=gen, device=dev)
+    out_ch = torch.stack([torch.randperm(128, generator=gen, device=dev)[:8] for _ in range(Hkv)])
+    for h in range(Hkv):
+        k[:, h, :, out_ch[h]] *= 20.0
+    k = k.half()
+    v = torch.randn((B, Hkv, T, 128), generator=gen, device=dev).half()
+    needles = torch.stack([torch.sort(torch.randperm(T, generator=gen, device=dev)[:16])[0] for _ in range(B)])
+    g = Hq // Hkv
+    q = torch.zeros((B, Hq, 128), device=dev)
+    for h in range(Hq):
+        kvh = h // g
+        kn = k[torch.arange(B, device=dev), kvh, needles[:, h % 16]].float()  # [B, 128]
+        kn[:, out_ch[kvh]] = 0.0
+        q[:, h] = 3.0 * math.sqrt(128) * kn / kn.norm(dim=1, keepdim=True)
+    q = q.half()
+    kf, vf = TK.turbo_k(4), TK.mse(2)
+    kp, vp = TK.alloc_packed(kf, n_vec), TK.alloc_packed(vf, n_vec)
+    TK.tq_encode_kv(ctx, k.view(-1, 128), v.view(-1, 128), n_vec, kf, vf, kp.buf, vp.buf)
+    del k, v
+    kept = kept_v_rows(TK, ctx, q, kp.buf, kf, B, Hq, Hkv, T, tau, dev)
+    ws, wsb = TK.alloc_workspace(B, Hq, Hkv, T, kf, vf)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    def call():
+        TK.tq_attn_decode(ctx, q, kp.buf, vp.buf, kf, vf, B, Hq, Hkv, T, None, tau, out, ws, wsb)
+
+    t = graph_time(call, reps, warm, None)
+    kb = int(kp.layout.total_bytes)
+    moved = kb + v_bytes_read(TK, vf, n_vec, kept) + B * Hq * 128 * 6
+    logical = kb + int(vp.layout.total_bytes) + B * Hq * 128 * 6
+    res = {"workload": "batched needle decode: 64 x 8192 tokens, 32 q / 8 KV heads; turbo4 K + 2-bit V, tau 1e-6",
+           "us": round(t * 1e6, 2), "v_rows_kept": kept, "moved_gbs": round(moved / t / 1e9, 1),
+           "frac_hbm": round(moved / t / 1e9 / HBM_PEAK_GBS, 4), "logical_gbs": round(logical / t / 1e9, 1)}
+    del kp, vp, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -259,6 +426,11 @@ def main():
         "roofline_encode_k": roof("encode_tq_kernel<3,true>"),
         "source_hash": source_hash(),
     }
+    del kps, vps, ks, vs, ws
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["decode_70b"] = bench_70b(TK, ctx, dev)
+        res["decode_needle"] = bench_needle(TK, ctx, dev)
     TK.tq_ctx_destroy(ctx)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)

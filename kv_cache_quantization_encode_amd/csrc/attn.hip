@@ -37,7 +37,6 @@ namespace tq {
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 constexpr float kQjlOverSqrtD = 1.2533141373155003f / 128.0f * 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSuper = 1024;   // tokens compacted together in the values pass
 constexpr int kVThreads = 512;  // threads per values block
 constexpr int kVWaves = kVThreads / 64;
 
@@ -535,6 +534,9 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
 // ------------------------------------------------------------------ values
 template <int G, int KIND, int BITS>
 __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
+    // tokens compacted together (one super-slice); fewer for 8 heads, whose
+    // accumulators take twice the registers
+    constexpr int kSuper = G >= 8 ? 512 : 1024;
     constexpr int R = kSuper / kVThreads;  // tokens per thread per super-slice
     // s_vpair[f]: the two levels of a 2-code field f = c0 | c1 << BITS
     constexpr int kVPairs = KIND == TQ_KIND_Q8 ? 1 : 1 << (2 * BITS);
@@ -601,12 +603,16 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    const int tk = lane >> 4, cg = lane & 15;  // token slot within the wave, coordinate group
-    float acc[G][8];
+    // V accumulation layout: CPL coordinates per lane, LPT lanes per token,
+    // TPW tokens per wave and pass (fewer coordinates per lane for 8 heads,
+    // whose accumulators take twice the registers)
+    constexpr int CPL = G >= 8 ? 4 : 8, LPT = 128 / CPL, TPW = 64 / LPT;
+    const int tk = lane / LPT, cg = lane % LPT;  // token slot within the wave, coordinate group
+    float acc[G][CPL];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
+        for (int j = 0; j < CPL; ++j) acc[g][j] = 0.0f;
 
     bool kept_any = false;  // uniform over the block
     for (int base = t0; base < t1; base += kSuper) {
@@ -652,12 +658,17 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
         kept_any |= total > 0;
         __syncthreads();
         if (base + kSuper < t1) load_super(base + kSuper);  // next super-slice in flight
-        // 3) accumulate kept rows: 4 tokens per wave and pass, 8
+        // 3) accumulate kept rows: TPW tokens per wave and pass, CPL
         //    coordinates per lane.  All row loads of a batch are issued before
         //    any is used (a slot past `total` reads a kept row), and passes run
         //    four at a time without branches (such slots carry weight 0); the
         //    number of groups of four is uniform over the block.
-        constexpr int PASSES = 8, PER_PASS = 4 * kVWaves;
+        constexpr int PASSES = 8, PER_PASS = TPW * kVWaves;
+        // codes of this lane: CPL * BITS bits from bit CPL * BITS * cg of the
+        // row; within one dword unless 3-bit codes straddle two
+        constexpr int NB = CPL * (KIND == TQ_KIND_Q8 ? 8 : BITS);
+        constexpr bool TWO = (32 % NB) != 0;
+        const int bit0 = NB * cg;
         for (int k0 = 0; k0 < total; k0 += PER_PASS * PASSES) {
             const int npass = min((total - k0 + PER_PASS - 1) / PER_PASS, PASSES);
             uint32_t raw[PASSES][2];
@@ -665,28 +676,22 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
             Unroll<PASSES>::run([&](auto P) {
                 constexpr int ps = decltype(P)::value;
                 {
-                    const int slot = min(k0 + PER_PASS * ps + wave * 4 + tk, total - 1);
+                    const int slot = min(k0 + PER_PASS * ps + wave * TPW + tk, total - 1);
                     const int64_t vec = int64_t(row) * a.T + s_tok[slot];
                     raw[ps][1] = 0u;
                     if constexpr (KIND == TQ_KIND_Q8) {
-                        const uint2 u = *reinterpret_cast<const uint2 *>(a.vidx + vec * 128 + 8 * cg);
-                        raw[ps][0] = u.x;
-                        raw[ps][1] = u.y;
-                        bsc[ps] = h2f(reinterpret_cast<const uint16_t *>(a.vnorm)[vec * 4 + (cg >> 2)]);
-                    } else {
-                        const uint8_t *rowp = a.vidx + vec * (16 * BITS);
-                        if constexpr (BITS == 4) {
-                            raw[ps][0] = reinterpret_cast<const uint32_t *>(rowp)[cg];
-                        } else if constexpr (BITS == 2) {
-                            raw[ps][0] = reinterpret_cast<const uint16_t *>(rowp)[cg];
-                        } else if constexpr (BITS == 1) {
-                            raw[ps][0] = rowp[cg];
-                        } else {  // 3 bits: 24 bits starting at byte 3*cg
-                            const uint32_t *wp = reinterpret_cast<const uint32_t *>(rowp);
-                            const int byte = 3 * cg;
-                            raw[ps][0] = wp[byte >> 2];
-                            raw[ps][1] = wp[(byte + 2) >> 2];
+                        if constexpr (CPL == 8) {
+                            const uint2 u = *reinterpret_cast<const uint2 *>(a.vidx + vec * 128 + 8 * cg);
+                            raw[ps][0] = u.x;
+                            raw[ps][1] = u.y;
+                        } else {
+                            raw[ps][0] = *reinterpret_cast<const uint32_t *>(a.vidx + vec * 128 + 4 * cg);
                         }
+                        bsc[ps] = h2f(reinterpret_cast<const uint16_t *>(a.vnorm)[vec * 4 + ((CPL * cg) >> 5)]);
+                    } else {
+                        const uint32_t *wp = reinterpret_cast<const uint32_t *>(a.vidx + vec * (16 * BITS));
+                        raw[ps][0] = wp[bit0 >> 5];
+                        if constexpr (TWO) raw[ps][1] = wp[(bit0 + NB - 1) >> 5];
                     }
                 }
             });
@@ -698,24 +703,23 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int ps = 4 * q4 + u;
-                        const int slot = k0 + PER_PASS * ps + wave * 4 + tk;
+                        const int slot = k0 + PER_PASS * ps + wave * TPW + tk;
                         const bool live = slot < total;
-                        float val[8];
+                        float val[CPL];
                         if constexpr (KIND == TQ_KIND_Q8) {
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                val[j] = float(int8_t((raw[ps][0] >> (8 * j)) & 0xFFu)) * bsc[ps];
-                                val[4 + j] = float(int8_t((raw[ps][1] >> (8 * j)) & 0xFFu)) * bsc[ps];
-                            }
+                            for (int j = 0; j < CPL; ++j)
+                                val[j] = float(int8_t((raw[ps][j >> 2] >> (8 * (j & 3))) & 0xFFu)) * bsc[ps];
                         } else {
-                            uint32_t bitsw = raw[ps][0];
-                            if constexpr (BITS == 3) {
-                                const uint64_t both = (uint64_t(raw[ps][1]) << 32) | raw[ps][0];
-                                bitsw = uint32_t(both >> (8 * ((3 * cg) & 3)));
+                            uint32_t bitsw;
+                            if constexpr (TWO) {
+                                bitsw = __builtin_amdgcn_alignbit(raw[ps][1], raw[ps][0], bit0 & 31);
+                            } else {
+                                bitsw = raw[ps][0] >> (bit0 & 31);
                             }
                             // 2-code fields: one table read gives two levels
 #pragma unroll
-                            for (int f = 0; f < 4; ++f) {
+                            for (int f = 0; f < CPL / 2; ++f) {
                                 const float2 lv = s_vpair[(bitsw >> (2 * BITS * f)) & ((1u << (2 * BITS)) - 1u)];
                                 val[2 * f] = lv.x;
                                 val[2 * f + 1] = lv.y;
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
                         for (int g = 0; g < G; ++g) {
                             const float wg = live ? s_w[g][slot] : 0.0f;
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
+                            for (int j = 0; j < CPL; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
                         }
                     }
                 }
@@ -733,16 +737,24 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
         }
         __syncthreads();
     }
-    // reduce over the 4 token slots of each wave, then over the waves
+    // reduce over the token slots of each wave, then over the waves
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[g][j] = quad_sum(acc[g][j]);
+        for (int j = 0; j < CPL; ++j) {
+            if constexpr (TPW == 4) {
+                acc[g][j] = quad_sum(acc[g][j]);
+            } else {
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[g][j]),
+                                                                __float_as_uint(acc[g][j]), false, false);
+                acc[g][j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            }
+        }
     if (tk == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s_acc[wave][g][8 * cg + j] = acc[g][j];
+            for (int j = 0; j < CPL; ++j) s_acc[wave][g][CPL * cg + j] = acc[g][j];
     }
     __syncthreads();
     // the chunk's share of each head, rotated back (out = R^T acc = D H acc /
