@@ -18,7 +18,8 @@
 //               q_proj of the g query heads of its kv head (q_proj on MFMA)
 //               while its first K tiles are being fetched, then scores 16-token
 //               tiles with v_mfma_f32_16x16x32_f16 (rows = query heads), two
-//               256-token slices in flight.  Scores go to the workspace with
+//               slices of kSlice tokens in flight ahead of the one scored.
+//               Scores go to the workspace with
 //               per-chunk (max, sum exp) per head.
 //   2. values   same grid; combines the chunk statistics into the exact softmax
 //               normaliser, keeps tokens with some weight >= tau, compacts them
@@ -37,7 +38,9 @@ namespace tq {
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 constexpr float kQjlOverSqrtD = 1.2533141373155003f / 128.0f * 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kVThreads = 512;  // threads per values block
+constexpr int kSliceTiles = 4;            // 16-token tiles per wave and slice
+constexpr int kSlice = 64 * kSliceTiles;  // tokens per slice of the scores pass (4 waves)
+constexpr int kVThreads = 512;            // threads per values block
 constexpr int kVWaves = kVThreads / 64;
 
 struct AttnArgs {
@@ -207,13 +210,13 @@ __device__ __forceinline__ void build_query_rows(const QueryLoads<G, PROJ> &ql, 
 // fp16.  q8 keys use k-steps = the four 32-element scale blocks.
 template <int KIND, int BITS>
 struct KTiles {
-    static constexpr int NT = 4;  // tiles of 16 tokens per wave per 256-token slice
+    static constexpr int NT = kSliceTiles;  // tiles of 16 tokens per wave per slice
     static constexpr int W = KIND == TQ_KIND_Q8 ? 8 : BITS;
     uint32_t wk[NT][W], sw[NT], nn[NT];
     uint2 q8s[NT];
 };
 
-// Loads the K tiles of one 256-token slice.  Tokens at or past t1 read row
+// Loads the K tiles of one slice (kSlice tokens).  Tokens at or past t1 read row
 // tmax instead (any valid row: the scores of such tokens are discarded), so
 // every call issues the same loads and the waits before scoring stay exact.
 template <int KIND, int BITS>
@@ -266,20 +269,61 @@ __device__ __forceinline__ void fold_rows(float (&e)[4]) {
     }
 }
 
-// Whether lane group kq, register j holds the score of head 4 kq + j.
+// The value of x in lane l ^ 16 (resp. l ^ 32).  permlane16_swap(x, x)
+// leaves a lane of an even 16-lane row with (x[l], x[l + 16]) and one of an
+// odd row with (x[l - 16], x[l]); permlane32_swap likewise with halves.
+__device__ __forceinline__ float partner16(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float partner32(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+
+// After fold_rows, each lane group kq (lanes 16 kq .. 16 kq + 15, one token
+// per lane) takes over kOwn<G> heads: head kq + 4i for G >= 4, head kq % G
+// below (duplicated across groups).  own_scores moves the scores there.
 template <int G>
-__device__ __forceinline__ bool holds_head(int kq, int j) {
-    return G >= 4 ? kq < G / 4 : (kq == 0 && j < G);
+constexpr int kOwn = G >= 8 ? 2 : 1;
+template <int G>
+__device__ __forceinline__ int own_head(int kq, int i) {
+    return G >= 4 ? kq + 4 * i : kq % G;
+}
+template <int G>
+__device__ __forceinline__ void own_scores(const float (&e)[4], int lane, float (&o)[kOwn<G>]) {
+    const int kq = lane >> 4;
+    if constexpr (G == 1) {
+        // head 0 sits in e[0] of group 0; every other group holds zero there
+        o[0] = quad_sum(e[0]);
+    } else if constexpr (G == 2) {
+        // heads 0, 1 in e[0], e[1] of group 0, zeros elsewhere
+        const float h0 = quad_sum(e[0]), h1 = quad_sum(e[1]);
+        o[0] = (kq & 1) ? h1 : h0;
+    } else if constexpr (G == 4) {
+        // groups 0 and 1 both hold heads 0..3 in e[0..3]; groups 2, 3 zeros
+        const float lo = (kq & 1) ? e[1] : e[0];
+        const float hi = partner32((kq & 1) ? e[3] : e[2], lane);
+        o[0] = kq < 2 ? lo : hi;
+    } else {
+        // groups 0, 2 hold heads 0..3 and groups 1, 3 heads 4..7 in e[0..3]
+        const float own = kq == 0 ? e[0] : kq == 1 ? e[1] : kq == 2 ? e[2] : e[3];
+        const int want = kq ^ 1;  // what the partner group needs from this lane
+        const float send = want == 0 ? e[0] : want == 1 ? e[1] : want == 2 ? e[2] : e[3];
+        const float recv = partner16(send, lane);
+        o[0] = (kq & 1) ? recv : own;  // head kq
+        o[1] = (kq & 1) ? own : recv;  // head kq + 4
+    }
 }
 
 template <bool FULL, int G, int KIND, int BITS>
 __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
                                              int kq, const uint2 *s_pair, const half8 *s_sgn,
                                              const half8 (&aq)[8], const half8 (&ap)[4],
-                                             float *__restrict__ scores, int64_t head0, int T, float (&m)[4],
-                                             float (&l)[4]) {
+                                             float *__restrict__ scores, int64_t head0, int T,
+                                             float (&m)[kOwn<G>], float (&l)[kOwn<G>]) {
     using KT = KTiles<KIND, BITS>;
-    float scv[KT::NT][4];  // this lane's scores of the slice in log2 units, -inf where absent
+    float scv[KT::NT][kOwn<G>];  // this lane's scores of the slice in log2 units, -inf where absent
     // B operands of the rotated-key path.  Field f (codes 2f, 2f+1 of the
     // lane) gives (hi(c0) hi(c1) | lo(c0) lo(c1)); fields 2u and 2u+1 side by
     // side are the B operand of k-step u, whose A operand repeats each query
@@ -289,7 +333,7 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         uint2 ef[16];
         half8 sg[4];
     };
-    Ops ops[2];
+    Ops ops[1];
     auto fetch = [&](int i, Ops &o) {
         Unroll<16>::run([&](auto P) {
             constexpr int pr = decltype(P)::value;
@@ -300,7 +344,6 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
             for (int s = 0; s < 4; ++s) o.sg[s] = s_sgn[(d.sw[i] >> (8 * s)) & 0xFFu];
         }
     };
-    if constexpr (KIND != TQ_KIND_Q8) fetch(0, ops[0]);
     Unroll<KT::NT>::run([&](auto I) {
         constexpr int i = decltype(I)::value;
         const int tok = base + wave * 16 + 64 * i + t;
@@ -328,9 +371,9 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
 #pragma unroll
             for (int j = 0; j < 4; ++j) e[j] *= kRsqrtD;
         } else {
-            if constexpr (i + 1 < KT::NT) fetch(i + 1, ops[(i + 1) & 1]);
+            fetch(i, ops[0]);
             __builtin_amdgcn_sched_barrier(0);
-            const Ops &o = ops[i & 1];
+            const Ops &o = ops[0];
             floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -349,18 +392,20 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
             for (int j = 0; j < 4; ++j) e[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
         }
         fold_rows<G>(e);
-        // lane (t, kq) now holds heads 4 kq + j of token tok where holds_head
-        if (valid && holds_head<G>(kq, 0)) {
+        float o[kOwn<G>];
+        own_scores<G>(e, 16 * kq + t, o);
+        // lane (t, kq) now holds the scores of its own heads for token tok;
+        // one store per head and lane (on the whole-slice path without a
+        // branch, so the memory counters stay exact)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (holds_head<G>(kq, j)) scores[(head0 + 4 * kq + j) * T + tok] = e[j];
+        for (int j = 0; j < kOwn<G>; ++j) {
+            if (valid) scores[(head0 + own_head<G>(kq, j)) * T + tok] = o[j];
+            scv[i][j] = valid ? o[j] * kLog2e : -INFINITY;
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) scv[i][j] = (valid && holds_head<G>(kq, j)) ? e[j] * kLog2e : -INFINITY;
     });
-    // running (max, sum) per lane and head, once per slice, in log2 units
+    // running (max, sum) per lane and own head, once per slice, in log2 units
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kOwn<G>; ++j) {
         float mx = scv[0][j];
 #pragma unroll
         for (int i = 1; i < KT::NT; ++i) mx = fmaxf(mx, scv[i][j]);
@@ -419,12 +464,15 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     // keep these small loads ahead of the K tiles in the memory queue, so
     // the query setup below does not wait for the (slower) K tiles
     asm volatile("" ::: "memory");
-    // rows past the sequence (or of an empty chunk) read row tmax instead
+    // rows past the sequence (or of an empty chunk) read row tmax instead.
+    // Three slices rotate through ta, tb, tc: two are in flight while the
+    // third is scored, enough bytes in flight to cover the memory latency.
     const int n_tok = max(t1 - t0, 0);
-    const bool whole = (n_tok & 511) == 0;
+    const bool whole = n_tok % kSlice == 0;
     const int tmax = max(t1 - 1, 0);
-    KTiles<KIND, BITS> ta, tb;
+    KTiles<KIND, BITS> ta, tb, tc;
     load_ktiles(ta, t0, tmax, wave, t, kq, kid, ksg, knm);
+    load_ktiles(tb, t0 + kSlice, tmax, wave, t, kq, kid, ksg, knm);
 
     // the output rows of this kv head start at zero; the values pass adds
     // every chunk's share into them
@@ -483,25 +531,28 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
             for (int s = 0; s < 4; ++s) ap[s] = *reinterpret_cast<const half8 *>(rp + 32 * kq + 8 * s);
         }
     }
-    float m[4], l[4];
+    float m[kOwn<G>], l[kOwn<G>];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
+    for (int j = 0; j < kOwn<G>; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
 
-    // two 256-token slices in flight: while one is scored the next is fetched
+    // the scan: every load is unconditional (clamped rows), so the wait
+    // before scoring a slice covers exactly that slice's loads
     auto scan = [&](auto full_c) {
         constexpr bool F = decltype(full_c)::value;
         if (t0 >= t1) return;
-        for (int base = t0;; base += 512) {
-            load_ktiles(tb, base + 256, tmax, wave, t, kq, kid, ksg, knm);
+        for (int base = t0;;) {
+            load_ktiles(tc, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
             score_ktiles<F, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
-            if (base + 512 >= t1) {
-                if (F || base + 256 < t1)
-                    score_ktiles<F, G>(tb, base + 256, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0,
-                                       a.T, m, l);
-                break;
-            }
-            load_ktiles(ta, base + 512, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(tb, base + 256, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            base += kSlice;
+            if (base >= t1) break;
+            load_ktiles(ta, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            base += kSlice;
+            if (base >= t1) break;
+            load_ktiles(tb, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            base += kSlice;
+            if (base >= t1) break;
         }
     };
     if (whole) scan(std::true_type{});
@@ -509,13 +560,13 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     // (max, sum) per head: over the 16 token lanes of each lane group, then
     // over the waves; m is kept in log2 units and stored in natural units
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kOwn<G>; ++j) {
         const float mx = row16_max(m[j]);
         l[j] = row16_sum(m[j] == -INFINITY ? 0.0f : l[j] * fast_exp2(m[j] - mx));
         m[j] = mx;
-        if (t == 0) {
-            s_red[wave][4 * kq + j][0] = m[j];
-            s_red[wave][4 * kq + j][1] = l[j];
+        if (t == 0 && (G >= 4 || kq < G)) {
+            s_red[wave][own_head<G>(kq, j)][0] = m[j];
+            s_red[wave][own_head<G>(kq, j)][1] = l[j];
         }
     }
     __syncthreads();
