@@ -46,7 +46,7 @@ def parse():
                     help="tokens of the workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the 70B-like full-cache step and the batched needle decode")
+                    help="skip the tiny, min-max, 70B-like full-cache and batched needle measurements")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
     return ap.parse_args()
@@ -292,6 +292,80 @@ def bench_needle(TK, ctx, dev, reps=20, warm=5):
     return res
 
 
+def bench_tiny(TK, ctx, dev, reps=50, warm=10):
+    """Tiny case: 1 KV head x 1024 tokens, K/V N(0,1) with 4 channels x20,
+    turbo3 K (2-bit codebook + QJL) + 2-bit V; latency of one encode of all
+    tokens and of one decode-attention step (each a HIP graph replay)."""
+    import torch
+    T = 1024
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(101)
+    k = outlier_normal_gpu(gen, (T, 128), 4, dev)
+    v = outlier_normal_gpu(gen, (T, 128), 4, dev)
+    q = torch.randn((1, 1, 128), generator=gen, device=dev).half()
+    kf, vf = TK.turbo_k(3), TK.mse(2)
+    kp, vp = TK.alloc_packed(kf, T), TK.alloc_packed(vf, T)
+    ws, wsb = TK.alloc_workspace(1, 1, 1, T, kf, vf)
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device=dev)
+    t_enc = graph_time(lambda: TK.tq_encode_kv(ctx, k, v, T, kf, vf, kp.buf, vp.buf), reps, warm, None)
+    t_att = graph_time(lambda: TK.tq_attn_decode(ctx, q, kp.buf, vp.buf, kf, vf, 1, 1, 1, T, None, 1e-6, out, ws,
+                                                 wsb), reps, warm, None)
+    return {"workload": "tiny: 1 KV head x 1024 tokens; turbo3 K + 2-bit V", "encode_us": round(t_enc * 1e6, 2),
+            "decode_attn_us": round(t_att * 1e6, 2)}
+
+
+def bench_minmax(TK, dev, reps=10, warm=3):
+    """Per-group asymmetric min-max baseline: K and V tensors of 32 layers x
+    8 KV heads x 4096 tokens x 128 (2 x 134M fp16 elements), N(0,1) times a
+    per-64-group scale log-uniform in [1e-3, 8] (drawn on the GPU, seed 303);
+    group 64 at 2/3/4 bits.  Quantise and dequantise GB/s (bytes read +
+    written), MSE and cosine (flattened and mean per 128-vector)."""
+    import torch
+    n = 32 * 8 * 4096 * 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(303)
+    res = {"workload": "min-max: 2 x 32 layers x 8 KV heads x 4096 tokens x 128, group 64"}
+    xs = []
+    for _ in range(2):
+        x = torch.randn((n // 64, 64), generator=gen, device=dev)
+        sc = torch.exp(torch.empty((n // 64, 1), device=dev).uniform_(math.log(1e-3), math.log(8.0), generator=gen))
+        xs.append((x * sc).half().view(-1))
+        del x, sc
+    for bits in (2, 3, 4):
+        codes = [torch.empty(n * bits // 8, dtype=torch.uint8, device=dev) for _ in xs]
+        scale = [torch.empty(n // 64, dtype=torch.float16, device=dev) for _ in xs]
+        zero = [torch.empty(n // 64, dtype=torch.float16, device=dev) for _ in xs]
+        outs = [torch.empty(n, dtype=torch.float16, device=dev) for _ in xs]
+
+        def quant():
+            for i, x in enumerate(xs):
+                TK.tq_minmax_quant(x, n, 64, bits, codes[i], scale[i], zero[i])
+
+        def dequant():
+            for i in range(len(xs)):
+                TK.tq_minmax_dequant(codes[i], scale[i], zero[i], n, 64, bits, outs[i])
+
+        tq_ = graph_time(quant, reps, warm, None)
+        td_ = graph_time(dequant, reps, warm, None)
+        per_elem = 2 + bits / 8 + 4 / 64
+        mse = cos = cosv = 0.0
+        for i, x in enumerate(xs):
+            xf, yf = x.float(), outs[i].float()
+            mse += float(((xf - yf) ** 2).mean()) / len(xs)
+            cos += float(torch.dot(xf, yf) / (xf.norm() * yf.norm())) / len(xs)
+            xv, yv = xf.view(-1, 128), yf.view(-1, 128)
+            cosv += float((torch.sum(xv * yv, 1) / (xv.norm(dim=1) * yv.norm(dim=1)).clamp_min(1e-30)).mean()) / len(xs)
+            del xf, yf, xv, yv
+        res[f"b{bits}"] = {"quant_gbs": round(2 * n * per_elem / tq_ / 1e9, 1),
+                           "dequant_gbs": round(2 * n * per_elem / td_ / 1e9, 1),
+                           "quant_gelem_s": round(2 * n / tq_ / 1e9, 2), "mse": mse, "cosine": round(cos, 5),
+                           "cosine_per_vector": round(cosv, 5)}
+        del codes, scale, zero, outs
+    del xs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calib:
@@ -429,6 +503,8 @@ def main():
     del kps, vps, ks, vs, ws
     torch.cuda.empty_cache()
     if not args.no_extra:
+        res["tiny"] = bench_tiny(TK, ctx, dev)
+        res["minmax"] = bench_minmax(TK, dev)
         res["decode_70b"] = bench_70b(TK, ctx, dev)
         res["decode_needle"] = bench_needle(TK, ctx, dev)
     TK.tq_ctx_destroy(ctx)
