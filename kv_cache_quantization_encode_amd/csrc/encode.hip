@@ -9,7 +9,8 @@
 //
 // Work split: one wavefront = 16 tokens.  Both dense products run on the
 // MFMA units (v_mfma_f32_16x16x32_f16, columns = the 16 tokens):
-//   y = H diag(D) x  with the +-1 matrix as A operand (exact in fp16) and the
+//   y = H diag(D) x  with the +-1 matrix as A operand (exact in fp16; built
+//   from four per-lane register patterns, see below) and the sign-flipped
 //   fp16 input rows as B operand, so no conversion or butterfly is spent on
 //   the rotation; lane (t, q) receives coordinates 32q + [0,32) of token t;
 //   P = S e  (K only) with the rotated residual e split into hi + lo fp16
@@ -59,7 +60,6 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
                                                         uint8_t *__restrict__ norm_plane, int64_t n_tiles) {
     __shared__ float s_levels[16];
     __shared__ __attribute__((aligned(16))) QBucket s_lut[kBuckets];
-    __shared__ half8 s_rot[32 * 64];
     __shared__ half8 s_frag[PROD ? 32 * 64 : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // K works with 2^8-scaled levels (the residual is formed scaled)
@@ -70,10 +70,6 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
         qb.c_lo *= lscale;
         qb.c_hi *= lscale;
         s_lut[tid] = qb;
-    }
-    {
-        const half8 *src = reinterpret_cast<const half8 *>(tab->R_enc);
-        for (int i = tid; i < 32 * 64; i += 256) s_rot[i] = src[i];
     }
     if constexpr (PROD) {
         const half8 *src = reinterpret_cast<const half8 *>(tab->S_enc);
@@ -86,8 +82,42 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
 #pragma unroll
     for (int k = 0; k < 3; ++k) bnd[k] = tab->bounds[BITS - 1][k];
 
+    // Rotation operands.  k-step s of lane group q carries input coordinates
+    // k = 32q + 8s + j (j = 0..7); MFMA row i of block rb is output coordinate
+    // c = 32(i>>2) + 4rb + (i&3), so lane group q receives c = 32q + [0,32).
+    // Sylvester H[c][k] = (-1)^popcount(c & k) then factors as
+    //   (-1)^popcount(((i&3) | (rb&1)<<2) & j) * (-1)^popcount((rb>>1) & s)
+    //   * (-1)^popcount((i>>2) & q):
+    // an 8-entry pattern chosen by rb&1, a sign fixed by (rb, s) at compile
+    // time and a sign fixed per lane, so every A operand is one of four
+    // register constants (pat[rb&1][sign]).  D is applied to the fp16 inputs
+    // by flipping their sign bits (dmask).
+    half8 pat[2][2];
+    {
+        const int ri = lane & 15;
+        const int tau = __builtin_popcount(unsigned((ri >> 2) & q)) & 1;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int cl = (ri & 3) | (p << 2);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool neg = ((__builtin_popcount(unsigned(cl & j)) & 1) ^ tau) != 0;
+                pat[p][0][j] = neg ? _Float16(-1.0f) : _Float16(1.0f);
+                pat[p][1][j] = neg ? _Float16(1.0f) : _Float16(-1.0f);
+            }
+        }
+    }
+    uint32_t dmask[4][4];  // sign flips of D on the lane's fp16 pairs
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int c0 = 32 * q + 8 * s + 2 * w;
+            dmask[s][w] = (tab->signs[c0] < 0.0f ? 0x8000u : 0u) | (tab->signs[c0 + 1] < 0.0f ? 0x80000000u : 0u);
+        }
+
     // row counts are below 2^31 (checked on the host), so 32-bit indices.
-    // B operand of k-step s: input coordinates 32s + 8q + [0,8) of token t.
+    // B operand of k-step s: input coordinates 32q + 8s + [0,8) of token t.
     // The next tile's rows are loaded while this one is processed; rows past
     // the end (and the prefetch after the last tile) read row nv - 1, whose
     // results are not stored.
@@ -95,9 +125,9 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
     const int stride = int(gridDim.x) * 4;
     auto load_rows = [&](int tl, half8 (&xr)[4]) {
         const int tk = min(tl * 16 + t, nv - 1);
-        const uint16_t *row = x + size_t(tk) * kHeadDim + 8 * q;
+        const uint16_t *row = x + size_t(tk) * kHeadDim + 32 * q;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xr[s] = *reinterpret_cast<const half8 *>(row + 32 * s);
+        for (int s = 0; s < 4; ++s) xr[s] = *reinterpret_cast<const half8 *>(row + 8 * s);
     };
     half8 xb[4], xn[4];
     load_rows(min(int(blockIdx.x) * 4 + wave, ntl - 1), xb);
@@ -117,20 +147,22 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
         ss = quad_sum(ss);
         const float n = sqrtf(ss);
         const float inv = n > 0.0f ? 1.0f / n : 0.0f;
-        // y = H D x; lane (t, q) ends with coordinates 32q + 4rb + j in yb[rb][j].
-        // The fragments are read at their use (opaque index: not hoisted).
+        // y = H D x; lane (t, q) ends with coordinates 32q + 4rb + j in yb[rb][j]
         floatx4 yb[8];
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb) yb[rb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        {
-            int fl = lane;
-            asm volatile("" : "+v"(fl));
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+            uint4 u = __builtin_bit_cast(uint4, xb[s]);
+            u.x ^= dmask[s][0];
+            u.y ^= dmask[s][1];
+            u.z ^= dmask[s][2];
+            u.w ^= dmask[s][3];
+            const half8 xd = __builtin_bit_cast(half8, u);
 #pragma unroll
-                for (int rb = 0; rb < 8; ++rb)
-                    yb[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_rot[(rb * 4 + s) * 64 + fl], xb[s], yb[rb], 0,
-                                                                    0, 0);
+            for (int rb = 0; rb < 8; ++rb)
+                yb[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    pat[rb & 1][__builtin_popcount(unsigned((rb >> 1) & s)) & 1], xd, yb[rb], 0, 0, 0);
         }
         uint32_t packed[BITS];
 #pragma unroll
@@ -263,8 +295,8 @@ template <int BITS, bool PROD>
 static int launch_tq(const DevTables *tab, const uint16_t *x, int64_t n_vec, uint8_t *base,
                      const tq_planes_desc &lay, hipStream_t s) {
     const int64_t n_tiles = (n_vec + 15) / 16;
-    // persistent blocks amortise the 32 KB (64 KB with S) of LDS fragments:
-    // as many as are resident at once, each wave striding over the tiles
+    // persistent blocks amortise the 32 KB of S fragments (K) in LDS: as many
+    // as are resident at once, each wave striding over the tiles
     static int cache[kMaxDevices];
     const int64_t blocks = persistent_grid(n_tiles, resident_blocks(encode_tq_kernel<BITS, PROD>, 256, cache));
     hipLaunchKernelGGL((encode_tq_kernel<BITS, PROD>), dim3(unsigned(blocks)), dim3(256), 0, s, tab, x,

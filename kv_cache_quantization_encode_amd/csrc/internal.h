@@ -29,7 +29,6 @@ struct DevTables {
     float signs[kHeadDim];           // D
     uint16_t S[kHeadDim * kHeadDim]; // QJL matrix, fp16 bits, row-major [m][d]
     uint16_t ST[kHeadDim * kHeadDim];// its transpose [d][m]
-    uint16_t R_enc[32 * 64 * 8];     // H diag(D) (rows permuted) as encode MFMA A-fragments
     uint16_t S_enc[32 * 64 * 8];     // S as encode MFMA A-fragments
     uint16_t St_dec[32 * 64 * 8];    // S^T as dequant MFMA A-fragments
 };

@@ -176,25 +176,6 @@ bool build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
             t->qlut[b - 1][j] = qb;
         }
     }
-    // Encode rotation fragments: the unnormalised transform y = H diag(D) x
-    // as the A operand of a 16x16x32 MFMA (entries +-1, exact in fp16; rows =
-    // output coordinates, k = input coordinates).  Fragment f = rb*4 + s; lane
-    // l = 16*q + i supplies  H[c][k] D[k]  for  c = 32*(i/4) + 4*rb + i%4  and
-    // k = 32*s + 8*q + j (j = 0..7), so that output row 4*q + j' of block rb
-    // is coordinate 32*q + 4*rb + j' and the B operand of k-step s is the
-    // eight input coordinates 32*s + 8*q + j of the lane's token.  Sylvester
-    // H: H[c][k] = (-1)^popcount(c & k).
-    for (int rb = 0; rb < 8; ++rb)
-        for (int s = 0; s < 4; ++s)
-            for (int l = 0; l < 64; ++l) {
-                const int i = l & 15, q = l >> 4;
-                const int c = 32 * (i >> 2) + 4 * rb + (i & 3);
-                for (int j = 0; j < 8; ++j) {
-                    const int k = 32 * s + 8 * q + j;
-                    const bool neg = (__builtin_popcount(unsigned(c & k)) & 1) != (t->signs[k] < 0);
-                    t->R_enc[((rb * 4 + s) * 64 + l) * 8 + j] = neg ? 0xBC00u : 0x3C00u;
-                }
-            }
     // Encode QJL fragments (A operand of a 16x16x32 MFMA, rows = projections).
     // Fragment f = mb*4 + s; lane l = 16*q + i supplies the eight fp16 values
     //   S[32*(i/4) + 4*mb + i%4][32*q + 8*s + j],  j = 0..7,
