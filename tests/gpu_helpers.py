@@ -209,6 +209,23 @@ def oracle_attention(case, kpacked, vpacked, kk, kb, vk, vb, tab, tau, seq_lens=
     return out
 
 
+def oracle_attention_heads(case, kpacked, vpacked, kk, kb, vk, vb, tab, tau, kv_heads):
+    """Oracle outputs of the query heads of the listed kv heads (batch 0 only,
+    full length): [len(kv_heads), g, 128].  Only those heads' rows are
+    dequantised, so full-size layers stay cheap for the oracle."""
+    B, Hq, Hkv, Tn = case.shape
+    g = Hq // Hkv
+    n_total = B * Hkv * Tn
+    outs = []
+    for h in kv_heads:
+        k = _dequant_rows(kpacked, kk, kb, tab, n_total, h * Tn, Tn).reshape(1, 1, Tn, 128)
+        v = _dequant_rows(vpacked, vk, vb, tab, n_total, h * Tn, Tn).reshape(1, 1, Tn, 128)
+        q = case.q[:1, h * g:(h + 1) * g].astype(np.float64)
+        out, _ = O.attention_decode(q, k, v, tau)
+        outs.append(out[0])
+    return np.stack(outs)
+
+
 def sub_packed(packed, kind, bits, n_total, start, count):
     """Bytes of rows [start, start+count) of a packed tensor, re-laid out as a
     packed tensor of `count` rows (plane by plane)."""

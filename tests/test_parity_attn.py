@@ -87,3 +87,21 @@ def test_attention_70b_boundary_and_middle_layers(ctx, oracle_tables):
         kf = c.meta["kf"]
         vf = c.meta["vf"]
         _run(ctx, oracle_tables, c, kf, vf, 1e-6)
+
+
+@pytest.mark.parametrize("layer", [40, 79])
+def test_attention_70b_full_layer_sampled(ctx, oracle_tables, layer):
+    """One 70B-like layer at its full size (8 KV / 64 query heads, 131072
+    tokens, the chunking the benchmark runs) on the GPU; the oracle checks the
+    query heads of KV heads 0 and 7.  Layer 40: turbo3 K + 2-bit V; layer 79:
+    q8 boundary layer."""
+    c = W.llama70b_layer(layer)
+    kf, vf = c.meta["kf"], c.meta["vf"]
+    kp, vp = _encode_case(ctx, c, kf, vf)
+    got = G.gpu_attention(ctx, c, kp, vp, G.tf(*kf), G.tf(*vf), 1e-6)
+    heads = [0, 7]
+    ref = G.oracle_attention_heads(c, kp, vp, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6, heads)
+    g = c.shape[1] // c.shape[2]
+    sel = np.stack([got[0, h * g:(h + 1) * g] for h in heads])
+    err = np.max(np.abs(sel - ref))
+    assert err <= G.ATTN_ATOL, f"max abs error {err:.3g}"
