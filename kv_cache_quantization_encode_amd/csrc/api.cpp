@@ -72,7 +72,10 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     p.chunk = int(chunk);
     const int64_t heads = int64_t(B) * Hq;
     int64_t off = 0;
-    p.off_scores = size_t(off); off = align256(off + heads * int64_t(T) * 4);
+    // score rows padded to 32 tokens, so that a 32-token group of a row can
+    // be read whole (16-byte aligned) near the end of the sequence
+    p.ld_scores = int((int64_t(T) + 31) / 32 * 32);
+    p.off_scores = size_t(off); off = align256(off + heads * int64_t(p.ld_scores) * 4);
     p.off_stats = size_t(off); off = align256(off + heads * nc * 2 * 4);
     p.total = size_t(off);
     return p;

@@ -19,16 +19,20 @@
 //               while its first K tiles are being fetched, then scores 16-token
 //               tiles with v_mfma_f32_16x16x32_f16 (rows = query heads), two
 //               slices of kSlice tokens in flight ahead of the one scored.
-//               Scores go to the workspace with
-//               per-chunk (max, sum exp) per head.
-//   2. values   same grid; combines the chunk statistics into the exact softmax
-//               normaliser, keeps tokens with some weight >= tau, compacts them
-//               (up to 1024 tokens at a time, all loads issued together),
-//               accumulates weight * level over 8 coordinates per lane and
-//               writes the chunk's partial sum.
-//   3. merge    one block per (batch, q head): sum of the partials, then R^T.
+//               Scores go to the workspace with per-chunk (max, sum exp) per
+//               head; the block of chunk 0 zeroes the output.
+//   2. values   combines the chunk statistics into the exact softmax
+//               normaliser and accumulates the kept weights times V in the
+//               rotated domain, then rotates each block's share back (R^T) and
+//               adds it into the output with fp32 atomics.  Two kernels:
+//               - compacting (same grid): keeps tokens with some weight >= tau,
+//                 compacts them (up to 1024 at a time, all loads issued
+//                 together) and accumulates weight * level per coordinate;
+//               - matrix cores (8 query heads, 2-bit codebook V): every 32-token
+//                 group is one set of MFMA products, see below.
 // Exact sparse V needs the global softmax statistics before any V row is
 // skipped, hence the kernel boundary between passes 1 and 2.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -53,6 +57,8 @@ struct AttnArgs {
     float *out;
     float tau;
     int B, Hq, Hkv, T, chunk, n_chunks;
+    int ld_scores;  // score row stride (floats)
+    int vsub;       // tokens per block of the MFMA values pass (multiple of 32)
     int k_rotated;  // K codec works in the rotated domain
     int v_rotated;  // V codec works in the rotated domain
 };
@@ -320,7 +326,7 @@ template <bool FULL, int G, int KIND, int BITS>
 __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
                                              int kq, const uint2 *s_pair, const half8 *s_sgn,
                                              const half8 (&aq)[8], const half8 (&ap)[4],
-                                             float *__restrict__ scores, int64_t head0, int T,
+                                             float *__restrict__ scores, int64_t head0, int ld,
                                              float (&m)[kOwn<G>], float (&l)[kOwn<G>]) {
     using KT = KTiles<KIND, BITS>;
     float scv[KT::NT][kOwn<G>];  // this lane's scores of the slice in log2 units, -inf where absent
@@ -399,7 +405,7 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         // branch, so the memory counters stay exact)
 #pragma unroll
         for (int j = 0; j < kOwn<G>; ++j) {
-            if (valid) scores[(head0 + own_head<G>(kq, j)) * T + tok] = o[j];
+            if (valid) scores[(head0 + own_head<G>(kq, j)) * ld + tok] = o[j];
             scv[i][j] = valid ? o[j] * kLog2e : -INFINITY;
         }
     });
@@ -542,15 +548,15 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
         if (t0 >= t1) return;
         for (int base = t0;;) {
             load_ktiles(tc, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            score_ktiles<F, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, m, l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(ta, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            score_ktiles<F, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, m, l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(tb, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.T, m, l);
+            score_ktiles<F, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, m, l);
             base += kSlice;
             if (base >= t1) break;
         }
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
     const int t1 = min(t0 + a.chunk, L);
     if (t0 >= t1) return;  // an empty chunk adds nothing (uniform over the block)
     const int tmax = t1 - 1;
-    const float *sc_base = a.scores + head0 * a.T;
+    const float *sc_base = a.scores + head0 * a.ld_scores;
     const uint16_t *vn_base = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
 
     // every global read of the prologue is issued before any is used: the
@@ -627,7 +633,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
         for (int r = 0; r < R; ++r) {
             const int tt = min(base + kVThreads * r + tid, tmax);
 #pragma unroll
-            for (int g = 0; g < G; ++g) sv[r][g] = sc_base[int64_t(g) * a.T + tt];
+            for (int g = 0; g < G; ++g) sv[r][g] = sc_base[int64_t(g) * a.ld_scores + tt];
             if constexpr (KIND != TQ_KIND_Q8) vraw[r] = vn_base[tt];
         }
     };
@@ -841,6 +847,288 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------- values pass, 2-bit V on MFMA
+// A symmetric 4-level codebook (c0 = -c3, c1 = -c2) is a sum of two signed
+// constants chosen by the two bits of the code:
+//   c[2 b1 + b0] = a1 (2 b1 - 1) + a0 (2 b0 - 1),  a1 = (c3 + c2) / 2,  a0 = (c3 - c2) / 2.
+// The rotated-domain V sum of head h over coordinate x is therefore
+//   sum_t w_ht n_t c[code_tx] / sqrt(d) = -(a1 X1 + a0 X0) / sqrt(d),
+//   X_p[h][x] = sum_t w_ht n_t (1 - 2 bit_p(code_tx)),
+// and each X_p is a [2G x T] x [T x 128] product on the matrix cores
+// (v_mfma_f32_16x16x32_f16, 32 tokens per step): A = the kept weights as fp16
+// hi (rows h) and lo (rows G + h) halves, scaled by 2^15 so both stay in
+// range; B = the token's fp16 norm with the code bit as its sign, exact.
+// Lane (kq, n) of a wave holds tokens 8kq + [0, 8) of the 32-token group as
+// k-slots, for A row n and for B column n; column n of product m is
+// coordinate 8n + m, whose two code bits are bits 2m, 2m + 1 of the 16-bit
+// word n of the token's row.  Every token of a chunk is stepped over; a group
+// in which no head keeps a token is skipped as a whole.
+constexpr int kMThreads = 256;
+constexpr int kMWaves = kMThreads / 64;
+constexpr float kWScale = 32768.0f;  // 2^15
+
+template <int G>
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) void attn_values_mfma_kernel(AttnArgs a) {
+    static_assert(G == 8, "rows: 8 heads x (hi, lo)");
+    __shared__ float s_M[G], s_invL[G];
+    __shared__ int s_any[kMWaves];
+    __shared__ __attribute__((aligned(16))) float s_acc[kMWaves][G][128];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.y;
+    const int b = row / a.Hkv, kvh = row - b * a.Hkv;
+    const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
+    const int L = seq_len_of(a, b);
+    const int t0 = int(blockIdx.x) * a.vsub;
+    const int t1 = min(t0 + a.vsub, L);
+    if (t0 >= t1) return;  // uniform over the block
+    const int tmax = t1 - 1;
+    const int kq = lane >> 4, n = lane & 15;
+    // A row n: head hn, fp16 hi half (n < G) or lo half (G <= n < 2G); rows
+    // from 2G on stay zero
+    const bool arow = n < 2 * G;
+    const bool lo_half = n >= G;
+    const int hn = n < G ? n : (n < 2 * G ? n - G : 0);
+    const float *srow = a.scores + (head0 + hn) * int64_t(a.ld_scores);
+    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(row) * a.T * 8 + (n >> 1);
+    // v_perm selector joining half (n & 1) of two dwords: that half of the
+    // second operand (bytes 0-3) in bits 0-15, of the first (bytes 4-7) in 16-31
+    const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
+    const uint16_t *vn = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
+
+    // 32-token groups: lane (kq, n) reads the scores of head hn for tokens
+    // 8kq + [0, 8) (score rows are padded to 32 tokens, so a group is always
+    // in bounds), and code word n and the fp16 norm of the same tokens.  Whole
+    // groups lie inside [t0, t1); only the last group of a block may be
+    // partial, and its code words and norms clamp to the last token.
+    const int nfull = (t1 - t0) >> 5;  // whole groups of the block
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int ng = wv < nfull ? (nfull - 1 - wv) / kMWaves + 1 : 0;  // whole groups of this wave
+    auto gbase = [&](int k) { return t0 + 32 * (wv + kMWaves * min(k, ng - 1)); };
+    // scores of groups k and k+1 alternate between two register sets
+    float4 S[2][2];
+    auto load_scores = [&](int tb, float4 (&sd)[2]) {
+        const float4 *sp = reinterpret_cast<const float4 *>(srow + tb + 8 * kq);
+        sd[0] = sp[0];
+        sd[1] = sp[1];
+    };
+    // code words and norms of a whole group; a group that keeps no token
+    // reads the block's first tokens instead (the same cache lines every
+    // time), so that every step issues the same loads and the memory waits
+    // stay exact
+    // (the code words come in as the dword that holds word n; products()
+    // picks the half)
+    auto load_codes = [&](int tb, bool real, uint32_t (&c)[8], uint32_t (&nr)[4]) {
+        const int tk = real ? tb + 8 * kq : t0;
+        const uint32_t *cp = cwd32 + int64_t(tk) * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = cp[8 * j];
+        __builtin_memcpy(nr, vn + tk, 16);
+    };
+    auto load_tail = [&](int tb, uint32_t (&c)[8], uint32_t (&nr)[4]) {
+        const int tk = tb + 8 * kq;
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int tj = min(tk + j, tmax);
+            c[j] = cwd32[int64_t(tj) * 8];
+            h[j] = vn[tj];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nr[i] = h[2 * i] | (h[2 * i + 1] << 16);
+    };
+    if (ng > 0) load_scores(gbase(0), S[0]);
+    const float c2 = a.tab->levels[1][2], c3 = a.tab->levels[1][3];
+    const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
+    const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
+    asm volatile("" ::: "memory");
+
+    // exact softmax statistics of every head from all chunk statistics
+    for (int h = wave; h < G; h += kMWaves) {
+        const float *sth = a.stats + (head0 + h) * a.n_chunks * 2;
+        const float2 f0 = h == wave ? st0 : *reinterpret_cast<const float2 *>(sth + 2 * min(lane, a.n_chunks - 1));
+        float mm = lane < a.n_chunks ? f0.x : -INFINITY;
+        for (int c = lane + 64; c < a.n_chunks; c += 64) mm = fmaxf(mm, sth[2 * c]);
+        mm = quad_max(row16_max(mm));
+        float ll = 0.0f;
+        if (mm != -INFINITY) {
+            if (lane < a.n_chunks) ll = f0.y * fast_exp2((f0.x - mm) * kLog2e);
+            for (int c = lane + 64; c < a.n_chunks; c += 64) ll += sth[2 * c + 1] * fast_exp2((sth[2 * c] - mm) * kLog2e);
+        }
+        ll = quad_sum(row16_sum(ll));
+        if (lane == 0) {
+            s_M[h] = mm;
+            s_invL[h] = ll > 0.0f ? 1.0f / ll : 0.0f;
+        }
+    }
+    __syncthreads();
+    const float Ml2 = s_M[hn] * kLog2e;
+    const float invL = s_invL[hn] * kWScale;  // weights leave scaled by 2^15
+    // p = 2^x / L >= tau  <=>  x >= log2(tau L), x = (s - M) log2(e): the keep
+    // test needs no exponential (rows >= 2G keep nothing)
+    const float keep_x = arow ? log2f(a.tau) - log2f(s_invL[hn]) : INFINITY;
+
+    floatx4 acc[8][2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m][0] = acc[m][1] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    bool any = false;  // uniform over the wave
+    // weights of head hn for tokens tb + 8kq + j: p = exp(s - M) / L, kept
+    // when p >= tau, as this row's fp16 half; returns whether any lane of the
+    // wave keeps a token (uniform)
+    auto weights = [&](int tb, const float4 (&sd)[2], uint32_t (&aw)[4], auto whole) -> bool {
+        const float sv[8] = {sd[0].x, sd[0].y, sd[0].z, sd[0].w, sd[1].x, sd[1].y, sd[1].z, sd[1].w};
+        float x[8];
+        bool kj[8], kept = false;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = fmaf(sv[j], kLog2e, -Ml2);
+            kj[j] = x[j] >= keep_x;
+            if constexpr (!decltype(whole)::value) kj[j] = kj[j] && tb + 8 * kq + j < t1;
+            kept |= kj[j];
+        }
+        if (__ballot(kept) == 0) return false;
+        float ws[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ws[j] = kj[j] ? fast_exp2(x[j]) * invL : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half2v hi = __builtin_convertvector(float2v{ws[2 * i], ws[2 * i + 1]}, half2v);
+            const half2v lo =
+                __builtin_convertvector(float2v{ws[2 * i] - float(hi[0]), ws[2 * i + 1] - float(hi[1])}, half2v);
+            aw[i] = __builtin_bit_cast(uint32_t, lo_half ? lo : hi);
+        }
+        return true;
+    };
+    auto products = [&](const uint32_t (&aw)[4], const uint32_t (&c)[8], const uint32_t (&nr)[4]) {
+        const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+        uint32_t cwd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cwd[i] = __builtin_amdgcn_perm(c[2 * i + 1], c[2 * i], half_sel);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                // bit p of coordinate 8n + m moved to the fp16 sign bit of
+                // both token halves, over the (positive) norms
+                const int sh = 15 - 2 * m - p;
+                uint32_t bw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bw[i] = ((cwd[i] << sh) & 0x80008000u) | nr[i];
+                acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    A, __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[m][p], 0, 0, 0);
+            }
+    };
+    // software pipeline over this wave's whole groups k = 0 .. ng-1.  Step k
+    // starts the scores of group k+2, forms the weights of group k+1 (scores
+    // issued a step earlier), starts its code words and norms, and runs the
+    // products of group k (code words issued a step earlier); step -1 only
+    // fills the pipeline.  Register sets alternate with the parity of k, so
+    // nothing is copied while its load is outstanding.
+    if (ng > 0) {
+        uint32_t aw[2][4], c[2][8], nr[2][4];
+        bool kp[2] = {false, false};
+        // the loop starts with nothing in flight but its own loads (so the
+        // compiler's memory waits inside it stay exact): vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        auto step = [&](int k, auto P) {
+            constexpr int p = decltype(P)::value;
+            load_scores(gbase(k + 2), S[p]);
+            asm volatile("" ::: "memory");
+            const bool more = k + 1 < ng;
+            kp[p ^ 1] = more && weights(gbase(k + 1), S[p ^ 1], aw[p ^ 1], std::true_type{});
+            load_codes(gbase(k + 1), kp[p ^ 1], c[p ^ 1], nr[p ^ 1]);
+            asm volatile("" ::: "memory");
+            if (kp[p]) {
+                any = true;
+                products(aw[p], c[p], nr[p]);
+            } else {
+                // a skipped group still takes delivery of its (cache-resident)
+                // loads here, so no later reuse of these registers has to wait
+                // for everything in flight
+                asm volatile("" ::"v"(c[p][0]), "v"(c[p][1]), "v"(c[p][2]), "v"(c[p][3]), "v"(c[p][4]),
+                             "v"(c[p][5]), "v"(c[p][6]), "v"(c[p][7]), "v"(nr[p][0]), "v"(nr[p][1]),
+                             "v"(nr[p][2]), "v"(nr[p][3]));
+            }
+        };
+        // steps run in pairs (the last pair may end with a step past ng,
+        // which only issues its cache-resident loads), so the loop has a
+        // single exit
+        for (int k = -1; k < ng; k += 2) {
+            step(k, std::integral_constant<int, 1>{});
+            step(k + 1, std::integral_constant<int, 0>{});
+        }
+    }
+    if (((t1 - t0) & 31) != 0 && wv == (nfull & (kMWaves - 1))) {
+        const int tb = t0 + 32 * nfull;
+        uint32_t aw[4], c[8], nr[4];
+        load_scores(tb, S[0]);
+        if (weights(tb, S[0], aw, std::false_type{})) {
+            any = true;
+            load_tail(tb, c, nr);
+            products(aw, c, nr);
+        }
+    }
+    // lane (kq, n) holds rows 4kq + j, column n of every product: coordinate
+    // 8n + m of row 4kq + j is -(a1 X1 + a0 X0) (times 2^-15 / sqrt(d), applied
+    // with R^T below); add each head's lo row to its hi row
+    const float a1 = 0.5f * (c3 + c2), a0 = 0.5f * (c3 - c2);
+    float y[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[m][j] = fmaf(a1, acc[m][1][j], a0 * acc[m][0][j]);
+    // rows 4kq + j and 4(kq + 2) + j are the hi and lo rows of head 4kq + j
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const auto r =
+                __builtin_amdgcn_permlane32_swap(__float_as_uint(y[m][j]), __float_as_uint(y[m][j]), false, false);
+            y[m][j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    // heads 4kq + j (kq < 2) go to this wave's slot
+    if (kq < 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 *dst = reinterpret_cast<float4 *>(&s_acc[wave][4 * kq + j][8 * n]);
+            dst[0] = make_float4(y[0][j], y[1][j], y[2][j], y[3][j]);
+            dst[1] = make_float4(y[4][j], y[5][j], y[6][j], y[7][j]);
+        }
+    }
+    if (lane == 0) s_any[wave] = any ? 1 : 0;
+    __syncthreads();
+    bool kept_any = false;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) kept_any |= s_any[w] != 0;
+    // the block's share of each head, rotated back (R^T = D H / sqrt(d)) and
+    // added into the output, which the scores pass zeroed
+    if (kept_any) {
+        const float sc = -kRsqrtD * kRsqrtD / kWScale;
+        for (int g = wave; g < G; g += kMWaves) {
+            float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kMWaves; ++w) {
+                v0 += s_acc[w][g][lane];
+                v1 += s_acc[w][g][lane + 64];
+            }
+            const float s0 = v0 + v1, s1 = v0 - v1;
+            v0 = s0;
+            v1 = s1;
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                const float sg = (lane & s) ? -1.0f : 1.0f;
+                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+                v0 = fmaf(sg, v0, p0);
+                v1 = fmaf(sg, v1, p1);
+            }
+            v0 *= a.tab->signs[lane] * sc;
+            v1 *= a.tab->signs[lane + 64] * sc;
+            float *o = a.out + (head0 + g) * 128;
+            __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ launch
 template <int G, int KK, int KB, int VK, int VB>
 static int launch_passes(const AttnArgs &a, hipStream_t s) {
@@ -849,7 +1137,20 @@ static int launch_passes(const AttnArgs &a, hipStream_t s) {
                        a.scores);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return int(e);
-    hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(kVThreads), 0, s, a);
+    if constexpr (G == 8 && VK == TQ_KIND_MSE && VB == 2) {
+        // 8 query heads: the kept rows of all heads together are most of the
+        // tokens unless attention is very peaked, and the per-row cost of the
+        // compacting pass grows with the head count, so the whole range goes
+        // through the matrix cores.  Blocks of vsub tokens, ~1024 blocks in all.
+        const int64_t rows = int64_t(a.B) * a.Hkv;
+        const int64_t per = (int64_t(a.T) * rows + 1023) / 1024;
+        AttnArgs v = a;
+        v.vsub = int(std::min<int64_t>(std::max<int64_t>((per + 255) / 256 * 256, 256), (int64_t(a.T) + 31) / 32 * 32));
+        const dim3 vgrid(unsigned((a.T + v.vsub - 1) / v.vsub), unsigned(rows));
+        hipLaunchKernelGGL((attn_values_mfma_kernel<G>), vgrid, dim3(kMThreads), 0, s, v);
+    } else {
+        hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(kVThreads), 0, s, a);
+    }
     return int(hipGetLastError());
 }
 
@@ -911,6 +1212,7 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.T = T;
     a.chunk = plan.chunk;
     a.n_chunks = plan.n_chunks;
+    a.ld_scores = plan.ld_scores;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
     switch (Hq / Hkv) {

@@ -49,9 +49,6 @@ __device__ __forceinline__ uint32_t quantise(float z, const float *bnd, const fl
     }
 }
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-
 template <int BITS, bool PROD>
 __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restrict__ tab,
                                                         const uint16_t *__restrict__ x, int64_t n_vec,

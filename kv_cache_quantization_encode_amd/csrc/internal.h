@@ -47,6 +47,7 @@ bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out);
 struct AttnPlan {
     int n_chunks;    // token chunks per (batch, kv head)
     int chunk;       // tokens per chunk (multiple of 256)
+    int ld_scores;   // score row stride in floats: T rounded up to 32
     size_t off_scores, off_stats, total;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
