@@ -49,6 +49,8 @@ def parse():
                     help="skip the tiny, min-max, 70B-like full-cache and batched needle measurements")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle"],
+                    help="run only this extra measurement and print its JSON (for profiling)")
     return ap.parse_args()
 
 
@@ -385,6 +387,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.only:
+        if args.only == "minmax":
+            r = bench_minmax(TK, dev)
+        else:
+            ctx1 = TK.tq_codebook_init(128, 128, 42)
+            fn = {"tiny": bench_tiny, "decode_70b": bench_70b, "decode_needle": bench_needle}[args.only]
+            r = fn(TK, ctx1, dev, reps=5, warm=2)
+        print(json.dumps({args.only: r}), flush=True)
+        return
 
     case = W.llama8b()
     B, Hq, Hkv, T = case.shape

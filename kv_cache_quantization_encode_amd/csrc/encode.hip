@@ -40,8 +40,10 @@ __device__ __forceinline__ uint32_t quantise(float z, const float *bnd, const fl
         zhat = s_levels[c];
         return c;
     } else {
-        int j = int(fmaf(z, 4.0f, 12.5f));
-        j = j < 0 ? 0 : (j > kBuckets - 1 ? kBuckets - 1 : j);
+        // bucket floor(4 z + 48.5): 4 z + 48 + 1.5 * 2^23 rounded to an integer
+        // (a tie lands in either neighbour, both give the same index) leaves
+        // the bucket number in the low mantissa bits; |z| <= 12.125 always
+        const uint32_t j = __float_as_uint(fmaf(z, 4.0f, 12582960.0f)) - 0x4B400000u;
         const uint4 qb = reinterpret_cast<const uint4 *>(s_lut)[j];  // {thr, base, c_lo, c_hi}
         const bool up = z >= __uint_as_float(qb.x);
         zhat = __uint_as_float(up ? qb.w : qb.z);
@@ -59,6 +61,23 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
     __shared__ __attribute__((aligned(16))) QBucket s_lut[kBuckets];
     __shared__ half8 s_frag[PROD ? 32 * 64 : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = lane & 15, q = lane >> 4;
+    // row counts are below 2^31 (checked on the host), so 32-bit indices.
+    // B operand of k-step s: input coordinates 32q + 8s + [0,8) of token t.
+    // The next tile's rows are loaded while this one is processed; rows past
+    // the end (and the prefetch after the last tile) read row nv - 1, whose
+    // results are not stored.  The first tile's rows are in flight while the
+    // tables are set up.
+    const int ntl = int(n_tiles), nv = int(n_vec);
+    const int stride = int(gridDim.x) * 4;
+    auto load_rows = [&](int tl, half8 (&xr)[4]) {
+        const int tk = min(tl * 16 + t, nv - 1);
+        const uint16_t *row = x + size_t(tk) * kHeadDim + 32 * q;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xr[s] = *reinterpret_cast<const half8 *>(row + 8 * s);
+    };
+    half8 xb[4], xn[4];
+    load_rows(min(int(blockIdx.x) * 4 + wave, ntl - 1), xb);
     // K works with 2^8-scaled levels (the residual is formed scaled)
     const float lscale = PROD ? 256.0f : 1.0f;
     if (tid < 16) s_levels[tid] = tab->levels[BITS - 1][tid] * lscale;
@@ -74,7 +93,6 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
     }
     __syncthreads();
 
-    const int t = lane & 15, q = lane >> 4;
     float bnd[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) bnd[k] = tab->bounds[BITS - 1][k];
@@ -113,21 +131,6 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
             dmask[s][w] = (tab->signs[c0] < 0.0f ? 0x8000u : 0u) | (tab->signs[c0 + 1] < 0.0f ? 0x80000000u : 0u);
         }
 
-    // row counts are below 2^31 (checked on the host), so 32-bit indices.
-    // B operand of k-step s: input coordinates 32q + 8s + [0,8) of token t.
-    // The next tile's rows are loaded while this one is processed; rows past
-    // the end (and the prefetch after the last tile) read row nv - 1, whose
-    // results are not stored.
-    const int ntl = int(n_tiles), nv = int(n_vec);
-    const int stride = int(gridDim.x) * 4;
-    auto load_rows = [&](int tl, half8 (&xr)[4]) {
-        const int tk = min(tl * 16 + t, nv - 1);
-        const uint16_t *row = x + size_t(tk) * kHeadDim + 32 * q;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) xr[s] = *reinterpret_cast<const half8 *>(row + 8 * s);
-    };
-    half8 xb[4], xn[4];
-    load_rows(min(int(blockIdx.x) * 4 + wave, ntl - 1), xb);
     for (int tile = int(blockIdx.x) * 4 + wave; tile < ntl; tile += stride) {
         const int tok = tile * 16 + t;
         const bool valid = tok < nv;

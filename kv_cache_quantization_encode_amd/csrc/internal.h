@@ -18,14 +18,16 @@ struct QBucket {
     uint32_t base;
     float c_lo, c_hi;
 };
-constexpr int kBuckets = 26;  // bucket j = clamp(floor(4 z + 12.5), 0, 25)
+// Bucket j = floor(4 z + 48.5) for j = 0..96 covers |z| <= 12.125, more than
+// the largest standardised coordinate sqrt(128) (|(Rx)_i| <= ||x||).
+constexpr int kBuckets = 97;
 
 // Tables uploaded once per ctx.  Plain data, identical on host and device.
 struct DevTables {
     float levels[4][16];             // row b-1: 2^b ascending N(0,1) Lloyd-Max levels
     float bounds[4][16];             // row b-1: 2^b-1 midpoints, then +inf padding
     uint32_t sign_pair_xor[4][16];   // fp16-pair sign flips of D per lane quarter (load layout A)
-    QBucket qlut[4][32];             // row b-1: quantiser buckets of the b-bit codebook
+    QBucket qlut[4][kBuckets];       // row b-1: quantiser buckets of the b-bit codebook
     float signs[kHeadDim];           // D
     uint16_t S[kHeadDim * kHeadDim]; // QJL matrix, fp16 bits, row-major [m][d]
     uint16_t ST[kHeadDim * kHeadDim];// its transpose [d][m]

@@ -147,32 +147,30 @@ bool build_device_tables(int d, int m, uint64_t seed, DevTables *t) {
             if (t->signs[c0 + 1] < 0) msk |= 0x80000000u;
             t->sign_pair_xor[q][p] = msk;
         }
-    // Quantiser buckets: edges e_j = -3.125 + 0.25 j (j = 1..25), bucket 0 below
-    // e_1, bucket 25 above e_25.  Every Lloyd-Max boundary of 1..4 bits lies at
+    // Quantiser buckets: bucket j (0..96) is [-12.125 + 0.25 j, -11.875 + 0.25 j),
+    // the outer two open-ended.  Every Lloyd-Max boundary of 1..4 bits lies at
     // least 0.02 from an edge and no bucket holds two boundaries, so
-    // idx = #{t_k <= z} = base_j + (z >= thr_j) even when rounding moves a z
-    // next to an edge into the neighbouring bucket.
+    // idx = base_j + (z >= thr_j) even when rounding moves a z next to an edge
+    // into the neighbouring bucket.
     for (int b = 1; b <= 4; ++b) {
         double lv[16], bd[15];
         lloyd_max_gaussian(b, lv, bd);
         const int L = 1 << b;
-        for (int j = 0; j < 32; ++j) {
+        for (int j = 0; j < kBuckets; ++j) {
             QBucket qb{INFINITY, 0u, 0.0f, 0.0f};
-            if (j < kBuckets) {
-                const double lo = j == 0 ? -INFINITY : -3.125 + 0.25 * j;
-                const double hi = j == kBuckets - 1 ? INFINITY : -3.125 + 0.25 * (j + 1);
-                int base = 0, inside = 0;
-                double thr = INFINITY;
-                for (int k = 0; k + 1 < L; ++k) {
-                    if (bd[k] < lo) ++base;
-                    else if (bd[k] < hi) { ++inside; thr = bd[k]; }
-                }
-                if (inside > 1) return false;  // cannot happen for these codebooks
-                qb.thr = float(thr);
-                qb.base = uint32_t(base);
-                qb.c_lo = float(lv[base]);
-                qb.c_hi = float(lv[base + 1 < L ? base + 1 : base]);
+            const double lo = j == 0 ? -INFINITY : -12.125 + 0.25 * j;
+            const double hi = j == kBuckets - 1 ? INFINITY : -11.875 + 0.25 * j;
+            int base = 0, inside = 0;
+            double thr = INFINITY;
+            for (int k = 0; k + 1 < L; ++k) {
+                if (bd[k] < lo) ++base;
+                else if (bd[k] < hi) { ++inside; thr = bd[k]; }
             }
+            if (inside > 1) return false;  // cannot happen for these codebooks
+            qb.thr = float(thr);
+            qb.base = uint32_t(base);
+            qb.c_lo = float(lv[base]);
+            qb.c_hi = float(lv[base + 1 < L ? base + 1 : base]);
             t->qlut[b - 1][j] = qb;
         }
     }
