@@ -69,6 +69,20 @@ def test_attention_single_token_and_seq_lens(ctx, oracle_tables):
     assert np.all(got[2] == 0.0)
 
 
+def test_attention_eight_heads_ragged_batch(ctx, oracle_tables):
+    """8 query heads per KV head with 2-bit V (the matrix-core values pass):
+    a batch of 4 whose lengths give a partial last 32-token group, a
+    one-token and an empty sequence, at tau 0, 1e-6 and 0.5; then a peaked
+    (needle) batch where most 32-token groups keep nothing."""
+    c = W.llama8b(T=1100, Hq=16, Hkv=2, B=4)
+    lens = np.array([1100, 33, 1, 0], np.int32)
+    for tau in (0.0, 1e-6, 0.5):
+        got, _, _ = _run(ctx, oracle_tables, c, ("prod", 2), ("mse", 2), tau, seq_lens=lens)
+        assert np.all(got[3] == 0.0)
+    n = W.needle(B=2, T=2048, Hq=16, Hkv=2)
+    _run(ctx, oracle_tables, n, ("prod", 3), ("mse", 2), 1e-6)
+
+
 def test_attention_llama8b_full(ctx, oracle_tables):
     """The benchmark's workload at full size: 32 query / 8 KV heads, 32768 tokens."""
     c = W.llama8b()
