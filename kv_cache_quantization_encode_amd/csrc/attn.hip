@@ -868,7 +868,7 @@ constexpr int kMWaves = kMThreads / 64;
 constexpr float kWScale = 32768.0f;  // 2^15
 
 template <int G>
-__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) void attn_values_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a) {
     static_assert(G == 8, "rows: 8 heads x (hi, lo)");
     __shared__ float s_M[G], s_invL[G];
     __shared__ int s_any[kMWaves];
@@ -904,12 +904,13 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int ng = wv < nfull ? (nfull - 1 - wv) / kMWaves + 1 : 0;  // whole groups of this wave
     auto gbase = [&](int k) { return t0 + 32 * (wv + kMWaves * min(k, ng - 1)); };
-    // scores of groups k and k+1 alternate between two register sets
-    float4 S[2][2];
-    auto load_scores = [&](int tb, float4 (&sd)[2]) {
-        const float4 *sp = reinterpret_cast<const float4 *>(srow + tb + 8 * kq);
-        sd[0] = sp[0];
-        sd[1] = sp[1];
+    // scores of three consecutive groups rotate through three register sets
+    float4 S[3];
+    // lanes n and n + 8 (the hi and lo rows of head hn) each take four of
+    // the eight tokens 8kq + [0, 8): tokens jo + [0, 4)
+    const int jo = lo_half ? 4 : 0;
+    auto load_scores = [&](int tb, float4 &sd) {
+        sd = *reinterpret_cast<const float4 *>(srow + tb + 8 * kq + jo);
     };
     // code words and norms of a whole group; a group that keeps no token
     // reads the block's first tokens instead (the same cache lines every
@@ -936,7 +937,10 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) nr[i] = h[2 * i] | (h[2 * i + 1] << 16);
     };
-    if (ng > 0) load_scores(gbase(0), S[0]);
+    if (ng > 0) {
+        load_scores(gbase(0), S[0]);
+        load_scores(gbase(1), S[1]);
+    }
     const float c2 = a.tab->levels[1][2], c3 = a.tab->levels[1][3];
     const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
     const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
@@ -974,28 +978,41 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     // weights of head hn for tokens tb + 8kq + j: p = exp(s - M) / L, kept
     // when p >= tau, as this row's fp16 half; returns whether any lane of the
     // wave keeps a token (uniform)
-    auto weights = [&](int tb, const float4 (&sd)[2], uint32_t (&aw)[4], auto whole) -> bool {
-        const float sv[8] = {sd[0].x, sd[0].y, sd[0].z, sd[0].w, sd[1].x, sd[1].y, sd[1].z, sd[1].w};
-        float x[8];
-        bool kj[8], kept = false;
+    auto weights = [&](int tb, const float4 &sd, uint32_t (&aw)[4], auto whole) -> bool {
+        const float sv[4] = {sd.x, sd.y, sd.z, sd.w};
+        float x[4];
+        bool kj[4], kept = false;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             x[j] = fmaf(sv[j], kLog2e, -Ml2);
             kj[j] = x[j] >= keep_x;
-            if constexpr (!decltype(whole)::value) kj[j] = kj[j] && tb + 8 * kq + j < t1;
+            if constexpr (!decltype(whole)::value) kj[j] = kj[j] && tb + 8 * kq + jo + j < t1;
             kept |= kj[j];
         }
         if (__ballot(kept) == 0) return false;
-        float ws[8];
+        float ws[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ws[j] = kj[j] ? fast_exp2(x[j]) * invL : 0.0f;
+        for (int j = 0; j < 4; ++j) ws[j] = kj[j] ? fast_exp2(x[j]) * invL : 0.0f;
+        uint32_t hi[2], lo[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const half2v hi = __builtin_convertvector(float2v{ws[2 * i], ws[2 * i + 1]}, half2v);
-            const half2v lo =
-                __builtin_convertvector(float2v{ws[2 * i] - float(hi[0]), ws[2 * i + 1] - float(hi[1])}, half2v);
-            aw[i] = __builtin_bit_cast(uint32_t, lo_half ? lo : hi);
+        for (int i = 0; i < 2; ++i) {
+            const half2v h = __builtin_convertvector(float2v{ws[2 * i], ws[2 * i + 1]}, half2v);
+            const half2v l =
+                __builtin_convertvector(float2v{ws[2 * i] - float(h[0]), ws[2 * i + 1] - float(h[1])}, half2v);
+            hi[i] = __builtin_bit_cast(uint32_t, h);
+            lo[i] = __builtin_bit_cast(uint32_t, l);
         }
+        // the partner lane (n ^ 8, same DPP row) needs the other half of
+        // these four tokens: hi rows take tokens 4-7's hi halves from their lo
+        // partner, lo rows tokens 0-3's lo halves from their hi partner
+        uint32_t got[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            got[i] = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_half ? hi[i] : lo[i]), 0x128, 0xF, 0xF, false));
+        aw[0] = lo_half ? got[0] : hi[0];
+        aw[1] = lo_half ? got[1] : hi[1];
+        aw[2] = lo_half ? lo[0] : got[0];
+        aw[3] = lo_half ? lo[1] : got[1];
         return true;
     };
     auto products = [&](const uint32_t (&aw)[4], const uint32_t (&c)[8], const uint32_t (&nr)[4]) {
@@ -1017,25 +1034,26 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
                     A, __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[m][p], 0, 0, 0);
             }
     };
-    // software pipeline over this wave's whole groups k = 0 .. ng-1.  Step k
-    // starts the scores of group k+2, forms the weights of group k+1 (scores
-    // issued a step earlier), starts its code words and norms, and runs the
-    // products of group k (code words issued a step earlier); step -1 only
-    // fills the pipeline.  Register sets alternate with the parity of k, so
-    // nothing is copied while its load is outstanding.
+    // software pipeline over this wave's whole groups k = 0 .. ng-1, two
+    // groups deep.  Step k starts the scores of group k+4, forms the weights
+    // of group k+2 (scores issued two steps earlier), starts its code words
+    // and norms, and runs the products of group k (code words issued two
+    // steps earlier); steps -2 and -1 only fill the pipeline.  Three register
+    // sets rotate with k mod 3, so nothing is copied while its load is
+    // outstanding.
     if (ng > 0) {
-        uint32_t aw[2][4], c[2][8], nr[2][4];
-        bool kp[2] = {false, false};
+        uint32_t aw[3][4], c[3][8], nr[3][4];
+        bool kp[3] = {false, false, false};
         // the loop starts with nothing in flight but its own loads (so the
         // compiler's memory waits inside it stay exact): vmcnt(0)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         auto step = [&](int k, auto P) {
-            constexpr int p = decltype(P)::value;
-            load_scores(gbase(k + 2), S[p]);
+            constexpr int p = decltype(P)::value, p1 = (p + 1) % 3, p2 = (p + 2) % 3;
+            load_scores(gbase(k + 4), S[p1]);
             asm volatile("" ::: "memory");
-            const bool more = k + 1 < ng;
-            kp[p ^ 1] = more && weights(gbase(k + 1), S[p ^ 1], aw[p ^ 1], std::true_type{});
-            load_codes(gbase(k + 1), kp[p ^ 1], c[p ^ 1], nr[p ^ 1]);
+            const bool more = k + 2 < ng;
+            kp[p2] = more && weights(gbase(k + 2), S[p2], aw[p2], std::true_type{});
+            load_codes(gbase(k + 2), kp[p2], c[p2], nr[p2]);
             asm volatile("" ::: "memory");
             if (kp[p]) {
                 any = true;
@@ -1049,12 +1067,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
                              "v"(nr[p][2]), "v"(nr[p][3]));
             }
         };
-        // steps run in pairs (the last pair may end with a step past ng,
-        // which only issues its cache-resident loads), so the loop has a
-        // single exit
-        for (int k = -1; k < ng; k += 2) {
+        // steps run in threes (the last ones may lie past ng and only issue
+        // cache-resident loads), so the loop has a single exit
+        for (int k = -2; k < ng; k += 3) {
             step(k, std::integral_constant<int, 1>{});
-            step(k + 1, std::integral_constant<int, 0>{});
+            step(k + 1, std::integral_constant<int, 2>{});
+            step(k + 2, std::integral_constant<int, 0>{});
         }
     }
     if (((t1 - t0) & 31) != 0 && wv == (nfull & (kMWaves - 1))) {
@@ -1141,9 +1159,9 @@ static int launch_passes(const AttnArgs &a, hipStream_t s) {
         // 8 query heads: the kept rows of all heads together are most of the
         // tokens unless attention is very peaked, and the per-row cost of the
         // compacting pass grows with the head count, so the whole range goes
-        // through the matrix cores.  Blocks of vsub tokens, ~1024 blocks in all.
+        // through the matrix cores.  Blocks of vsub tokens, ~512 blocks in all.
         const int64_t rows = int64_t(a.B) * a.Hkv;
-        const int64_t per = (int64_t(a.T) * rows + 1023) / 1024;
+        const int64_t per = (int64_t(a.T) * rows + 511) / 512;
         AttnArgs v = a;
         v.vsub = int(std::min<int64_t>(std::max<int64_t>((per + 255) / 256 * 256, 256), (int64_t(a.T) + 31) / 32 * 32));
         const dim3 vgrid(unsigned((a.T + v.vsub - 1) / v.vsub), unsigned(rows));
