@@ -847,7 +847,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
     }
 }
 
-// ------------------------------------------------- values pass, 2-bit V on MFMA
+// ------------------------------------- values pass on MFMA: 2-bit V and q8 V
 // A symmetric 4-level codebook (c0 = -c3, c1 = -c2) is a sum of two signed
 // constants chosen by the two bits of the code:
 //   c[2 b1 + b0] = a1 (2 b1 - 1) + a0 (2 b0 - 1),  a1 = (c3 + c2) / 2,  a0 = (c3 - c2) / 2.
@@ -863,13 +863,28 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
 // coordinate 8n + m, whose two code bits are bits 2m, 2m + 1 of the 16-bit
 // word n of the token's row.  Every token of a chunk is stepped over; a group
 // in which no head keeps a token is skipped as a whole.
+//
+// q8 V (boundary layers): x = q s_blk with int8 q and one fp16 scale per 32
+// coordinates.  B = q as fp16 (exact: the byte becomes the mantissa of
+// 1024 + (q + 128) through v_perm and an xor, then one packed fp16 subtract
+// of 1152), and the scale goes into A: four A operands per group, the kept
+// weights times the scale of block 0..3, each as hi/lo halves.  Column n of
+// product m is coordinate 4n + (m & 3) + 64 (m >> 2), so product m needs the
+// blocks 2 (m >> 2) and 2 (m >> 2) + 1: two products per m, and lane n keeps
+// the one for its own block (n < 8 or n >= 8).
 constexpr int kMThreads = 256;
 constexpr int kMWaves = kMThreads / 64;
 constexpr float kWScale = 32768.0f;  // 2^15
 
-template <int G>
+template <int G, int VK>
 __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a) {
     static_assert(G == 8, "rows: 8 heads x (hi, lo)");
+    static_assert(VK == TQ_KIND_MSE || VK == TQ_KIND_Q8, "2-bit codebook V or q8 V");
+    constexpr bool Q8 = VK == TQ_KIND_Q8;
+    constexpr int NC = Q8 ? 16 : 8;  // code dwords per lane and group
+    constexpr int NN = Q8 ? 1 : 4;   // norm dwords per lane and group
+    constexpr int NA = Q8 ? 16 : 4;  // A-operand dwords (q8: one operand per block)
+    constexpr int NS = Q8 ? 4 : 1;   // q8 scale pairs (uint2) per lane and group
     __shared__ float s_M[G], s_invL[G];
     __shared__ int s_any[kMWaves];
     __shared__ __attribute__((aligned(16))) float s_acc[kMWaves][G][128];
@@ -894,6 +909,10 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // second operand (bytes 0-3) in bits 0-15, of the first (bytes 4-7) in 16-31
     const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
     const uint16_t *vn = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
+    // q8: dwords n and 16 + n of each 128-byte row (coordinates 4n.. and
+    // 64 + 4n..), and the four fp16 block scales of each token
+    const uint32_t *q8w = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(row) * a.T * 32 + n;
+    const uint2 *q8s = reinterpret_cast<const uint2 *>(a.vnorm) + int64_t(row) * a.T;
 
     // 32-token groups: lane (kq, n) reads the scores of head hn for tokens
     // 8kq + [0, 8) (score rows are padded to 32 tokens, so a group is always
@@ -904,13 +923,19 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int ng = wv < nfull ? (nfull - 1 - wv) / kMWaves + 1 : 0;  // whole groups of this wave
     auto gbase = [&](int k) { return t0 + 32 * (wv + kMWaves * min(k, ng - 1)); };
-    // scores of three consecutive groups rotate through three register sets
+    // scores (and q8 scales) of three consecutive groups rotate through
+    // three register sets
     float4 S[3];
+    uint2 SC[3][NS];
     // lanes n and n + 8 (the hi and lo rows of head hn) each take four of
     // the eight tokens 8kq + [0, 8): tokens jo + [0, 4)
     const int jo = lo_half ? 4 : 0;
-    auto load_scores = [&](int tb, float4 &sd) {
+    auto load_scores = [&](int tb, float4 &sd, uint2 (&sc)[NS]) {
         sd = *reinterpret_cast<const float4 *>(srow + tb + 8 * kq + jo);
+        if constexpr (Q8) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = q8s[min(tb + 8 * kq + jo + j, tmax)];
+        }
     };
     // code words and norms of a whole group; a group that keeps no token
     // reads the block's first tokens instead (the same cache lines every
@@ -918,30 +943,48 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // stay exact
     // (the code words come in as the dword that holds word n; products()
     // picks the half)
-    auto load_codes = [&](int tb, bool real, uint32_t (&c)[8], uint32_t (&nr)[4]) {
+    auto load_codes = [&](int tb, bool real, uint32_t (&c)[NC], uint32_t (&nr)[NN]) {
         const int tk = real ? tb + 8 * kq : t0;
-        const uint32_t *cp = cwd32 + int64_t(tk) * 8;
+        if constexpr (Q8) {
+            const uint32_t *cp = q8w + int64_t(tk) * 32;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = cp[8 * j];
-        __builtin_memcpy(nr, vn + tk, 16);
-    };
-    auto load_tail = [&](int tb, uint32_t (&c)[8], uint32_t (&nr)[4]) {
-        const int tk = tb + 8 * kq;
-        uint32_t h[8];
+            for (int j = 0; j < 8; ++j) {
+                c[2 * j] = cp[32 * j];
+                c[2 * j + 1] = cp[32 * j + 16];
+            }
+        } else {
+            const uint32_t *cp = cwd32 + int64_t(tk) * 8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tj = min(tk + j, tmax);
-            c[j] = cwd32[int64_t(tj) * 8];
-            h[j] = vn[tj];
+            for (int j = 0; j < 8; ++j) c[j] = cp[8 * j];
+            __builtin_memcpy(nr, vn + tk, 16);
         }
+    };
+    auto load_tail = [&](int tb, uint32_t (&c)[NC], uint32_t (&nr)[NN]) {
+        const int tk = tb + 8 * kq;
+        if constexpr (Q8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nr[i] = h[2 * i] | (h[2 * i + 1] << 16);
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t *cp = q8w + int64_t(min(tk + j, tmax)) * 32;
+                c[2 * j] = cp[0];
+                c[2 * j + 1] = cp[16];
+            }
+        } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tj = min(tk + j, tmax);
+                c[j] = cwd32[int64_t(tj) * 8];
+                h[j] = vn[tj];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nr[i] = h[2 * i] | (h[2 * i + 1] << 16);
+        }
     };
     if (ng > 0) {
-        load_scores(gbase(0), S[0]);
-        load_scores(gbase(1), S[1]);
+        load_scores(gbase(0), S[0], SC[0]);
+        load_scores(gbase(1), S[1], SC[1]);
     }
-    const float c2 = a.tab->levels[1][2], c3 = a.tab->levels[1][3];
+    const float c2 = Q8 ? 0.0f : a.tab->levels[1][2], c3 = Q8 ? 0.0f : a.tab->levels[1][3];
     const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
     const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
     asm volatile("" ::: "memory");
@@ -978,7 +1021,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // weights of head hn for tokens tb + 8kq + j: p = exp(s - M) / L, kept
     // when p >= tau, as this row's fp16 half; returns whether any lane of the
     // wave keeps a token (uniform)
-    auto weights = [&](int tb, const float4 &sd, uint32_t (&aw)[4], auto whole) -> bool {
+    auto weights = [&](int tb, const float4 &sd, const uint2 (&sc)[NS], uint32_t (&aw)[NA], auto whole) -> bool {
         const float sv[4] = {sd.x, sd.y, sd.z, sd.w};
         float x[4];
         bool kj[4], kept = false;
@@ -993,29 +1036,70 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
         float ws[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) ws[j] = kj[j] ? fast_exp2(x[j]) * invL : 0.0f;
-        uint32_t hi[2], lo[2];
+        // one A operand per block scale (q8) or a single one (2-bit)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const half2v h = __builtin_convertvector(float2v{ws[2 * i], ws[2 * i + 1]}, half2v);
-            const half2v l =
-                __builtin_convertvector(float2v{ws[2 * i] - float(h[0]), ws[2 * i + 1] - float(h[1])}, half2v);
-            hi[i] = __builtin_bit_cast(uint32_t, h);
-            lo[i] = __builtin_bit_cast(uint32_t, l);
+        for (int blk = 0; blk < NA / 4; ++blk) {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (Q8) {
+                    const uint32_t sp = blk < 2 ? sc[j].x : sc[j].y;
+                    v[j] = ws[j] * h2f((sp >> (16 * (blk & 1))) & 0xFFFFu);
+                } else {
+                    v[j] = ws[j];
+                }
+            }
+            uint32_t hi[2], lo[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const half2v h = __builtin_convertvector(float2v{v[2 * i], v[2 * i + 1]}, half2v);
+                const half2v l =
+                    __builtin_convertvector(float2v{v[2 * i] - float(h[0]), v[2 * i + 1] - float(h[1])}, half2v);
+                hi[i] = __builtin_bit_cast(uint32_t, h);
+                lo[i] = __builtin_bit_cast(uint32_t, l);
+            }
+            // the partner lane (n ^ 8, same DPP row) needs the other half of
+            // these four tokens: hi rows take tokens 4-7's hi halves from
+            // their lo partner, lo rows tokens 0-3's lo halves from their hi
+            // partner
+            uint32_t got[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                got[i] = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_half ? hi[i] : lo[i]), 0x128, 0xF, 0xF, false));
+            aw[4 * blk + 0] = lo_half ? got[0] : hi[0];
+            aw[4 * blk + 1] = lo_half ? got[1] : hi[1];
+            aw[4 * blk + 2] = lo_half ? lo[0] : got[0];
+            aw[4 * blk + 3] = lo_half ? lo[1] : got[1];
         }
-        // the partner lane (n ^ 8, same DPP row) needs the other half of
-        // these four tokens: hi rows take tokens 4-7's hi halves from their lo
-        // partner, lo rows tokens 0-3's lo halves from their hi partner
-        uint32_t got[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            got[i] = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_half ? hi[i] : lo[i]), 0x128, 0xF, 0xF, false));
-        aw[0] = lo_half ? got[0] : hi[0];
-        aw[1] = lo_half ? got[1] : hi[1];
-        aw[2] = lo_half ? lo[0] : got[0];
-        aw[3] = lo_half ? lo[1] : got[1];
         return true;
     };
-    auto products = [&](const uint32_t (&aw)[4], const uint32_t (&c)[8], const uint32_t (&nr)[4]) {
+    auto products = [&](const uint32_t (&aw)[NA], const uint32_t (&c)[NC], const uint32_t (&nr)[NN]) {
+        if constexpr (Q8) {
+            half8 A[4];
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+                A[blk] = __builtin_bit_cast(half8, make_uint4(aw[4 * blk], aw[4 * blk + 1], aw[4 * blk + 2],
+                                                              aw[4 * blk + 3]));
+            const half2v k1152 = half2v{_Float16(1152.0f), _Float16(1152.0f)};
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                // byte m & 3 of dword (m >> 2) of tokens 2i and 2i + 1 as the
+                // low bytes of two fp16 halves 0x64..: 1024 + (q + 128)
+                const int w = m >> 2, by = m & 3;
+                const uint32_t sel = uint32_t(by) | (12u << 8) | (uint32_t(4 + by) << 16) | (12u << 24);
+                uint32_t bw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = __builtin_amdgcn_perm(c[4 * i + 2 + w], c[4 * i + w], sel) ^ 0x64806480u;
+                    bw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, x) - k1152);
+                }
+                const half8 B = __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2 * w + p], B, acc[m][p], 0, 0, 0);
+            }
+            return;
+        }
         const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
         uint32_t cwd[4];
 #pragma unroll
@@ -1029,7 +1113,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 const int sh = 15 - 2 * m - p;
                 uint32_t bw[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) bw[i] = ((cwd[i] << sh) & 0x80008000u) | nr[i];
+                for (int i = 0; i < 4; ++i) bw[i] = ((cwd[i] << sh) & 0x80008000u) | nr[i % NN];
                 acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     A, __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[m][p], 0, 0, 0);
             }
@@ -1042,17 +1126,17 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // sets rotate with k mod 3, so nothing is copied while its load is
     // outstanding.
     if (ng > 0) {
-        uint32_t aw[3][4], c[3][8], nr[3][4];
+        uint32_t aw[3][NA], c[3][NC], nr[3][NN];
         bool kp[3] = {false, false, false};
         // the loop starts with nothing in flight but its own loads (so the
         // compiler's memory waits inside it stay exact): vmcnt(0)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         auto step = [&](int k, auto P) {
             constexpr int p = decltype(P)::value, p1 = (p + 1) % 3, p2 = (p + 2) % 3;
-            load_scores(gbase(k + 4), S[p1]);
+            load_scores(gbase(k + 4), S[p1], SC[p1]);
             asm volatile("" ::: "memory");
             const bool more = k + 2 < ng;
-            kp[p2] = more && weights(gbase(k + 2), S[p2], aw[p2], std::true_type{});
+            kp[p2] = more && weights(gbase(k + 2), S[p2], SC[p2], aw[p2], std::true_type{});
             load_codes(gbase(k + 2), kp[p2], c[p2], nr[p2]);
             asm volatile("" ::: "memory");
             if (kp[p]) {
@@ -1063,8 +1147,12 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 // loads here, so no later reuse of these registers has to wait
                 // for everything in flight
                 asm volatile("" ::"v"(c[p][0]), "v"(c[p][1]), "v"(c[p][2]), "v"(c[p][3]), "v"(c[p][4]),
-                             "v"(c[p][5]), "v"(c[p][6]), "v"(c[p][7]), "v"(nr[p][0]), "v"(nr[p][1]),
-                             "v"(nr[p][2]), "v"(nr[p][3]));
+                             "v"(c[p][5]), "v"(c[p][6]), "v"(c[p][7]), "v"(nr[p][0]), "v"(nr[p][NN - 1]));
+                if constexpr (Q8)
+                    asm volatile("" ::"v"(c[p][8]), "v"(c[p][9]), "v"(c[p][10]), "v"(c[p][11]), "v"(c[p][12]),
+                                 "v"(c[p][13]), "v"(c[p][14]), "v"(c[p][15]));
+                else
+                    asm volatile("" ::"v"(nr[p][1]), "v"(nr[p][2]));
             }
         };
         // steps run in threes (the last ones may lie past ng and only issue
@@ -1077,9 +1165,9 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     }
     if (((t1 - t0) & 31) != 0 && wv == (nfull & (kMWaves - 1))) {
         const int tb = t0 + 32 * nfull;
-        uint32_t aw[4], c[8], nr[4];
-        load_scores(tb, S[0]);
-        if (weights(tb, S[0], aw, std::false_type{})) {
+        uint32_t aw[NA], c[NC], nr[NN];
+        load_scores(tb, S[0], SC[0]);
+        if (weights(tb, S[0], SC[0], aw, std::false_type{})) {
             any = true;
             load_tail(tb, c, nr);
             products(aw, c, nr);
@@ -1088,12 +1176,14 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // lane (kq, n) holds rows 4kq + j, column n of every product: coordinate
     // 8n + m of row 4kq + j is -(a1 X1 + a0 X0) (times 2^-15 / sqrt(d), applied
     // with R^T below); add each head's lo row to its hi row
+    // (q8: the product of this lane's own block, 2^15 sum w s q)
     const float a1 = 0.5f * (c3 + c2), a0 = 0.5f * (c3 - c2);
     float y[8][4];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[m][j] = fmaf(a1, acc[m][1][j], a0 * acc[m][0][j]);
+        for (int j = 0; j < 4; ++j)
+            y[m][j] = Q8 ? (n >= 8 ? acc[m][1][j] : acc[m][0][j]) : fmaf(a1, acc[m][1][j], a0 * acc[m][0][j]);
     // rows 4kq + j and 4(kq + 2) + j are the hi and lo rows of head 4kq + j
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -1107,9 +1197,11 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     if (kq < 2) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float4 *dst = reinterpret_cast<float4 *>(&s_acc[wave][4 * kq + j][8 * n]);
-            dst[0] = make_float4(y[0][j], y[1][j], y[2][j], y[3][j]);
-            dst[1] = make_float4(y[4][j], y[5][j], y[6][j], y[7][j]);
+            float *hrow = &s_acc[wave][4 * kq + j][0];
+            float4 *d0 = reinterpret_cast<float4 *>(hrow + (Q8 ? 4 * n : 8 * n));
+            float4 *d1 = reinterpret_cast<float4 *>(hrow + (Q8 ? 64 + 4 * n : 8 * n + 4));
+            *d0 = make_float4(y[0][j], y[1][j], y[2][j], y[3][j]);
+            *d1 = make_float4(y[4][j], y[5][j], y[6][j], y[7][j]);
         }
     }
     if (lane == 0) s_any[wave] = any ? 1 : 0;
@@ -1117,8 +1209,9 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     bool kept_any = false;
 #pragma unroll
     for (int w = 0; w < kMWaves; ++w) kept_any |= s_any[w] != 0;
-    // the block's share of each head, rotated back (R^T = D H / sqrt(d)) and
-    // added into the output, which the scores pass zeroed
+    // the block's share of each head, rotated back (R^T = D H / sqrt(d); q8
+    // V is not rotated) and added into the output, which the scores pass
+    // zeroed
     if (kept_any) {
         const float sc = -kRsqrtD * kRsqrtD / kWScale;
         for (int g = wave; g < G; g += kMWaves) {
@@ -1127,6 +1220,13 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
             for (int w = 0; w < kMWaves; ++w) {
                 v0 += s_acc[w][g][lane];
                 v1 += s_acc[w][g][lane + 64];
+            }
+            if constexpr (Q8) {
+                float *o = a.out + (head0 + g) * 128;
+                __hip_atomic_fetch_add(o + lane, v0 * (1.0f / kWScale), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(o + lane + 64, v1 * (1.0f / kWScale), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                continue;
             }
             const float s0 = v0 + v1, s1 = v0 - v1;
             v0 = s0;
@@ -1155,7 +1255,7 @@ static int launch_passes(const AttnArgs &a, hipStream_t s) {
                        a.scores);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return int(e);
-    if constexpr (G == 8 && VK == TQ_KIND_MSE && VB == 2) {
+    if constexpr (G == 8 && ((VK == TQ_KIND_MSE && VB == 2) || VK == TQ_KIND_Q8)) {
         // 8 query heads: the kept rows of all heads together are most of the
         // tokens unless attention is very peaked, and the per-row cost of the
         // compacting pass grows with the head count, so the whole range goes
@@ -1165,7 +1265,7 @@ static int launch_passes(const AttnArgs &a, hipStream_t s) {
         AttnArgs v = a;
         v.vsub = int(std::min<int64_t>(std::max<int64_t>((per + 255) / 256 * 256, 256), (int64_t(a.T) + 31) / 32 * 32));
         const dim3 vgrid(unsigned((a.T + v.vsub - 1) / v.vsub), unsigned(rows));
-        hipLaunchKernelGGL((attn_values_mfma_kernel<G>), vgrid, dim3(kMThreads), 0, s, v);
+        hipLaunchKernelGGL((attn_values_mfma_kernel<G, VK>), vgrid, dim3(kMThreads), 0, s, v);
     } else {
         hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(kVThreads), 0, s, a);
     }

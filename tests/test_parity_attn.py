@@ -70,7 +70,7 @@ def test_attention_single_token_and_seq_lens(ctx, oracle_tables):
 
 
 def test_attention_eight_heads_ragged_batch(ctx, oracle_tables):
-    """8 query heads per KV head with 2-bit V (the matrix-core values pass):
+    """8 query heads per KV head with 2-bit or q8 V (the matrix-core values pass):
     a batch of 4 whose lengths give a partial last 32-token group, a
     one-token and an empty sequence, at tau 0, 1e-6 and 0.5; then a peaked
     (needle) batch where most 32-token groups keep nothing."""
@@ -78,6 +78,10 @@ def test_attention_eight_heads_ragged_batch(ctx, oracle_tables):
     lens = np.array([1100, 33, 1, 0], np.int32)
     for tau in (0.0, 1e-6, 0.5):
         got, _, _ = _run(ctx, oracle_tables, c, ("prod", 2), ("mse", 2), tau, seq_lens=lens)
+        assert np.all(got[3] == 0.0)
+    # q8 V (boundary layers) takes the same pass with the block scales in A
+    for kf in (("q8", 8), ("prod", 2)):
+        got, _, _ = _run(ctx, oracle_tables, c, kf, ("q8", 8), 1e-6, seq_lens=lens)
         assert np.all(got[3] == 0.0)
     n = W.needle(B=2, T=2048, Hq=16, Hkv=2)
     _run(ctx, oracle_tables, n, ("prod", 3), ("mse", 2), 1e-6)
