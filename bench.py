@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn GB/s (% of HBM peak) over turbo KV; encode Mtokens/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the MI355X
 N_COPIES = 8
 LAG = 4
 KERNEL_SOURCES = ["encode.hip", "attn.hip", "device_common.h"]
@@ -76,9 +77,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
-    were taken on the current kernel sources."""
+def load_profile(kernel: str, section: str = "kernels"):
+    """Per-launch figures from committed rocprofv3 --pmc summaries (HBM bytes
+    under "kernels", MFMA utilisation under "mfma"), if they were taken on the
+    current kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic_llama8b.json")
     if not os.path.exists(p):
         return None
@@ -86,7 +88,7 @@ def load_traffic(kernel: str):
         t = json.load(f)
     if t.get("source_hash") != source_hash():
         return None
-    return t.get("kernels", {}).get(kernel)
+    return t.get(section, {}).get(kernel)
 
 
 def cpu_baseline(tokens: int):
@@ -480,9 +482,17 @@ def main():
     def roof(name):
         t, by = kernels[name]
         ach = by / t / 1e9
-        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(name), "kernel": name,
-                "avg_us": round(t * 1e6, 2), "alg_bytes_per_launch": by}
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_profile(name), "kernel": name,
+             "avg_us": round(t * 1e6, 2), "alg_bytes_per_launch": by}
+        mf = load_profile(name, "mfma")
+        if mf and mf.get("flops_per_launch"):
+            # matrix-core side of the same kernel: busy share from the counters,
+            # fp16 MFMA rate from the counted flops and the live duration
+            r["mfma"] = {"util": round(mf["util_pct"] / 100.0, 3),
+                         "achieved_tflops": round(mf["flops_per_launch"] / t / 1e12, 1),
+                         "peak_tflops": MFMA_F16_PEAK_TFLOPS}
+        return r
 
     res = {
         "metric": METRIC,
