@@ -1098,25 +1098,36 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 for (int p = 0; p < 2; ++p)
                     acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2 * w + p], B, acc[m][p], 0, 0, 0);
             }
-            return;
+        } else {
+            const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+            uint32_t cwd[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cwd[i] = __builtin_amdgcn_perm(c[2 * i + 1], c[2 * i], half_sel);
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    // bit p of coordinate 8n + m moved to the fp16 sign bit of
+                    // both token halves, over the (positive) norms
+                    const int sh = 15 - 2 * m - p;
+                    uint32_t bw[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bw[i] = ((cwd[i] << sh) & 0x80008000u) | nr[i];
+                    acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A, __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[m][p], 0, 0, 0);
+                }
         }
-        const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
-        uint32_t cwd[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cwd[i] = __builtin_amdgcn_perm(c[2 * i + 1], c[2 * i], half_sel);
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                // bit p of coordinate 8n + m moved to the fp16 sign bit of
-                // both token halves, over the (positive) norms
-                const int sh = 15 - 2 * m - p;
-                uint32_t bw[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) bw[i] = ((cwd[i] << sh) & 0x80008000u) | nr[i % NN];
-                acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    A, __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[m][p], 0, 0, 0);
-            }
+    };
+    // a group that keeps no token still takes delivery of its (cache-resident)
+    // loads, so that no later reuse of these registers has to wait for
+    // everything in flight
+    auto take = [&](const uint32_t (&c)[NC], const uint32_t (&nr)[NN]) {
+        asm volatile("" ::"v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(c[4]), "v"(c[5]), "v"(c[6]), "v"(c[7]));
+        if constexpr (Q8)
+            asm volatile("" ::"v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]), "v"(c[14]),
+                         "v"(c[15]));
+        else
+            asm volatile("" ::"v"(nr[0]), "v"(nr[1]), "v"(nr[2]), "v"(nr[3]));
     };
     // software pipeline over this wave's whole groups k = 0 .. ng-1, two
     // groups deep.  Step k starts the scores of group k+4, forms the weights
@@ -1143,16 +1154,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 any = true;
                 products(aw[p], c[p], nr[p]);
             } else {
-                // a skipped group still takes delivery of its (cache-resident)
-                // loads here, so no later reuse of these registers has to wait
-                // for everything in flight
-                asm volatile("" ::"v"(c[p][0]), "v"(c[p][1]), "v"(c[p][2]), "v"(c[p][3]), "v"(c[p][4]),
-                             "v"(c[p][5]), "v"(c[p][6]), "v"(c[p][7]), "v"(nr[p][0]), "v"(nr[p][NN - 1]));
-                if constexpr (Q8)
-                    asm volatile("" ::"v"(c[p][8]), "v"(c[p][9]), "v"(c[p][10]), "v"(c[p][11]), "v"(c[p][12]),
-                                 "v"(c[p][13]), "v"(c[p][14]), "v"(c[p][15]));
-                else
-                    asm volatile("" ::"v"(nr[p][1]), "v"(nr[p][2]));
+                take(c[p], nr[p]);
             }
         };
         // steps run in threes (the last ones may lie past ng and only issue
@@ -1222,24 +1224,22 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 v1 += s_acc[w][g][lane + 64];
             }
             if constexpr (Q8) {
-                float *o = a.out + (head0 + g) * 128;
-                __hip_atomic_fetch_add(o + lane, v0 * (1.0f / kWScale), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_add(o + lane + 64, v1 * (1.0f / kWScale), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                continue;
-            }
-            const float s0 = v0 + v1, s1 = v0 - v1;
-            v0 = s0;
-            v1 = s1;
+                v0 *= 1.0f / kWScale;
+                v1 *= 1.0f / kWScale;
+            } else {
+                const float s0 = v0 + v1, s1 = v0 - v1;
+                v0 = s0;
+                v1 = s1;
 #pragma unroll
-            for (int s = 1; s < 64; s <<= 1) {
-                const float sg = (lane & s) ? -1.0f : 1.0f;
-                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-                v0 = fmaf(sg, v0, p0);
-                v1 = fmaf(sg, v1, p1);
+                for (int s = 1; s < 64; s <<= 1) {
+                    const float sg = (lane & s) ? -1.0f : 1.0f;
+                    const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+                    v0 = fmaf(sg, v0, p0);
+                    v1 = fmaf(sg, v1, p1);
+                }
+                v0 *= a.tab->signs[lane] * sc;
+                v1 *= a.tab->signs[lane + 64] * sc;
             }
-            v0 *= a.tab->signs[lane] * sc;
-            v1 *= a.tab->signs[lane + 64] * sc;
             float *o = a.out + (head0 + g) * 128;
             __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
