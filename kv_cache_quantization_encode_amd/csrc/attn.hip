@@ -99,6 +99,45 @@ __device__ __forceinline__ float quad_max(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// The value of lane l ^ S (S = 1 .. 32) without LDS traffic: DPP quad
+// permutes (1, 2) and row rotate (8), a bit-mode swizzle (4), and the
+// permlane swaps (16, 32), whose pair holds both halves of the exchange.
+template <int S>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+    if constexpr (S == 1) {
+        return dpp_mov<0xB1>(x);
+    } else if constexpr (S == 2) {
+        return dpp_mov<0x4E>(x);
+    } else if constexpr (S == 4) {
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));  // and 31, xor 4
+    } else if constexpr (S == 8) {
+        return dpp_mov<0x128>(x);  // rotate a row of 16 by 8
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    } else {
+        static_assert(S == 32, "lane bit");
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    }
+}
+
+// Unnormalised 128-point Walsh-Hadamard transform of the coordinates held
+// as v0 = coordinate lane, v1 = coordinate lane + 64 (bit 6 in-lane, bits
+// 0..5 across lanes).
+__device__ __forceinline__ void fwht128_lanes(float &v0, float &v1, int lane) {
+    const float s0 = v0 + v1, s1 = v0 - v1;
+    v0 = s0;
+    v1 = s1;
+    Unroll<6>::run([&](auto I) {
+        constexpr int S = 1 << decltype(I)::value;
+        const float sg = (lane & S) ? -1.0f : 1.0f;
+        const float p0 = lane_xor<S>(v0, lane), p1 = lane_xor<S>(v1, lane);
+        v0 = fmaf(sg, v0, p0);
+        v1 = fmaf(sg, v1, p1);
+    });
+}
+
 // ------------------------------------------------------------ query operands
 // The MFMA A operands of the scores pass hold each query twice: row h < G is
 // the fp16 hi half and row G + h the fp16 lo half of head h (rows >= 2G are
@@ -159,17 +198,7 @@ __device__ __forceinline__ void build_query_rows(const QueryLoads<G, PROJ> &ql, 
         if (a.k_rotated) {
             v0 *= ql.sg0;
             v1 *= ql.sg1;
-            // H over coordinate bit 6 in-lane, bits 0..5 across lanes
-            const float s0 = v0 + v1, s1 = v0 - v1;
-            v0 = s0;
-            v1 = s1;
-#pragma unroll
-            for (int s = 1; s < 64; s <<= 1) {
-                const float sg = (lane & s) ? -1.0f : 1.0f;
-                const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-                v0 = fmaf(sg, v0, p0);
-                v1 = fmaf(sg, v1, p1);
-            }
+            fwht128_lanes(v0, v1, lane);
             v0 *= kRsqrtD;
             v1 *= kRsqrtD;
         }
@@ -827,16 +856,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
                 v1 += s_acc[w][g][lane + 64];
             }
             if (a.v_rotated) {
-                const float s0 = v0 + v1, s1 = v0 - v1;
-                v0 = s0;
-                v1 = s1;
-#pragma unroll
-                for (int s = 1; s < 64; s <<= 1) {
-                    const float sg = (lane & s) ? -1.0f : 1.0f;
-                    const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-                    v0 = fmaf(sg, v0, p0);
-                    v1 = fmaf(sg, v1, p1);
-                }
+                fwht128_lanes(v0, v1, lane);
                 v0 *= a.tab->signs[lane] * kRsqrtD;
                 v1 *= a.tab->signs[lane + 64] * kRsqrtD;
             }
@@ -1227,16 +1247,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 v0 *= 1.0f / kWScale;
                 v1 *= 1.0f / kWScale;
             } else {
-                const float s0 = v0 + v1, s1 = v0 - v1;
-                v0 = s0;
-                v1 = s1;
-#pragma unroll
-                for (int s = 1; s < 64; s <<= 1) {
-                    const float sg = (lane & s) ? -1.0f : 1.0f;
-                    const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-                    v0 = fmaf(sg, v0, p0);
-                    v1 = fmaf(sg, v1, p1);
-                }
+                fwht128_lanes(v0, v1, lane);
                 v0 *= a.tab->signs[lane] * sc;
                 v1 *= a.tab->signs[lane + 64] * sc;
             }
