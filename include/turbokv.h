@@ -114,6 +114,23 @@ tq_status tq_packed_layout(tq_format f, int head_dim, int64_t n_vec, tq_planes_d
 tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, int64_t n_vec,
                        tq_format kf, tq_format vf, void *k_packed, void *v_packed, void *stream);
 
+/* Append the new token of each sequence to a packed cache during decode: the
+ * per-token encode of [QPQ] Stage 1 and Stage 2 applied to one row per
+ * (sequence, KV head), written in place into a cache laid out for
+ * n_cache = B*Hkv*T_cap rows in [B, Hkv, T_cap] order (the layout that
+ * tq_attn_decode reads with T = T_cap).
+ * k_new_f16, v_new_f16: device [B, Hkv, d] fp16 (either may be NULL to skip
+ * it); pos: device int32 [B], the cache position of sequence b's new token;
+ * k_packed, v_packed: device, tq_packed_layout(kf|vf, d, n_cache) each,
+ * 256-byte aligned.  Row (b, h) is encoded exactly as tq_encode_kv encodes
+ * it and lands in cache row (b*Hkv + h)*T_cap + pos[b]; a sequence whose pos
+ * is outside [0, T_cap) gets nothing written, and every other row of the
+ * cache is left untouched.  Order this call before a tq_attn_decode that
+ * should see the new token (same stream, seq_lens[b] = pos[b] + 1). */
+tq_status tq_append_kv(const tq_ctx *ctx, const void *k_new_f16, const void *v_new_f16, int B, int Hkv,
+                       int T_cap, const int32_t *pos, tq_format kf, tq_format vf, void *k_packed,
+                       void *v_packed, void *stream);
+
 /* Reconstruct fp16 rows from one packed tensor: MSE -> n R^T c[idx]/sqrt(d);
  * PROD -> R^T (n c[idx]/sqrt(d) + sqrt(pi/2)/m * gamma * S^T (2 bit - 1));
  * Q8 -> int8 * block scale.  packed: device; out_f16: device [n_vec, d]. */

@@ -26,7 +26,8 @@ SOURCES = ["tables.cpp", "api.cpp", "encode.hip", "dequant.hip", "attn.hip", "mi
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form",
-          "-Wall", "-Wno-unused-function", "-I" + os.path.join(HERE, "..", "include")]
+          "-Wall", "-Werror=shadow", "-Werror=uninitialized", "-Wno-unused-function",
+          "-I" + os.path.join(HERE, "..", "include")]
 
 
 def _hipcc() -> str:

@@ -191,6 +191,30 @@ tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, 
     return TQ_OK;
 }
 
+tq_status tq_append_kv(const tq_ctx *ctx, const void *k_new_f16, const void *v_new_f16, int B, int Hkv,
+                       int T_cap, const int32_t *pos, tq_format kf, tq_format vf, void *k_packed,
+                       void *v_packed, void *stream) {
+    if (!ctx || !pos || B < 1 || Hkv < 1 || T_cap < 1) return TQ_ERR_INVALID_ARG;
+    if (!k_new_f16 && !v_new_f16) return TQ_ERR_INVALID_ARG;
+    if (!aligned(pos, 4)) return TQ_ERR_INVALID_ARG;
+    const int64_t n_cache = int64_t(B) * Hkv * T_cap;
+    if (n_cache > kMaxRows) return TQ_ERR_UNSUPPORTED;
+    tq_planes_desc kl{}, vl{};
+    if (k_new_f16) {
+        if (!k_packed || !aligned(k_new_f16, 16) || !aligned(k_packed, 256)) return TQ_ERR_INVALID_ARG;
+        if (!plane_layout(kf, ctx->head_dim, n_cache, &kl)) return TQ_ERR_INVALID_ARG;
+    }
+    if (v_new_f16) {
+        if (!v_packed || !aligned(v_new_f16, 16) || !aligned(v_packed, 256)) return TQ_ERR_INVALID_ARG;
+        if (!plane_layout(vf, ctx->head_dim, n_cache, &vl)) return TQ_ERR_INVALID_ARG;
+    }
+    if (k_new_f16 && launch_append(ctx->dev, k_new_f16, B, Hkv, T_cap, pos, kf, k_packed, kl, stream) != 0)
+        return TQ_ERR_HIP;
+    if (v_new_f16 && launch_append(ctx->dev, v_new_f16, B, Hkv, T_cap, pos, vf, v_packed, vl, stream) != 0)
+        return TQ_ERR_HIP;
+    return TQ_OK;
+}
+
 tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64_t n_vec,
                        void *out_f16, void *stream) {
     if (!ctx || !packed || !out_f16 || n_vec < 0) return TQ_ERR_INVALID_ARG;

@@ -51,12 +51,33 @@ __device__ __forceinline__ uint32_t quantise(float z, const float *bnd, const fl
     }
 }
 
-template <int BITS, bool PROD>
+// Destination rows of an append: input row r = b*hkv + h (one new token per
+// sequence and KV head) goes to cache row r*tcap + pos[b]; a position outside
+// [0, tcap) writes nothing.  Without APPEND the destination is the input row.
+struct RowMap {
+    const int32_t *pos;
+    int hkv, tcap;
+};
+
+template <bool APPEND>
+__device__ __forceinline__ int dest_row(const RowMap &m, int tok, bool &valid) {
+    if constexpr (!APPEND) {
+        return tok;
+    } else {
+        if (!valid) return 0;
+        const int p = m.pos[tok / m.hkv];
+        valid = p >= 0 && p < m.tcap;
+        return valid ? tok * m.tcap + p : 0;
+    }
+}
+
+template <int BITS, bool PROD, bool APPEND>
 __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restrict__ tab,
                                                         const uint16_t *__restrict__ x, int64_t n_vec,
                                                         uint8_t *__restrict__ idx_plane,
                                                         uint8_t *__restrict__ sign_plane,
-                                                        uint8_t *__restrict__ norm_plane, int64_t n_tiles) {
+                                                        uint8_t *__restrict__ norm_plane, int64_t n_tiles,
+                                                        RowMap map) {
     __shared__ float s_levels[16];
     __shared__ __attribute__((aligned(16))) QBucket s_lut[kBuckets];
     __shared__ half8 s_frag[PROD ? 32 * 64 : 1];
@@ -133,7 +154,8 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
 
     for (int tile = int(blockIdx.x) * 4 + wave; tile < ntl; tile += stride) {
         const int tok = tile * 16 + t;
-        const bool valid = tok < nv;
+        bool valid = tok < nv;
+        const int dst = dest_row<APPEND>(map, tok, valid);
         load_rows(min(tile + stride, ntl - 1), xn);
         // n^2: packed fp16 products, fp32 accumulation, then over the 4 lanes
         float ss = 0.0f;
@@ -203,13 +225,13 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
             asm volatile("" : "+v"(xb[s]));
         }
         if (valid) {
-            uint32_t *dst = reinterpret_cast<uint32_t *>(idx_plane + size_t(tok) * (16 * BITS) + q * (4 * BITS));
+            uint32_t *out = reinterpret_cast<uint32_t *>(idx_plane + size_t(dst) * (16 * BITS) + q * (4 * BITS));
 #pragma unroll
-            for (int i = 0; i < BITS; ++i) dst[i] = packed[i];
+            for (int i = 0; i < BITS; ++i) out[i] = packed[i];
         }
         if constexpr (!PROD) {
             if (valid && q == 0)
-                reinterpret_cast<uint16_t *>(norm_plane)[tok] = uint16_t(f2h(n));
+                reinterpret_cast<uint16_t *>(norm_plane)[dst] = uint16_t(f2h(n));
         } else {
             se = quad_sum(se);
             const float gamma = n * sqrtf(se) * (kInvSqrtD / 256.0f);
@@ -242,22 +264,27 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
                 for (int j = 3; j >= 0; --j) neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(acc[mb][j]), 31);
             const uint32_t bits = se > 0.0f ? ~neg : 0u;
             if (valid) {
-                reinterpret_cast<uint32_t *>(sign_plane + size_t(tok) * 16)[q] = bits;
+                reinterpret_cast<uint32_t *>(sign_plane + size_t(dst) * 16)[q] = bits;
                 if (q == 0)
-                    reinterpret_cast<uint32_t *>(norm_plane)[tok] = f2h(n) | (f2h(gamma) << 16);
+                    reinterpret_cast<uint32_t *>(norm_plane)[dst] = f2h(n) | (f2h(gamma) << 16);
             }
         }
     }
 }
 
-// q8 boundary blocks: lane l owns token l&15, block (l>>4) of 32 elements.
+// q8 boundary blocks: four consecutive lanes share a token, lane l taking
+// block (l & 3) of 32 elements.
+template <bool APPEND>
 __global__ __launch_bounds__(256) void encode_q8_kernel(const uint16_t *__restrict__ x, int64_t n_vec,
                                                         int8_t *__restrict__ qplane,
-                                                        uint16_t *__restrict__ scale_plane) {
+                                                        uint16_t *__restrict__ scale_plane, RowMap map) {
     const int64_t gl = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t tok = gl >> 2;
     const int blk = int(gl & 3);
     if (tok >= n_vec) return;
+    bool valid = true;
+    const int64_t dst = dest_row<APPEND>(map, int(tok), valid);
+    if (!valid) return;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + tok * kHeadDim + 32 * blk);
     float v[32];
     float amax = 0.0f;
@@ -285,54 +312,66 @@ __global__ __launch_bounds__(256) void encode_q8_kernel(const uint16_t *__restri
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         out[j >> 2] |= (uint32_t(int32_t(r)) & 0xFFu) << (8 * (j & 3));
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(qplane + tok * kHeadDim + 32 * blk);
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-    scale_plane[tok * 4 + blk] = uint16_t(sbits);
+    uint4 *qd = reinterpret_cast<uint4 *>(qplane + dst * kHeadDim + 32 * blk);
+    qd[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    qd[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    scale_plane[dst * 4 + blk] = uint16_t(sbits);
 }
 
-template <int BITS, bool PROD>
+template <int BITS, bool PROD, bool APPEND>
 static int launch_tq(const DevTables *tab, const uint16_t *x, int64_t n_vec, uint8_t *base,
-                     const tq_planes_desc &lay, hipStream_t s) {
+                     const tq_planes_desc &lay, const RowMap &map, hipStream_t s) {
     const int64_t n_tiles = (n_vec + 15) / 16;
     // persistent blocks amortise the 32 KB of S fragments (K) in LDS: as many
     // as are resident at once, each wave striding over the tiles
     static int cache[kMaxDevices];
-    const int64_t blocks = persistent_grid(n_tiles, resident_blocks(encode_tq_kernel<BITS, PROD>, 256, cache));
-    hipLaunchKernelGGL((encode_tq_kernel<BITS, PROD>), dim3(unsigned(blocks)), dim3(256), 0, s, tab, x,
+    const int64_t blocks =
+        persistent_grid(n_tiles, resident_blocks(encode_tq_kernel<BITS, PROD, APPEND>, 256, cache));
+    hipLaunchKernelGGL((encode_tq_kernel<BITS, PROD, APPEND>), dim3(unsigned(blocks)), dim3(256), 0, s, tab, x,
                        n_vec, base + lay.idx_offset, PROD ? base + lay.sign_offset : nullptr,
-                       base + lay.norm_offset, n_tiles);
+                       base + lay.norm_offset, n_tiles, map);
     return int(hipGetLastError());
 }
 
-int launch_encode(const DevTables *tab, const void *xv, int64_t n_vec, tq_format f, void *packed,
-                  const tq_planes_desc &lay, void *stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint16_t *x = static_cast<const uint16_t *>(xv);
-    uint8_t *base = static_cast<uint8_t *>(packed);
+template <bool APPEND>
+static int launch_format(const DevTables *tab, const uint16_t *x, int64_t n_vec, tq_format f, uint8_t *base,
+                         const tq_planes_desc &lay, const RowMap &map, hipStream_t s) {
     if (f.kind == TQ_KIND_Q8) {
         const int64_t threads = n_vec * 4;
         const int64_t blocks = (threads + 255) / 256;
-        hipLaunchKernelGGL(encode_q8_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, x, n_vec,
+        hipLaunchKernelGGL(encode_q8_kernel<APPEND>, dim3(unsigned(blocks)), dim3(256), 0, s, x, n_vec,
                            reinterpret_cast<int8_t *>(base + lay.idx_offset),
-                           reinterpret_cast<uint16_t *>(base + lay.norm_offset));
+                           reinterpret_cast<uint16_t *>(base + lay.norm_offset), map);
         return int(hipGetLastError());
     }
     if (f.kind == TQ_KIND_PROD) {
         switch (f.bits) {
-            case 1: return launch_tq<1, true>(tab, x, n_vec, base, lay, s);
-            case 2: return launch_tq<2, true>(tab, x, n_vec, base, lay, s);
-            case 3: return launch_tq<3, true>(tab, x, n_vec, base, lay, s);
+            case 1: return launch_tq<1, true, APPEND>(tab, x, n_vec, base, lay, map, s);
+            case 2: return launch_tq<2, true, APPEND>(tab, x, n_vec, base, lay, map, s);
+            case 3: return launch_tq<3, true, APPEND>(tab, x, n_vec, base, lay, map, s);
         }
     } else {
         switch (f.bits) {
-            case 1: return launch_tq<1, false>(tab, x, n_vec, base, lay, s);
-            case 2: return launch_tq<2, false>(tab, x, n_vec, base, lay, s);
-            case 3: return launch_tq<3, false>(tab, x, n_vec, base, lay, s);
-            case 4: return launch_tq<4, false>(tab, x, n_vec, base, lay, s);
+            case 1: return launch_tq<1, false, APPEND>(tab, x, n_vec, base, lay, map, s);
+            case 2: return launch_tq<2, false, APPEND>(tab, x, n_vec, base, lay, map, s);
+            case 3: return launch_tq<3, false, APPEND>(tab, x, n_vec, base, lay, map, s);
+            case 4: return launch_tq<4, false, APPEND>(tab, x, n_vec, base, lay, map, s);
         }
     }
     return int(hipErrorInvalidValue);
+}
+
+int launch_encode(const DevTables *tab, const void *xv, int64_t n_vec, tq_format f, void *packed,
+                  const tq_planes_desc &lay, void *stream) {
+    return launch_format<false>(tab, static_cast<const uint16_t *>(xv), n_vec, f, static_cast<uint8_t *>(packed),
+                                lay, RowMap{nullptr, 1, 1}, static_cast<hipStream_t>(stream));
+}
+
+int launch_append(const DevTables *tab, const void *xv, int B, int hkv, int tcap, const int32_t *pos,
+                  tq_format f, void *packed, const tq_planes_desc &lay, void *stream) {
+    return launch_format<true>(tab, static_cast<const uint16_t *>(xv), int64_t(B) * hkv, f,
+                               static_cast<uint8_t *>(packed), lay, RowMap{pos, hkv, tcap},
+                               static_cast<hipStream_t>(stream));
 }
 
 }  // namespace tq

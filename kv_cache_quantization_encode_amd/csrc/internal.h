@@ -57,6 +57,8 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
 // Kernel launchers (HIP translation units).  All return a hipError_t as int.
 int launch_encode(const DevTables *tab, const void *x, int64_t n_vec, tq_format f, void *packed,
                   const tq_planes_desc &lay, void *stream);
+int launch_append(const DevTables *tab, const void *x, int B, int hkv, int tcap, const int32_t *pos,
+                  tq_format f, void *packed, const tq_planes_desc &lay, void *stream);
 int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t n_vec,
                   const tq_planes_desc &lay, void *out, void *stream);
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,

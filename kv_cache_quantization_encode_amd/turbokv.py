@@ -79,6 +79,7 @@ def load() -> ctypes.CDLL:
     lib.tq_host_tables.argtypes = [i32, i32, u64, vp, vp, vp, vp]
     lib.tq_packed_layout.argtypes = [tq_format, i32, i64, ctypes.POINTER(tq_planes_desc)]
     lib.tq_encode_kv.argtypes = [vp, vp, vp, i64, tq_format, tq_format, vp, vp, vp]
+    lib.tq_append_kv.argtypes = [vp, vp, vp, i32, i32, i32, vp, tq_format, tq_format, vp, vp, vp]
     lib.tq_decode_kv.argtypes = [vp, vp, tq_format, i64, vp, vp]
     lib.tq_attn_decode.argtypes = [vp, vp, vp, vp, tq_format, tq_format, i32, i32, i32, i32, vp,
                                    ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
@@ -89,7 +90,7 @@ def load() -> ctypes.CDLL:
     lib.tq_status_str.argtypes = [i32]
     lib.tq_status_str.restype = ctypes.c_char_p
     for name in ("tq_codebook_init", "tq_ctx_destroy", "tq_host_tables", "tq_packed_layout",
-                 "tq_encode_kv", "tq_decode_kv", "tq_attn_decode", "tq_minmax_quant",
+                 "tq_encode_kv", "tq_append_kv", "tq_decode_kv", "tq_attn_decode", "tq_minmax_quant",
                  "tq_minmax_dequant"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -158,6 +159,12 @@ def tq_packed_layout(f: tq_format, head_dim: int, n_vec: int) -> tq_planes_desc:
 def tq_encode_kv(ctx, k, v, n_vec, kf: tq_format, vf: tq_format, k_packed, v_packed, stream=None) -> None:
     _check(load().tq_encode_kv(ctx, _ptr(k), _ptr(v), n_vec, kf, vf, _ptr(k_packed), _ptr(v_packed),
                                _stream(stream)), "tq_encode_kv")
+
+
+def tq_append_kv(ctx, k_new, v_new, B, Hkv, T_cap, pos, kf: tq_format, vf: tq_format, k_packed, v_packed,
+                 stream=None) -> None:
+    _check(load().tq_append_kv(ctx, _ptr(k_new), _ptr(v_new), B, Hkv, T_cap, _ptr(pos), kf, vf,
+                               _ptr(k_packed), _ptr(v_packed), _stream(stream)), "tq_append_kv")
 
 
 def tq_decode_kv(ctx, packed, f: tq_format, n_vec, out, stream=None) -> None:

@@ -25,7 +25,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "turbokv.h")).read()
     names = sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", hdr)))
-    assert len(names) == 11 and "tq_attn_decode" in names and "tq_status_str" in names
+    assert len(names) == 12 and "tq_attn_decode" in names and "tq_append_kv" in names and "tq_status_str" in names
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -110,6 +110,21 @@ def test_invalid_arguments_are_rejected_on_host(lib):
     assert L.tq_encode_kv(cp, A + 2, A, 16, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG  # misaligned input
     assert L.tq_encode_kv(cp, A, A, 16, f3, v2, A + 16, A, None) == T.TQ_ERR_INVALID_ARG  # planes not 256-aligned
     assert L.tq_encode_kv(cp, A, A, 0, f3, v2, A, A, None) == T.TQ_OK  # nothing to do
+    # append (one new row per sequence and KV head into a [B, Hkv, T_cap] cache)
+    ap = L.tq_append_kv
+    assert ap(None, A, A, 2, 8, 64, A, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 2, 8, 64, None, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG  # no positions
+    assert ap(cp, None, None, 2, 8, 64, A, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 0, 8, 64, A, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 2, 0, 64, A, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 2, 8, 0, A, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 2, 8, 64, A + 2, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG  # misaligned pos
+    assert ap(cp, A + 2, A, 2, 8, 64, A, f3, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 2, 8, 64, A, f3, v2, A + 16, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 2, 8, 64, A, bad, v2, A, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, None, A, 2, 8, 64, A, f3, bad, None, A, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, None, 2, 8, 64, A, f3, v2, None, None, None) == T.TQ_ERR_INVALID_ARG
+    assert ap(cp, A, A, 1 << 20, 8, 1 << 20, A, f3, v2, A, A, None) == T.TQ_ERR_UNSUPPORTED
     # decode
     assert L.tq_decode_kv(cp, None, f3, 16, A, None) == T.TQ_ERR_INVALID_ARG
     assert L.tq_decode_kv(cp, A, bad, 16, A, None) == T.TQ_ERR_INVALID_ARG
