@@ -50,7 +50,7 @@ def parse():
                     help="skip the tiny, min-max, 70B-like full-cache and batched needle measurements")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
-    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle"],
+    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle", "decode_loop"],
                     help="run only this extra measurement and print its JSON (for profiling)")
     return ap.parse_args()
 
@@ -318,6 +318,61 @@ def bench_tiny(TK, ctx, dev, reps=50, warm=10):
             "decode_attn_us": round(t_att * 1e6, 2)}
 
 
+def bench_decode_loop(TK, ctx, dev, reps=10, warm=3):
+    """Decode loop on the llama8b-like layer (32 q / 8 KV heads, 32768-token
+    cache capacity, turbo4 K + 4-bit V, tau 1e-6): one step appends the new
+    token's K and V for the 8 KV heads at position 32767 (tq_append_kv) and
+    then attends over all 32768 tokens.  Eight caches are rotated so that the
+    packed bytes do not stay in the 256 MB MALL; one HIP graph holds eight
+    steps.  K = lognormal(0, 0.5) per (head, channel) x Student-t(3), V and q
+    N(0, 1), drawn on the GPU from a seeded generator."""
+    import torch
+    B, Hq, Hkv, T, copies = 1, 32, 8, 32768, 8
+    n_vec = B * Hkv * T
+    kf, vf, tau = TK.turbo_k(4), TK.mse(4), 1e-6
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(606)
+
+    def student_k(shape):
+        z = torch.randn(shape, generator=gen, device=dev)
+        chi = torch.randn((3,) + tuple(shape), generator=gen, device=dev).pow(2).sum(0)
+        return z / torch.sqrt(chi / 3.0)
+
+    scale = torch.exp(0.5 * torch.randn((Hkv, 1, 128), generator=gen, device=dev))
+    kps, vps = [], []
+    for _ in range(copies):
+        k = (student_k((Hkv, T, 128)) * scale).half().reshape(-1, 128)
+        v = torch.randn((n_vec, 128), generator=gen, device=dev).half()
+        kp, vp = TK.alloc_packed(kf, n_vec), TK.alloc_packed(vf, n_vec)
+        TK.tq_encode_kv(ctx, k, v, n_vec, kf, vf, kp.buf, vp.buf)
+        kps.append(kp)
+        vps.append(vp)
+        del k, v
+    k_new = (student_k((Hkv, 128)) * scale[:, 0]).half().reshape(B, Hkv, 128)
+    v_new = torch.randn((B, Hkv, 128), generator=gen, device=dev).half()
+    q = torch.randn((B, Hq, 128), generator=gen, device=dev).half()
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+    lens = pos + 1
+    ws, wsb = TK.alloc_workspace(B, Hq, Hkv, T, kf, vf)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def appends():
+        for c in range(copies):
+            TK.tq_append_kv(ctx, k_new, v_new, B, Hkv, T, pos, kf, vf, kps[c].buf, vps[c].buf)
+
+    def steps():
+        for c in range(copies):
+            TK.tq_append_kv(ctx, k_new, v_new, B, Hkv, T, pos, kf, vf, kps[c].buf, vps[c].buf)
+            TK.tq_attn_decode(ctx, q, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T, lens, tau, out, ws, wsb)
+
+    t_app = graph_time(appends, reps, warm, None) / copies
+    t_step = graph_time(steps, reps, warm, None) / copies
+    return {"workload": "decode loop, llama8b-like layer: append 1 token (K+V, 8 KV heads) then attend over "
+                        "32768 tokens; turbo4 K + 4-bit V, tau 1e-6",
+            "append_us": round(t_app * 1e6, 2), "step_us": round(t_step * 1e6, 2)}
+
+
 def bench_minmax(TK, dev, reps=10, warm=3):
     """Per-group asymmetric min-max baseline: K and V tensors of 32 layers x
     8 KV heads x 4096 tokens x 128 (2 x 134M fp16 elements), N(0,1) times a
@@ -394,7 +449,8 @@ def main():
             r = bench_minmax(TK, dev)
         else:
             ctx1 = TK.tq_codebook_init(128, 128, 42)
-            fn = {"tiny": bench_tiny, "decode_70b": bench_70b, "decode_needle": bench_needle}[args.only]
+            fn = {"tiny": bench_tiny, "decode_70b": bench_70b, "decode_needle": bench_needle,
+                  "decode_loop": bench_decode_loop}[args.only]
             r = fn(TK, ctx1, dev, reps=5, warm=2)
         print(json.dumps({args.only: r}), flush=True)
         return
@@ -528,6 +584,7 @@ def main():
         res["minmax"] = bench_minmax(TK, dev)
         res["decode_70b"] = bench_70b(TK, ctx, dev)
         res["decode_needle"] = bench_needle(TK, ctx, dev)
+        res["decode_loop"] = bench_decode_loop(TK, ctx, dev)
     TK.tq_ctx_destroy(ctx)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
