@@ -123,3 +123,14 @@ def test_attention_70b_full_layer_sampled(ctx, oracle_tables, layer):
     sel = np.stack([got[0, h * g:(h + 1) * g] for h in heads])
     err = np.max(np.abs(sel - ref))
     assert err <= G.ATTN_ATOL, f"max abs error {err:.3g}"
+
+
+def test_attention_long_chunks_ragged_batch(ctx, oracle_tables):
+    """A grid of more than one block per CU takes longer chunks (8 sequences x
+    8 KV heads x 3000 tokens: 4 chunks of 768 tokens, the last one ragged);
+    the lengths end sequences inside, at and just past chunk edges, and leave
+    whole chunks empty."""
+    c = W.llama8b(T=3000, B=8)
+    lens = np.array([3000, 1, 0, 769, 2304, 2305, 1500, 2999], np.int32)
+    got, _, _ = _run(ctx, oracle_tables, c, ("prod", 3), ("mse", 4), 1e-6, seq_lens=lens)
+    assert np.all(got[2] == 0.0)
