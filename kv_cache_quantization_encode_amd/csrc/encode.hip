@@ -191,27 +191,56 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
         for (int i = 0; i < BITS; ++i) packed[i] = 0;
         // K: residual e = z - c[idx], scaled by 2^8 so that its fp16 lo half
         // stays normal (levels in s_levels / s_lut are pre-scaled by 2^8 for
-        // K), split into the hi/lo MFMA operands a pair at a time
-        uint32_t bhi[PROD ? 16 : 1], blo[PROD ? 16 : 1];
+        // K), split into the hi/lo MFMA operands a pair at a time.  The
+        // coordinates of QJL k-step s (32q + 8s + [0,8), i.e. yb[2s], yb[2s+1])
+        // are quantised together and their 16 products issued right away, so
+        // only one k-step's operands are live and the matrix work overlaps the
+        // quantiser of the next k-step.
         float se = 0.0f;  // sum of (2^8 e)^2
-        float es_prev = 0.0f;
-        Unroll<32>::run([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            const float z = yb[j >> 2][j & 3] * inv;  // z = H(Dx)/n = sqrt(d) R x / n
-            float zhat;
-            const uint32_t c = quantise<BITS>(z, bnd, s_levels, s_lut, zhat);
-            put_code<BITS, j>(packed, c);
+        floatx4 acc[PROD ? 8 : 1];
+#pragma unroll
+        for (int mb = 0; mb < (PROD ? 8 : 1); ++mb) acc[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        int fl = lane;
+        asm volatile("" : "+v"(fl));
+        Unroll<4>::run([&](auto S) {
+            constexpr int s = decltype(S)::value;
+            // this k-step's S fragments are requested first and land while its
+            // coordinates are quantised; nothing moves across k-steps
+            __builtin_amdgcn_sched_barrier(0);
+            half8 sa[PROD ? 8 : 1];
             if constexpr (PROD) {
-                const float es = fmaf(z, 256.0f, -zhat);
-                se = fmaf(es, es, se);
-                if constexpr (j & 1) {
-                    const half2v hi = __builtin_convertvector(float2v{es_prev, es}, half2v);
-                    const half2v lo = __builtin_convertvector(
-                        float2v{es_prev - float(hi[0]), es - float(hi[1])}, half2v);
-                    bhi[j >> 1] = __builtin_bit_cast(uint32_t, hi);
-                    blo[j >> 1] = __builtin_bit_cast(uint32_t, lo);
-                } else {
-                    es_prev = es;
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) sa[mb] = s_frag[(mb * 4 + s) * 64 + fl];
+            }
+            uint32_t bhi[4], blo[4];
+            float es_prev = 0.0f;
+            Unroll<8>::run([&](auto J) {
+                constexpr int j = 8 * s + decltype(J)::value;
+                const float z = yb[j >> 2][j & 3] * inv;  // z = H(Dx)/n = sqrt(d) R x / n
+                float zhat;
+                const uint32_t c = quantise<BITS>(z, bnd, s_levels, s_lut, zhat);
+                put_code<BITS, j>(packed, c);
+                if constexpr (PROD) {
+                    const float es = fmaf(z, 256.0f, -zhat);
+                    se = fmaf(es, es, se);
+                    if constexpr (j & 1) {
+                        const half2v hi = __builtin_convertvector(float2v{es_prev, es}, half2v);
+                        const half2v lo = __builtin_convertvector(
+                            float2v{es_prev - float(hi[0]), es - float(hi[1])}, half2v);
+                        bhi[(j >> 1) & 3] = __builtin_bit_cast(uint32_t, hi);
+                        blo[(j >> 1) & 3] = __builtin_bit_cast(uint32_t, lo);
+                    } else {
+                        es_prev = es;
+                    }
+                }
+            });
+            if constexpr (PROD) {
+                const half8 bh = __builtin_bit_cast(half8, make_uint4(bhi[0], bhi[1], bhi[2], bhi[3]));
+                const half8 bl = __builtin_bit_cast(half8, make_uint4(blo[0], blo[1], blo[2], blo[3]));
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) {
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa[mb], bh, acc[mb], 0, 0, 0);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa[mb], bl, acc[mb], 0, 0, 0);
                 }
             }
         });
@@ -235,24 +264,6 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
         } else {
             se = quad_sum(se);
             const float gamma = n * sqrtf(se) * (kInvSqrtD / 256.0f);
-            floatx4 acc[8];
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) acc[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            int fl = lane;
-            asm volatile("" : "+v"(fl));
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const half8 bh = __builtin_bit_cast(half8, make_uint4(bhi[4 * s], bhi[4 * s + 1], bhi[4 * s + 2],
-                                                                      bhi[4 * s + 3]));
-                const half8 bl = __builtin_bit_cast(half8, make_uint4(blo[4 * s], blo[4 * s + 1], blo[4 * s + 2],
-                                                                      blo[4 * s + 3]));
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb) {
-                    const half8 a = s_frag[(mb * 4 + s) * 64 + fl];
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, acc[mb], 0, 0, 0);
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[mb], 0, 0, 0);
-                }
-            }
             // lane (t, q) now holds projections 32q + 4mb + j of token t.  Bit
             // (4mb + j) = [P > 0]: shift the sign bits in from the top, from
             // projection 31 down to 0, then invert; a zero residual (all P = 0)
