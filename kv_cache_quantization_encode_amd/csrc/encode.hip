@@ -71,13 +71,13 @@ __device__ __forceinline__ int dest_row(const RowMap &m, int tok, bool &valid) {
     }
 }
 
+// The encode of one packed tensor by a block of 256 threads (4 waves), the
+// waves of the grid striding over 16-row tiles.
 template <int BITS, bool PROD, bool APPEND>
-__global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restrict__ tab,
-                                                        const uint16_t *__restrict__ x, int64_t n_vec,
-                                                        uint8_t *__restrict__ idx_plane,
-                                                        uint8_t *__restrict__ sign_plane,
-                                                        uint8_t *__restrict__ norm_plane, int64_t n_tiles,
-                                                        RowMap map) {
+__device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, const uint16_t *__restrict__ x,
+                                            int64_t n_vec, uint8_t *__restrict__ idx_plane,
+                                            uint8_t *__restrict__ sign_plane, uint8_t *__restrict__ norm_plane,
+                                            int64_t n_tiles, const RowMap &map) {
     __shared__ float s_levels[16];
     __shared__ __attribute__((aligned(16))) QBucket s_lut[kBuckets];
     __shared__ half8 s_frag[PROD ? 32 * 64 : 1];
@@ -283,6 +283,33 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
     }
 }
 
+template <int BITS, bool PROD, bool APPEND>
+__global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restrict__ tab,
+                                                        const uint16_t *__restrict__ x, int64_t n_vec,
+                                                        uint8_t *__restrict__ idx_plane,
+                                                        uint8_t *__restrict__ sign_plane,
+                                                        uint8_t *__restrict__ norm_plane, int64_t n_tiles,
+                                                        RowMap map) {
+    encode_rows<BITS, PROD, APPEND>(tab, x, n_vec, idx_plane, sign_plane, norm_plane, n_tiles, map);
+}
+
+// One decode step's append of K (Stage 1 + QJL) and V (Stage 1) rows in a
+// single launch: blocks with blockIdx.y = 0 encode the K rows, = 1 the V rows.
+struct AppendPlanes {
+    const uint16_t *x;
+    uint8_t *idx, *sign, *norm;
+};
+
+template <int KB, int VB>
+__global__ __launch_bounds__(256) void append_kv_kernel(const DevTables *__restrict__ tab, int64_t n_vec,
+                                                        int64_t n_tiles, AppendPlanes k, AppendPlanes v,
+                                                        RowMap map) {
+    if (blockIdx.y == 0)
+        encode_rows<KB, true, true>(tab, k.x, n_vec, k.idx, k.sign, k.norm, n_tiles, map);
+    else
+        encode_rows<VB, false, true>(tab, v.x, n_vec, v.idx, nullptr, v.norm, n_tiles, map);
+}
+
 // q8 boundary blocks: four consecutive lanes share a token, lane l taking
 // block (l & 3) of 32 elements.
 template <bool APPEND>
@@ -376,6 +403,48 @@ int launch_encode(const DevTables *tab, const void *xv, int64_t n_vec, tq_format
                   const tq_planes_desc &lay, void *stream) {
     return launch_format<false>(tab, static_cast<const uint16_t *>(xv), n_vec, f, static_cast<uint8_t *>(packed),
                                 lay, RowMap{nullptr, 1, 1}, static_cast<hipStream_t>(stream));
+}
+
+template <int KB, int VB>
+static int launch_append_pair(const DevTables *tab, int64_t n_vec, const AppendPlanes &k, const AppendPlanes &v,
+                              const RowMap &map, hipStream_t s) {
+    const int64_t n_tiles = (n_vec + 15) / 16;
+    static int cache[kMaxDevices];
+    const int64_t blocks = persistent_grid(n_tiles, resident_blocks(append_kv_kernel<KB, VB>, 256, cache));
+    hipLaunchKernelGGL((append_kv_kernel<KB, VB>), dim3(unsigned(blocks), 2), dim3(256), 0, s, tab, n_vec, n_tiles,
+                       k, v, map);
+    return int(hipGetLastError());
+}
+
+template <int KB>
+static int dispatch_append_v(const DevTables *tab, int64_t n_vec, int vbits, const AppendPlanes &k,
+                             const AppendPlanes &v, const RowMap &map, hipStream_t s) {
+    switch (vbits) {
+        case 1: return launch_append_pair<KB, 1>(tab, n_vec, k, v, map, s);
+        case 2: return launch_append_pair<KB, 2>(tab, n_vec, k, v, map, s);
+        case 3: return launch_append_pair<KB, 3>(tab, n_vec, k, v, map, s);
+        case 4: return launch_append_pair<KB, 4>(tab, n_vec, k, v, map, s);
+    }
+    return int(hipErrorInvalidValue);
+}
+
+int launch_append_kv(const DevTables *tab, const void *k, const void *v, int B, int hkv, int tcap,
+                     const int32_t *pos, tq_format kf, tq_format vf, void *kp, void *vp,
+                     const tq_planes_desc &kl, const tq_planes_desc &vl, void *stream) {
+    if (kf.kind != TQ_KIND_PROD || vf.kind != TQ_KIND_MSE) return int(hipErrorInvalidValue);
+    uint8_t *kb = static_cast<uint8_t *>(kp), *vb = static_cast<uint8_t *>(vp);
+    const AppendPlanes ka{static_cast<const uint16_t *>(k), kb + kl.idx_offset, kb + kl.sign_offset,
+                          kb + kl.norm_offset};
+    const AppendPlanes va{static_cast<const uint16_t *>(v), vb + vl.idx_offset, nullptr, vb + vl.norm_offset};
+    const RowMap map{pos, hkv, tcap};
+    const int64_t n_vec = int64_t(B) * hkv;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (kf.bits) {
+        case 1: return dispatch_append_v<1>(tab, n_vec, vf.bits, ka, va, map, s);
+        case 2: return dispatch_append_v<2>(tab, n_vec, vf.bits, ka, va, map, s);
+        case 3: return dispatch_append_v<3>(tab, n_vec, vf.bits, ka, va, map, s);
+    }
+    return int(hipErrorInvalidValue);
 }
 
 int launch_append(const DevTables *tab, const void *xv, int B, int hkv, int tcap, const int32_t *pos,

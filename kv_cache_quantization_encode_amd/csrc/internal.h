@@ -59,6 +59,10 @@ int launch_encode(const DevTables *tab, const void *x, int64_t n_vec, tq_format 
                   const tq_planes_desc &lay, void *stream);
 int launch_append(const DevTables *tab, const void *x, int B, int hkv, int tcap, const int32_t *pos,
                   tq_format f, void *packed, const tq_planes_desc &lay, void *stream);
+// K (PROD) and V (MSE) appends of one decode step in one launch.
+int launch_append_kv(const DevTables *tab, const void *k, const void *v, int B, int hkv, int tcap,
+                     const int32_t *pos, tq_format kf, tq_format vf, void *kp, void *vp,
+                     const tq_planes_desc &kl, const tq_planes_desc &vl, void *stream);
 int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t n_vec,
                   const tq_planes_desc &lay, void *out, void *stream);
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
