@@ -572,6 +572,7 @@ def main():
         "v_rows_read_frac": round(kept_rows / n_vec, 4),
         "encode_mtok_s": round(enc_mtok, 2),
         "encode_gbs": round((enc_k_bytes + enc_v_bytes) / (t_k + t_v) / 1e9, 1),
+        "encode_frac_hbm": round((enc_k_bytes + enc_v_bytes) / (t_k + t_v) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof(dom),
         "roofline_attn": roof("attention (scores+values)"),
         "roofline_encode_k": roof("encode_tq_kernel<3,true>"),

@@ -113,3 +113,34 @@ def test_decode_loop_append_then_attend(ctx, oracle_tables):
     # the rows the loop appended are the oracle's encode of the new tokens
     G.check_encode(k.reshape(-1, 128), *kf, kb.host()[: klay.total_bytes], oracle_tables)
     G.check_encode(v.reshape(-1, 128), *vf, vb.host()[: vlay.total_bytes], oracle_tables)
+
+
+def test_append_many_sequences(ctx, oracle_tables):
+    """64 sequences x 8 KV heads (512 new rows: several blocks per tensor in
+    the joint K+V launch), each sequence at its own position of a 24-token
+    cache; turbo4 K + 2-bit V as in the batched needle workload."""
+    rng = np.random.default_rng(613)
+    B, Hkv, Tc = 64, 8, 24
+    kf, vf = ("prod", 3), ("mse", 2)
+    k = _rows(rng, (B, Hkv, Tc, 128))
+    v = _rows(rng, (B, Hkv, Tc, 128))
+    k_new = _rows(rng, (B, Hkv, 128))
+    v_new = _rows(rng, (B, Hkv, 128))
+    pos = rng.integers(0, Tc, size=B).astype(np.int32)
+    kb, klay = _bulk(ctx, k.reshape(-1, 128), kf, False)
+    vb, vlay = _bulk(ctx, v.reshape(-1, 128), vf, True)
+    G.note(f"append B={B} Hkv={Hkv} Tc={Tc}")
+    T.tq_append_kv(ctx, G.to_dev_f16(k_new), G.to_dev_f16(v_new), B, Hkv, Tc, torch.from_numpy(pos).cuda(),
+                   G.tf(*kf), G.tf(*vf), kb.ptr, vb.ptr)
+    got_k, got_v = kb.host(), vb.host()
+    kb.check_guard(got_k, G.plane_ranges(klay))
+    vb.check_guard(got_v, G.plane_ranges(vlay))
+    for b in range(B):
+        k[b, :, pos[b]] = k_new[b]
+        v[b, :, pos[b]] = v_new[b]
+    ek, _ = _bulk(ctx, k.reshape(-1, 128), kf, False)
+    ev, _ = _bulk(ctx, v.reshape(-1, 128), vf, True)
+    assert np.array_equal(got_k, ek.host()), "appended K cache differs from the bulk encode"
+    assert np.array_equal(got_v, ev.host()), "appended V cache differs from the bulk encode"
+    G.check_encode(k.reshape(-1, 128), *kf, got_k[: klay.total_bytes], oracle_tables)
+    G.check_encode(v.reshape(-1, 128), *vf, got_v[: vlay.total_bytes], oracle_tables)
