@@ -1,0 +1,66 @@
+"""HIP-graph replays of a decode step (append, then attention) must equal the
+eager result on every replay, with eager work and synchronisations between
+replays (the benchmark captures attention calls in graphs)."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_encode_amd import turbokv as T
+from kv_cache_quantization_encode_amd import workloads as W
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("kf,vf,hq", [(("prod", 3), ("mse", 4), 8), (("prod", 2), ("mse", 2), 16),
+                                      (("q8", 8), ("q8", 8), 16)])
+def test_graph_replays_match_eager(oracle_tables, kf, vf, hq):
+    B, Hkv, Tc = 2, 2, 2100
+    c = W.llama8b(T=Tc, Hq=hq, Hkv=Hkv, B=B)
+    K, V = G.tf(*kf), G.tf(*vf)
+    n = B * Hkv * Tc
+    with G.Ctx(42) as ctx:
+        kp, vp = T.alloc_packed(K, n), T.alloc_packed(V, n)
+        T.tq_encode_kv(ctx, G.to_dev_f16(c.k.reshape(-1, 128)), G.to_dev_f16(c.v.reshape(-1, 128)), n, K, V,
+                       kp.buf, vp.buf)
+        rng = np.random.default_rng(614)
+        k_new = G.to_dev_f16(rng.standard_normal((B, Hkv, 128), dtype=np.float32))
+        v_new = G.to_dev_f16(rng.standard_normal((B, Hkv, 128), dtype=np.float32))
+        q = G.to_dev_f16(c.q)
+        pos = torch.tensor([Tc - 1, 1500], dtype=torch.int32, device="cuda")
+        lens = pos + 1
+        ws, wsb = T.alloc_workspace(B, hq, Hkv, Tc, K, V)
+        out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+
+        def step():
+            T.tq_append_kv(ctx, k_new, v_new, B, Hkv, Tc, pos, K, V, kp.buf, vp.buf)
+            T.tq_attn_decode(ctx, q, kp.buf, vp.buf, K, V, B, hq, Hkv, Tc, lens, 1e-6, out, ws, wsb)
+
+        G.note(f"graph eager kf={kf} vf={vf} Hq={hq}")
+        step()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                step()
+        torch.cuda.synchronize()
+        for r in range(4):
+            out.fill_(float("nan"))  # eager work between replays
+            torch.cuda.synchronize()
+            G.note(f"graph replay {r}")
+            g.replay()
+            torch.cuda.synchronize()
+            err = float((out - ref).abs().max())
+            # fp32 atomics add chunk shares in any order: last bits only
+            assert err <= 1e-5, f"replay {r}: max abs difference {err:.3g}"
+        # and the eager result itself matches the oracle on the same bytes
+        got = out.cpu().numpy()
+        kb = kp.buf.cpu().numpy()[: kp.layout.total_bytes]
+        vb = vp.buf.cpu().numpy()[: vp.layout.total_bytes]
+        case = W.AttnCase("graph", c.k, c.v, c.q)
+        exp = G.oracle_attention(case, kb, vb, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6,
+                                 lens.cpu().numpy())
+        assert np.max(np.abs(got - exp)) <= G.ATTN_ATOL
