@@ -453,6 +453,31 @@ def attention_decode(q, k_hat, v_hat, tau: float = 1e-6, seq_lens=None):
     return out, probs
 
 
+def attention_prefill(q, k_hat, v_hat, tau: float = 1e-6, seq_lens=None):
+    """Causal attention of the last Tq positions of each sequence over dense
+    dequantised K/V (the prompt-processing counterpart of the decode step of
+    [CXT] 1.1, whose prefill speed the pages report).
+
+    q: [B, Tq, Hq, d]; k_hat, v_hat: [B, Hkv, T, d].  With L_b = seq_lens[b]
+    (or T), query i of sequence b sits at position L_b - Tq + i and sees the
+    first L_b - Tq + i + 1 tokens (none when that is <= 0); for each query the
+    computation is the decode step above with that length: scores
+    <q, k>/sqrt(d), full softmax, V rows below tau dropped, no
+    renormalisation.  Returns out [B, Tq, Hq, d] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Tq, Hq, d = q.shape
+    T = k_hat.shape[2]
+    out = np.zeros((B, Tq, Hq, d))
+    for b in range(B):
+        L = T if seq_lens is None else min(max(int(seq_lens[b]), 0), T)
+        for i in range(Tq):
+            n = max(L - Tq + i + 1, 0)
+            o, _ = attention_decode(q[b:b + 1, i], k_hat[b:b + 1], v_hat[b:b + 1], tau, [n])
+            out[b, i] = o[0]
+    return out
+
+
 # --------------------------------------------------------------------------
 # Per-group asymmetric min-max baseline  [MAC section 2.1]
 # --------------------------------------------------------------------------

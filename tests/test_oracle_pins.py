@@ -497,6 +497,54 @@ def test_attention_special_cases():
     assert np.allclose(out[0], ref[0]) and np.all(out[1] == 0)
 
 
+def test_prefill_tau0_equals_library_causal_sdpa():
+    """Causal prefill at tau = 0 equals the library's attention with an explicit
+    boolean mask (query i of a sequence of length L sees L - Tq + i + 1 keys)."""
+    rng = np.random.default_rng(21)
+    B, Tq, Hq, Hkv, T, d = 2, 5, 4, 2, 11, 16
+    q = rng.standard_normal((B, Tq, Hq, d))
+    k = rng.standard_normal((B, Hkv, T, d)) * 2
+    v = rng.standard_normal((B, Hkv, T, d))
+    lens = np.array([T, 8])
+    out = O.attention_prefill(q, k, v, tau=0.0, seq_lens=lens)
+    g = Hq // Hkv
+    for b in range(B):
+        L = lens[b]
+        mask = np.zeros((Tq, L), bool)
+        for i in range(Tq):
+            mask[i, :L - Tq + i + 1] = True
+        kt = torch.from_numpy(np.repeat(k[b:b + 1, :, :L], g, axis=1))
+        vt = torch.from_numpy(np.repeat(v[b:b + 1, :, :L], g, axis=1))
+        qt = torch.from_numpy(q[b:b + 1].transpose(0, 2, 1, 3).copy())  # [1, Hq, Tq, d]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask))
+        assert np.allclose(out[b], ref[0].numpy().transpose(1, 0, 2), atol=1e-12)
+
+
+def test_prefill_special_cases():
+    rng = np.random.default_rng(22)
+    B, Tq, Hq, Hkv, T, d = 2, 4, 4, 2, 9, 8
+    q = rng.standard_normal((B, Tq, Hq, d))
+    k = rng.standard_normal((B, Hkv, T, d)) * 3
+    v = rng.standard_normal((B, Hkv, T, d))
+    lens = np.array([9, 2])
+    out = O.attention_prefill(q, k, v, tau=1e-6, seq_lens=lens)
+    # the last query of each sequence is the decode step over the whole sequence
+    dec, _ = O.attention_decode(q[:, -1], k, v, tau=1e-6, seq_lens=lens)
+    assert np.allclose(out[:, -1], dec, atol=1e-13)
+    # a sequence shorter than the query block: the first queries see nothing
+    assert np.all(out[1, :2] == 0) and np.any(out[1, 2] != 0)
+    # query 2 of sequence 1 sees exactly token 0: its output is that V row
+    g = Hq // Hkv
+    assert np.allclose(out[1, 2], np.repeat(v[1, :, 0], g, axis=0), atol=1e-14)
+    # causality: keys and values after a query's position do not change it
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, 7:] = rng.standard_normal(k2[0, :, 7:].shape) * 5
+    v2[0, :, 7:] = 1e3
+    out2 = O.attention_prefill(q, k2, v2, tau=1e-6, seq_lens=lens)
+    assert np.allclose(out2[0, :2], out[0, :2], atol=1e-13)  # positions 5, 6
+    assert not np.allclose(out2[0, 2:], out[0, 2:])
+
+
 def test_rotated_domain_scores_equal_dense_scores(oracle_tables):
     """The score of a packed K row computed without dequantising (rotated query
     dotted with codebook values, plus the QJL term on S R q) equals the score
