@@ -154,7 +154,29 @@ tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_pac
                          const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
                          int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
                          void *workspace, size_t ws_bytes, void *stream);
+/* Workspace of tq_attn_decode (0 for an invalid shape, or when B*Hkv > 65535). */
 size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_format vf);
+
+/* Causal prefill attention over a packed cache: the last Tq positions of each
+ * sequence attend to the cache, each exactly as the decode step above does
+ * with its own prefix ([CXT] 1.1 scores and softmax, [YYL] item 4 and
+ * [CXT] 3.3 sparse V, per query and head).  The Tq new tokens must already be
+ * in the cache (tq_encode_kv or tq_append_kv).
+ * q_f16: device [B, Tq, Hq, d]; out_f32: device [B, Tq, Hq, d].  With
+ * L_b = seq_lens[b] clamped to [0, T] (or T when seq_lens is NULL), query i
+ * of sequence b sits at position L_b - Tq + i and sees the first
+ * L_b - Tq + i + 1 tokens; a query that sees none gets a zero row.
+ * B*Tq*Hkv must not exceed 65535.  Other arguments, formats, ownership and
+ * the last-bit nondeterminism of the fp32 atomics as for tq_attn_decode;
+ * workspace: tq_attn_prefill_workspace_bytes(...) bytes, 256-byte aligned.
+ * Tq = 1 is exactly tq_attn_decode.  Each query reads its visible K rows and
+ * kept V rows itself (no sharing of loads between the queries of a sequence
+ * beyond what the caches hold). */
+tq_status tq_attn_prefill(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                          const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                          int T, int Tq, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                          void *workspace, size_t ws_bytes, void *stream);
+size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf);
 
 /* Per-group asymmetric min-max quantisation ([MAC] 2.1): for each group of
  * group_size consecutive elements, fp16 scale = (max-min)/(2^bits-1) (from the

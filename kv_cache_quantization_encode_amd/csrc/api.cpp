@@ -242,18 +242,25 @@ tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64
 }
 
 size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_format vf) {
-    (void)kf;
-    (void)vf;
-    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv) return 0;
-    return attn_plan(B, Hq, Hkv, T).total;
+    return tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, 1, kf, vf);
 }
 
-tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
-                         const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
-                         int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
-                         void *workspace, size_t ws_bytes, void *stream) {
+size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf) {
+    (void)kf;
+    (void)vf;
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return 0;
+    if (int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
+    return attn_plan(B * Tq, Hq, Hkv, T).total;
+}
+
+// Decode (Tq = 1) and causal prefill (Tq queries per sequence) share one path:
+// query i of sequence b becomes virtual sequence b * Tq + i over b's cache.
+static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_packed, const void *v_packed,
+                           tq_format kf, tq_format vf, int B, int Hq, int Hkv, int T, int Tq,
+                           const int32_t *seq_lens, float sparse_v_tau, float *out_f32, void *workspace,
+                           size_t ws_bytes, void *stream) {
     if (!ctx || !q_f16 || !k_packed || !v_packed || !out_f32) return TQ_ERR_INVALID_ARG;
-    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv) return TQ_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return TQ_ERR_INVALID_ARG;
     if (!(sparse_v_tau >= 0.0f) || !std::isfinite(sparse_v_tau)) return TQ_ERR_INVALID_ARG;
     if (!aligned(q_f16, 16) || !aligned(k_packed, 256) || !aligned(v_packed, 256) ||
         !aligned(out_f32, 16) || (seq_lens && !aligned(seq_lens, 4)))
@@ -263,16 +270,33 @@ tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_pac
     const int g = Hq / Hkv;
     if (g != 1 && g != 2 && g != 4 && g != 8) return TQ_ERR_UNSUPPORTED;
     if (int64_t(B) * Hkv * T > kMaxRows || int64_t(T) * 128 >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
+    if (int64_t(B) * Tq * Hkv > kMaxGridY) return TQ_ERR_UNSUPPORTED;
     const int64_t n_vec = int64_t(B) * Hkv * T;
     tq_planes_desc kl{}, vl{};
     if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))
         return TQ_ERR_INVALID_ARG;
-    const AttnPlan plan = attn_plan(B, Hq, Hkv, T);
+    const AttnPlan plan = attn_plan(B * Tq, Hq, Hkv, T);
     if (!workspace || !aligned(workspace, 256) || ws_bytes < plan.total) return TQ_ERR_WORKSPACE;
-    return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, seq_lens,
+    return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, Tq, seq_lens,
                        sparse_v_tau, out_f32, workspace, plan, stream) == 0
                ? TQ_OK
                : TQ_ERR_HIP;
+}
+
+tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                         const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                         int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    return attn_call(ctx, q_f16, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, 1, seq_lens, sparse_v_tau, out_f32,
+                     workspace, ws_bytes, stream);
+}
+
+tq_status tq_attn_prefill(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                          const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                          int T, int Tq, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                          void *workspace, size_t ws_bytes, void *stream) {
+    return attn_call(ctx, q_f16, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, Tq, seq_lens, sparse_v_tau, out_f32,
+                     workspace, ws_bytes, stream);
 }
 
 tq_status tq_minmax_quant(const void *x_f16, int64_t n, int group_size, int bits, void *codes,

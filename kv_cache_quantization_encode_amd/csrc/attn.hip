@@ -59,14 +59,28 @@ struct AttnArgs {
     int B, Hq, Hkv, T, chunk, n_chunks;
     int ld_scores;  // score row stride (floats)
     int vsub;       // tokens per block of the MFMA values pass (multiple of 32)
+    int tq;         // queries per sequence: virtual sequence b is query b % tq of sequence b / tq
     int k_rotated;  // K codec works in the rotated domain
     int v_rotated;  // V codec works in the rotated domain
 };
 
+// Tokens seen by virtual sequence b: query i = b % tq of sequence s = b / tq
+// sits at position L_s - tq + i and sees the first L_s - tq + i + 1 tokens
+// (causal prefill); with tq = 1 that is the whole sequence (decode).
 __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
-    if (!a.seq_lens) return a.T;
-    int L = a.seq_lens[b];
-    return L < 0 ? 0 : (L > a.T ? a.T : L);
+    const int s = b / a.tq, i = b - s * a.tq;
+    int L = a.seq_lens ? a.seq_lens[s] : a.T;
+    L = L < 0 ? 0 : (L > a.T ? a.T : L);
+    L -= a.tq - 1 - i;
+    return L < 0 ? 0 : L;
+}
+
+// Packed K/V row (batch * Hkv + kv head) of virtual row vb * Hkv + kvh: the
+// tq queries of one sequence share its cache.
+__device__ __forceinline__ int kv_row(const AttnArgs &a, int row) {
+    if (a.tq == 1) return row;
+    const int vb = row / a.Hkv;
+    return (vb / a.tq) * a.Hkv + (row - vb * a.Hkv);
 }
 
 // 2^x on the transcendental unit (v_exp_f32); only used for softmax weights
@@ -479,9 +493,10 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     const int t1 = min(t0 + a.chunk, L);
     // per-(batch, kv head) bases of the planes; token offsets below are 32-bit
     // (T * 128 < 2^31 is checked on the host)
-    const uint8_t *kid = kidx + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 128 : 16 * BITS);
-    const uint8_t *ksg = ksign + int64_t(row) * a.T * 16;
-    const uint8_t *knm = knorm + int64_t(row) * a.T * (KIND == TQ_KIND_Q8 ? 8 : (KIND == TQ_KIND_PROD ? 4 : 2));
+    const int krow = kv_row(a, row);
+    const uint8_t *kid = kidx + int64_t(krow) * a.T * (KIND == TQ_KIND_Q8 ? 128 : 16 * BITS);
+    const uint8_t *ksg = ksign + int64_t(krow) * a.T * 16;
+    const uint8_t *knm = knorm + int64_t(krow) * a.T * (KIND == TQ_KIND_Q8 ? 8 : (KIND == TQ_KIND_PROD ? 4 : 2));
 
     // global reads first: query, D, S fragments, levels and the first slice's
     // K tiles are all in flight while the tables are built.  A chunk whose
@@ -642,7 +657,8 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
     if (t0 >= t1) return;  // an empty chunk adds nothing (uniform over the block)
     const int tmax = t1 - 1;
     const float *sc_base = a.scores + head0 * a.ld_scores;
-    const uint16_t *vn_base = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
+    const int vrow = kv_row(a, row);
+    const uint16_t *vn_base = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(vrow) * a.T;
 
     // every global read of the prologue is issued before any is used: the
     // levels, the chunk statistics of head `wave`, and the scores and V norms
@@ -763,7 +779,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
                 constexpr int ps = decltype(P)::value;
                 {
                     const int slot = min(k0 + PER_PASS * ps + wave * TPW + tk, total - 1);
-                    const int64_t vec = int64_t(row) * a.T + s_tok[slot];
+                    const int64_t vec = int64_t(vrow) * a.T + s_tok[slot];
                     raw[ps][1] = 0u;
                     if constexpr (KIND == TQ_KIND_Q8) {
                         if constexpr (CPL == 8) {
@@ -924,15 +940,16 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     const bool lo_half = n >= G;
     const int hn = n < G ? n : (n < 2 * G ? n - G : 0);
     const float *srow = a.scores + (head0 + hn) * int64_t(a.ld_scores);
-    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(row) * a.T * 8 + (n >> 1);
+    const int vrow = kv_row(a, row);
+    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 8 + (n >> 1);
     // v_perm selector joining half (n & 1) of two dwords: that half of the
     // second operand (bytes 0-3) in bits 0-15, of the first (bytes 4-7) in 16-31
     const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
-    const uint16_t *vn = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(row) * a.T;
+    const uint16_t *vn = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(vrow) * a.T;
     // q8: dwords n and 16 + n of each 128-byte row (coordinates 4n.. and
     // 64 + 4n..), and the four fp16 block scales of each token
-    const uint32_t *q8w = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(row) * a.T * 32 + n;
-    const uint2 *q8s = reinterpret_cast<const uint2 *>(a.vnorm) + int64_t(row) * a.T;
+    const uint32_t *q8w = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 32 + n;
+    const uint2 *q8s = reinterpret_cast<const uint2 *>(a.vnorm) + int64_t(vrow) * a.T;
 
     // 32-token groups: lane (kq, n) reads the scores of head hn for tokens
     // 8kq + [0, 8) (score rows are padded to 32 tokens, so a group is always
@@ -1317,7 +1334,7 @@ static int dispatch_k(const AttnArgs &a, tq_format kf, tq_format vf, hipStream_t
 
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
                 tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
-                int Hkv, int T, const int32_t *seq_lens, float tau, float *out, void *ws,
+                int Hkv, int T, int tq, const int32_t *seq_lens, float tau, float *out, void *ws,
                 const AttnPlan &plan, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *w = static_cast<uint8_t *>(ws);
@@ -1335,7 +1352,8 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.stats = reinterpret_cast<float *>(w + plan.off_stats);
     a.out = out;
     a.tau = tau;
-    a.B = B;
+    a.B = B * tq;  // virtual sequences: tq queries per sequence
+    a.tq = tq;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.T = T;

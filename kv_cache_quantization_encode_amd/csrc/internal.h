@@ -10,6 +10,7 @@ namespace tq {
 
 constexpr int kHeadDim = 128;  // head_dim (= QJL dimension m) of this build
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 16;  // rows per packed tensor (32-bit row indices)
+constexpr int64_t kMaxGridY = 65535;  // attention grids put (sequence, kv head) pairs on y
 
 // One bucket of the quantiser lookup: z in bucket j gets index
 // base + (z >= thr) and level (z >= thr ? c_hi : c_lo).
@@ -67,7 +68,7 @@ int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t
                   const tq_planes_desc &lay, void *out, void *stream);
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
                 tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
-                int Hkv, int T, const int32_t *seq_lens, float tau, float *out, void *ws,
+                int Hkv, int T, int tq, const int32_t *seq_lens, float tau, float *out, void *ws,
                 const AttnPlan &plan, void *stream);
 int launch_minmax_quant(const void *x, int64_t n, int bits, void *codes, void *scale, void *zero,
                         void *stream);

@@ -85,12 +85,17 @@ def load() -> ctypes.CDLL:
                                    ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.tq_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, tq_format, tq_format]
     lib.tq_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq_attn_prefill.argtypes = [vp, vp, vp, vp, tq_format, tq_format, i32, i32, i32, i32, i32, vp,
+                                    ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.tq_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, tq_format, tq_format]
+    lib.tq_attn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_minmax_quant.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     lib.tq_minmax_dequant.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp]
     lib.tq_status_str.argtypes = [i32]
     lib.tq_status_str.restype = ctypes.c_char_p
     for name in ("tq_codebook_init", "tq_ctx_destroy", "tq_host_tables", "tq_packed_layout",
-                 "tq_encode_kv", "tq_append_kv", "tq_decode_kv", "tq_attn_decode", "tq_minmax_quant",
+                 "tq_encode_kv", "tq_append_kv", "tq_decode_kv", "tq_attn_decode", "tq_attn_prefill",
+                 "tq_minmax_quant",
                  "tq_minmax_dequant"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -180,6 +185,17 @@ def tq_attn_decode(ctx, q, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, seq_lens, 
     _check(load().tq_attn_decode(ctx, _ptr(q), _ptr(k_packed), _ptr(v_packed), kf, vf, B, Hq, Hkv, T,
                                  _ptr(seq_lens), float(tau), _ptr(out), _ptr(workspace), ws_bytes,
                                  _stream(stream)), "tq_attn_decode")
+
+
+def tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, Tq, kf: tq_format, vf: tq_format) -> int:
+    return int(load().tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, Tq, kf, vf))
+
+
+def tq_attn_prefill(ctx, q, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, Tq, seq_lens, tau, out, workspace,
+                    ws_bytes, stream=None) -> None:
+    _check(load().tq_attn_prefill(ctx, _ptr(q), _ptr(k_packed), _ptr(v_packed), kf, vf, B, Hq, Hkv, T, Tq,
+                                  _ptr(seq_lens), float(tau), _ptr(out), _ptr(workspace), ws_bytes,
+                                  _stream(stream)), "tq_attn_prefill")
 
 
 def tq_minmax_quant(x, n, group_size, bits, codes, scale, zero, stream=None) -> None:

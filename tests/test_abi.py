@@ -25,7 +25,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "turbokv.h")).read()
     names = sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", hdr)))
-    assert len(names) == 12 and "tq_attn_decode" in names and "tq_append_kv" in names and "tq_status_str" in names
+    assert len(names) == 14 and "tq_attn_decode" in names and "tq_append_kv" in names
+    assert "tq_attn_prefill" in names and "tq_attn_prefill_workspace_bytes" in names and "tq_status_str" in names
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -155,6 +156,30 @@ def test_invalid_arguments_are_rejected_on_host(lib):
     assert attn(ws=None) == T.TQ_ERR_WORKSPACE
     assert attn(wsb=ws - 1) == T.TQ_ERR_WORKSPACE
     assert attn(ws=A + 128) == T.TQ_ERR_WORKSPACE
+    assert T.tq_attn_workspace_bytes(16384, 32, 8, 64, f3, v2) == 0  # 131072 (batch, kv head) pairs
+    assert attn(B=16384) == T.TQ_ERR_UNSUPPORTED
+    # prefill: Tq queries per sequence share its cache
+    pws = T.tq_attn_prefill_workspace_bytes(1, 32, 8, 1024, 16, f3, v2)
+    assert pws > ws
+    assert T.tq_attn_prefill_workspace_bytes(1, 32, 8, 1024, 1, f3, v2) == ws
+    assert T.tq_attn_prefill_workspace_bytes(1, 32, 8, 1024, 0, f3, v2) == 0
+    assert T.tq_attn_prefill_workspace_bytes(2, 32, 8, 1024, 4096, f3, v2) == 0  # 65536 pairs
+
+    def prefill(**kw):
+        a = dict(ctx=cp, q=A, k=A, v=A, kf=f3, vf=v2, B=1, Hq=32, Hkv=8, T=1024, Tq=16, lens=None, tau=1e-6,
+                 out=A, ws=A, wsb=pws)
+        a.update(kw)
+        return L.tq_attn_prefill(a["ctx"], a["q"], a["k"], a["v"], a["kf"], a["vf"], a["B"], a["Hq"], a["Hkv"],
+                                 a["T"], a["Tq"], a["lens"], a["tau"], a["out"], a["ws"], a["wsb"], None)
+
+    assert prefill(ctx=None) == T.TQ_ERR_INVALID_ARG
+    assert prefill(Tq=0) == T.TQ_ERR_INVALID_ARG
+    assert prefill(Tq=-3) == T.TQ_ERR_INVALID_ARG
+    assert prefill(q=A + 2) == T.TQ_ERR_INVALID_ARG
+    assert prefill(vf=T.turbo_k(3)) == T.TQ_ERR_UNSUPPORTED
+    assert prefill(B=2, Tq=4096) == T.TQ_ERR_UNSUPPORTED
+    assert prefill(wsb=pws - 1) == T.TQ_ERR_WORKSPACE
+    assert prefill(wsb=ws) == T.TQ_ERR_WORKSPACE  # the decode workspace is too small for 16 queries
     # min-max
     mq = L.tq_minmax_quant
     assert mq(None, 64, 64, 3, A, A, A, None) == T.TQ_ERR_INVALID_ARG

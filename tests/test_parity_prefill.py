@@ -1,0 +1,94 @@
+"""GPU parity of causal prefill attention (tq_attn_prefill) over the packed
+cache against the oracle's prefill over its own dequantisation of the same
+bytes: the last Tq positions of each sequence attend to their prefixes, each
+query with its own softmax and sparse-V decision."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_encode_amd import turbokv as T
+from kv_cache_quantization_encode_amd import workloads as W
+from oracle import turbokv_oracle as O
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    with G.Ctx(42) as h:
+        yield h
+
+
+def _prefill(ctx, tab, case, q, kf, vf, tau, lens, kv_batches=None):
+    """Run the GPU prefill and the oracle's on the same packed bytes."""
+    B, _, Hkv, Tn = case.shape
+    Tq, Hq = q.shape[1], q.shape[2]
+    k = np.ascontiguousarray(case.k.reshape(-1, 128))
+    v = np.ascontiguousarray(case.v.reshape(-1, 128))
+    kp, _ = G.gpu_encode(ctx, k, *kf)
+    vp, _ = G.gpu_encode(ctx, v, *vf, as_v=True)
+    K, V = G.tf(*kf), G.tf(*vf)
+    wsb = T.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, Tn, Tq, K, V)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = G.Guarded(B * Tq * Hq * 128 * 4)
+    lt = None if lens is None else torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    G.note(f"prefill B={B} Tq={Tq} Hq={Hq} Hkv={Hkv} T={Tn} kf={kf} vf={vf} tau={tau} lens={lens}")
+    T.tq_attn_prefill(ctx, G.to_dev_f16(q), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), K, V, B, Hq,
+                      Hkv, Tn, Tq, lt, tau, out.ptr, ws, wsb)
+    h = out.host()
+    out.check_guard(h)
+    got = h[: B * Tq * Hq * 128 * 4].view(np.float32).reshape(B, Tq, Hq, 128)
+    bs = list(range(B)) if kv_batches is None else list(kv_batches)
+    n_per, n_all = Hkv * Tn, B * Hkv * Tn
+    ks = np.stack([G._dequant_rows(kp, kf[0], kf[1], tab, n_all, b * n_per, n_per).reshape(Hkv, Tn, 128) for b in bs])
+    vs = np.stack([G._dequant_rows(vp, vf[0], vf[1], tab, n_all, b * n_per, n_per).reshape(Hkv, Tn, 128) for b in bs])
+    ref = O.attention_prefill(q[bs].astype(np.float64), ks, vs, tau, None if lens is None else np.asarray(lens)[bs])
+    err = float(np.max(np.abs(got[bs] - ref)))
+    assert err <= G.ATTN_ATOL, f"max abs error {err:.3g}"
+    return got, ref
+
+
+def _queries(seed, B, Tq, Hq):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((B, Tq, Hq, 128), dtype=np.float32).astype(np.float16)
+
+
+@pytest.mark.parametrize("kf,vf,hq", [(("prod", 3), ("mse", 4), 8), (("prod", 2), ("mse", 2), 16),
+                                      (("q8", 8), ("q8", 8), 16), (("prod", 1), ("mse", 3), 4)])
+def test_prefill_formats_ragged(ctx, oracle_tables, kf, vf, hq):
+    """Two sequences of a 1500-token cache, 16 queries each; the second
+    sequence is 700 tokens long."""
+    c = W.llama8b(T=1500, Hq=hq, Hkv=2, B=2)
+    q = _queries(701, 2, 16, hq)
+    _prefill(ctx, oracle_tables, c, q, kf, vf, 1e-6, [1500, 700])
+
+
+def test_prefill_short_sequences_and_tau(ctx, oracle_tables):
+    """Sequences shorter than the query block (the first queries see nothing
+    and return zero rows), an empty sequence, and tau 0 / 0.5."""
+    c = W.llama8b(T=300, Hq=8, Hkv=2, B=3)
+    q = _queries(702, 3, 8, 8)
+    lens = [5, 0, 300]
+    for tau in (0.0, 1e-6, 0.5):
+        got, _ = _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), tau, lens)
+        assert np.all(got[0, :3] == 0.0) and np.all(got[1] == 0.0)
+
+
+def test_prefill_single_query_equals_decode(ctx, oracle_tables):
+    """Tq = 1 is the decode step (same kernels, same launch shape)."""
+    c = W.llama8b(T=2000, Hq=16, Hkv=4, B=1)
+    q = _queries(703, 1, 1, 16)
+    got, _ = _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 4), 1e-6, None)
+    kp, _ = G.gpu_encode(ctx, np.ascontiguousarray(c.k.reshape(-1, 128)), "prod", 3)
+    vp, _ = G.gpu_encode(ctx, np.ascontiguousarray(c.v.reshape(-1, 128)), "mse", 4, as_v=True)
+    dec = G.gpu_attention(ctx, W.AttnCase("dec", c.k, c.v, q[:, 0]), kp, vp, G.tf("prod", 3), G.tf("mse", 4), 1e-6)
+    assert np.max(np.abs(got[:, 0] - dec)) <= 1e-5
+
+
+def test_prefill_llama8b_layer_sampled(ctx, oracle_tables):
+    """The llama8b-like layer at full size (32768 tokens, 32 query / 8 KV
+    heads), the last 16 positions as queries; the oracle checks every query."""
+    c = W.llama8b()
+    q = _queries(704, 1, 16, 32)
+    _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 4), 1e-6, None)
