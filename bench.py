@@ -50,7 +50,7 @@ def parse():
                     help="skip the tiny, min-max, 70B-like full-cache and batched needle measurements")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
-    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle", "decode_loop"],
+    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle", "decode_loop", "prefill"],
                     help="run only this extra measurement and print its JSON (for profiling)")
     return ap.parse_args()
 
@@ -373,6 +373,48 @@ def bench_decode_loop(TK, ctx, dev, reps=10, warm=3):
             "append_us": round(t_app * 1e6, 2), "step_us": round(t_step * 1e6, 2)}
 
 
+def bench_prefill(TK, ctx, dev, reps=10, warm=3, Tq=16):
+    """Causal prefill attention on the llama8b-like layer (32 q / 8 KV heads,
+    32768 tokens, turbo4 K + 4-bit V, tau 1e-6): the last Tq positions attend
+    to their prefixes (tq_attn_prefill).  Eight rotating caches, one HIP graph
+    of eight calls; inputs drawn on the GPU from a seeded generator (K
+    lognormal(0, 0.5) per (head, channel) x Student-t(3), V and q N(0, 1))."""
+    import torch
+    B, Hq, Hkv, T, copies = 1, 32, 8, 32768, 8
+    n_vec = B * Hkv * T
+    kf, vf, tau = TK.turbo_k(4), TK.mse(4), 1e-6
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(707)
+    scale = torch.exp(0.5 * torch.randn((Hkv, 1, 128), generator=gen, device=dev))
+    kps, vps = [], []
+    for _ in range(copies):
+        z = torch.randn((Hkv, T, 128), generator=gen, device=dev)
+        chi = torch.randn((3, Hkv, T, 128), generator=gen, device=dev).pow(2).sum(0)
+        k = (z / torch.sqrt(chi / 3.0) * scale).half().reshape(-1, 128)
+        v = torch.randn((n_vec, 128), generator=gen, device=dev).half()
+        kp, vp = TK.alloc_packed(kf, n_vec), TK.alloc_packed(vf, n_vec)
+        TK.tq_encode_kv(ctx, k, v, n_vec, kf, vf, kp.buf, vp.buf)
+        kps.append(kp)
+        vps.append(vp)
+        del k, v, z, chi
+    q = torch.randn((B, Tq, Hq, 128), generator=gen, device=dev).half()
+    wsb = TK.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, Tq, kf, vf)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Tq, Hq, 128), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def calls():
+        for c in range(copies):
+            TK.tq_attn_prefill(ctx, q, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T, Tq, None, tau, out, ws, wsb)
+
+    t = graph_time(calls, reps, warm, None) / copies
+    k_bytes = n_vec * 68
+    return {"workload": f"causal prefill attention, llama8b-like layer: last {Tq} of 32768 positions as queries, "
+                        "32 q / 8 KV heads; turbo4 K + 4-bit V, tau 1e-6",
+            "us": round(t * 1e6, 2), "queries_per_s": round(Tq / t, 1),
+            "k_read_gbs_per_query": round(k_bytes * Tq / t / 1e9, 1)}
+
+
 def bench_minmax(TK, dev, reps=10, warm=3):
     """Per-group asymmetric min-max baseline: K and V tensors of 32 layers x
     8 KV heads x 4096 tokens x 128 (2 x 134M fp16 elements), N(0,1) times a
@@ -450,7 +492,7 @@ def main():
         else:
             ctx1 = TK.tq_codebook_init(128, 128, 42)
             fn = {"tiny": bench_tiny, "decode_70b": bench_70b, "decode_needle": bench_needle,
-                  "decode_loop": bench_decode_loop}[args.only]
+                  "decode_loop": bench_decode_loop, "prefill": bench_prefill}[args.only]
             r = fn(TK, ctx1, dev, reps=5, warm=2)
         print(json.dumps({args.only: r}), flush=True)
         return
@@ -586,6 +628,7 @@ def main():
         res["decode_70b"] = bench_70b(TK, ctx, dev)
         res["decode_needle"] = bench_needle(TK, ctx, dev)
         res["decode_loop"] = bench_decode_loop(TK, ctx, dev)
+        res["prefill"] = bench_prefill(TK, ctx, dev)
     TK.tq_ctx_destroy(ctx)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
