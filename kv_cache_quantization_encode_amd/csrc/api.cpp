@@ -196,6 +196,10 @@ tq_status tq_encode_kv(const tq_ctx *ctx, const void *k_f16, const void *v_f16, 
         if (!plane_layout(vf, ctx->head_dim, n_vec, &vl)) return TQ_ERR_INVALID_ARG;
     }
     if (n_vec == 0) return TQ_OK;
+    if (k_f16 && v_f16) {
+        const int r = launch_encode_pair(ctx->dev, k_f16, v_f16, n_vec, kf, vf, k_packed, v_packed, kl, vl, stream);
+        if (r != kPairDeclined) return r == 0 ? TQ_OK : TQ_ERR_HIP;
+    }
     if (k_f16 && launch_encode(ctx->dev, k_f16, n_vec, kf, k_packed, kl, stream) != 0) return TQ_ERR_HIP;
     if (v_f16 && launch_encode(ctx->dev, v_f16, n_vec, vf, v_packed, vl, stream) != 0) return TQ_ERR_HIP;
     return TQ_OK;
@@ -218,11 +222,11 @@ tq_status tq_append_kv(const tq_ctx *ctx, const void *k_new_f16, const void *v_n
         if (!v_packed || !aligned(v_new_f16, 16) || !aligned(v_packed, 256)) return TQ_ERR_INVALID_ARG;
         if (!plane_layout(vf, ctx->head_dim, n_cache, &vl)) return TQ_ERR_INVALID_ARG;
     }
-    if (k_new_f16 && v_new_f16 && kf.kind == TQ_KIND_PROD && vf.kind == TQ_KIND_MSE)  // one launch
-        return launch_append_kv(ctx->dev, k_new_f16, v_new_f16, B, Hkv, T_cap, pos, kf, vf, k_packed, v_packed,
-                                kl, vl, stream) == 0
-                   ? TQ_OK
-                   : TQ_ERR_HIP;
+    if (k_new_f16 && v_new_f16) {
+        const int r = launch_append_kv(ctx->dev, k_new_f16, v_new_f16, B, Hkv, T_cap, pos, kf, vf, k_packed,
+                                       v_packed, kl, vl, stream);
+        if (r != kPairDeclined) return r == 0 ? TQ_OK : TQ_ERR_HIP;
+    }
     if (k_new_f16 && launch_append(ctx->dev, k_new_f16, B, Hkv, T_cap, pos, kf, k_packed, kl, stream) != 0)
         return TQ_ERR_HIP;
     if (v_new_f16 && launch_append(ctx->dev, v_new_f16, B, Hkv, T_cap, pos, vf, v_packed, vl, stream) != 0)

@@ -293,21 +293,23 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restr
     encode_rows<BITS, PROD, APPEND>(tab, x, n_vec, idx_plane, sign_plane, norm_plane, n_tiles, map);
 }
 
-// One decode step's append of K (Stage 1 + QJL) and V (Stage 1) rows in a
-// single launch: blocks with blockIdx.y = 0 encode the K rows, = 1 the V rows.
-struct AppendPlanes {
+// K (Stage 1 + QJL) and V (Stage 1) rows in a single launch, for encodes
+// small enough that one launch each would leave most of the GPU idle (a
+// decode step's append, short prompts): blocks with blockIdx.y = 0 encode the
+// K rows, = 1 the V rows.
+struct PairPlanes {
     const uint16_t *x;
     uint8_t *idx, *sign, *norm;
 };
 
-template <int KB, int VB>
-__global__ __launch_bounds__(256) void append_kv_kernel(const DevTables *__restrict__ tab, int64_t n_vec,
-                                                        int64_t n_tiles, AppendPlanes k, AppendPlanes v,
-                                                        RowMap map) {
+template <int KB, int VB, bool APPEND>
+__global__ __launch_bounds__(256) void encode_pair_kernel(const DevTables *__restrict__ tab, int64_t n_vec,
+                                                          int64_t n_tiles, PairPlanes k, PairPlanes v,
+                                                          RowMap map) {
     if (blockIdx.y == 0)
-        encode_rows<KB, true, true>(tab, k.x, n_vec, k.idx, k.sign, k.norm, n_tiles, map);
+        encode_rows<KB, true, APPEND>(tab, k.x, n_vec, k.idx, k.sign, k.norm, n_tiles, map);
     else
-        encode_rows<VB, false, true>(tab, v.x, n_vec, v.idx, nullptr, v.norm, n_tiles, map);
+        encode_rows<VB, false, APPEND>(tab, v.x, n_vec, v.idx, nullptr, v.norm, n_tiles, map);
 }
 
 // q8 boundary blocks: four consecutive lanes share a token, lane l taking
@@ -405,46 +407,63 @@ int launch_encode(const DevTables *tab, const void *xv, int64_t n_vec, tq_format
                                 lay, RowMap{nullptr, 1, 1}, static_cast<hipStream_t>(stream));
 }
 
-template <int KB, int VB>
-static int launch_append_pair(const DevTables *tab, int64_t n_vec, const AppendPlanes &k, const AppendPlanes &v,
-                              const RowMap &map, hipStream_t s) {
+// Returns kPairDeclined (nothing launched) when the encode is too large for
+// one joint launch: each of K and V then gets a full persistent grid.
+template <int KB, int VB, bool APPEND>
+static int launch_pair(const DevTables *tab, int64_t n_vec, const PairPlanes &k, const PairPlanes &v,
+                       const RowMap &map, hipStream_t s) {
     const int64_t n_tiles = (n_vec + 15) / 16;
     static int cache[kMaxDevices];
-    const int64_t blocks = persistent_grid(n_tiles, resident_blocks(append_kv_kernel<KB, VB>, 256, cache));
-    hipLaunchKernelGGL((append_kv_kernel<KB, VB>), dim3(unsigned(blocks), 2), dim3(256), 0, s, tab, n_vec, n_tiles,
-                       k, v, map);
+    const int resident = resident_blocks(encode_pair_kernel<KB, VB, APPEND>, 256, cache);
+    // one tile per wave and both halves of the grid resident at once
+    if (n_tiles > int64_t(resident) * 2) return kPairDeclined;
+    const int64_t blocks = (n_tiles + 3) / 4;
+    hipLaunchKernelGGL((encode_pair_kernel<KB, VB, APPEND>), dim3(unsigned(blocks), 2), dim3(256), 0, s, tab, n_vec,
+                       n_tiles, k, v, map);
     return int(hipGetLastError());
 }
 
-template <int KB>
-static int dispatch_append_v(const DevTables *tab, int64_t n_vec, int vbits, const AppendPlanes &k,
-                             const AppendPlanes &v, const RowMap &map, hipStream_t s) {
+template <int KB, bool APPEND>
+static int dispatch_pair_v(const DevTables *tab, int64_t n_vec, int vbits, const PairPlanes &k,
+                           const PairPlanes &v, const RowMap &map, hipStream_t s) {
     switch (vbits) {
-        case 1: return launch_append_pair<KB, 1>(tab, n_vec, k, v, map, s);
-        case 2: return launch_append_pair<KB, 2>(tab, n_vec, k, v, map, s);
-        case 3: return launch_append_pair<KB, 3>(tab, n_vec, k, v, map, s);
-        case 4: return launch_append_pair<KB, 4>(tab, n_vec, k, v, map, s);
+        case 1: return launch_pair<KB, 1, APPEND>(tab, n_vec, k, v, map, s);
+        case 2: return launch_pair<KB, 2, APPEND>(tab, n_vec, k, v, map, s);
+        case 3: return launch_pair<KB, 3, APPEND>(tab, n_vec, k, v, map, s);
+        case 4: return launch_pair<KB, 4, APPEND>(tab, n_vec, k, v, map, s);
     }
     return int(hipErrorInvalidValue);
+}
+
+template <bool APPEND>
+static int dispatch_pair(const DevTables *tab, const void *k, const void *v, int64_t n_vec, tq_format kf,
+                         tq_format vf, void *kp, void *vp, const tq_planes_desc &kl, const tq_planes_desc &vl,
+                         const RowMap &map, void *stream) {
+    if (kf.kind != TQ_KIND_PROD || vf.kind != TQ_KIND_MSE) return kPairDeclined;
+    uint8_t *kb = static_cast<uint8_t *>(kp), *vb = static_cast<uint8_t *>(vp);
+    const PairPlanes ka{static_cast<const uint16_t *>(k), kb + kl.idx_offset, kb + kl.sign_offset,
+                        kb + kl.norm_offset};
+    const PairPlanes va{static_cast<const uint16_t *>(v), vb + vl.idx_offset, nullptr, vb + vl.norm_offset};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (kf.bits) {
+        case 1: return dispatch_pair_v<1, APPEND>(tab, n_vec, vf.bits, ka, va, map, s);
+        case 2: return dispatch_pair_v<2, APPEND>(tab, n_vec, vf.bits, ka, va, map, s);
+        case 3: return dispatch_pair_v<3, APPEND>(tab, n_vec, vf.bits, ka, va, map, s);
+    }
+    return int(hipErrorInvalidValue);
+}
+
+int launch_encode_pair(const DevTables *tab, const void *k, const void *v, int64_t n_vec, tq_format kf,
+                       tq_format vf, void *kp, void *vp, const tq_planes_desc &kl, const tq_planes_desc &vl,
+                       void *stream) {
+    return dispatch_pair<false>(tab, k, v, n_vec, kf, vf, kp, vp, kl, vl, RowMap{nullptr, 1, 1}, stream);
 }
 
 int launch_append_kv(const DevTables *tab, const void *k, const void *v, int B, int hkv, int tcap,
                      const int32_t *pos, tq_format kf, tq_format vf, void *kp, void *vp,
                      const tq_planes_desc &kl, const tq_planes_desc &vl, void *stream) {
-    if (kf.kind != TQ_KIND_PROD || vf.kind != TQ_KIND_MSE) return int(hipErrorInvalidValue);
-    uint8_t *kb = static_cast<uint8_t *>(kp), *vb = static_cast<uint8_t *>(vp);
-    const AppendPlanes ka{static_cast<const uint16_t *>(k), kb + kl.idx_offset, kb + kl.sign_offset,
-                          kb + kl.norm_offset};
-    const AppendPlanes va{static_cast<const uint16_t *>(v), vb + vl.idx_offset, nullptr, vb + vl.norm_offset};
-    const RowMap map{pos, hkv, tcap};
-    const int64_t n_vec = int64_t(B) * hkv;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (kf.bits) {
-        case 1: return dispatch_append_v<1>(tab, n_vec, vf.bits, ka, va, map, s);
-        case 2: return dispatch_append_v<2>(tab, n_vec, vf.bits, ka, va, map, s);
-        case 3: return dispatch_append_v<3>(tab, n_vec, vf.bits, ka, va, map, s);
-    }
-    return int(hipErrorInvalidValue);
+    return dispatch_pair<true>(tab, k, v, int64_t(B) * hkv, kf, vf, kp, vp, kl, vl, RowMap{pos, hkv, tcap},
+                               stream);
 }
 
 int launch_append(const DevTables *tab, const void *xv, int B, int hkv, int tcap, const int32_t *pos,

@@ -60,7 +60,13 @@ int launch_encode(const DevTables *tab, const void *x, int64_t n_vec, tq_format 
                   const tq_planes_desc &lay, void *stream);
 int launch_append(const DevTables *tab, const void *x, int B, int hkv, int tcap, const int32_t *pos,
                   tq_format f, void *packed, const tq_planes_desc &lay, void *stream);
-// K (PROD) and V (MSE) appends of one decode step in one launch.
+// K (PROD) and V (MSE) of a small encode, or of one decode step's append,
+// in one launch.  kPairDeclined: nothing launched (formats or size), the
+// caller encodes K and V separately.
+constexpr int kPairDeclined = -1;
+int launch_encode_pair(const DevTables *tab, const void *k, const void *v, int64_t n_vec, tq_format kf,
+                       tq_format vf, void *kp, void *vp, const tq_planes_desc &kl, const tq_planes_desc &vl,
+                       void *stream);
 int launch_append_kv(const DevTables *tab, const void *k, const void *v, int B, int hkv, int tcap,
                      const int32_t *pos, tq_format kf, tq_format vf, void *kp, void *vp,
                      const tq_planes_desc &kl, const tq_planes_desc &vl, void *stream);

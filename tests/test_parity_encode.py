@@ -2,6 +2,7 @@
 import numpy as np
 import pytest
 
+from kv_cache_quantization_encode_amd import turbokv as T
 from kv_cache_quantization_encode_amd import workloads as W
 from oracle import turbokv_oracle as O
 from tests import gpu_helpers as G
@@ -120,3 +121,27 @@ def test_decode_quality_sanity(ctx, tab):
         got = G.gpu_decode(ctx, packed, "mse", bits, 4096).astype(np.float64)
         rel = np.sum((got - x) ** 2, axis=1) / np.sum(x.astype(np.float64) ** 2, axis=1)
         assert abs(rel.mean() - mse) / mse < 0.06
+
+
+@pytest.mark.parametrize("n", [1, 1037, 40000])
+@pytest.mark.parametrize("kf,vf", [(("prod", 3), ("mse", 4)), (("prod", 1), ("mse", 2)), (("q8", 8), ("mse", 3))])
+def test_encode_k_and_v_in_one_call_equals_separate_calls(n, kf, vf):
+    """tq_encode_kv with K and V together (one joint launch for small inputs
+    with a QJL K format and a codebook V format, two launches otherwise)
+    writes the same bytes as two single-tensor calls."""
+    rng = np.random.default_rng(615 + n)
+    k16 = (rng.standard_normal((n, 128), dtype=np.float32) * 3).astype(np.float16)
+    v16 = rng.standard_normal((n, 128), dtype=np.float32).astype(np.float16)
+    K, V = G.tf(*kf), G.tf(*vf)
+    kl, vl = T.tq_packed_layout(K, 128, n), T.tq_packed_layout(V, 128, n)
+    with G.Ctx(42) as ctx:
+        kb, vb = G.Guarded(int(kl.total_bytes)), G.Guarded(int(vl.total_bytes))
+        G.note(f"encode K+V together n={n} kf={kf} vf={vf}")
+        T.tq_encode_kv(ctx, G.to_dev_f16(k16), G.to_dev_f16(v16), n, K, V, kb.ptr, vb.ptr)
+        hk, hv = kb.host(), vb.host()
+        kb.check_guard(hk, G.plane_ranges(kl))
+        vb.check_guard(hv, G.plane_ranges(vl))
+        ek, _ = G.gpu_encode(ctx, k16, *kf)
+        ev, _ = G.gpu_encode(ctx, v16, *vf, as_v=True)
+    assert np.array_equal(hk[: kl.total_bytes], ek)
+    assert np.array_equal(hv[: vl.total_bytes], ev)
