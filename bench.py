@@ -50,7 +50,8 @@ def parse():
                     help="skip the tiny, min-max, 70B-like full-cache and batched needle measurements")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
-    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle", "decode_loop", "prefill"],
+    ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle", "decode_loop", "prefill",
+                                       "quality"],
                     help="run only this extra measurement and print its JSON (for profiling)")
     return ap.parse_args()
 
@@ -467,6 +468,69 @@ def bench_minmax(TK, dev, reps=10, warm=3):
     return res
 
 
+def bench_quality(TK, ctx, dev):
+    """Reconstruction quality of the codecs (tq_encode_kv then tq_decode_kv)
+    next to the min-max baseline at similar bits, on two inputs drawn on the
+    GPU: (a) one tensor of the min-max workload (32 layers x 8 KV heads x 4096
+    tokens x 128, N(0,1) times a per-64-group scale log-uniform in [1e-3, 8],
+    seed 303) and (b) llama8b-like K (8 KV heads x 32768 tokens x 128,
+    lognormal(0, 0.5) per (head, channel) x Student-t(3), seed 808), whose
+    outlier channels the rotation spreads out.  Bits per element include the
+    stored norms / scales; ratio = 16 / bits."""
+    import torch
+    res = {"workload": "reconstruction quality: turboN K (QJL), b-bit V, q8 and min-max (group 64) on the "
+                       "min-max workload's K tensor and on llama8b-like K"}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(303)
+    n_a = 32 * 8 * 4096 * 128
+    x = torch.randn((n_a // 64, 64), generator=gen, device=dev)
+    sc = torch.exp(torch.empty((n_a // 64, 1), device=dev).uniform_(math.log(1e-3), math.log(8.0), generator=gen))
+    data_a = (x * sc).half().view(-1, 128)
+    del x, sc
+    gen.manual_seed(808)
+    z = torch.randn((8, 32768, 128), generator=gen, device=dev)
+    chi = torch.randn((3, 8, 32768, 128), generator=gen, device=dev).pow(2).sum(0)
+    scale = torch.exp(0.5 * torch.randn((8, 1, 128), generator=gen, device=dev))
+    data_b = (z / torch.sqrt(chi / 3.0) * scale).half().view(-1, 128)
+    del z, chi
+
+    def stats(xh, yh):
+        xf, yf = xh.float(), yh.float()
+        cos = float(torch.dot(xf.view(-1), yf.view(-1)) / (xf.norm() * yf.norm()))
+        cv = float((torch.sum(xf * yf, 1) / (xf.norm(dim=1) * yf.norm(dim=1)).clamp_min(1e-30)).mean())
+        return {"mse": float(((xf - yf) ** 2).mean()), "cosine": round(cos, 5), "cosine_per_vector": round(cv, 5)}
+
+    fmts = [("turbo2_k", TK.turbo_k(2), 2.25), ("turbo3_k", TK.turbo_k(3), 3.25), ("turbo4_k", TK.turbo_k(4), 4.25),
+            ("v2", TK.mse(2), 2.125), ("v3", TK.mse(3), 3.125), ("v4", TK.mse(4), 4.125), ("q8", TK.Q8, 8.5)]
+    for name, data in (("minmax_data", data_a), ("llama8b_k", data_b)):
+        n_vec = data.shape[0]
+        out = {}
+        y = torch.empty_like(data)
+        for fname, f, bpe in fmts:
+            pk = TK.alloc_packed(f, n_vec)
+            TK.tq_encode_kv(ctx, data, None, n_vec, f, f, pk.buf, None)
+            TK.tq_decode_kv(ctx, pk.buf, f, n_vec, y)
+            torch.cuda.synchronize()
+            out[fname] = {"bits_per_elem": bpe, "ratio": round(16 / bpe, 2), **stats(data, y)}
+            del pk
+        n = data.numel()
+        for bits in (2, 3, 4):
+            codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=dev)
+            sz = torch.empty(n // 64, dtype=torch.float16, device=dev)
+            zz = torch.empty(n // 64, dtype=torch.float16, device=dev)
+            TK.tq_minmax_quant(data.view(-1), n, 64, bits, codes, sz, zz)
+            TK.tq_minmax_dequant(codes, sz, zz, n, 64, bits, y.view(-1))
+            torch.cuda.synchronize()
+            bpe = bits + 0.5
+            out[f"minmax_b{bits}"] = {"bits_per_elem": bpe, "ratio": round(16 / bpe, 2), **stats(data, y)}
+            del codes, sz, zz
+        res[name] = out
+        del y
+    del data_a, data_b
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calib:
@@ -489,6 +553,8 @@ def main():
     if args.only:
         if args.only == "minmax":
             r = bench_minmax(TK, dev)
+        elif args.only == "quality":
+            r = bench_quality(TK, TK.tq_codebook_init(128, 128, 42), dev)
         else:
             ctx1 = TK.tq_codebook_init(128, 128, 42)
             fn = {"tiny": bench_tiny, "decode_70b": bench_70b, "decode_needle": bench_needle,
@@ -629,6 +695,7 @@ def main():
         res["decode_needle"] = bench_needle(TK, ctx, dev)
         res["decode_loop"] = bench_decode_loop(TK, ctx, dev)
         res["prefill"] = bench_prefill(TK, ctx, dev)
+        res["quality"] = bench_quality(TK, ctx, dev)
     TK.tq_ctx_destroy(ctx)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
