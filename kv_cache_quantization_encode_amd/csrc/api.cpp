@@ -254,7 +254,8 @@ size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq
     (void)vf;
     if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return 0;
     if (int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
-    return attn_plan(B * Tq, Hq, Hkv, T).total;
+    const int qp = prefill_group(Hq / Hkv, Tq);
+    return attn_plan(B * (Tq / qp), Hq * qp, Hkv, T).total;
 }
 
 // Decode (Tq = 1) and causal prefill (Tq queries per sequence) share one path:
@@ -279,7 +280,8 @@ static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_p
     tq_planes_desc kl{}, vl{};
     if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))
         return TQ_ERR_INVALID_ARG;
-    const AttnPlan plan = attn_plan(B * Tq, Hq, Hkv, T);
+    const int qp = prefill_group(g, Tq);
+    const AttnPlan plan = attn_plan(B * (Tq / qp), Hq * qp, Hkv, T);
     if (!workspace || !aligned(workspace, 256) || ws_bytes < plan.total) return TQ_ERR_WORKSPACE;
     return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, Tq, seq_lens,
                        sparse_v_tau, out_f32, workspace, plan, stream) == 0

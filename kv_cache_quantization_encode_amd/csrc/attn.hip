@@ -59,28 +59,50 @@ struct AttnArgs {
     int B, Hq, Hkv, T, chunk, n_chunks;
     int ld_scores;  // score row stride (floats)
     int vsub;       // tokens per block of the MFMA values pass (multiple of 32)
-    int tq;         // queries per sequence: virtual sequence b is query b % tq of sequence b / tq
+    // Prefill: tq queries per sequence, taken qp at a time.  Virtual sequence
+    // b holds queries qp * (b % (tq / qp)) + [0, qp) of sequence b / (tq / qp);
+    // its G = qg * qp rows are those queries' qg heads of one kv head (query
+    // u = row / qg, head row % qg), so the queries share every K load.  Hq is
+    // the virtual head count (real heads x qp), hq_io the real one.  Decode:
+    // tq = qp = 1.
+    int tq, qp, qg, hq_io;
     int k_rotated;  // K codec works in the rotated domain
     int v_rotated;  // V codec works in the rotated domain
 };
 
-// Tokens seen by virtual sequence b: query i = b % tq of sequence s = b / tq
-// sits at position L_s - tq + i and sees the first L_s - tq + i + 1 tokens
-// (causal prefill); with tq = 1 that is the whole sequence (decode).
+// Query i of sequence s sits at position L_s - tq + i and sees the first
+// L_s - tq + i + 1 tokens (causal prefill; with tq = 1 the whole sequence).
+// seq_len_of gives what the last query of virtual sequence b sees; row_shift
+// how many tokens fewer its row g sees.
 __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
-    const int s = b / a.tq, i = b - s * a.tq;
+    if (a.tq == 1) {  // decode: no integer divisions on the setup path
+        if (!a.seq_lens) return a.T;
+        const int L = a.seq_lens[b];
+        return L < 0 ? 0 : (L > a.T ? a.T : L);
+    }
+    const int groups = a.tq / a.qp;
+    const int s = b / groups, grp = b - s * groups;
     int L = a.seq_lens ? a.seq_lens[s] : a.T;
     L = L < 0 ? 0 : (L > a.T ? a.T : L);
-    L -= a.tq - 1 - i;
+    L -= a.tq - a.qp * (grp + 1);
     return L < 0 ? 0 : L;
 }
+__device__ __forceinline__ int row_shift(const AttnArgs &a, int g) { return a.qp - 1 - g / a.qg; }
 
-// Packed K/V row (batch * Hkv + kv head) of virtual row vb * Hkv + kvh: the
-// tq queries of one sequence share its cache.
+// Packed K/V row (batch * Hkv + kv head) of virtual row b * Hkv + kvh: the
+// queries of one sequence share its cache.
 __device__ __forceinline__ int kv_row(const AttnArgs &a, int row) {
     if (a.tq == 1) return row;
-    const int vb = row / a.Hkv;
-    return (vb / a.tq) * a.Hkv + (row - vb * a.Hkv);
+    const int b = row / a.Hkv;
+    return (b / (a.tq / a.qp)) * a.Hkv + (row - b * a.Hkv);
+}
+
+// Row of q and out ([B, tq, Hq, d]) of row g of (virtual sequence b, kv head kvh).
+__device__ __forceinline__ int64_t io_row(const AttnArgs &a, int b, int kvh, int g) {
+    if (a.tq == 1) return int64_t(b) * a.hq_io + int64_t(kvh) * a.qg + g;
+    const int groups = a.tq / a.qp;
+    const int s = b / groups, grp = b - s * groups, u = g / a.qg;
+    return (int64_t(s) * a.tq + a.qp * grp + u) * a.hq_io + int64_t(kvh) * a.qg + (g - u * a.qg);
 }
 
 // 2^x on the transcendental unit (v_exp_f32); only used for softmax weights
@@ -171,12 +193,12 @@ struct QueryLoads {
 };
 
 template <int G, bool PROJ>
-__device__ __forceinline__ void load_query(QueryLoads<G, PROJ> &ql, const AttnArgs &a, int64_t head0) {
+__device__ __forceinline__ void load_query(QueryLoads<G, PROJ> &ql, const AttnArgs &a, int b, int kvh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < ql.NH; ++i) {
         const int g = wave + 4 * i;
-        const uint16_t *q = a.q + (head0 + (g < G ? g : 0)) * 128;
+        const uint16_t *q = a.q + io_row(a, b, kvh, g < G ? g : 0) * 128;
         ql.q0[i] = q[lane];
         ql.q1[i] = q[lane + 64];
     }
@@ -365,12 +387,13 @@ __device__ __forceinline__ void own_scores(const float (&e)[4], int lane, float 
     }
 }
 
-template <bool FULL, int G, int KIND, int BITS>
+template <bool FULL, bool ROWLIM, int G, int KIND, int BITS>
 __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
                                              int kq, const uint2 *s_pair, const half8 *s_sgn,
                                              const half8 (&aq)[8], const half8 (&ap)[4],
                                              float *__restrict__ scores, int64_t head0, int ld,
-                                             float (&m)[kOwn<G>], float (&l)[kOwn<G>]) {
+                                             const int (&lim)[kOwn<G>], float (&m)[kOwn<G>],
+                                             float (&l)[kOwn<G>]) {
     using KT = KTiles<KIND, BITS>;
     float scv[KT::NT][kOwn<G>];  // this lane's scores of the slice in log2 units, -inf where absent
     // B operands of the rotated-key path.  Field f (codes 2f, 2f+1 of the
@@ -445,11 +468,14 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         own_scores<G>(e, 16 * kq + t, o);
         // lane (t, kq) now holds the scores of its own heads for token tok;
         // one store per head and lane (on the whole-slice path without a
-        // branch, so the memory counters stay exact)
+        // branch, so the memory counters stay exact).  A row whose query sees
+        // fewer tokens (the earlier queries of a prefill group) stores -inf
+        // past its limit, so the values pass gives those tokens no weight.
 #pragma unroll
         for (int j = 0; j < kOwn<G>; ++j) {
-            if (valid) scores[(head0 + own_head<G>(kq, j)) * ld + tok] = o[j];
-            scv[i][j] = valid ? o[j] * kLog2e : -INFINITY;
+            const bool vj = valid && (!ROWLIM || tok < lim[j]);
+            if (valid) scores[(head0 + own_head<G>(kq, j)) * ld + tok] = vj ? o[j] : -INFINITY;
+            scv[i][j] = vj ? o[j] * kLog2e : -INFINITY;
         }
     });
     // running (max, sum) per lane and own head, once per slice, in log2 units
@@ -503,7 +529,7 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     // length is a multiple of 512 has only whole slices and takes the path
     // without per-token bounds checks.
     QueryLoads<G, KIND == TQ_KIND_PROD> ql;
-    load_query(ql, a, head0);
+    load_query(ql, a, b, kvh);
     float lv[2] = {0.0f, 0.0f};
     if constexpr (KIND != TQ_KIND_Q8) {
         if (tid < kPairs) {
@@ -527,7 +553,7 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     // the output rows of this kv head start at zero; the values pass adds
     // every chunk's share into them
     if (chunk_id == 0) {
-        for (int i = tid; i < G * 128; i += 256) a.out[head0 * 128 + i] = 0.0f;
+        for (int i = tid; i < G * 128; i += 256) a.out[io_row(a, b, kvh, i >> 7) * 128 + (i & 127)] = 0.0f;
     }
     // zero stacked rows 2G .. 15
     for (int i = tid; i < (16 - 2 * G) * 32; i += 256) {
@@ -582,31 +608,46 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
         }
     }
     float m[kOwn<G>], l[kOwn<G>];
+    int lim[kOwn<G>];  // tokens seen by the row of each own head
 #pragma unroll
-    for (int j = 0; j < kOwn<G>; ++j) { m[j] = -INFINITY; l[j] = 0.0f; }
+    for (int j = 0; j < kOwn<G>; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.0f;
+        lim[j] = L - row_shift(a, own_head<G>(kq, j));
+    }
 
     // the scan: every load is unconditional (clamped rows), so the wait
     // before scoring a slice covers exactly that slice's loads
-    auto scan = [&](auto full_c) {
+    auto scan = [&](auto full_c, auto rowlim_c) {
         constexpr bool F = decltype(full_c)::value;
+        constexpr bool RL = decltype(rowlim_c)::value;
         if (t0 >= t1) return;
         for (int base = t0;;) {
             load_ktiles(tc, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, m, l);
+            score_ktiles<F, RL, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, lim, m,
+                                   l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(ta, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, m, l);
+            score_ktiles<F, RL, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, lim, m,
+                                   l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(tb, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, m, l);
+            score_ktiles<F, RL, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, lim, m,
+                                   l);
             base += kSlice;
             if (base >= t1) break;
         }
     };
-    if (whole) scan(std::true_type{});
-    else scan(std::false_type{});
+    // rows with their own causal limit only in multi-query prefill groups
+    if (a.qp > 1) {
+        if (whole) scan(std::true_type{}, std::true_type{});
+        else scan(std::false_type{}, std::true_type{});
+    } else {
+        if (whole) scan(std::true_type{}, std::false_type{});
+        else scan(std::false_type{}, std::false_type{});
+    }
     // (max, sum) per head: over the 16 token lanes of each lane group, then
     // over the waves; m is kept in log2 units and stored in natural units
 #pragma unroll
@@ -876,7 +917,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
                 v0 *= a.tab->signs[lane] * kRsqrtD;
                 v1 *= a.tab->signs[lane + 64] * kRsqrtD;
             }
-            float *o = a.out + (head0 + g) * 128;
+            float *o = a.out + io_row(a, b, kvh, g) * 128;
             __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1268,7 +1309,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 v0 *= a.tab->signs[lane] * sc;
                 v1 *= a.tab->signs[lane + 64] * sc;
             }
-            float *o = a.out + (head0 + g) * 128;
+            float *o = a.out + io_row(a, b, kvh, g) * 128;
             __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1352,9 +1393,13 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.stats = reinterpret_cast<float *>(w + plan.off_stats);
     a.out = out;
     a.tau = tau;
-    a.B = B * tq;  // virtual sequences: tq queries per sequence
+    const int qp = prefill_group(Hq / Hkv, tq);
+    a.B = B * (tq / qp);  // virtual sequences of qp queries each
     a.tq = tq;
-    a.Hq = Hq;
+    a.qp = qp;
+    a.qg = Hq / Hkv;
+    a.hq_io = Hq;
+    a.Hq = Hq * qp;
     a.Hkv = Hkv;
     a.T = T;
     a.chunk = plan.chunk;
@@ -1362,7 +1407,7 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.ld_scores = plan.ld_scores;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
-    switch (Hq / Hkv) {
+    switch (a.Hq / Hkv) {
         case 1: return dispatch_k<1>(a, kf, vf, s);
         case 2: return dispatch_k<2>(a, kf, vf, s);
         case 4: return dispatch_k<4>(a, kf, vf, s);

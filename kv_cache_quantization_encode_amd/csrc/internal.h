@@ -54,6 +54,14 @@ struct AttnPlan {
     size_t off_scores, off_stats, total;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
+// Prefill queries of one sequence that share a scores pass: the largest of
+// 8/g, ..., 2, 1 (g = query heads per kv head) dividing Tq, so that the
+// group's g * qp rows fill at most the 8 query rows of one pass.
+inline int prefill_group(int g, int tq) {
+    for (int qp = 8 / g; qp > 1; qp /= 2)
+        if (tq % qp == 0) return qp;
+    return 1;
+}
 
 // Kernel launchers (HIP translation units).  All return a hipError_t as int.
 int launch_encode(const DevTables *tab, const void *x, int64_t n_vec, tq_format f, void *packed,

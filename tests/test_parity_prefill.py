@@ -92,3 +92,14 @@ def test_prefill_llama8b_layer_sampled(ctx, oracle_tables):
     c = W.llama8b()
     q = _queries(704, 1, 16, 32)
     _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 4), 1e-6, None)
+
+
+@pytest.mark.parametrize("tq,hq,hkv", [(5, 8, 2), (6, 4, 2), (4, 2, 2), (8, 2, 2), (3, 16, 2)])
+def test_prefill_query_grouping_shapes(ctx, oracle_tables, tq, hq, hkv):
+    """Queries of a sequence share a scores pass in groups of the largest of
+    8/g, ..., 2 dividing Tq (g = query heads per kv head): here groups of 1
+    (odd Tq), 2 (Tq = 6, g = 2), 4 (Tq = 4, g = 1), 8 (Tq = 8, g = 1) and 1 with
+    g = 8; ragged lengths put the group's rows at different causal limits."""
+    c = W.llama8b(T=900, Hq=hq, Hkv=hkv, B=2)
+    q = _queries(705 + tq, 2, tq, hq)
+    _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), 1e-6, [900, tq + 2])
