@@ -204,7 +204,9 @@ def oracle_attention(case, kpacked, vpacked, kk, kb, vk, vb, tab, tau, seq_lens=
     for b in bs:
         ks.append(_dequant_rows(kpacked, kk, kb, tab, B * n_per, b * n_per, n_per).reshape(Hkv, Tn, 128))
         vs.append(_dequant_rows(vpacked, vk, vb, tab, B * n_per, b * n_per, n_per).reshape(Hkv, Tn, 128))
-    lens = None if seq_lens is None else np.asarray(seq_lens)[bs]
+    # the library reads lengths outside [0, T] as clamped to it (its documented
+    # convention); the oracle is given the clamped lengths
+    lens = None if seq_lens is None else np.clip(np.asarray(seq_lens), 0, Tn)[bs]
     out, _ = O.attention_decode(case.q[bs].astype(np.float64), np.stack(ks), np.stack(vs), tau, lens)
     return out
 

@@ -176,6 +176,10 @@ def test_invalid_arguments_are_rejected_on_host(lib):
     assert prefill(Tq=0) == T.TQ_ERR_INVALID_ARG
     assert prefill(Tq=-3) == T.TQ_ERR_INVALID_ARG
     assert prefill(q=A + 2) == T.TQ_ERR_INVALID_ARG
+    assert prefill(lens=A + 2) == T.TQ_ERR_INVALID_ARG
+    assert prefill(out=A + 4) == T.TQ_ERR_INVALID_ARG
+    assert prefill(tau=float("inf")) == T.TQ_ERR_INVALID_ARG
+    assert prefill(Hq=24) == T.TQ_ERR_UNSUPPORTED
     assert prefill(vf=T.turbo_k(3)) == T.TQ_ERR_UNSUPPORTED
     assert prefill(B=2, Tq=4096) == T.TQ_ERR_UNSUPPORTED
     assert prefill(wsb=pws - 1) == T.TQ_ERR_WORKSPACE

@@ -67,6 +67,10 @@ def test_attention_single_token_and_seq_lens(ctx, oracle_tables):
     lens = np.array([300, 1, 0, 157], np.int32)
     got, _, _ = _run(ctx, oracle_tables, c, ("prod", 3), ("mse", 2), 1e-6, seq_lens=lens)
     assert np.all(got[2] == 0.0)
+    # lengths outside [0, T] are clamped: 5000 reads as 300, -4 as 0
+    clamped, _, _ = _run(ctx, oracle_tables, c, ("prod", 3), ("mse", 2), 1e-6,
+                         seq_lens=np.array([5000, 1, -4, 157], np.int32))
+    assert np.all(clamped[2] == 0.0) and np.max(np.abs(clamped - got)) <= 1e-5
 
 
 def test_attention_eight_heads_ragged_batch(ctx, oracle_tables):

@@ -70,6 +70,10 @@ def test_prefill_short_sequences_and_tau(ctx, oracle_tables):
     c = W.llama8b(T=300, Hq=8, Hkv=2, B=3)
     q = _queries(702, 3, 8, 8)
     lens = [5, 0, 300]
+    # lengths are clamped to [0, T]: above T reads as T, below 0 as 0
+    got_hi, _ = _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), 1e-6, [5, -7, 1000])
+    got_eq, _ = _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), 1e-6, [5, 0, 300])
+    assert np.all(got_hi[1] == 0.0) and np.max(np.abs(got_hi - got_eq)) <= 1e-5
     for tau in (0.0, 1e-6, 0.5):
         got, _ = _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), tau, lens)
         assert np.all(got[0, :3] == 0.0) and np.all(got[1] == 0.0)
