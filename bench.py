@@ -400,7 +400,7 @@ def bench_prefill(TK, ctx, dev, reps=10, warm=3, Tq=16):
         del k, v, z, chi
     q = torch.randn((B, Tq, Hq, 128), generator=gen, device=dev).half()
     wsb = TK.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, Tq, kf, vf)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     out = torch.empty((B, Tq, Hq, 128), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 

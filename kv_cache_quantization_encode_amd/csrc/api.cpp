@@ -91,6 +91,34 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     return p;
 }
 
+AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int capacity) {
+    const int g = Hq / Hkv;
+    const int qp = prefill_group(g, Tq);
+    AttnPlan p = attn_plan(B * (Tq / qp), Hq * qp, Hkv, T);
+    // single launch: decode with 8 query heads per kv head and a V codec the
+    // fused kernel reads (2-bit codebook, q8); every block of a row is resident
+    // at once, and a block's scores (tb tokens x 8 heads) fit its LDS
+    if (Tq != 1 || g != 8 || capacity <= 0) return p;
+    if (!(vf.kind == TQ_KIND_Q8 || (vf.kind == TQ_KIND_MSE && vf.bits == 2))) return p;
+    const int64_t rows = int64_t(B) * Hkv;
+    const int64_t slices = (int64_t(T) + kFusedSlice - 1) / kFusedSlice;
+    int64_t nblk = capacity / rows;
+    if (nblk < 1) nblk = 1;
+    if (nblk > slices) nblk = slices;
+    const int64_t tb = (slices + nblk - 1) / nblk * kFusedSlice;
+    if (tb > kFusedMaxTokens) return p;
+    nblk = (int64_t(T) + tb - 1) / tb;
+    AttnPlan f{};
+    f.fused = 1;
+    f.nblk = int(nblk);
+    f.tb = int(tb);
+    int64_t off = 0;
+    f.off_sync = size_t(off); off = align256(rows * 2 * 4);
+    f.off_stats = size_t(off); off = align256(off + rows * nblk * 8 * 2 * 4);
+    f.total = size_t(off);
+    return f;
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -251,11 +279,9 @@ size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_f
 
 size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf) {
     (void)kf;
-    (void)vf;
     if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return 0;
     if (int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
-    const int qp = prefill_group(Hq / Hkv, Tq);
-    return attn_plan(B * (Tq / qp), Hq * qp, Hkv, T).total;
+    return attn_call_plan(B, Hq, Hkv, T, Tq, vf, fused_capacity()).total;
 }
 
 // Decode (Tq = 1) and causal prefill (Tq queries per sequence) share one path:
@@ -280,8 +306,7 @@ static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_p
     tq_planes_desc kl{}, vl{};
     if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))
         return TQ_ERR_INVALID_ARG;
-    const int qp = prefill_group(g, Tq);
-    const AttnPlan plan = attn_plan(B * (Tq / qp), Hq * qp, Hkv, T);
+    const AttnPlan plan = attn_call_plan(B, Hq, Hkv, T, Tq, vf, fused_capacity());
     if (!workspace || !aligned(workspace, 256) || ws_bytes < plan.total) return TQ_ERR_WORKSPACE;
     return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, Tq, seq_lens,
                        sparse_v_tau, out_f32, workspace, plan, stream) == 0

@@ -32,468 +32,9 @@
 //                 group is one set of MFMA products, see below.
 // Exact sparse V needs the global softmax statistics before any V row is
 // skipped, hence the kernel boundary between passes 1 and 2.
-#include <algorithm>
-#include <type_traits>
-
-#include "device_common.h"
+#include "attn_common.h"
 
 namespace tq {
-
-constexpr float kRsqrtD = 0.08838834764831845f;  // 1/sqrt(128)
-constexpr float kQjlOverSqrtD = 1.2533141373155003f / 128.0f * 0.08838834764831845f;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSliceTiles = 4;            // 16-token tiles per wave and slice
-constexpr int kSlice = 64 * kSliceTiles;  // tokens per slice of the scores pass (4 waves)
-constexpr int kVThreads = 512;            // threads per values block
-constexpr int kVWaves = kVThreads / 64;
-
-struct AttnArgs {
-    const DevTables *tab;
-    const uint16_t *q;
-    const uint8_t *kidx, *ksign, *knorm;  // K planes
-    const uint8_t *vidx, *vnorm;          // V planes
-    const int32_t *seq_lens;
-    float *scores, *stats;
-    float *out;
-    float tau;
-    int B, Hq, Hkv, T, chunk, n_chunks;
-    int ld_scores;  // score row stride (floats)
-    int vsub;       // tokens per block of the MFMA values pass (multiple of 32)
-    // Prefill: tq queries per sequence, taken qp at a time.  Virtual sequence
-    // b holds queries qp * (b % (tq / qp)) + [0, qp) of sequence b / (tq / qp);
-    // its G = qg * qp rows are those queries' qg heads of one kv head (query
-    // u = row / qg, head row % qg), so the queries share every K load.  Hq is
-    // the virtual head count (real heads x qp), hq_io the real one.  Decode:
-    // tq = qp = 1.
-    int tq, qp, qg, hq_io;
-    int k_rotated;  // K codec works in the rotated domain
-    int v_rotated;  // V codec works in the rotated domain
-};
-
-// Query i of sequence s sits at position L_s - tq + i and sees the first
-// L_s - tq + i + 1 tokens (causal prefill; with tq = 1 the whole sequence).
-// seq_len_of gives what the last query of virtual sequence b sees; row_shift
-// how many tokens fewer its row g sees.
-__device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
-    if (a.tq == 1) {  // decode: no integer divisions on the setup path
-        if (!a.seq_lens) return a.T;
-        const int L = a.seq_lens[b];
-        return L < 0 ? 0 : (L > a.T ? a.T : L);
-    }
-    const int groups = a.tq / a.qp;
-    const int s = b / groups, grp = b - s * groups;
-    int L = a.seq_lens ? a.seq_lens[s] : a.T;
-    L = L < 0 ? 0 : (L > a.T ? a.T : L);
-    L -= a.tq - a.qp * (grp + 1);
-    return L < 0 ? 0 : L;
-}
-__device__ __forceinline__ int row_shift(const AttnArgs &a, int g) { return a.qp - 1 - g / a.qg; }
-
-// Packed K/V row (batch * Hkv + kv head) of virtual row b * Hkv + kvh: the
-// queries of one sequence share its cache.
-__device__ __forceinline__ int kv_row(const AttnArgs &a, int row) {
-    if (a.tq == 1) return row;
-    const int b = row / a.Hkv;
-    return (b / (a.tq / a.qp)) * a.Hkv + (row - b * a.Hkv);
-}
-
-// Row of q and out ([B, tq, Hq, d]) of row g of (virtual sequence b, kv head kvh).
-__device__ __forceinline__ int64_t io_row(const AttnArgs &a, int b, int kvh, int g) {
-    if (a.tq == 1) return int64_t(b) * a.hq_io + int64_t(kvh) * a.qg + g;
-    const int groups = a.tq / a.qp;
-    const int s = b / groups, grp = b - s * groups, u = g / a.qg;
-    return (int64_t(s) * a.tq + a.qp * grp + u) * a.hq_io + int64_t(kvh) * a.qg + (g - u * a.qg);
-}
-
-// 2^x on the transcendental unit (v_exp_f32); only used for softmax weights
-// of arguments <= 0, where its flush of results below 2^-126 is immaterial.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Reductions over the 16 lanes of a DPP row: quad_perm xor 1, quad_perm
-// xor 2, row_half_mirror, row_mirror; every lane ends with the result.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp_mov<0xB1>(x));
-    x = fmaxf(x, dpp_mov<0x4E>(x));
-    x = fmaxf(x, dpp_mov<0x141>(x));
-    return fmaxf(x, dpp_mov<0x140>(x));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp_mov<0xB1>(x);
-    x += dpp_mov<0x4E>(x);
-    x += dpp_mov<0x141>(x);
-    return x + dpp_mov<0x140>(x);
-}
-// Max over lanes l, l^16, l^32, l^48 (result in every lane).
-__device__ __forceinline__ float quad_max(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// The value of lane l ^ S (S = 1 .. 32) without LDS traffic: DPP quad
-// permutes (1, 2) and row rotate (8), a bit-mode swizzle (4), and the
-// permlane swaps (16, 32), whose pair holds both halves of the exchange.
-template <int S>
-__device__ __forceinline__ float lane_xor(float x, int lane) {
-    if constexpr (S == 1) {
-        return dpp_mov<0xB1>(x);
-    } else if constexpr (S == 2) {
-        return dpp_mov<0x4E>(x);
-    } else if constexpr (S == 4) {
-        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));  // and 31, xor 4
-    } else if constexpr (S == 8) {
-        return dpp_mov<0x128>(x);  // rotate a row of 16 by 8
-    } else if constexpr (S == 16) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return __uint_as_float((lane & 16) ? r[0] : r[1]);
-    } else {
-        static_assert(S == 32, "lane bit");
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return __uint_as_float((lane & 32) ? r[0] : r[1]);
-    }
-}
-
-// Unnormalised 128-point Walsh-Hadamard transform of the coordinates held
-// as v0 = coordinate lane, v1 = coordinate lane + 64 (bit 6 in-lane, bits
-// 0..5 across lanes).
-__device__ __forceinline__ void fwht128_lanes(float &v0, float &v1, int lane) {
-    const float s0 = v0 + v1, s1 = v0 - v1;
-    v0 = s0;
-    v1 = s1;
-    Unroll<6>::run([&](auto I) {
-        constexpr int S = 1 << decltype(I)::value;
-        const float sg = (lane & S) ? -1.0f : 1.0f;
-        const float p0 = lane_xor<S>(v0, lane), p1 = lane_xor<S>(v1, lane);
-        v0 = fmaf(sg, v0, p0);
-        v1 = fmaf(sg, v1, p1);
-    });
-}
-
-// ------------------------------------------------------------ query operands
-// The MFMA A operands of the scores pass hold each query twice: row h < G is
-// the fp16 hi half and row G + h the fp16 lo half of head h (rows >= 2G are
-// zero), so that the two rows together carry the fp32 value to about 2^-22.
-//   s_a:  q_rot = H D q / sqrt(d) for rotated keys, q itself for q8 keys;
-//   s_ap: q_proj = S q_rot (unscaled; the score scales are applied per token).
-// q_proj runs on the MFMA units: rows = 128 projections (wave w takes row
-// blocks 2w, 2w+1), columns = heads (hi rows, then lo rows), k = coordinates;
-// S is exact in fp16.  All global reads of this setup are issued at kernel
-// entry (QueryLoads) and consumed after the lookup tables are built.
-template <int G, bool PROJ>
-struct QueryLoads {
-    static constexpr int NH = (G + 3) / 4;  // heads per wave
-    uint32_t q0[NH], q1[NH];                // fp16 bits of coordinates lane, lane + 64
-    float sg0, sg1;                         // D entries of those coordinates
-    half8 sf[PROJ ? 8 : 1];                 // S fragments (row block, k-step)
-};
-
-template <int G, bool PROJ>
-__device__ __forceinline__ void load_query(QueryLoads<G, PROJ> &ql, const AttnArgs &a, int b, int kvh) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < ql.NH; ++i) {
-        const int g = wave + 4 * i;
-        const uint16_t *q = a.q + io_row(a, b, kvh, g < G ? g : 0) * 128;
-        ql.q0[i] = q[lane];
-        ql.q1[i] = q[lane + 64];
-    }
-    ql.sg0 = a.tab->signs[lane];
-    ql.sg1 = a.tab->signs[lane + 64];
-    if constexpr (PROJ) {
-        const int h = lane & 15, kq = lane >> 4;
-        const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);  // row-major [128][128]
-#pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2)
-#pragma unroll
-            for (int st = 0; st < 4; ++st) ql.sf[4 * rb2 + st] = S8[(16 * (2 * wave + rb2) + h) * 16 + 4 * kq + st];
-    }
-}
-
-__device__ __forceinline__ void put_hi_lo(_Float16 *hi, _Float16 *lo, float x) {
-    const _Float16 h = _Float16(x);
-    *hi = h;
-    *lo = _Float16(x - float(h));
-}
-
-// Fills s_a (and s_ap) rows 0 .. 2G-1; rows 2G .. 15 must already be zero.
-// Ends with a barrier.
-template <int G, bool PROJ>
-__device__ __forceinline__ void build_query_rows(const QueryLoads<G, PROJ> &ql, const AttnArgs &a,
-                                                 _Float16 (*s_a)[128], _Float16 (*s_ap)[128]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < ql.NH; ++i) {
-        const int g = wave + 4 * i;
-        if (g >= G) break;
-        float v0 = h2f(ql.q0[i]), v1 = h2f(ql.q1[i]);
-        if (a.k_rotated) {
-            v0 *= ql.sg0;
-            v1 *= ql.sg1;
-            fwht128_lanes(v0, v1, lane);
-            v0 *= kRsqrtD;
-            v1 *= kRsqrtD;
-        }
-        put_hi_lo(&s_a[g][lane], &s_a[G + g][lane], v0);
-        put_hi_lo(&s_a[g][lane + 64], &s_a[G + g][lane + 64], v1);
-    }
-    __syncthreads();
-    if constexpr (PROJ) {
-        const int c = lane & 15, kq = lane >> 4;
-        // B operand: column c = hi row c of s_a for c < G, lo row c - G + G
-        // (= row c) for G <= c < 2G, zero above; i.e. simply row c of s_a
-        half8 bq[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) bq[st] = *reinterpret_cast<const half8 *>(&s_a[c][32 * kq + 8 * st]);
-#pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2) {
-            const int rb = 2 * wave + rb2;
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql.sf[4 * rb2 + st], bq[st], acc, 0, 0, 0);
-            // lane (c, kq) holds projections 16 rb + 4 kq + j of column c;
-            // q_proj of head h = column h + column G + h (lanes c and c + G)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float other = __shfl_down(acc[j], G, 16);
-                if (c < G) put_hi_lo(&s_ap[c][16 * rb + 4 * kq + j], &s_ap[G + c][16 * rb + 4 * kq + j],
-                                     acc[j] + other);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// ------------------------------------------------------------------ scores
-// One wavefront scores 16 tokens of one kv head at a time with
-// v_mfma_f32_16x16x32_f16: columns = tokens, k = coordinates, and the 16 rows
-// carry the query of the G heads twice, as fp16 hi halves (rows h) and fp16
-// lo halves (rows G + h), so that row h plus row G + h is the fp32 query to
-// about 2^-22.  Lane l supplies token l&15 and the 32 coordinates
-// 32*(l>>4)+[0,32) of its packed row (8 per MFMA k-step), so a lane unpacks
-// exactly the b dwords it loaded.  Codebook levels enter as fp16 hi + lo
-// halves (two MFMAs into one accumulator); the QJL operand is +-1, exact in
-// fp16.  q8 keys use k-steps = the four 32-element scale blocks.
-template <int KIND, int BITS>
-struct KTiles {
-    static constexpr int NT = kSliceTiles;  // tiles of 16 tokens per wave per slice
-    static constexpr int W = KIND == TQ_KIND_Q8 ? 8 : BITS;
-    uint32_t wk[NT][W], sw[NT], nn[NT];
-    uint2 q8s[NT];
-};
-
-// Loads the K tiles of one slice (kSlice tokens).  Tokens at or past t1 read row
-// tmax instead (any valid row: the scores of such tokens are discarded), so
-// every call issues the same loads and the waits before scoring stay exact.
-template <int KIND, int BITS>
-__device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int tmax, int wave, int t, int kq,
-                                            const uint8_t *kid, const uint8_t *ksg, const uint8_t *knm) {
-    using KT = KTiles<KIND, BITS>;
-#pragma unroll
-    for (int i = 0; i < KT::NT; ++i) {
-        const int tok = min(base + wave * 16 + 64 * i + t, tmax);
-        if constexpr (KIND == TQ_KIND_Q8) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
-                d.wk[i][2 * s] = u.x;
-                d.wk[i][2 * s + 1] = u.y;
-            }
-            d.q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
-        } else {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
-#pragma unroll
-            for (int w = 0; w < KT::W; ++w) d.wk[i][w] = src[w];
-            if constexpr (KIND == TQ_KIND_PROD) {
-                d.sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
-                d.nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
-            } else {
-                d.nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
-            }
-        }
-    }
-}
-
-// Adds row G + h of the MFMA result to row h: lane (t, kq) holds rows
-// 4 kq + j, so for G <= 2 both rows are in the lane, for G = 4 in lanes l and
-// l ^ 16, for G = 8 in lanes l and l ^ 32.
-template <int G>
-__device__ __forceinline__ void fold_rows(float (&e)[4]) {
-    if constexpr (G == 1) {
-        e[0] += e[1];
-    } else if constexpr (G == 2) {
-        e[0] += e[2];
-        e[1] += e[3];
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t x = __float_as_uint(e[j]);
-            const auto r = G == 4 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
-                                  : __builtin_amdgcn_permlane32_swap(x, x, false, false);
-            e[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        }
-    }
-}
-
-// The value of x in lane l ^ 16 (resp. l ^ 32).  permlane16_swap(x, x)
-// leaves a lane of an even 16-lane row with (x[l], x[l + 16]) and one of an
-// odd row with (x[l - 16], x[l]); permlane32_swap likewise with halves.
-__device__ __forceinline__ float partner16(float x, int lane) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float partner32(float x, int lane) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
-}
-
-// After fold_rows, each lane group kq (lanes 16 kq .. 16 kq + 15, one token
-// per lane) takes over kOwn<G> heads: head kq + 4i for G >= 4, head kq % G
-// below (duplicated across groups).  own_scores moves the scores there.
-template <int G>
-constexpr int kOwn = G >= 8 ? 2 : 1;
-template <int G>
-__device__ __forceinline__ int own_head(int kq, int i) {
-    return G >= 4 ? kq + 4 * i : kq % G;
-}
-template <int G>
-__device__ __forceinline__ void own_scores(const float (&e)[4], int lane, float (&o)[kOwn<G>]) {
-    const int kq = lane >> 4;
-    if constexpr (G == 1) {
-        // head 0 sits in e[0] of group 0; every other group holds zero there
-        o[0] = quad_sum(e[0]);
-    } else if constexpr (G == 2) {
-        // heads 0, 1 in e[0], e[1] of group 0, zeros elsewhere
-        const float h0 = quad_sum(e[0]), h1 = quad_sum(e[1]);
-        o[0] = (kq & 1) ? h1 : h0;
-    } else if constexpr (G == 4) {
-        // groups 0 and 1 both hold heads 0..3 in e[0..3]; groups 2, 3 zeros
-        const float lo = (kq & 1) ? e[1] : e[0];
-        const float hi = partner32((kq & 1) ? e[3] : e[2], lane);
-        o[0] = kq < 2 ? lo : hi;
-    } else {
-        // groups 0, 2 hold heads 0..3 and groups 1, 3 heads 4..7 in e[0..3]
-        const float own = kq == 0 ? e[0] : kq == 1 ? e[1] : kq == 2 ? e[2] : e[3];
-        const int want = kq ^ 1;  // what the partner group needs from this lane
-        const float send = want == 0 ? e[0] : want == 1 ? e[1] : want == 2 ? e[2] : e[3];
-        const float recv = partner16(send, lane);
-        o[0] = (kq & 1) ? recv : own;  // head kq
-        o[1] = (kq & 1) ? own : recv;  // head kq + 4
-    }
-}
-
-template <bool FULL, bool ROWLIM, int G, int KIND, int BITS>
-__device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
-                                             int kq, const uint2 *s_pair, const half8 *s_sgn,
-                                             const half8 (&aq)[8], const half8 (&ap)[4],
-                                             float *__restrict__ scores, int64_t head0, int ld,
-                                             const int (&lim)[kOwn<G>], float (&m)[kOwn<G>],
-                                             float (&l)[kOwn<G>]) {
-    using KT = KTiles<KIND, BITS>;
-    float scv[KT::NT][kOwn<G>];  // this lane's scores of the slice in log2 units, -inf where absent
-    // B operands of the rotated-key path.  Field f (codes 2f, 2f+1 of the
-    // lane) gives (hi(c0) hi(c1) | lo(c0) lo(c1)); fields 2u and 2u+1 side by
-    // side are the B operand of k-step u, whose A operand repeats each query
-    // value against its level's hi and lo half.  The table reads of tile i+1
-    // are issued before the MFMAs of tile i, so LDS latency overlaps them.
-    struct Ops {
-        uint2 ef[16];
-        half8 sg[4];
-    };
-    Ops ops[1];
-    auto fetch = [&](int i, Ops &o) {
-        Unroll<16>::run([&](auto P) {
-            constexpr int pr = decltype(P)::value;
-            o.ef[pr] = s_pair[code_at<2 * BITS, pr>(d.wk[i])];
-        });
-        if constexpr (KIND == TQ_KIND_PROD) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) o.sg[s] = s_sgn[(d.sw[i] >> (8 * s)) & 0xFFu];
-        }
-    };
-    Unroll<KT::NT>::run([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        const int tok = base + wave * 16 + 64 * i + t;
-        const bool valid = FULL || tok < t1;
-        float e[4];
-        if constexpr (KIND == TQ_KIND_Q8) {
-            const uint2 scl = d.q8s[i];
-            const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8 bv;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t w = d.wk[i][2 * s + (j >> 2)];
-                    bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
-                }
-                floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
-                ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bv, ds, 0, 0, 0);  // aq[0..3] only
-                // scale of block s of token t
-#pragma unroll
-                for (int j = 0; j < 4; ++j) e[j] = fmaf(bs[s], ds[j], e[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] *= kRsqrtD;
-        } else {
-            fetch(i, ops[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            const Ops &o = ops[0];
-            floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint4 bv = make_uint4(o.ef[2 * u].x, o.ef[2 * u].y, o.ef[2 * u + 1].x, o.ef[2 * u + 1].y);
-                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[u], __builtin_bit_cast(half8, bv), d0, 0, 0, 0);
-            }
-            if constexpr (KIND == TQ_KIND_PROD) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[s], o.sg[s], d1, 0, 0, 0);
-            }
-            // s = (1/sqrt d)(n/sqrt d)<q_rot, c> + (1/sqrt d) sqrt(pi/2)/m gamma <q_proj, sign>
-            const float n = h2f(d.nn[i] & 0xFFFFu) * (1.0f / 128.0f);
-            const float gq = h2f(d.nn[i] >> 16) * kQjlOverSqrtD;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
-        }
-        fold_rows<G>(e);
-        float o[kOwn<G>];
-        own_scores<G>(e, 16 * kq + t, o);
-        // lane (t, kq) now holds the scores of its own heads for token tok;
-        // one store per head and lane (on the whole-slice path without a
-        // branch, so the memory counters stay exact).  A row whose query sees
-        // fewer tokens (the earlier queries of a prefill group) stores -inf
-        // past its limit, so the values pass gives those tokens no weight.
-#pragma unroll
-        for (int j = 0; j < kOwn<G>; ++j) {
-            const bool vj = valid && (!ROWLIM || tok < lim[j]);
-            if (valid) scores[(head0 + own_head<G>(kq, j)) * ld + tok] = vj ? o[j] : -INFINITY;
-            scv[i][j] = vj ? o[j] * kLog2e : -INFINITY;
-        }
-    });
-    // running (max, sum) per lane and own head, once per slice, in log2 units
-#pragma unroll
-    for (int j = 0; j < kOwn<G>; ++j) {
-        float mx = scv[0][j];
-#pragma unroll
-        for (int i = 1; i < KT::NT; ++i) mx = fmaxf(mx, scv[i][j]);
-        const float nm = fmaxf(m[j], mx);
-        if (nm != -INFINITY) {
-            float acc = l[j] * fast_exp2(m[j] - nm);
-#pragma unroll
-            for (int i = 0; i < KT::NT; ++i) acc += fast_exp2(scv[i][j] - nm);
-            l[j] = acc;
-            m[j] = nm;
-        }
-    }
-}
 
 template <int G, int KIND, int BITS>
 __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
@@ -616,6 +157,7 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
         lim[j] = L - row_shift(a, own_head<G>(kq, j));
     }
 
+    auto sink = [&](int h, int tok, float v) { scores[(head0 + h) * a.ld_scores + tok] = v; };
     // the scan: every load is unconditional (clamped rows), so the wait
     // before scoring a slice covers exactly that slice's loads
     auto scan = [&](auto full_c, auto rowlim_c) {
@@ -624,18 +166,15 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
         if (t0 >= t1) return;
         for (int base = t0;;) {
             load_ktiles(tc, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, RL, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, lim, m,
-                                   l);
+            score_ktiles<F, RL, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(ta, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, RL, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, lim, m,
-                                   l);
+            score_ktiles<F, RL, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(tb, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, RL, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, scores, head0, a.ld_scores, lim, m,
-                                   l);
+            score_ktiles<F, RL, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
             base += kSlice;
             if (base >= t1) break;
         }
@@ -962,7 +501,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     constexpr int NN = Q8 ? 1 : 4;   // norm dwords per lane and group
     constexpr int NA = Q8 ? 16 : 4;  // A-operand dwords (q8: one operand per block)
     constexpr int NS = Q8 ? 4 : 1;   // q8 scale pairs (uint2) per lane and group
-    __shared__ float s_M[G], s_invL[G];
+    __shared__ float s_M[G], s_invL[G], s_qmax[kMWaves];
     __shared__ int s_any[kMWaves];
     __shared__ __attribute__((aligned(16))) float s_acc[kMWaves][G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1066,6 +605,17 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
     const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
     asm volatile("" ::: "memory");
+    // q8 V: the A operands are weight x block scale; the block's largest scale
+    // bounds them (codebook V: weights <= 1, scaled by 2^15)
+    if constexpr (Q8) {
+        uint32_t mx = 0;
+        for (int tk = t0 + tid; tk < t1; tk += kMThreads) {
+            const uint2 u = q8s[tk];
+            mx = max(mx, max(max(u.x & 0xFFFFu, u.x >> 16), max(u.y & 0xFFFFu, u.y >> 16)));
+        }
+        const float mf = quad_max(row16_max(h2f(mx)));
+        if (lane == 0) s_qmax[wave] = mf;
+    }
 
     // exact softmax statistics of every head from all chunk statistics
     for (int h = wave; h < G; h += kMWaves) {
@@ -1087,7 +637,16 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     }
     __syncthreads();
     const float Ml2 = s_M[hn] * kLog2e;
-    const float invL = s_invL[hn] * kWScale;  // weights leave scaled by 2^15
+    float ash = kWScale;
+    if constexpr (Q8) {
+        float mf = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kMWaves; ++w) mf = fmaxf(mf, s_qmax[w]);
+        int e = 0;
+        (void)frexpf(mf, &e);
+        ash = ldexpf(16384.0f, -e);  // weight x scale x ash < 2^14
+    }
+    const float invL = s_invL[hn] * ash;  // weights leave scaled by ash
     // p = 2^x / L >= tau  <=>  x >= log2(tau L), x = (s - M) log2(e): the keep
     // test needs no exponential (rows >= 2G keep nothing)
     const float keep_x = arow ? log2f(a.tau) - log2f(s_invL[hn]) : INFINITY;
@@ -1293,7 +852,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // V is not rotated) and added into the output, which the scores pass
     // zeroed
     if (kept_any) {
-        const float sc = -kRsqrtD * kRsqrtD / kWScale;
+        const float sc = -kRsqrtD * kRsqrtD / ash;
         for (int g = wave; g < G; g += kMWaves) {
             float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
@@ -1302,8 +861,8 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 v1 += s_acc[w][g][lane + 64];
             }
             if constexpr (Q8) {
-                v0 *= 1.0f / kWScale;
-                v1 *= 1.0f / kWScale;
+                v0 *= 1.0f / ash;
+                v1 *= 1.0f / ash;
             } else {
                 fwht128_lanes(v0, v1, lane);
                 v0 *= a.tab->signs[lane] * sc;
@@ -1407,6 +966,12 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.ld_scores = plan.ld_scores;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
+    if (plan.fused) {
+        a.sync = reinterpret_cast<uint32_t *>(w + plan.off_sync);
+        a.nblk = plan.nblk;
+        a.tb = plan.tb;
+        return launch_attn_fused(a, kf, vf, stream);
+    }
     switch (a.Hq / Hkv) {
         case 1: return dispatch_k<1>(a, kf, vf, s);
         case 2: return dispatch_k<2>(a, kf, vf, s);

@@ -1,0 +1,683 @@
+// Single-launch decode attention for 8 query heads per KV head (gfx950).
+//
+// The same computation as the two passes of attn.hip (chenxutan.com,
+// "TurboQuant+ deep dive", 1.1 cached decode attention; quidproquo.cc,
+// "TurboQuant+ KV cache compression", Stage 2: the QJL term of the K score;
+// yeyulingfeng.com TurboQuant+ introduction, core item 4, and chenxutan.com
+// 3.3: V rows below the weight threshold are skipped, kept weights are not
+// renormalised), in one kernel:
+//
+//   phase 1  each block scores its token range [t0, t1) of one (sequence, KV
+//            head) row exactly as the scores pass does (query rows on the
+//            matrix cores, 16-token MFMA tiles) and keeps the scores in LDS;
+//            its (max, sum exp) per head go to the workspace.
+//   barrier  the nblk blocks of a row wait for each other (one counter per
+//            row, bounded spin): exact sparse V needs the row's global softmax
+//            statistics before any V row is skipped.  The launcher sizes the
+//            grid so that every block is resident at once (one block per CU).
+//   phase 2  the exact (M, L) from all blocks' statistics; the V products of
+//            the block's range on the matrix cores, reading the scores from
+//            LDS; the block's share is rotated back (R^T) and added into the
+//            output (fp32 atomics; block 0 zeroes the output before the
+//            barrier).  A row served by one block stores its output directly.
+//
+// V products, 2-bit codebook: the symmetric 4-level codebook is exactly
+// c[2 b1 + b0] = a1 (2 b1 - 1) + a0 (2 b0 - 1) (a1 = (c3 + c2) / 2,
+// a0 = (c3 - c2) / 2), so the rotated-domain sum of head h over coordinate x
+//   y[h][x] = sum_t w_ht n_t c[code_tx] = 2 a1 X1 + 2 a0 X0 - (a1 + a0) W,
+//   X_p[h][x] = sum_t w_ht n_t bit_p(code_tx),  W[h] = sum_t w_ht n_t,
+// and each X_p is an MFMA product whose A operand carries w_ht n_t (fp16 hi
+// and lo rows, scaled below 2^14 by the block's largest V norm) and whose B
+// operand is the code bit itself: a half with only bit k set is the exact
+// fp16 power of two bitval(k), so B = (two tokens' code words) & (bit k of
+// each half) costs one AND per two k-slots, and the product's power of two is
+// divided out of its accumulator at the end.  q8 V keeps the int8-as-fp16 B
+// operand of attn.hip with the per-32 block scales in A.
+#include "attn_common.h"
+
+namespace tq {
+
+constexpr int kFW = 8;                           // waves per block
+constexpr int kFThreads = 64 * kFW;
+constexpr int kFSlice = 16 * kFW * kSliceTiles;  // tokens scored per slice (512)
+static_assert(kFSlice == kFusedSlice, "slice size shared with the host plan");
+constexpr int kFTokens = kFusedMaxTokens;        // most tokens per block (scores held in LDS)
+constexpr int kFLd = kFTokens + 16;              // LDS score row stride: head rows 16 banks apart
+constexpr float kAMax = 16384.0f;                // V-product A operands stay below 2^14
+constexpr uint64_t kSpinTicks = 25000000;        // barrier spin budget: 0.25 s of the 100 MHz clock
+
+// fp16 value of a half whose only set bit is bit k (k <= 14)
+__host__ __device__ constexpr float bitval(int k) {
+    return k <= 9 ? 1.0f / float(1 << (24 - k))
+                  : (k == 10 ? 1.0f / 16384.0f
+                             : (k == 11 ? 1.0f / 8192.0f : (k == 12 ? 1.0f / 2048.0f : (k == 13 ? 1.0f / 128.0f : 2.0f))));
+}
+
+// Fused kernel for rows whose tokens fit the block range; rows of the grid y
+// = (sequence, kv head), x = block of the row.  a.sync: two counters per row
+// (arrivals, departures), zero between calls; a.stats: [rows][nblk][8] float2.
+template <int KK, int KB, int VK>
+__global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
+                                                               const uint8_t *__restrict__ ksign,
+                                                               const uint8_t *__restrict__ knorm) {
+    constexpr int G = 8;
+    constexpr bool PROJ = KK == TQ_KIND_PROD;
+    constexpr bool VQ8 = VK == TQ_KIND_Q8;
+    static_assert(VK == TQ_KIND_Q8 || VK == TQ_KIND_MSE, "2-bit codebook V or q8 V");
+    constexpr int kPairs = KK == TQ_KIND_Q8 ? 1 : 1 << (2 * KB);
+    __shared__ uint2 s_pair[kPairs];
+    __shared__ half8 s_sgn[PROJ ? 256 : 1];
+    __shared__ float s_red[kFW][G][2];
+    __shared__ __attribute__((aligned(16))) _Float16 s_a[16][128];
+    __shared__ __attribute__((aligned(16))) _Float16 s_ap[PROJ ? 16 : 1][128];
+    // scores of the block: head h, token t0 + i at s_sc[h * kFLd + i]; after
+    // the V products, the per-wave partial sums [kFW][G][128]
+    __shared__ __attribute__((aligned(16))) float s_sc[G * kFLd];
+    __shared__ float s_M[G], s_invL[G], s_W[kFW][G];
+    __shared__ float s_vmax[kFW];
+    __shared__ int s_ok;
+    static_assert(kFW * G * 128 <= G * kFLd, "partial sums fit the score area");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = lane & 15, kq = lane >> 4;
+    const int blk = blockIdx.x, row = blockIdx.y;  // row = b * Hkv + kvh
+    const int b = row / a.Hkv, kvh = row - b * a.Hkv;
+    const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
+    const int L = seq_len_of(a, b);
+    const int t0 = blk * a.tb;
+    const int t1 = min(t0 + a.tb, L);
+    const int n_tok = max(t1 - t0, 0);
+    const int tmax = max(t1 - 1, 0);
+    const uint8_t *kid = kidx + int64_t(row) * a.T * (KK == TQ_KIND_Q8 ? 128 : 16 * KB);
+    const uint8_t *ksg = ksign + int64_t(row) * a.T * 16;
+    const uint8_t *knm = knorm + int64_t(row) * a.T * (KK == TQ_KIND_Q8 ? 8 : (PROJ ? 4 : 2));
+
+    // ---- global reads first: query, tables, V scale bound, first K slices
+    QueryLoads<G, PROJ, kFW> ql;
+    load_query(ql, a, b, kvh);
+    float lv[2] = {0.0f, 0.0f};
+    if constexpr (KK != TQ_KIND_Q8) {
+        if (tid < kPairs) {
+            lv[0] = a.tab->levels[KB - 1][tid & ((1 << KB) - 1)];
+            lv[1] = a.tab->levels[KB - 1][tid >> KB];
+        }
+    }
+    // largest V norm (codebook V) or block scale (q8 V) of the block's tokens,
+    // as fp16 bits (non-negative halves order like their bit patterns)
+    constexpr int kVR = kFTokens / kFThreads;  // tokens per thread
+    uint32_t vraw[kVR][VQ8 ? 2 : 1];
+#pragma unroll
+    for (int r = 0; r < kVR; ++r) {
+        const int tok = min(t0 + kFThreads * r + tid, tmax);
+        if constexpr (VQ8) {
+            const uint2 u = reinterpret_cast<const uint2 *>(a.vnorm)[int64_t(row) * a.T + tok];
+            vraw[r][0] = u.x;
+            vraw[r][1] = u.y;
+        } else {
+            vraw[r][0] = reinterpret_cast<const uint16_t *>(a.vnorm)[int64_t(row) * a.T + tok];
+        }
+    }
+    asm volatile("" ::: "memory");
+    const bool whole = n_tok % kFSlice == 0;
+    KTiles<KK, KB> ta, tb, tc;
+    load_ktiles<kFW>(ta, t0, tmax, wave, t, kq, kid, ksg, knm);
+    load_ktiles<kFW>(tb, t0 + kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+    // (the scale words were requested first: reducing them now waits for
+    // them only, not for the K tiles behind them)
+    uint32_t vmx = 0;
+#pragma unroll
+    for (int r = 0; r < kVR; ++r) {
+        if constexpr (VQ8) {
+            vmx = max(vmx, max(max(vraw[r][0] & 0xFFFFu, vraw[r][0] >> 16), max(vraw[r][1] & 0xFFFFu, vraw[r][1] >> 16)));
+        } else {
+            vmx = max(vmx, vraw[r][0]);
+        }
+    }
+
+    // a row shared by several blocks is summed with atomics: block 0 zeroes
+    // it before the barrier
+    if (a.nblk > 1 && blk == 0) {
+        for (int i = tid; i < G * 128; i += kFThreads)
+            __hip_atomic_store(a.out + (head0 + (i >> 7)) * 128 + (i & 127), 0.0f, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int i = tid; i < (16 - 2 * G) * 32; i += kFThreads) {
+        reinterpret_cast<uint2 *>(&s_a[2 * G][0])[i] = uint2{0u, 0u};
+        if constexpr (PROJ) reinterpret_cast<uint2 *>(&s_ap[2 * G][0])[i] = uint2{0u, 0u};
+    }
+    if constexpr (PROJ) {
+        if (tid < 256) {
+            half8 v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = ((tid >> j) & 1) ? _Float16(1.0f) : _Float16(-1.0f);
+            s_sgn[tid] = v;
+        }
+    }
+    if constexpr (KK != TQ_KIND_Q8) {
+        if (tid < kPairs) {
+            uint32_t hp = 0, lp = 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const _Float16 hi = _Float16(lv[u]);
+                const _Float16 lo = _Float16(lv[u] - float(hi));
+                hp |= uint32_t(__builtin_bit_cast(uint16_t, hi)) << (16 * u);
+                lp |= uint32_t(__builtin_bit_cast(uint16_t, lo)) << (16 * u);
+            }
+            s_pair[tid] = uint2{hp, lp};
+        }
+    }
+    build_query_rows<G>(ql, a, s_a, s_ap);
+
+    half8 aq[8], ap[4];
+    {
+        const _Float16 *ra = s_a[lane & 15];
+        if constexpr (KK == TQ_KIND_Q8) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) aq[s] = *reinterpret_cast<const half8 *>(ra + 32 * s + 8 * kq);
+#pragma unroll
+            for (int s = 4; s < 8; ++s) aq[s] = half8{};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(ra + 32 * kq + 4 * u);
+                aq[u] = __builtin_bit_cast(half8, make_uint4(v.x, v.x, v.y, v.y));
+            }
+        }
+        if constexpr (PROJ) {
+            const _Float16 *rp = s_ap[lane & 15];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ap[s] = *reinterpret_cast<const half8 *>(rp + 32 * kq + 8 * s);
+        }
+    }
+
+    // ---- phase 1: scores into LDS, running (max, sum) per own head
+    float m[kOwn<G>], l[kOwn<G>];
+    int lim[kOwn<G>];
+#pragma unroll
+    for (int j = 0; j < kOwn<G>; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.0f;
+        lim[j] = L;
+    }
+    auto sink = [&](int h, int tok, float v) { s_sc[h * kFLd + (tok - t0)] = v; };
+    auto scan = [&](auto full_c) {
+        constexpr bool F = decltype(full_c)::value;
+        if (t0 >= t1) return;
+        for (int base = t0;;) {
+            load_ktiles<kFW>(tc, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, false, G, kFW>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
+            base += kFSlice;
+            if (base >= t1) break;
+            load_ktiles<kFW>(ta, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, false, G, kFW>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
+            base += kFSlice;
+            if (base >= t1) break;
+            load_ktiles<kFW>(tb, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+            score_ktiles<F, false, G, kFW>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
+            base += kFSlice;
+            if (base >= t1) break;
+        }
+    };
+    if (whole) scan(std::true_type{});
+    else scan(std::false_type{});
+#pragma unroll
+    for (int j = 0; j < kOwn<G>; ++j) {
+        const float mx = row16_max(m[j]);
+        l[j] = row16_sum(m[j] == -INFINITY ? 0.0f : l[j] * fast_exp2(m[j] - mx));
+        m[j] = mx;
+        if (t == 0) {
+            s_red[wave][own_head<G>(kq, j)][0] = m[j];
+            s_red[wave][own_head<G>(kq, j)][1] = l[j];
+        }
+    }
+    // V scale bound of the block
+    {
+        const float vf = quad_max(row16_max(h2f(vmx)));
+        if (lane == 0) s_vmax[wave] = vf;
+    }
+    __syncthreads();
+    // block statistics per head, in natural-log units
+    float bm = -INFINITY, bl = 0.0f;
+    if (tid < G) {
+        for (int w = 0; w < kFW; ++w) bm = fmaxf(bm, s_red[w][tid][0]);
+        if (bm != -INFINITY)
+            for (int w = 0; w < kFW; ++w) bl += s_red[w][tid][1] * fast_exp2(s_red[w][tid][0] - bm);
+        bm = bm == -INFINITY ? bm : bm / kLog2e;
+        if (a.nblk > 1) {
+            float *st = a.stats + ((int64_t(row) * a.nblk + blk) * G + tid) * 2;
+            __hip_atomic_store(st, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(st + 1, bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // ---- barrier of the row's blocks (arrive, wait with a bounded spin,
+    // depart; the last block to depart resets both counters for the next call)
+    if (a.nblk > 1) {
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t *arrive = a.sync + 2 * row, *depart = arrive + 1;
+            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t tstart = __builtin_amdgcn_s_memrealtime();
+            int ok = 1;
+            while (__hip_atomic_load(arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < uint32_t(a.nblk)) {
+                __builtin_amdgcn_s_sleep(2);
+                if (__builtin_amdgcn_s_memrealtime() - tstart > kSpinTicks) {
+                    ok = 0;
+                    break;
+                }
+            }
+            s_ok = ok;
+            if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                uint32_t(a.nblk) - 1) {
+                __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(depart, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+        // exact softmax statistics of every head from all blocks of the row
+        if (wave < G) {
+            const float *st = a.stats + int64_t(row) * a.nblk * G * 2 + wave * 2;
+            float mm = -INFINITY;
+            for (int c = lane; c < a.nblk; c += 64)
+                mm = fmaxf(mm, __hip_atomic_load(st + c * G * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            mm = quad_max(row16_max(mm));
+            float ll = 0.0f;
+            if (mm != -INFINITY)
+                for (int c = lane; c < a.nblk; c += 64) {
+                    const float mc = __hip_atomic_load(st + c * G * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float lc = __hip_atomic_load(st + c * G * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ll += lc * fast_exp2((mc - mm) * kLog2e);
+                }
+            ll = quad_sum(row16_sum(ll));
+            if (lane == 0) {
+                s_M[wave] = mm;
+                s_invL[wave] = ll > 0.0f ? 1.0f / ll : 0.0f;
+            }
+        }
+    } else {
+        if (tid < G) {
+            s_M[tid] = bm;
+            s_invL[tid] = bl > 0.0f ? 1.0f / bl : 0.0f;
+        }
+        if (tid == 0) s_ok = 1;
+    }
+    __syncthreads();
+
+    // ---- phase 2: V products of the block's range
+    float vmaxf = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kFW; ++w) vmaxf = fmaxf(vmaxf, s_vmax[w]);
+    // A operands: weight x (V norm | q8 block scale) x vsh < 2^14
+    int vexp = 0;
+    (void)frexpf(vmaxf, &vexp);
+    const float vsh = ldexpf(kAMax, -vexp);
+    const int n = lane & 15;
+    const bool lo_half = n >= G;
+    const int hn = n & (G - 1);
+    const int jo = lo_half ? 4 : 0;  // lanes n and n + 8 weigh tokens 0-3 and 4-7 of their eight
+    const float Ml2 = s_M[hn] * kLog2e;
+    const float invL = s_invL[hn] * vsh;
+    const float keep_x = log2f(a.tau) - log2f(s_invL[hn]);  // p >= tau  <=>  x >= log2(tau L)
+    const int vrow = row;
+    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 8 + (n >> 1);
+    const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
+    const uint16_t *vn = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(vrow) * a.T;
+    const uint32_t *q8w = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 32 + n;
+    const uint2 *q8s = reinterpret_cast<const uint2 *>(a.vnorm) + int64_t(vrow) * a.T;
+    constexpr int NC = VQ8 ? 16 : 8;  // code dwords per lane and group
+    constexpr int NA = VQ8 ? 16 : 4;  // A-operand dwords
+
+    const int nfull = n_tok >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int ng = wv < nfull ? (nfull - 1 - wv) / kFW + 1 : 0;
+    auto gbase = [&](int k) { return t0 + 32 * (wv + kFW * min(k, ng - 1)); };
+    // q8 scales need all four blocks of each token: kept as four uint2
+    auto load_q8scl = [&](int tbs, uint2 (&sc)[4], bool tail) {
+        const int tk = tbs + 8 * kq + jo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j] = q8s[tail ? min(tk + j, tmax) : tk + j];
+    };
+    auto load_norms = [&](int tbs, uint32_t (&nr)[2], bool tail) {
+        const int tk = tbs + 8 * kq + jo;
+        if (tail) {
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = vn[min(tk + j, tmax)];
+            nr[0] = h[0] | (h[1] << 16);
+            nr[1] = h[2] | (h[3] << 16);
+        } else {
+            __builtin_memcpy(nr, vn + tk, 8);
+        }
+    };
+    auto load_codes = [&](int tbs, bool real, uint32_t (&c)[NC]) {
+        const int tk = real ? tbs + 8 * kq : t0;
+        if constexpr (VQ8) {
+            const uint32_t *cp = q8w + int64_t(tk) * 32;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                c[2 * j] = cp[32 * j];
+                c[2 * j + 1] = cp[32 * j + 16];
+            }
+        } else {
+            const uint32_t *cp = cwd32 + int64_t(tk) * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = cp[8 * j];
+        }
+    };
+    auto load_tail_codes = [&](int tbs, uint32_t (&c)[NC]) {
+        const int tk = tbs + 8 * kq;
+        if constexpr (VQ8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t *cp = q8w + int64_t(min(tk + j, tmax)) * 32;
+                c[2 * j] = cp[0];
+                c[2 * j + 1] = cp[16];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = cwd32[int64_t(min(tk + j, tmax)) * 8];
+        }
+    };
+
+    floatx4 acc[8][2];
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) acc[mm][0] = acc[mm][1] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float wsum = 0.0f;  // this lane's sum of A values (head hn), codebook V
+    // weights of head hn for tokens tbs + 8kq + jo + [0, 4): p = exp(s - M)/L,
+    // kept when p >= tau, times the token's V scale, as this row's fp16 half;
+    // returns whether any lane of the wave keeps a token (uniform)
+    auto weights = [&](int tbs, const uint32_t (&nr)[2], const uint2 (&sc)[4], uint32_t (&aw)[NA],
+                       auto whole_c) -> bool {
+        const float4 sd = *reinterpret_cast<const float4 *>(&s_sc[hn * kFLd + (tbs - t0) + 8 * kq + jo]);
+        const float sv[4] = {sd.x, sd.y, sd.z, sd.w};
+        float x[4];
+        bool kj[4], kept = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = fmaf(sv[j], kLog2e, -Ml2);
+            kj[j] = x[j] >= keep_x;
+            if constexpr (!decltype(whole_c)::value) kj[j] = kj[j] && tbs + 8 * kq + jo + j < t1;
+            kept |= kj[j];
+        }
+        if (__ballot(kept) == 0) return false;
+        float ws[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ws[j] = kj[j] ? fast_exp2(x[j]) * invL : 0.0f;
+#pragma unroll
+        for (int blkq = 0; blkq < NA / 4; ++blkq) {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (VQ8) {
+                    const uint32_t sp = blkq < 2 ? sc[j].x : sc[j].y;
+                    v[j] = ws[j] * h2f((sp >> (16 * (blkq & 1))) & 0xFFFFu);
+                } else {
+                    v[j] = ws[j] * h2f((nr[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+                    wsum += v[j];  // lanes n and n + 8 weigh different tokens
+                }
+            }
+            uint32_t hi[2], lo[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const half2v h = __builtin_convertvector(float2v{v[2 * i], v[2 * i + 1]}, half2v);
+                const half2v lw =
+                    __builtin_convertvector(float2v{v[2 * i] - float(h[0]), v[2 * i + 1] - float(h[1])}, half2v);
+                hi[i] = __builtin_bit_cast(uint32_t, h);
+                lo[i] = __builtin_bit_cast(uint32_t, lw);
+            }
+            uint32_t got[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                got[i] = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_half ? hi[i] : lo[i]), 0x128, 0xF, 0xF, false));
+            aw[4 * blkq + 0] = lo_half ? got[0] : hi[0];
+            aw[4 * blkq + 1] = lo_half ? got[1] : hi[1];
+            aw[4 * blkq + 2] = lo_half ? lo[0] : got[0];
+            aw[4 * blkq + 3] = lo_half ? lo[1] : got[1];
+        }
+        return true;
+    };
+    auto products = [&](const uint32_t (&aw)[NA], const uint32_t (&c)[NC]) {
+        if constexpr (VQ8) {
+            half8 A[4];
+#pragma unroll
+            for (int blkq = 0; blkq < 4; ++blkq)
+                A[blkq] = __builtin_bit_cast(half8, make_uint4(aw[4 * blkq], aw[4 * blkq + 1], aw[4 * blkq + 2],
+                                                               aw[4 * blkq + 3]));
+            const half2v k1152 = half2v{_Float16(1152.0f), _Float16(1152.0f)};
+#pragma unroll
+            for (int mq = 0; mq < 8; ++mq) {
+                const int w = mq >> 2, by = mq & 3;
+                const uint32_t sel = uint32_t(by) | (12u << 8) | (uint32_t(4 + by) << 16) | (12u << 24);
+                uint32_t bw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = __builtin_amdgcn_perm(c[4 * i + 2 + w], c[4 * i + w], sel) ^ 0x64806480u;
+                    bw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, x) - k1152);
+                }
+                const half8 Bv = __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    acc[mq][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2 * w + p], Bv, acc[mq][p], 0, 0, 0);
+            }
+        } else {
+            const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+            uint32_t cwd[4], cwd1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cwd[i] = __builtin_amdgcn_perm(c[2 * i + 1], c[2 * i], half_sel);
+                cwd1[i] = cwd[i] >> 1;
+            }
+#pragma unroll
+            for (int mq = 0; mq < 8; ++mq)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    // bit 2m + p of both token halves, alone in its half: an
+                    // exact fp16 power of two (bit 15, the sign, via bit 14)
+                    const int k = 2 * mq + p;
+                    const uint32_t mask = k == 15 ? 0x40004000u : (0x00010001u << k);
+                    uint32_t bw[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bw[i] = (k == 15 ? cwd1[i] : cwd[i]) & mask;
+                    acc[mq][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A, __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[mq][p], 0, 0, 0);
+                }
+        }
+    };
+    auto take = [&](const uint32_t (&c)[NC]) {
+        asm volatile("" ::"v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(c[4]), "v"(c[5]), "v"(c[6]), "v"(c[7]));
+        if constexpr (VQ8)
+            asm volatile("" ::"v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]), "v"(c[14]),
+                         "v"(c[15]));
+    };
+    if (s_ok && ng > 0) {
+        // software pipeline two groups deep: step k starts the scale words of
+        // group k + 4, forms the A operands of group k + 2 (scale words issued
+        // two steps earlier, scores from LDS), starts its code words, and runs
+        // the products of group k; three register sets rotate with k mod 3
+        uint32_t aw[3][NA], c[3][NC];
+        uint32_t NR[3][2];
+        uint2 SC[3][4];
+        bool kp[3] = {false, false, false};
+        auto load_scale = [&](int tbs, int p) {
+            if constexpr (VQ8) load_q8scl(tbs, SC[p], false);
+            else load_norms(tbs, NR[p], false);
+        };
+        load_scale(gbase(0), 0);
+        load_scale(gbase(1), 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        auto step = [&](int k, auto P) {
+            constexpr int p = decltype(P)::value, p1 = (p + 1) % 3, p2 = (p + 2) % 3;
+            load_scale(gbase(k + 4), p1);
+            asm volatile("" ::: "memory");
+            const bool more = k + 2 < ng;
+            kp[p2] = more && weights(gbase(k + 2), NR[p2], SC[p2], aw[p2], std::true_type{});
+            load_codes(gbase(k + 2), kp[p2], c[p2]);
+            asm volatile("" ::: "memory");
+            if (kp[p]) {
+                products(aw[p], c[p]);
+            } else {
+                take(c[p]);
+            }
+        };
+        for (int k = -2; k < ng; k += 3) {
+            step(k, std::integral_constant<int, 1>{});
+            step(k + 1, std::integral_constant<int, 2>{});
+            step(k + 2, std::integral_constant<int, 0>{});
+        }
+    }
+    if (s_ok && (n_tok & 31) != 0 && wv == (nfull & (kFW - 1))) {
+        const int tbs = t0 + 32 * nfull;
+        // the partial group's scores past t1 are not in LDS: the weights test
+        // masks them by position before any use of their value
+        uint32_t aw[NA], c[NC], nr[2] = {0u, 0u};
+        uint2 sc[4] = {};
+        if constexpr (VQ8) load_q8scl(tbs, sc, true);
+        else load_norms(tbs, nr, true);
+        if (weights(tbs, nr, sc, aw, std::false_type{})) {
+            load_tail_codes(tbs, c);
+            products(aw, c);
+        }
+    }
+
+    // ---- combine: rows 4kq + j of column n; rows G + h are the lo halves
+    float y[8][4];
+    if constexpr (VQ8) {
+#pragma unroll
+        for (int mq = 0; mq < 8; ++mq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[mq][j] = n >= 8 ? acc[mq][1][j] : acc[mq][0][j];
+    } else {
+        const float c2 = a.tab->levels[1][2], c3 = a.tab->levels[1][3];
+        const float a1 = 0.5f * (c3 + c2), a0 = 0.5f * (c3 - c2);
+#pragma unroll
+        for (int mq = 0; mq < 8; ++mq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                y[mq][j] = (2.0f * a1 / bitval(2 * mq + 1)) * acc[mq][1][j] + (2.0f * a0 / bitval(2 * mq)) * acc[mq][0][j];
+    }
+#pragma unroll
+    for (int mq = 0; mq < 8; ++mq)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const auto r =
+                __builtin_amdgcn_permlane32_swap(__float_as_uint(y[mq][j]), __float_as_uint(y[mq][j]), false, false);
+            y[mq][j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    // W of head hn: lanes n, n ^ 8 and the four lane groups
+    if constexpr (!VQ8) {
+        wsum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(wsum), 0x128, 0xF, 0xF, false));
+        wsum = quad_sum(wsum);
+    }
+    __syncthreads();  // every wave is done with the scores in LDS
+    float *s_acc = s_sc;  // [kFW][G][128]
+    if (kq < 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float *hrow = s_acc + (wave * G + 4 * kq + j) * 128;
+            float4 *d0 = reinterpret_cast<float4 *>(hrow + (VQ8 ? 4 * n : 8 * n));
+            float4 *d1 = reinterpret_cast<float4 *>(hrow + (VQ8 ? 64 + 4 * n : 8 * n + 4));
+            *d0 = make_float4(y[0][j], y[1][j], y[2][j], y[3][j]);
+            *d1 = make_float4(y[4][j], y[5][j], y[6][j], y[7][j]);
+        }
+    }
+    if (lane < G) s_W[wave][lane] = VQ8 ? 0.0f : wsum;
+    __syncthreads();
+    // the block's share of head `wave`, rotated back (R^T = D H / sqrt(d);
+    // q8 V is not rotated)
+    {
+        const int g = wave;
+        float v0 = 0.0f, v1 = 0.0f, wt = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kFW; ++w) {
+            v0 += s_acc[(w * G + g) * 128 + lane];
+            v1 += s_acc[(w * G + g) * 128 + lane + 64];
+            wt += s_W[w][g];
+        }
+        const float unsh = 1.0f / vsh;
+        if constexpr (VQ8) {
+            v0 *= unsh;
+            v1 *= unsh;
+        } else {
+            const float wc = a.tab->levels[1][3] * wt;  // (a1 + a0) W = c3 W
+            v0 -= wc;
+            v1 -= wc;
+            fwht128_lanes(v0, v1, lane);
+            const float sc = kRsqrtD * kRsqrtD * unsh;
+            v0 *= a.tab->signs[lane] * sc;
+            v1 *= a.tab->signs[lane + 64] * sc;
+        }
+        if (!s_ok) {
+            v0 = __builtin_nanf("");
+            v1 = v0;
+        }
+        float *o = a.out + (head0 + g) * 128;
+        if (a.nblk > 1) {
+            if (n_tok > 0 || !s_ok) {
+                __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            o[lane] = v0;
+            o[lane + 64] = v1;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launch
+template <int KK, int KB, int VK>
+static int launch_fused_t(const AttnArgs &a, hipStream_t s) {
+    dim3 grid(unsigned(a.nblk), unsigned(a.B * a.Hkv));
+    hipLaunchKernelGGL((attn_fused_kernel<KK, KB, VK>), grid, dim3(kFThreads), 0, s, a, a.kidx, a.ksign, a.knorm);
+    return int(hipGetLastError());
+}
+
+template <int VK>
+static int fused_dispatch_k(const AttnArgs &a, tq_format kf, hipStream_t s) {
+    if (kf.kind == TQ_KIND_Q8) return launch_fused_t<TQ_KIND_Q8, 8, VK>(a, s);
+    if (kf.kind == TQ_KIND_PROD) {
+        switch (kf.bits) {
+            case 1: return launch_fused_t<TQ_KIND_PROD, 1, VK>(a, s);
+            case 2: return launch_fused_t<TQ_KIND_PROD, 2, VK>(a, s);
+            case 3: return launch_fused_t<TQ_KIND_PROD, 3, VK>(a, s);
+        }
+    } else {
+        switch (kf.bits) {
+            case 1: return launch_fused_t<TQ_KIND_MSE, 1, VK>(a, s);
+            case 2: return launch_fused_t<TQ_KIND_MSE, 2, VK>(a, s);
+            case 3: return launch_fused_t<TQ_KIND_MSE, 3, VK>(a, s);
+            case 4: return launch_fused_t<TQ_KIND_MSE, 4, VK>(a, s);
+        }
+    }
+    return int(hipErrorInvalidValue);
+}
+
+int launch_attn_fused(const AttnArgs &a, tq_format kf, tq_format vf, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (vf.kind == TQ_KIND_Q8) return fused_dispatch_k<TQ_KIND_Q8>(a, kf, s);
+    if (vf.kind == TQ_KIND_MSE && vf.bits == 2) return fused_dispatch_k<TQ_KIND_MSE>(a, kf, s);
+    return int(hipErrorInvalidValue);
+}
+
+// Blocks of the fused kernel resident at once on the current device (the
+// occupancy calculator's per-CU count times the CU count), cached per device;
+// 0 when the kernel cannot be resident.  The grid of the fused path never
+// exceeds it when a row spans several blocks.
+int fused_capacity() {
+    static int cache[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    const int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v != 0) return v > 0 ? v : 0;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(attn_fused_kernel<TQ_KIND_PROD, 2, TQ_KIND_MSE>), kFThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        per_cu = cus = 0;
+    const int cap = per_cu > 0 && cus > 0 ? per_cu * cus : 0;
+    __atomic_store_n(&cache[dev], cap > 0 ? cap : -1, __ATOMIC_RELAXED);
+    return cap;
+}
+
+}  // namespace tq

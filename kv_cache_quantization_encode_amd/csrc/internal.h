@@ -52,8 +52,19 @@ struct AttnPlan {
     int chunk;       // tokens per chunk (multiple of 256)
     int ld_scores;   // score row stride in floats: T rounded up to 32
     size_t off_scores, off_stats, total;
+    // single-launch path (decode, 8 query heads per kv head, 2-bit codebook or
+    // q8 V): nblk blocks of tb tokens per row; barrier counters at off_sync
+    int fused, nblk, tb;
+    size_t off_sync;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
+// The plan of one attention call: the single-launch path when its shape and
+// the device allow it, else the two-pass plan.  capacity = blocks of the
+// single-launch kernel resident at once on the current device (0: unknown).
+AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int capacity);
+// Tokens per block and block size limits of the single-launch kernel.
+constexpr int kFusedSlice = 512;
+constexpr int kFusedMaxTokens = 4096;
 // Prefill queries of one sequence that share a scores pass: the largest of
 // 8/g, ..., 2, 1 (g = query heads per kv head) dividing Tq, so that the
 // group's g * qp rows fill at most the 8 query rows of one pass.
@@ -84,6 +95,10 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
                 tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
                 int Hkv, int T, int tq, const int32_t *seq_lens, float tau, float *out, void *ws,
                 const AttnPlan &plan, void *stream);
+// Single-launch decode attention (attn_fused.hip); capacity of the current
+// device for it (0 when it cannot run).
+int launch_attn_fused(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
+int fused_capacity();
 int launch_minmax_quant(const void *x, int64_t n, int bits, void *codes, void *scale, void *zero,
                         void *stream);
 int launch_minmax_dequant(const void *codes, const void *scale, const void *zero, int64_t n,

@@ -232,6 +232,7 @@ def alloc_packed(f: tq_format, n_vec: int, device="cuda") -> Packed:
 def alloc_workspace(B, Hq, Hkv, T, kf, vf, device="cuda"):
     import torch
     n = tq_attn_workspace_bytes(B, Hq, Hkv, T, kf, vf)
-    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    # zero-filled: the barrier counters of the single-launch path start at 0
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
     assert ws.data_ptr() % 256 == 0
     return ws, n

@@ -431,7 +431,8 @@ def attention_decode(q, k_hat, v_hat, tau: float = 1e-6, seq_lens=None):
     q: [B, Hq, d]; k_hat, v_hat: [B, Hkv, T, d].  Scores <q, k>/sqrt(d), full
     softmax over the first seq_len tokens, then V rows whose normalised weight
     is below tau are dropped without renormalising.  q head h reads kv head
-    floor(h / (Hq/Hkv)).  Returns (out [B, Hq, d] float64, p [B, Hq, T]).
+    floor(h / (Hq/Hkv)).  seq_lens[b] is clamped to [0, T].  Returns
+    (out [B, Hq, d] float64, p [B, Hq, T]).
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
@@ -440,7 +441,8 @@ def attention_decode(q, k_hat, v_hat, tau: float = 1e-6, seq_lens=None):
     out = np.zeros((B, Hq, d))
     probs = np.zeros((B, Hq, T))
     for b in range(B):
-        L = T if seq_lens is None else int(seq_lens[b])
+        # a length outside [0, T] means the nearest end of that range
+        L = T if seq_lens is None else min(max(int(seq_lens[b]), 0), T)
         for h in range(Hq):
             kv = h // g
             if L == 0:

@@ -139,10 +139,18 @@ def check_encode(x16: np.ndarray, kind: str, bits: int, packed: np.ndarray, tab:
     bad = mism & ~near
     assert not bad.any(), f"{int(bad.sum())} code mismatches away from boundaries"
     stats = {"rows": int(len(sel)), "code_exempt": float(near.mean()), "code_mismatch": int(mism.sum())}
-    # the exceptions (all inside the band) are at most 0.01 % of coordinates;
-    # the band itself holds ~2e-5 * sum_k phi(t_k) of Gaussian coordinates
-    assert mism.mean() <= max_exempt
-    assert near.mean() <= 5 * max_exempt
+    # the mismatches (all inside the band) make up at most 0.01 % of the
+    # coordinates (one is allowed in inputs of fewer than 10^4 coordinates).
+    # The band population is a property of the data: ~2e-5 * sum_k phi(t_k) of
+    # Gaussian coordinates, 6.7e-5 at 4 bits, so it is held to the same 0.01 %
+    # with an allowance of three Poisson standard deviations for the sample
+    # size.  Hand-built rows that sit on boundaries on purpose pass
+    # max_exempt = 1.
+    cap = max(max_exempt * near.size, 1.0)
+    band_cap = cap + 3.0 * math.sqrt(cap)
+    assert mism.sum() <= cap, f"{int(mism.sum())} code mismatches in the band (cap {cap:.1f})"
+    assert near.sum() <= band_cap, \
+        f"{int(near.sum())} coordinates within {BOUNDARY_TOL} of a boundary (cap {band_cap:.1f})"
     assert np.all(_ulp_diff16(u["norm"][sel], enc["norm"]) <= 1), "norm differs by more than 1 fp16 ulp"
     if kind == "prod":
         P = O.qjl_projection_from_codes(xs, gidx, bits, tab)
@@ -150,8 +158,9 @@ def check_encode(x16: np.ndarray, kind: str, bits: int, packed: np.ndarray, tab:
         sb = u["bits_qjl"][sel]
         smis = (sb != (P > 0)) & ok
         assert not smis.any(), f"{int(smis.sum())} QJL sign mismatches away from zero"
-        assert (sb != (P > 0)).mean() <= max_exempt
-        assert (~ok).mean() <= 5 * max_exempt
+        assert (sb != (P > 0)).sum() <= cap
+        assert (~ok).sum() <= band_cap, \
+            f"{int((~ok).sum())} projections within {PROJ_TOL} of zero (cap {band_cap:.1f})"
         n64 = enc["n64"]
         e = enc["z"] - tab.levels[bits][gidx]
         gamma = n64 * np.sqrt(np.sum(e * e, axis=-1)) / math.sqrt(128)
@@ -187,7 +196,7 @@ def gpu_attention(ctx, case, kpacked, vpacked, kf, vf, tau, seq_lens=None):
     vp = torch.from_numpy(vpacked).cuda()
     out = Guarded(B * Hq * 128 * 4)
     wsb = T.tq_attn_workspace_bytes(B, Hq, Hkv, Tn, kf, vf)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     lens = None if seq_lens is None else torch.from_numpy(np.asarray(seq_lens, np.int32)).cuda()
     note(f"attention {case.name} B={B} Hq={Hq} Hkv={Hkv} T={Tn} kf={kf} vf={vf} tau={tau}")
     T.tq_attn_decode(ctx, q, kp, vp, kf, vf, B, Hq, Hkv, Tn, lens, tau, out.ptr, ws, wsb)

@@ -565,3 +565,72 @@ def test_rotated_domain_scores_equal_dense_scores(oracle_tables):
     rotated = (n / math.sqrt(128) * (zhat @ qrot) +
                math.sqrt(math.pi / 2) / 128 * gmm * (sgn @ qproj)) / math.sqrt(128)
     assert np.allclose(dense, rotated, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------
+# QJL projection from given codes (the checker behind every GPU sign-bit
+# comparison) and the reconstruction-quality measure
+# ----------------------------------------------------------------------------
+def test_qjl_projection_from_codes_matches_encode_and_permutation(oracle_tables):
+    """P = S (z - c[idx]) for the given codes [quidproquo.cc, Stage 2].  On the
+    encoder's own codes it is the encoder's projection; with a permutation
+    matrix as S it is the rotated residual permuted, where z comes from the
+    textbook FWHT here (not from the oracle's rotation): (S e)_i = e_pi(i)."""
+    tab = oracle_tables
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((12, 128))
+    x[:, :3] *= 15
+    perm = np.roll(np.arange(128), 5)  # a cyclic shift: not its own inverse
+    tabp = copy.copy(tab)
+    tabp.S = np.eye(128)[perm]
+    z = _fwht(x * tab.signs) / np.linalg.norm(x, axis=1)[:, None]  # sqrt(d) R x / ||x||
+    for bits in (1, 2, 3):
+        enc = O.encode(x, bits, True, tab)
+        P = O.qjl_projection_from_codes(x, enc["idx"], bits, tab)
+        assert np.allclose(P, enc["P"], rtol=0, atol=1e-12)
+        idx = rng.integers(0, 1 << bits, (12, 128))  # arbitrary codes, not the encoder's
+        e = z - np.asarray(MAX_1960_LEVELS_FULL[bits])[idx]
+        Pp = O.qjl_projection_from_codes(x, idx, bits, tabp)
+        assert np.allclose(Pp, e[:, perm], atol=2e-4)  # printed levels carry 4 decimals
+        Pe = O.qjl_projection_from_codes(x, idx, bits, tab)
+        assert np.allclose(Pe, (z - tab.levels[bits][idx]) @ tab.S.T, atol=1e-9)
+
+
+# all 2^b levels of Max (1960), ascending
+MAX_1960_LEVELS_FULL = {b: [-v for v in reversed(MAX_1960[b])] + list(MAX_1960[b]) for b in MAX_1960}
+
+
+def test_quality_closed_forms():
+    """MSE and cosine [mac-code issue #1, quality measure]: a scaled copy has
+    cosine 1 (or -1) and MSE (s - 1)^2 mean x^2; orthogonal rows (Hadamard rows)
+    have cosine 0; a 3-4-5 example by hand."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((6, 128))
+    q = O.quality(x, 2 * x)
+    assert abs(q["mse"] - np.mean(x ** 2)) < 1e-12
+    assert abs(q["cos_flat"] - 1) < 1e-12 and abs(q["cos_vec_mean"] - 1) < 1e-12
+    q = O.quality(x, -0.5 * x)
+    assert abs(q["mse"] - 2.25 * np.mean(x ** 2)) < 1e-12
+    assert abs(q["cos_flat"] + 1) < 1e-12 and abs(q["cos_vec_mean"] + 1) < 1e-12
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    q = O.quality(H[:4], H[4:8])
+    assert abs(q["cos_flat"]) < 1e-15 and abs(q["cos_vec_mean"]) < 1e-15
+    assert q["mse"] == 2.0  # distinct Hadamard rows differ in exactly half the entries, by 2
+    a = np.zeros((2, 128))
+    b = np.zeros((2, 128))
+    a[0, :2], b[0, :2] = (3, 4), (4, 3)   # cosine 24/25
+    a[1, 2], b[1, 3] = 1.0, 2.0           # orthogonal row: cosine 0
+    q = O.quality(a, b)
+    assert abs(q["cos_vec_mean"] - (24 / 25 + 0) / 2) < 1e-15
+    assert abs(q["cos_flat"] - 24 / math.sqrt(26 * 29)) < 1e-15
+    assert abs(q["mse"] - (1 + 1 + 1 + 4) / 256) < 1e-15
+
+
+def test_attention_decode_clamps_lengths():
+    """Lengths outside [0, T] mean the nearest end (the library's convention):
+    a negative length attends to nothing, a length past T to all T tokens."""
+    q, k, v = _rand_attn(T=7)
+    out, _ = O.attention_decode(q, k, v, tau=1e-6, seq_lens=np.array([-3, 12]))
+    full, _ = O.attention_decode(q, k, v, tau=1e-6)
+    assert np.all(out[0] == 0)
+    assert np.array_equal(out[1], full[1])

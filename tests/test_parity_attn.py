@@ -138,3 +138,74 @@ def test_attention_long_chunks_ragged_batch(ctx, oracle_tables):
     lens = np.array([3000, 1, 0, 769, 2304, 2305, 1500, 2999], np.int32)
     got, _, _ = _run(ctx, oracle_tables, c, ("prod", 3), ("mse", 4), 1e-6, seq_lens=lens)
     assert np.all(got[2] == 0.0)
+
+
+def test_attention_eight_heads_one_block_per_row(ctx, oracle_tables):
+    """More (sequence, KV head) rows than CUs (33 x 8): the single-launch path
+    gives each row one block, which writes its output directly; lengths cut
+    rows at 0, 1, a 32-token edge and a 512-token slice edge."""
+    c = W.llama8b(seed=203, T=900, Hq=64, Hkv=8, B=33)
+    lens = np.array([900, 0, 1, 513, 512, 33, 32] + [900 - 31 * i for i in range(26)], np.int32)
+    got, _, _ = _run(ctx, oracle_tables, c, ("prod", 2), ("mse", 2), 1e-6, seq_lens=lens)
+    assert np.all(got[1] == 0.0)
+
+
+def test_attention_eight_heads_repeated_calls_one_workspace(ctx, oracle_tables):
+    """The row barrier of the single-launch path leaves its counters at zero:
+    five calls on one workspace (a row spread over several blocks) agree with
+    each other and with the oracle."""
+    import torch
+    from kv_cache_quantization_encode_amd import turbokv as T
+    c = W.llama70b_layer(3, T=3000, Hkv=2, Hq=16)
+    kf, vf = ("prod", 2), ("mse", 2)
+    kp, vp = _encode_case(ctx, c, kf, vf)
+    B, Hq, Hkv, Tn = c.shape
+    K, V = G.tf(*kf), G.tf(*vf)
+    ws, wsb = T.alloc_workspace(B, Hq, Hkv, Tn, K, V)
+    q, kd, vd = G.to_dev_f16(c.q), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda()
+    outs = []
+    for r in range(5):
+        out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        G.note(f"repeated call {r}")
+        T.tq_attn_decode(ctx, q, kd, vd, K, V, B, Hq, Hkv, Tn, None, 1e-6, out, ws, wsb)
+        outs.append(out.cpu().numpy())
+    ref = G.oracle_attention(c, kp, vp, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6)
+    for o in outs:
+        assert np.isfinite(o).all()
+        assert np.max(np.abs(o - outs[0])) <= 1e-5
+        assert np.max(np.abs(o - ref)) <= G.ATTN_ATOL
+
+
+def test_attention_q8_v_large_values_peaked(ctx, oracle_tables):
+    """q8 V rows with |v| up to ~6e4 under a needle-peaked softmax, 8 query
+    heads per KV head: the A operands (weight x block scale) must stay inside
+    fp16 on the single-launch decode path and on the two-pass prefill path.
+    Outputs reach ~6e4, so the bound adds 1e-5 of the output scale (a few
+    fp32 ulps of a weighted sum) to the absolute tolerance."""
+    import torch
+    from kv_cache_quantization_encode_amd import turbokv as T
+    n = W.needle(B=2, T=1024, Hq=16, Hkv=2)
+    rng = np.random.default_rng(77)
+    v = np.clip(rng.standard_normal(n.v.shape) * 2e4, -65000, 65000).astype(np.float16)
+    c = W.AttnCase("needle.bigv", n.k, v, n.q)
+    kf, vf = ("prod", 3), ("q8", 8)
+    kp, vp = _encode_case(ctx, c, kf, vf)
+    got = G.gpu_attention(ctx, c, kp, vp, G.tf(*kf), G.tf(*vf), 1e-6)
+    ref = G.oracle_attention(c, kp, vp, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6)
+    scale = float(np.max(np.abs(ref)))
+    assert scale > 1e4 and np.isfinite(got).all()
+    assert np.max(np.abs(got - ref)) <= G.ATTN_ATOL + 1e-5 * scale
+    # prefill: the last 4 positions of each sequence as queries (two-pass kernels)
+    B, Hq, Hkv, Tn = c.shape
+    Tq = 4
+    qq = np.repeat(c.q[:, None], Tq, axis=1)
+    K, V = G.tf(*kf), G.tf(*vf)
+    wsb = T.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, Tn, Tq, K, V)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Tq, Hq, 128), dtype=torch.float32, device="cuda")
+    G.note("prefill q8 V large values")
+    T.tq_attn_prefill(ctx, G.to_dev_f16(qq), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), K, V, B, Hq,
+                      Hkv, Tn, Tq, None, 1e-6, out, ws, wsb)
+    gp = out.cpu().numpy()
+    assert np.isfinite(gp).all()
+    assert np.max(np.abs(gp[:, -1] - ref)) <= G.ATTN_ATOL + 1e-5 * scale

@@ -30,7 +30,7 @@ def _prefill(ctx, tab, case, q, kf, vf, tau, lens, kv_batches=None):
     vp, _ = G.gpu_encode(ctx, v, *vf, as_v=True)
     K, V = G.tf(*kf), G.tf(*vf)
     wsb = T.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, Tn, Tq, K, V)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     out = G.Guarded(B * Tq * Hq * 128 * 4)
     lt = None if lens is None else torch.from_numpy(np.asarray(lens, np.int32)).cuda()
     G.note(f"prefill B={B} Tq={Tq} Hq={Hq} Hkv={Hkv} T={Tn} kf={kf} vf={vf} tau={tau} lens={lens}")
