@@ -251,16 +251,22 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     }
 
     // ---- barrier of the row's blocks (arrive, wait with a bounded spin,
-    // depart; the last block to depart resets both counters for the next call)
+    // depart; the last block to depart resets both counters for the next call).
+    // Everything exchanged between blocks (statistics, counters, the zeroed
+    // output) goes through device-coherent atomic accesses, ordered by waiting
+    // for this thread's stores to complete before the arrival; acquire/release
+    // fences would write back and invalidate the whole L2 instead.
     if (a.nblk > 1) {
-        __threadfence();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have landed
+        asm volatile("" ::: "memory");
         __syncthreads();
         if (tid == 0) {
             uint32_t *arrive = a.sync + 2 * row, *depart = arrive + 1;
-            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const uint64_t tstart = __builtin_amdgcn_s_memrealtime();
             int ok = 1;
-            while (__hip_atomic_load(arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < uint32_t(a.nblk)) {
+            while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < uint32_t(a.nblk)) {
                 __builtin_amdgcn_s_sleep(2);
                 if (__builtin_amdgcn_s_memrealtime() - tstart > kSpinTicks) {
                     ok = 0;
@@ -268,10 +274,10 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
                 }
             }
             s_ok = ok;
-            if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+            if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 uint32_t(a.nblk) - 1) {
                 __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(depart, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         __syncthreads();
