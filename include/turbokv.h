@@ -154,6 +154,20 @@ tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_pac
                          const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
                          int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
                          void *workspace, size_t ws_bytes, void *stream);
+/* tq_attn_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and conventions as
+ * tq_attn_decode; the workspace is a library-owned device array of 8 MiB per
+ * GPU (held until the process ends), and this call allocates nothing.  The
+ * ctx's device must be current (TQ_ERR_INVALID_ARG otherwise).  A shape whose
+ * workspace (tq_attn_workspace_bytes) exceeds 8 MiB returns
+ * TQ_ERR_WORKSPACE without launching.  Calls on one GPU share the array:
+ * calls that overlap in time on that GPU (different streams, no ordering)
+ * race and must not be issued; calls ordered on one stream are safe. */
+tq_status tq_attn_decode_noalloc(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                                 const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                                 int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                                 void *stream);
 /* Workspace of tq_attn_decode (0 for an invalid shape, or when B*Hkv > 65535). */
 size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_format vf);
 

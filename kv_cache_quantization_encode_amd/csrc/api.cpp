@@ -185,6 +185,8 @@ tq_status tq_codebook_init(tq_ctx **ctx, int head_dim, int qjl_dim, uint64_t see
         delete host; delete c; return TQ_ERR_HIP;
     }
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) { delete host; delete c; return TQ_ERR_UNSUPPORTED; }
+    // this device's copy of the library-owned attention workspace
+    if (scratch_prepare(dev) != 0) { delete host; delete c; return TQ_ERR_HIP; }
     void *d = nullptr;
     if (hipMalloc(&d, sizeof(DevTables)) != hipSuccess) { delete host; delete c; return TQ_ERR_ALLOC; }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -312,6 +314,21 @@ static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_p
                        sparse_v_tau, out_f32, workspace, plan, stream) == 0
                ? TQ_OK
                : TQ_ERR_HIP;
+}
+
+tq_status tq_attn_decode_noalloc(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
+                                 const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
+                                 int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
+                                 void *stream) {
+    if (!ctx) return TQ_ERR_INVALID_ARG;
+    // the library-owned workspace lives on the ctx's device: it must be current
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TQ_ERR_HIP;
+    if (dev != ctx->device) return TQ_ERR_INVALID_ARG;
+    void *ws = scratch_device_ptr(dev);
+    if (!ws) return TQ_ERR_HIP;
+    return attn_call(ctx, q_f16, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, 1, seq_lens, sparse_v_tau, out_f32, ws,
+                     kScratchBytes, stream);
 }
 
 tq_status tq_attn_decode(const tq_ctx *ctx, const void *q_f16, const void *k_packed,

@@ -99,6 +99,14 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
 // device for it (0 when it cannot run).
 int launch_attn_fused(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
 int fused_capacity();
+// Library-owned attention workspace (scratch.hip): kScratchBytes on every
+// GPU the library runs on.  scratch_prepare looks up this device's copy (the
+// device must be current); scratch_device_ptr returns it (nullptr if not
+// prepared).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxScratchDevices = 64;
+int scratch_prepare(int device);
+void *scratch_device_ptr(int device);
 int launch_minmax_quant(const void *x, int64_t n, int bits, void *codes, void *scale, void *zero,
                         void *stream);
 int launch_minmax_dequant(const void *codes, const void *scale, const void *zero, int64_t n,
