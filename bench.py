@@ -1,19 +1,23 @@
 """Benchmark of the TurboQuant KV-cache hot path on one MI355X.
 
-Workload (one step = the whole hot path over one batch): a Llama-8B-like
-layer, 32 query / 8 KV heads, head_dim 128, 32768 cached tokens, batch 1.
-Each step encodes all 32768 tokens' K (turbo4: 3-bit codebook + 1-bit QJL)
-and V (4-bit codebook) and runs one decode-attention step (sparse V at
-1e-6) over a packed cache.  Inputs are synthetic (seeded, see workloads.py)
-and resident in HBM before the timed region.
+Headline (one step = one decode step of a 70B-like model over its whole
+compressed cache): 80 layers x 8 KV / 64 query heads x 131072 cached tokens,
+batch 1; turbo3 K (2-bit codebook + QJL) and 2-bit V, layers 0, 1, 78, 79 at
+q8 for K and V; sparse V at 1e-6.  The 80 per-layer attention calls are one
+HIP graph; the packed cache (8.0 GB) is resident in HBM before the timed
+region and far larger than the 256 MB Infinity Cache.  `value` = decode
+attention GB/s over the algorithmic bytes of the step (all K bytes, the V
+bytes of 128-byte lines that hold a kept row, q and out).
 
-The working set of one step (~170 MB) fits in the 256 MB Infinity Cache, so
-the benchmark rotates over 8 copies of the inputs and packed caches (~1.4 GB),
-and step i decodes the cache encoded at step i-4: every kernel reads data
-that was last touched >600 MB of traffic earlier.
+Extra lines in the same JSON: the llama8b-like layer (encode all 32768 tokens
+then decode), the tiny case, the min-max baseline, the batched needle decode,
+a decode loop with append, causal prefill and reconstruction quality.  The
+oracle (float64 NumPy on the host cores) is timed on bounded samples of the
+headline workload (`cpu_baseline`) and of the other configurations
+(`cpu_baselines`).
 
-Prints one JSON line.  The oracle (float64 NumPy on the host cores) is timed
-on a bounded slice of the same workload as `cpu_baseline`.
+Inputs are synthetic: seeded generators with the distributions of
+workloads.py.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -35,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the MI355X
 N_COPIES = 8
 LAG = 4
-KERNEL_SOURCES = ["encode.hip", "attn.hip", "device_common.h"]
+KERNEL_SOURCES = ["encode.hip", "attn.hip", "attn_fused.hip", "attn_common.h", "device_common.h"]
 
 
 def parse():
@@ -43,15 +47,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-tokens", type=int, default=32768,
-                    help="tokens of the workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the tiny, min-max, 70B-like full-cache and batched needle measurements")
+                    help="only the headline 70B-like decode step (no extra lines, no per-config oracle timings)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--only", choices=["tiny", "minmax", "decode_70b", "decode_needle", "decode_loop", "prefill",
-                                       "quality"],
+                                       "quality", "llama8b"],
                     help="run only this extra measurement and print its JSON (for profiling)")
     return ap.parse_args()
 
@@ -78,11 +80,11 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_profile(kernel: str, section: str = "kernels"):
-    """Per-launch figures from committed rocprofv3 --pmc summaries (HBM bytes
-    under "kernels", MFMA utilisation under "mfma"), if they were taken on the
-    current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic_llama8b.json")
+def load_profile(kernel: str, section: str = "kernels", name: str = "traffic_llama8b.json"):
+    """Per-launch figures from a committed rocprofv3 --pmc summary under
+    profiles/ (HBM bytes under "kernels", MFMA utilisation under "mfma"), if
+    it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -92,51 +94,102 @@ def load_profile(kernel: str, section: str = "kernels"):
     return t.get(section, {}).get(kernel)
 
 
-def cpu_baseline(tokens: int):
-    """Time the oracle on `tokens` positions of the same workload (all heads)."""
+def _threads():
     from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
 
-    from kv_cache_quantization_encode_amd import workloads as W
+
+def _oracle_decode(case, kf, vf, tab, tau=1e-6, batches=None):
+    """The oracle on one attention case: encode + pack K and V (timed apart),
+    then dense dequantisation of the packed bytes and fp64 attention.  Returns
+    (encode s, decode s, algorithmic decode bytes as the GPU counts them)."""
     from oracle import turbokv_oracle as O
-
-    case = W.llama8b(T=tokens)
-    tab = O.Tables(128, seed=42)
     B, Hq, Hkv, T = case.shape
-    k = case.k.reshape(-1, 128)
-    v = case.v.reshape(-1, 128)
-    t0 = time.perf_counter()
-    ek = O.encode(k, 3, True, tab)
-    ev = O.encode(v, 4, False, tab)
-    kp = O.pack_tq(ek, "prod", 3, 128)
-    vp = O.pack_tq(ev, "mse", 4, 128)
-    t1 = time.perf_counter()
+    bs = list(range(B)) if batches is None else list(batches)
+    k = case.k[bs].reshape(-1, 128)
+    v = case.v[bs].reshape(-1, 128)
     n = k.shape[0]
-    kh = O.dequant_packed(kp, "prod", 3, tab, n).reshape(B, Hkv, T, 128)
-    vh = O.dequant_packed(vp, "mse", 4, tab, n).reshape(B, Hkv, T, 128)
-    out, p = O.attention_decode(case.q.astype(np.float64), kh, vh, 1e-6)
+    t0 = time.perf_counter()
+    packed = []
+    for x, (kind, bits) in ((k, kf), (v, vf)):
+        if kind == "q8":
+            q, sc = O.q8_quant(x.astype(np.float64))
+            packed.append(O.pack_q8(q, sc, 128))
+        else:
+            packed.append(O.pack_tq(O.encode(x, bits, kind == "prod", tab), kind, bits, 128))
+    t1 = time.perf_counter()
+    kh = O.dequant_packed(packed[0], kf[0], kf[1], tab, n).reshape(len(bs), Hkv, T, 128)
+    vh = O.dequant_packed(packed[1], vf[0], vf[1], tab, n).reshape(len(bs), Hkv, T, 128)
+    _, p = O.attention_decode(case.q[bs].astype(np.float64), kh, vh, tau)
     t2 = time.perf_counter()
     g = Hq // Hkv
-    keep_rows = int(np.sum(np.any((p >= 1e-6).reshape(B, Hkv, g, T), axis=2)))
-    attn_bytes = n * 68 + keep_rows * 64 + n * 2 + B * Hq * 128 * 6
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {
-        "value": attn_bytes / (t2 - t1) / 1e9,
-        "unit": "GB/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{tokens} of 32768 tokens, all 8 KV / 32 query heads: oracle encode+pack "
-                  f"({t1 - t0:.1f} s, {tokens / (t1 - t0) / 1e6:.5f} Mtokens/s) then dense "
-                  f"dequant + fp64 attention ({t2 - t1:.1f} s); value = decode-attn GB/s",
-        "encode_mtok_s": tokens / (t1 - t0) / 1e6,
-        "host_cpus": os.cpu_count(),
-    }
+    keep = np.any((p >= tau).reshape(len(bs), Hkv, g, T), axis=2).reshape(-1)
+    kb = O.bytes_per_vector(kf[0], kf[1]) * n
+    dbytes = kb + v_line_bytes(vf[0], vf[1], keep) + len(bs) * Hq * 128 * 6
+    return t1 - t0, t2 - t1, dbytes
 
 
-def kept_v_rows(TK, ctx, q, kbuf, kf, B, Hq, Hkv, T, tau, dev):
-    """Number of V rows the exact sparse-V rule keeps (some query head of the
+def cpu_baseline_70b():
+    """The oracle on a sample of the headline workload: layers 0, 1, 40, 79
+    (q8 boundary and turbo3 K + 2-bit V middle layers), KV heads 0 and 7 with
+    their 8 query heads each, all 131072 tokens, from the NumPy recipe of
+    workloads.py.  value = decode GB/s (dense dequant + fp64 attention over
+    the packed bytes); the oracle's own encode is timed apart."""
+    from kv_cache_quantization_encode_amd import workloads as W
+    from oracle import turbokv_oracle as O
+    tab = O.Tables(128, seed=42)
+    te = td = by = 0.0
+    tokens = 0
+    for layer in (0, 1, 40, 79):
+        c = W.llama70b_layer(layer)
+        g = c.shape[1] // c.shape[2]
+        for h in (0, 7):
+            sub = W.AttnCase(c.name, np.ascontiguousarray(c.k[:, h:h + 1]), np.ascontiguousarray(c.v[:, h:h + 1]),
+                             np.ascontiguousarray(c.q[:, h * g:(h + 1) * g]))
+            e, d, b = _oracle_decode(sub, c.meta["kf"], c.meta["vf"], tab)
+            te, td, by, tokens = te + e, td + d, by + b, tokens + sub.shape[3]
+        del c
+    return {"value": by / td / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"70B-like decode, layers 0, 1, 40, 79 x KV heads 0 and 7 (8 query heads each) x 131072 "
+                      f"tokens: dense dequant + fp64 attention {td:.1f} s over {by / 1e9:.3f} GB; the oracle's "
+                      f"encode + pack of the same rows {te:.1f} s",
+            "encode_mtok_s": tokens / te / 1e6 if te > 0 else 0.0, "host_cpus": os.cpu_count()}
+
+
+def cpu_baselines_other():
+    """The oracle on the other configurations (same recipes as workloads.py):
+    tiny in full; the llama8b-like layer in full; the min-max workload on one
+    of its 32 layers (K and V); the needle batch on 8 of its 64 sequences."""
+    from kv_cache_quantization_encode_amd import workloads as W
+    from oracle import turbokv_oracle as O
+    tab = O.Tables(128, seed=42)
+    out = {"cores": _threads(), "host_cpus": os.cpu_count()}
+    for name, case, kf, vf, batches, note in (
+            ("tiny", W.tiny(), ("prod", 2), ("mse", 2), None, "1 KV head x 1024 tokens, in full"),
+            ("llama8b", W.llama8b(), ("prod", 3), ("mse", 4), None, "8 KV / 32 query heads x 32768 tokens, in full"),
+            ("needle", W.needle(), ("prod", 3), ("mse", 2), list(range(0, 64, 8)), "8 of 64 sequences x 8192 tokens")):
+        e, d, b = _oracle_decode(case, kf, vf, tab, batches=batches)
+        B = case.shape[0] if batches is None else len(batches)
+        tok = B * case.shape[3]
+        out[name] = {"decode_gbs": b / d / 1e9, "encode_mtok_s": tok / e / 1e6, "decode_s": round(d, 2),
+                     "encode_s": round(e, 2), "sample": note}
+    x = W.minmax_tensor(layers=1)
+    t0 = time.perf_counter()
+    for bits in (2, 3, 4):
+        code, scale, zero = O.minmax_quant(x, 64, bits)
+        O.minmax_dequant(code, scale, zero)
+    t = time.perf_counter() - t0
+    n = x.size
+    out["minmax"] = {"quant_dequant_gbs": 3 * 2 * n * (2 + 3 / 8 + 4 / 64) / t / 1e9, "seconds": round(t, 2),
+                     "sample": "one of 32 layers (8 KV heads x 4096 tokens x 128), quantise + dequantise at 2, 3, 4 bits"}
+    return out
+
+
+def kept_v_mask(TK, ctx, q, kbuf, kf, B, Hq, Hkv, T, tau, dev):
+    """Which V rows the exact sparse-V rule keeps (some query head of the
     group has weight >= tau), from the library's own dequantisation of the
-    packed K and a float32 softmax on the GPU.  Byte accounting only; it runs
-    outside every timed region."""
+    packed K and a float32 softmax on the GPU, as a host bool array [B*Hkv*T].
+    Byte accounting only; it runs outside every timed region."""
     import torch
     n_vec = B * Hkv * T
     khat = torch.empty((n_vec, 128), dtype=torch.float16, device=dev)
@@ -146,18 +199,35 @@ def kept_v_rows(TK, ctx, q, kbuf, kf, B, Hq, Hkv, T, tau, dev):
     qq = q.view(B * Hkv, g, 128).float().transpose(1, 2).contiguous()
     scores = torch.bmm(kh, qq) / math.sqrt(128)  # [B*Hkv, T, g]
     p = torch.softmax(scores, dim=1)
-    kept = int((p >= tau).any(dim=2).sum().item())
+    keep = (p >= tau).any(dim=2).reshape(-1).cpu().numpy()
     del khat, kh, scores, p
-    return kept
+    return keep
+
+
+def v_line_bytes(kind: str, bits: int, keep: np.ndarray) -> int:
+    """V bytes a decode must read at 128-byte line granularity: the lines of
+    the code plane and of the norm / scale plane that hold a kept row."""
+    row_codes = 128 if kind == "q8" else 16 * bits
+    row_norm = 8 if kind == "q8" else 2
+    total = 0
+    for per_row in (row_codes, row_norm):
+        rows_per_line = max(128 // per_row, 1)
+        n = keep.size // rows_per_line * rows_per_line
+        lines = keep[:n].reshape(-1, rows_per_line).any(axis=1)
+        total += int(lines.sum()) * 128 + (128 if keep[n:].any() else 0)
+    return total
 
 
 def v_bytes_read(TK, vf, n_vec, kept):
-    """V bytes the decode reads: index rows of kept tokens only, plus every
-    fp16 norm (codebook V: the norm scales each candidate's weight) or the
-    block scales of kept rows (q8 V)."""
+    """V bytes at row granularity (kept index rows plus every norm); kept for
+    the smaller extra lines."""
     if vf.kind == TK.KIND_Q8:
         return kept * (128 + 8)
     return kept * 16 * vf.bits + n_vec * 2
+
+
+def kept_v_rows(TK, ctx, q, kbuf, kf, B, Hq, Hkv, T, tau, dev):
+    return int(kept_v_mask(TK, ctx, q, kbuf, kf, B, Hq, Hkv, T, tau, dev).sum())
 
 
 def outlier_normal_gpu(gen, shape, n_out, dev, scale=20.0):
@@ -198,51 +268,146 @@ def graph_time(fn, reps, warm, stream):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
 
 
+MID_KERNEL = "attn_fused_kernel<PROD,2,MSE> (70B-like middle layer)"
+BND_KERNEL = "attn_fused_kernel<Q8,8,Q8> (70B-like boundary layer)"
+
+
 def bench_70b(TK, ctx, dev, reps=10, warm=3):
     """70B-like full cache on one GPU: 80 layers x 8 KV heads x 131072 tokens,
     64 query heads; turbo3 K (2-bit codebook + QJL) + 2-bit V, layers 0, 1,
     78, 79 at q8 for K and V.  K/V of each layer are N(0,1) with 4 channels
     x20 (seed 404 + layer, drawn on the GPU), encoded once; one decode step =
-    the 80 per-layer attention calls, replayed as one HIP graph."""
+    the 80 per-layer attention calls, replayed as one HIP graph.  The 76
+    middle-layer calls and the 4 boundary-layer calls are also timed as
+    graphs of their own (HIP events on the replay stream), which gives the
+    average launch duration of each attention kernel."""
     import torch
     L, Hkv, Hq, T, B = 80, 8, 64, 131072, 1
     n_vec = B * Hkv * T
     tau = 1e-6
     boundary = (0, 1, 78, 79)
     layers = []
-    moved = logical = 0
+    alg = logical = 0
+    alg_mid = alg_bnd = 0
     for l in range(L):
         gen = torch.Generator(device=dev)
         gen.manual_seed(404 + l)
         if l in boundary:
-            kf, vf = TK.Q8, TK.Q8
+            kf, vf, fk, fv = TK.Q8, TK.Q8, ("q8", 8), ("q8", 8)
         else:
-            kf, vf = TK.turbo_k(3), TK.mse(2)
+            kf, vf, fk, fv = TK.turbo_k(3), TK.mse(2), ("prod", 2), ("mse", 2)
         k = outlier_normal_gpu(gen, (Hkv, T, 128), 4, dev).view(-1, 128)
         v = outlier_normal_gpu(gen, (Hkv, T, 128), 4, dev).view(-1, 128)
         q = torch.randn((B, Hq, 128), generator=gen, device=dev).half()
         kp, vp = TK.alloc_packed(kf, n_vec), TK.alloc_packed(vf, n_vec)
         TK.tq_encode_kv(ctx, k, v, n_vec, kf, vf, kp.buf, vp.buf)
         del k, v
-        kept = kept_v_rows(TK, ctx, q, kp.buf, kf, B, Hq, Hkv, T, tau, dev)
-        kb = int(kp.layout.total_bytes)
-        moved += kb + v_bytes_read(TK, vf, n_vec, kept) + B * Hq * 128 * (2 + 4)
-        logical += kb + int(vp.layout.total_bytes) + B * Hq * 128 * (2 + 4)
+        keep = kept_v_mask(TK, ctx, q, kp.buf, kf, B, Hq, Hkv, T, tau, dev)
+        kb = n_vec * (136 if fk[0] == "q8" else 16 * fk[1] + 16 + 4)
+        by = kb + v_line_bytes(fv[0], fv[1], keep) + B * Hq * 128 * (2 + 4)
+        alg += by
+        if l in boundary:
+            alg_bnd += by
+        else:
+            alg_mid += by
+        logical += int(kp.layout.total_bytes) + int(vp.layout.total_bytes) + B * Hq * 128 * (2 + 4)
         out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
-        layers.append((q, kp, vp, kf, vf, out))
+        layers.append((l, q, kp, vp, kf, vf, out))
     ws, wsb = TK.alloc_workspace(B, Hq, Hkv, T, TK.turbo_k(3), TK.mse(2))
 
-    def step():
-        for q, kp, vp, kf, vf, out in layers:
-            TK.tq_attn_decode(ctx, q, kp.buf, vp.buf, kf, vf, B, Hq, Hkv, T, None, tau, out, ws, wsb)
+    def calls(which):
+        def run():
+            for l, q, kp, vp, kf, vf, out in layers:
+                if which(l):
+                    TK.tq_attn_decode(ctx, q, kp.buf, vp.buf, kf, vf, B, Hq, Hkv, T, None, tau, out, ws, wsb)
+        return run
 
-    t = graph_time(step, reps, warm, None)
+    t = graph_time(calls(lambda l: True), reps, warm, None)
+    t_mid = graph_time(calls(lambda l: l not in boundary), reps, warm, None) / (L - len(boundary))
+    t_bnd = graph_time(calls(lambda l: l in boundary), reps, warm, None) / len(boundary)
+    per_mid, per_bnd = alg_mid / (L - len(boundary)), alg_bnd / len(boundary)
     res = {"workload": "70B-like decode step: 80 layers x 8 KV / 64 q heads x 131072 tokens, batch 1; "
-                       "turbo3 K + 2-bit V, layers 0,1,78,79 q8; one HIP graph of 80 calls",
-           "step_ms": round(t * 1e3, 4), "moved_gb": round(moved / 1e9, 4), "logical_gb": round(logical / 1e9, 4),
-           "moved_gbs": round(moved / t / 1e9, 1), "frac_hbm": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
-           "logical_gbs": round(logical / t / 1e9, 1)}
+                       "turbo3 K + 2-bit V, layers 0,1,78,79 q8 K and V; sparse V tau 1e-6; one HIP graph of 80 calls",
+           "step_ms": round(t * 1e3, 4), "alg_gb": round(alg / 1e9, 4), "logical_gb": round(logical / 1e9, 4),
+           "alg_gbs": round(alg / t / 1e9, 1), "frac_hbm": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+           "logical_gbs": round(logical / t / 1e9, 1),
+           "middle_layer_us": round(t_mid * 1e6, 2), "middle_layer_alg_bytes": int(per_mid),
+           "middle_layer_frac_hbm": round(per_mid / t_mid / 1e9 / HBM_PEAK_GBS, 4),
+           "boundary_layer_us": round(t_bnd * 1e6, 2), "boundary_layer_alg_bytes": int(per_bnd),
+           "boundary_layer_frac_hbm": round(per_bnd / t_bnd / 1e9 / HBM_PEAK_GBS, 4),
+           "_t": t, "_alg": alg, "_t_mid": t_mid, "_per_mid": per_mid, "_t_bnd": t_bnd, "_per_bnd": per_bnd}
     del layers, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_llama8b(TK, ctx, dev, steps=20, warmup=5):
+    """Llama-8B-like layer: 32 query / 8 KV heads, head_dim 128, 32768 cached
+    tokens, batch 1.  One step encodes all 32768 tokens' K (turbo4: 3-bit
+    codebook + QJL) and V (4-bit codebook) and runs one decode-attention step
+    (sparse V at 1e-6) over a packed cache.  The working set of a step (~170
+    MB) fits in the 256 MB Infinity Cache, so the measurement rotates over 8
+    copies of inputs and packed caches (~1.4 GB) and step i decodes the cache
+    encoded at step i - 4.  HIP events on the launch stream per kernel group."""
+    import torch
+    from kv_cache_quantization_encode_amd import workloads as W
+    case = W.llama8b()
+    B, Hq, Hkv, T = case.shape
+    n_vec = B * Hkv * T
+    kf, vf, tau = TK.turbo_k(4), TK.mse(4), 1e-6
+    stream = torch.cuda.current_stream()
+    k0 = torch.from_numpy(case.k.reshape(-1, 128)).to(dev)
+    v0 = torch.from_numpy(case.v.reshape(-1, 128)).to(dev)
+    q = torch.from_numpy(case.q).to(dev)
+    ks = [k0] + [k0.clone() for _ in range(N_COPIES - 1)]
+    vs = [v0] + [v0.clone() for _ in range(N_COPIES - 1)]
+    kps = [TK.alloc_packed(kf, n_vec) for _ in range(N_COPIES)]
+    vps = [TK.alloc_packed(vf, n_vec) for _ in range(N_COPIES)]
+    ws, wsb = TK.alloc_workspace(B, Hq, Hkv, T, kf, vf)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        s = i % N_COPIES
+        d = (i - LAG) % N_COPIES
+        if ev is not None:
+            ev[0].record(stream)
+        TK.tq_encode_kv(ctx, ks[s], None, n_vec, kf, vf, kps[s].buf, None)
+        if ev is not None:
+            ev[1].record(stream)
+        TK.tq_encode_kv(ctx, None, vs[s], n_vec, kf, vf, None, vps[s].buf)
+        if ev is not None:
+            ev[2].record(stream)
+        TK.tq_attn_decode(ctx, q, kps[d].buf, vps[d].buf, kf, vf, B, Hq, Hkv, T, None, tau, out, ws, wsb)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(N_COPIES):
+        step(i)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    enc_k = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    enc_v = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+    d = (warmup + steps - 1 - LAG) % N_COPIES
+    keep = kept_v_mask(TK, ctx, q, kps[d].buf, kf, B, Hq, Hkv, T, tau, dev)
+    attn_alg = n_vec * 68 + v_line_bytes("mse", 4, keep) + B * Hq * 128 * 6
+    enc_k_bytes, enc_v_bytes = n_vec * (256 + 68), n_vec * (256 + 66)
+    res = {"workload": "llama8b-like layer: 32 q / 8 kv heads, head_dim 128, 32768 tokens, batch 1; turbo4 K "
+                       "(3-bit codebook + QJL) + 4-bit V, sparse V tau 1e-6",
+           "decode_attn_us": round(attn * 1e6, 2), "decode_attn_gbs": round(attn_alg / attn / 1e9, 1),
+           "decode_attn_frac_hbm": round(attn_alg / attn / 1e9 / HBM_PEAK_GBS, 4),
+           "v_rows_read_frac": round(float(keep.mean()), 4),
+           "encode_mtok_s": round(T / (enc_k + enc_v) / 1e6, 2),
+           "encode_gbs": round((enc_k_bytes + enc_v_bytes) / (enc_k + enc_v) / 1e9, 1),
+           "encode_k_us": round(enc_k * 1e6, 2), "encode_v_us": round(enc_v * 1e6, 2),
+           "encode_k_frac_hbm": round(enc_k_bytes / enc_k / 1e9 / HBM_PEAK_GBS, 4),
+           "encode_v_frac_hbm": round(enc_v_bytes / enc_v / 1e9 / HBM_PEAK_GBS, 4)}
+    del kps, vps, ks, vs, ws
     torch.cuda.empty_cache()
     return res
 
@@ -543,162 +708,70 @@ def main():
     import torch
 
     from kv_cache_quantization_encode_amd import turbokv as TK
-    from kv_cache_quantization_encode_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     TK.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    ctx = TK.tq_codebook_init(128, 128, 42)
     if args.only:
         if args.only == "minmax":
             r = bench_minmax(TK, dev)
         elif args.only == "quality":
-            r = bench_quality(TK, TK.tq_codebook_init(128, 128, 42), dev)
+            r = bench_quality(TK, ctx, dev)
+        elif args.only == "llama8b":
+            r = bench_llama8b(TK, ctx, dev, steps=10, warmup=2)
         else:
-            ctx1 = TK.tq_codebook_init(128, 128, 42)
             fn = {"tiny": bench_tiny, "decode_70b": bench_70b, "decode_needle": bench_needle,
                   "decode_loop": bench_decode_loop, "prefill": bench_prefill}[args.only]
-            r = fn(TK, ctx1, dev, reps=5, warm=2)
+            r = fn(TK, ctx, dev, reps=5, warm=2)
+        r = {k: v for k, v in r.items() if not k.startswith("_")}
         print(json.dumps({args.only: r}), flush=True)
         return
 
-    case = W.llama8b()
-    B, Hq, Hkv, T = case.shape
-    n_vec = B * Hkv * T
-    kf, vf, tau = TK.turbo_k(4), TK.mse(4), 1e-6
+    # headline: one decode step of the 70B-like model over its whole cache
+    h = bench_70b(TK, ctx, dev, reps=args.steps, warm=args.warmup)
 
-    k0 = torch.from_numpy(case.k.reshape(-1, 128)).to(dev)
-    v0 = torch.from_numpy(case.v.reshape(-1, 128)).to(dev)
-    q = torch.from_numpy(case.q).to(dev)
-    ks = [k0] + [k0.clone() for _ in range(N_COPIES - 1)]
-    vs = [v0] + [v0.clone() for _ in range(N_COPIES - 1)]
-    kps = [TK.alloc_packed(kf, n_vec) for _ in range(N_COPIES)]
-    vps = [TK.alloc_packed(vf, n_vec) for _ in range(N_COPIES)]
-    ws, wsb = TK.alloc_workspace(B, Hq, Hkv, T, kf, vf)
-    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
-    ctx = TK.tq_codebook_init(128, 128, 42)
-
-    def step(i, ev=None):
-        s = i % N_COPIES
-        d = (i - LAG) % N_COPIES
-        if ev is not None:
-            ev[0].record(stream)
-        TK.tq_encode_kv(ctx, ks[s], None, n_vec, kf, vf, kps[s].buf, None)
-        if ev is not None:
-            ev[1].record(stream)
-        TK.tq_encode_kv(ctx, None, vs[s], n_vec, kf, vf, None, vps[s].buf)
-        if ev is not None:
-            ev[2].record(stream)
-        TK.tq_attn_decode(ctx, q, kps[d].buf, vps[d].buf, kf, vf, B, Hq, Hkv, T, None, tau, out, ws, wsb)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for i in range(N_COPIES):  # every packed cache holds a valid encoding
-        step(i)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    enc_k = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    enc_v = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    attn = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
-
-    # sparse-V bookkeeping (byte accounting only, outside the timed region):
-    # which V rows does the exact rule keep?  Scores from the library's own
-    # dequantisation of the packed K, softmax in float64.
-    d = (args.warmup + args.steps - 1 - LAG) % N_COPIES
-    khat = torch.empty((n_vec, 128), dtype=torch.float16, device=dev)
-    TK.tq_decode_kv(ctx, kps[d].buf, kf, n_vec, khat)
-    kh = khat.view(B, Hkv, 1, T, 128).double()
-    qq = q.view(B, Hkv, Hq // Hkv, 128, 1).double()
-    scores = torch.matmul(kh, qq).squeeze(-1) / math.sqrt(128)  # [B, Hkv, g, T]
-    p = torch.softmax(scores, dim=-1)
-    keep = (p >= tau).any(dim=2)
-    kept_rows = int(keep.sum().item())
-    del khat, kh
-
-    k_bytes = n_vec * 68
-    v_row = 64
-    attn_alg = k_bytes + kept_rows * v_row + n_vec * 2 + B * Hq * 128 * (2 + 4)
-    attn_logical = k_bytes + n_vec * 66 + B * Hq * 128 * (2 + 4)
-    enc_k_bytes = n_vec * (256 + 68)
-    enc_v_bytes = n_vec * (256 + 66)
-    t_attn, t_k, t_v = float(np.mean(attn)), float(np.mean(enc_k)), float(np.mean(enc_v))
-    attn_gbs = attn_alg / t_attn / 1e9
-    enc_mtok = T / (t_k + t_v) / 1e6
-
-    kernels = {
-        "encode_tq_kernel<3,true>": (t_k, enc_k_bytes),
-        "encode_tq_kernel<4,false>": (t_v, enc_v_bytes),
-        "attention (scores+values)": (t_attn, attn_alg),
-    }
-    dom = max(kernels, key=lambda n: kernels[n][0])
-
-    def roof(name):
-        t, by = kernels[name]
+    def roof(name, t, by, profile_key):
         ach = by / t / 1e9
-        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_profile(name), "kernel": name,
-             "avg_us": round(t * 1e6, 2), "alg_bytes_per_launch": by}
-        mf = load_profile(name, "mfma")
-        if mf and mf.get("flops_per_launch"):
-            # matrix-core side of the same kernel: busy share from the counters,
-            # fp16 MFMA rate from the counted flops and the live duration
-            r["mfma"] = {"util": round(mf["util_pct"] / 100.0, 3),
-                         "achieved_tflops": round(mf["flops_per_launch"] / t / 1e12, 1),
-                         "peak_tflops": MFMA_F16_PEAK_TFLOPS}
-        return r
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": load_profile(profile_key, name="traffic_70b.json"),
+                "kernel": name, "avg_us": round(t * 1e6, 2), "alg_bytes_per_launch": int(by)}
 
     res = {
         "metric": METRIC,
-        "value": round(attn_gbs, 1),
+        "value": h["alg_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": h["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "llama8b-like layer: 32 q / 8 kv heads, head_dim 128, 32768 tokens, batch 1; "
-                               "turbo4 K (3-bit codebook + QJL) + 4-bit V, sparse V tau 1e-6",
-                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "decode_attn_us": round(t_attn * 1e6, 2),
-        "decode_attn_frac_hbm": round(attn_gbs / HBM_PEAK_GBS, 4),
-        "decode_attn_logical_gbs": round(attn_logical / t_attn / 1e9, 1),
-        "v_rows_read_frac": round(kept_rows / n_vec, 4),
-        "encode_mtok_s": round(enc_mtok, 2),
-        "encode_gbs": round((enc_k_bytes + enc_v_bytes) / (t_k + t_v) / 1e9, 1),
-        "encode_frac_hbm": round((enc_k_bytes + enc_v_bytes) / (t_k + t_v) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": roof(dom),
-        "roofline_attn": roof("attention (scores+values)"),
-        "roofline_encode_k": roof("encode_tq_kernel<3,true>"),
+        "config": {"workload": h["workload"], "global_batch": 1, "seq_len": 131072, "parallelism": "none (1 GPU)"},
+        "frac_hbm": h["frac_hbm"],
+        "decode_70b": {k: v for k, v in h.items() if not k.startswith("_")},
+        "roofline": roof(MID_KERNEL, h["_t_mid"], h["_per_mid"], "mid"),
+        "roofline_boundary": roof(BND_KERNEL, h["_t_bnd"], h["_per_bnd"], "bnd"),
         "source_hash": source_hash(),
     }
-    del kps, vps, ks, vs, ws
-    torch.cuda.empty_cache()
     if not args.no_extra:
+        res["llama8b"] = bench_llama8b(TK, ctx, dev)
         res["tiny"] = bench_tiny(TK, ctx, dev)
         res["minmax"] = bench_minmax(TK, dev)
-        res["decode_70b"] = bench_70b(TK, ctx, dev)
         res["decode_needle"] = bench_needle(TK, ctx, dev)
         res["decode_loop"] = bench_decode_loop(TK, ctx, dev)
         res["prefill"] = bench_prefill(TK, ctx, dev)
         res["quality"] = bench_quality(TK, ctx, dev)
     TK.tq_ctx_destroy(ctx)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline_70b()
+        if not args.no_extra:
+            res["cpu_baselines"] = cpu_baselines_other()
     print(json.dumps(res), flush=True)
 
 
