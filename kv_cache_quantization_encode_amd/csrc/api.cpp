@@ -105,6 +105,7 @@ AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int
     int64_t nblk = capacity / rows;
     if (nblk < 1) nblk = 1;
     if (nblk > slices) nblk = slices;
+    if (nblk > kFusedMaxBlocks) nblk = kFusedMaxBlocks;
     const int64_t tb = (slices + nblk - 1) / nblk * kFusedSlice;
     if (tb > kFusedMaxTokens) return p;
     nblk = (int64_t(T) + tb - 1) / tb;

@@ -335,12 +335,15 @@ __device__ __forceinline__ float partner32(float x, int lane) {
 }
 
 // After fold_rows, each lane group kq (lanes 16 kq .. 16 kq + 15, one token
-// per lane) takes over kOwn<G> heads: head kq + 4i for G >= 4, head kq % G
-// below (duplicated across groups).  own_scores moves the scores there.
+// per lane) takes over kOwn<G> heads: for G = 8, groups 0 and 2 hold heads
+// 0..3 and groups 1 and 3 heads 4..7 in e[0..3], and group kq keeps heads
+// 4 (kq & 1) + 2 (kq >> 1) + {0, 1}; G = 4: head kq (via a lane swap); below,
+// head kq % G (duplicated across groups).  own_scores moves the scores there.
 template <int G>
 constexpr int kOwn = G >= 8 ? 2 : 1;
 template <int G>
 __device__ __forceinline__ int own_head(int kq, int i) {
+    if constexpr (G >= 8) return 4 * (kq & 1) + 2 * (kq >> 1) + i;
     return G >= 4 ? kq + 4 * i : kq % G;
 }
 template <int G>
@@ -359,26 +362,154 @@ __device__ __forceinline__ void own_scores(const float (&e)[4], int lane, float 
         const float hi = partner32((kq & 1) ? e[3] : e[2], lane);
         o[0] = kq < 2 ? lo : hi;
     } else {
-        // groups 0, 2 hold heads 0..3 and groups 1, 3 heads 4..7 in e[0..3]
-        const float own = kq == 0 ? e[0] : kq == 1 ? e[1] : kq == 2 ? e[2] : e[3];
-        const int want = kq ^ 1;  // what the partner group needs from this lane
-        const float send = want == 0 ? e[0] : want == 1 ? e[1] : want == 2 ? e[2] : e[3];
-        const float recv = partner16(send, lane);
-        o[0] = (kq & 1) ? recv : own;  // head kq
-        o[1] = (kq & 1) ? own : recv;  // head kq + 4
+        const bool up = (kq & 2) != 0;
+        o[0] = up ? e[2] : e[0];
+        o[1] = up ? e[3] : e[1];
     }
 }
+
+// ------------------------------------------------------- bit-plane scoring
+// 1- and 2-bit codebooks are sums of signed constants chosen by single code
+// bits: c[b] = a (2b - 1) (1 bit, a = c1) and c[2 b1 + b0] = a1 (2 b1 - 1) +
+// a0 (2 b0 - 1) (2 bits, a1 = (c3 + c2) / 2, a0 = (c3 - c2) / 2), and the QJL
+// term is sum_p q_proj,p (2 bit_p - 1).  So every K product is
+//   sum over bits of (2 coef q) x bit  -  a per-head constant,
+// and its MFMA B operand is the packed code word itself: w & (bit k of both
+// 16-bit halves) is two fp16 halves whose only set bit is bit k, i.e. the
+// code bit times the exact power of two 2^(k - 24) (subnormal for k <= 9;
+// bits 10..15 are first shifted down to 4..9).  The query operand of each
+// k-slot carries 2 coef q 2^(S0 - k), so every product has the same scale
+// 2^(S0 - 24), which the epilogue divides out.  One AND per two k-slots, no
+// table reads.  Lane (r, kq) of source dword j, product u (0..3) holds k-slot
+// pairs i = 0..3 from bit k = 4u + i of the dword's low half (slot 2i) and
+// high half (slot 2i + 1).
+template <int G, int BITS, bool PROJ>
+struct PlaneOps {
+    half8 ab[4 * BITS];              // codebook products
+    half8 aq[PROJ ? 4 : 1];          // QJL products
+    float sc_cb, sc_q;               // 2^(24 - S0) of each term
+    float ccb[kOwn<G>], cq[kOwn<G>]; // constants of the own heads
+};
+
+// Bit k of a 16-bit half after the shift that brings bits 10..15 to 4..9.
+__device__ __forceinline__ constexpr int plane_pos(int k) { return k <= 9 ? k : k - 6; }
+
+// Coordinate (or projection) of k-slot half h (0 low, 1 high) for bit k of
+// source dword j of lane group kq.
+template <int BITS>
+__device__ __forceinline__ int plane_coord(int kq, int j, int k, int h) {
+    if constexpr (BITS == 2) return 32 * kq + 16 * j + 8 * h + (k >> 1);
+    return 32 * kq + 16 * h + k;  // 1-bit codes and QJL signs: one bit per coordinate
+}
+
+// Builds the plane operands from the stacked fp16 hi/lo query rows s_a
+// (q_rot) and s_ap (q_proj).  s_cst: 2 * G floats of LDS scratch, s_qmax: 2
+// floats, zero before the call.  Ends with a barrier.  NW = waves per block.
+template <int G, int BITS, bool PROJ, int NW>
+__device__ __forceinline__ void build_plane_ops(PlaneOps<G, BITS, PROJ> &po, const DevTables *tab,
+                                                const _Float16 (*s_a)[128], const _Float16 (*s_ap)[128],
+                                                float *s_cst, float *s_qmax) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, kq = lane >> 4;
+    auto q32 = [&](const _Float16 (*rows)[128], int h, int c) { return float(rows[h][c]) + float(rows[G + h][c]); };
+    // per-head sums and the largest |q| of each term (wave w takes heads w, w + NW, ..)
+    float mq = 0.0f, mp = 0.0f;
+    for (int h = wave; h < G; h += NW) {
+        const float x0 = q32(s_a, h, lane), x1 = q32(s_a, h, lane + 64);
+        float sx = x0 + x1;
+        mq = fmaxf(mq, fmaxf(fabsf(x0), fabsf(x1)));
+        float sp = 0.0f;
+        if constexpr (PROJ) {
+            const float p0 = q32(s_ap, h, lane), p1 = q32(s_ap, h, lane + 64);
+            sp = p0 + p1;
+            mp = fmaxf(mp, fmaxf(fabsf(p0), fabsf(p1)));
+        }
+        sx = quad_sum(row16_sum(sx));
+        sp = quad_sum(row16_sum(sp));
+        if (lane == 0) {
+            s_cst[h] = sx;
+            s_cst[G + h] = sp;
+        }
+    }
+    mq = quad_max(row16_max(mq));
+    mp = quad_max(row16_max(mp));
+    if (lane == 0) {
+        // non-negative floats order like their bit patterns
+        atomicMax(reinterpret_cast<int *>(&s_qmax[0]), __float_as_int(mq));
+        atomicMax(reinterpret_cast<int *>(&s_qmax[1]), __float_as_int(mp));
+    }
+    __syncthreads();
+    float a1, a0;
+    if constexpr (BITS == 2) {
+        a1 = 0.5f * (tab->levels[1][3] + tab->levels[1][2]);
+        a0 = 0.5f * (tab->levels[1][3] - tab->levels[1][2]);
+    } else {
+        a1 = a0 = tab->levels[0][1];
+    }
+    int e_cb = 0, e_q = 0;
+    (void)frexpf(s_qmax[0] * 2.0f * fmaxf(a1, a0), &e_cb);
+    (void)frexpf(s_qmax[1] * 2.0f, &e_q);
+    const int s0_cb = 14 - e_cb, s0_q = 14 - e_q;  // every |A| < 2^14
+    po.sc_cb = ldexpf(1.0f, 24 - s0_cb);
+    po.sc_q = ldexpf(1.0f, 24 - s0_q);
+    const bool arow = r < 2 * G, lo = r >= G;
+    const int hr = lo ? r - G : r;
+    auto part = [&](float x) -> _Float16 {
+        const _Float16 h = _Float16(x);
+        return !arow ? _Float16(0.0f) : (lo ? _Float16(x - float(h)) : h);
+    };
+#pragma unroll
+    for (int j = 0; j < BITS; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 4 * u + i;
+                    const int c = plane_coord<BITS>(kq, j, k, h);
+                    const float coef = 2.0f * ((BITS == 2 && (k & 1)) ? a1 : a0);
+                    const float x = arow ? q32(s_a, hr, c) * coef * ldexpf(1.0f, s0_cb - plane_pos(k)) : 0.0f;
+                    po.ab[4 * j + u][2 * i + h] = part(x);
+                }
+    if constexpr (PROJ) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 4 * u + i;
+                    const int c = plane_coord<1>(kq, 0, k, h);
+                    const float x = arow ? q32(s_ap, hr, c) * 2.0f * ldexpf(1.0f, s0_q - plane_pos(k)) : 0.0f;
+                    po.aq[u][2 * i + h] = part(x);
+                }
+    }
+    // constants: sum_i q c[idx] = sum (2 coef q) bit - (a1 + a0) sum q (1 bit:
+    // a sum q); sum_p q_proj (2 bit - 1) = sum 2 q_proj bit - sum q_proj
+#pragma unroll
+    for (int j = 0; j < kOwn<G>; ++j) {
+        const int h = own_head<G>(kq, j);
+        po.ccb[j] = (BITS == 2 ? a1 + a0 : a1) * s_cst[h];
+        po.cq[j] = PROJ ? s_cst[G + h] : 0.0f;
+    }
+    __syncthreads();
+}
+
+struct NoPlanes {};
 
 // Scores one slice (NT tiles per wave) and folds it into the running (max,
 // sum) of each own head; store(h, tok, s) receives the score of head h (in
 // the block's head numbering) and token tok, -inf past a row's causal limit.
 // NW = waves per block (token layout as in load_ktiles).
-template <bool FULL, bool ROWLIM, int G, int NW = 4, int KIND, int BITS, typename Store>
+template <bool FULL, bool ROWLIM, int G, int NW = 4, int KIND, int BITS, typename Store, typename PL = NoPlanes>
 __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
                                              int kq, const uint2 *s_pair, const half8 *s_sgn,
                                              const half8 (&aq)[8], const half8 (&ap)[4], Store &&store,
                                              const int (&lim)[kOwn<G>], float (&m)[kOwn<G>],
-                                             float (&l)[kOwn<G>]) {
+                                             float (&l)[kOwn<G>], const PL *pl = nullptr) {
+    constexpr bool PLANES = !std::is_same<PL, NoPlanes>::value;
+    static_assert(!PLANES || (KIND != TQ_KIND_Q8 && BITS <= 2), "bit planes: 1- and 2-bit codebooks");
     using KT = KTiles<KIND, BITS>;
     float scv[KT::NT][kOwn<G>];  // this lane's scores of the slice in log2 units, -inf where absent
     // B operands of the rotated-key path.  Field f (codes 2f, 2f+1 of the
@@ -406,7 +537,32 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         const int tok = base + wave * 16 + 16 * NW * i + t;
         const bool valid = FULL || tok < t1;
         float e[4];
-        if constexpr (KIND == TQ_KIND_Q8) {
+        float cn = 0.0f, cg = 0.0f;  // plane path: per-token factors of the head constants
+        if constexpr (PLANES) {
+            floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+            auto products = [&](uint32_t w, const half8 *A, floatx4 &acc) {
+                const uint32_t ws = w >> 6;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint32_t bw[4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int k = 4 * u + q4;
+                        bw[q4] = (k <= 9 ? w : ws) & (0x00010001u << plane_pos(k));
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A[u], __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc, 0, 0, 0);
+                }
+            };
+#pragma unroll
+            for (int j = 0; j < BITS; ++j) products(d.wk[i][j], pl->ab + 4 * j, d0);
+            if constexpr (KIND == TQ_KIND_PROD) products(d.sw[i], pl->aq, d1);
+            cn = h2f(d.nn[i] & 0xFFFFu) * (1.0f / 128.0f);
+            cg = KIND == TQ_KIND_PROD ? h2f(d.nn[i] >> 16) * kQjlOverSqrtD : 0.0f;
+            const float n = cn * pl->sc_cb, gq = cg * pl->sc_q;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
+        } else if constexpr (KIND == TQ_KIND_Q8) {
             const uint2 scl = d.q8s[i];
             const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
 #pragma unroll
@@ -451,6 +607,10 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         fold_rows<G>(e);
         float o[kOwn<G>];
         own_scores<G>(e, 16 * kq + t, o);
+        if constexpr (PLANES) {
+#pragma unroll
+            for (int j = 0; j < kOwn<G>; ++j) o[j] -= fmaf(cn, pl->ccb[j], cg * pl->cq[j]);
+        }
         // lane (t, kq) now holds the scores of its own heads for token tok;
         // one store per head and lane (on the whole-slice path without a
         // branch, so the memory counters stay exact).  A row whose query sees
@@ -464,19 +624,19 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         }
     });
     // running (max, sum) per lane and own head, once per slice, in log2 units
+    // (no branch: with every value -inf the base is 0 and each term exp2(-inf))
 #pragma unroll
     for (int j = 0; j < kOwn<G>; ++j) {
         float mx = scv[0][j];
 #pragma unroll
         for (int i = 1; i < KT::NT; ++i) mx = fmaxf(mx, scv[i][j]);
         const float nm = fmaxf(m[j], mx);
-        if (nm != -INFINITY) {
-            float acc = l[j] * fast_exp2(m[j] - nm);
+        const float base = nm == -INFINITY ? 0.0f : nm;
+        float acc = l[j] * fast_exp2(m[j] - base);
 #pragma unroll
-            for (int i = 0; i < KT::NT; ++i) acc += fast_exp2(scv[i][j] - nm);
-            l[j] = acc;
-            m[j] = nm;
-        }
+        for (int i = 0; i < KT::NT; ++i) acc += fast_exp2(scv[i][j] - base);
+        l[j] = acc;
+        m[j] = nm;
     }
 }
 

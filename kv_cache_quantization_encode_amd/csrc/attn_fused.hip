@@ -65,17 +65,31 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     constexpr bool VQ8 = VK == TQ_KIND_Q8;
     static_assert(VK == TQ_KIND_Q8 || VK == TQ_KIND_MSE, "2-bit codebook V or q8 V");
     constexpr int kPairs = KK == TQ_KIND_Q8 ? 1 : 1 << (2 * KB);
-    __shared__ uint2 s_pair[kPairs];
-    __shared__ half8 s_sgn[PROJ ? 256 : 1];
-    __shared__ float s_red[kFW][G][2];
-    __shared__ __attribute__((aligned(16))) _Float16 s_a[16][128];
-    __shared__ __attribute__((aligned(16))) _Float16 s_ap[PROJ ? 16 : 1][128];
-    // scores of the block: head h, token t0 + i at s_sc[h * kFLd + i]; after
-    // the V products, the per-wave partial sums [kFW][G][128]
-    __shared__ __attribute__((aligned(16))) float s_sc[G * kFLd];
-    __shared__ float s_M[G], s_invL[G], s_W[kFW][G];
-    __shared__ float s_vmax[kFW];
-    __shared__ int s_ok;
+    // one LDS block, small lookup tables first: their addresses then fit the
+    // 16-bit offset of ds_read and need no per-lookup address arithmetic
+    struct Lds {
+        uint2 pair[kPairs];
+        half8 sgn[PROJ ? 256 : 1];
+        float red[kFW][G][2];
+        float M[G], invL[G], W[kFW][G], vmax[kFW];
+        float cst[2 * G], qmax[2];
+        int ok;
+        __attribute__((aligned(16))) _Float16 a[16][128];
+        __attribute__((aligned(16))) _Float16 ap[PROJ ? 16 : 1][128];
+        // scores of the block: head h, token t0 + i at sc[h * kFLd + i];
+        // after the V products, the per-wave partial sums [kFW][G][128]
+        __attribute__((aligned(16))) float sc[G * kFLd];
+    };
+    __shared__ Lds lds;
+    uint2 *s_pair = lds.pair;
+    half8 *s_sgn = lds.sgn;
+    auto &s_red = lds.red;
+    _Float16 (*s_a)[128] = lds.a;
+    _Float16 (*s_ap)[128] = lds.ap;
+    float *s_sc = lds.sc;
+    float *s_M = lds.M, *s_invL = lds.invL, *s_vmax = lds.vmax;
+    auto &s_W = lds.W;
+    int &s_ok = lds.ok;
     static_assert(kFW * G * 128 <= G * kFLd, "partial sums fit the score area");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,7 +180,13 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             s_pair[tid] = uint2{hp, lp};
         }
     }
+    if (tid < 2) lds.qmax[tid] = 0.0f;
     build_query_rows<G>(ql, a, s_a, s_ap);
+    // 1- and 2-bit codebook keys: bit-plane products (code words as B operands)
+    constexpr bool USE_PLANES = KK != TQ_KIND_Q8 && KB <= 2;
+    using PO = typename std::conditional<USE_PLANES, PlaneOps<G, (KB <= 2 ? KB : 1), PROJ>, NoPlanes>::type;
+    PO po;
+    if constexpr (USE_PLANES) build_plane_ops<G, KB, PROJ, kFW>(po, a.tab, s_a, s_ap, lds.cst, lds.qmax);
 
     half8 aq[8], ap[4];
     {
@@ -200,20 +220,21 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         lim[j] = L;
     }
     auto sink = [&](int h, int tok, float v) { s_sc[h * kFLd + (tok - t0)] = v; };
+    const PO *pop = USE_PLANES ? &po : nullptr;
     auto scan = [&](auto full_c) {
         constexpr bool F = decltype(full_c)::value;
         if (t0 >= t1) return;
         for (int base = t0;;) {
             load_ktiles<kFW>(tc, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, false, G, kFW>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
+            score_ktiles<F, false, G, kFW>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
             base += kFSlice;
             if (base >= t1) break;
             load_ktiles<kFW>(ta, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, false, G, kFW>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
+            score_ktiles<F, false, G, kFW>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
             base += kFSlice;
             if (base >= t1) break;
             load_ktiles<kFW>(tb, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, false, G, kFW>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
+            score_ktiles<F, false, G, kFW>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
             base += kFSlice;
             if (base >= t1) break;
         }
@@ -262,39 +283,41 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         asm volatile("" ::: "memory");
         __syncthreads();
         if (tid == 0) {
-            uint32_t *arrive = a.sync + 2 * row, *depart = arrive + 1;
+            uint32_t *arrive = a.sync + 2 * row;
             __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const uint64_t tstart = __builtin_amdgcn_s_memrealtime();
             int ok = 1;
             while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < uint32_t(a.nblk)) {
-                __builtin_amdgcn_s_sleep(2);
+                __builtin_amdgcn_s_sleep(1);
                 if (__builtin_amdgcn_s_memrealtime() - tstart > kSpinTicks) {
                     ok = 0;
                     break;
                 }
             }
             s_ok = ok;
-            if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                uint32_t(a.nblk) - 1) {
-                __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
         }
         __syncthreads();
-        // exact softmax statistics of every head from all blocks of the row
+        // exact softmax statistics of every head from all blocks of the row:
+        // lane c of wave h reads block c's (max, sum) of head h once
         if (wave < G) {
             const float *st = a.stats + int64_t(row) * a.nblk * G * 2 + wave * 2;
-            float mm = -INFINITY;
-            for (int c = lane; c < a.nblk; c += 64)
-                mm = fmaxf(mm, __hip_atomic_load(st + c * G * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            float mc[4], lc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = lane + 64 * i;
+                mc[i] = -INFINITY;
+                lc[i] = 0.0f;
+                if (c < a.nblk) {
+                    mc[i] = __hip_atomic_load(st + c * G * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    lc[i] = __hip_atomic_load(st + c * G * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            float mm = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
             mm = quad_max(row16_max(mm));
             float ll = 0.0f;
             if (mm != -INFINITY)
-                for (int c = lane; c < a.nblk; c += 64) {
-                    const float mc = __hip_atomic_load(st + c * G * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float lc = __hip_atomic_load(st + c * G * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ll += lc * fast_exp2((mc - mm) * kLog2e);
-                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ll += mc[i] == -INFINITY ? 0.0f : lc[i] * fast_exp2((mc[i] - mm) * kLog2e);
             ll = quad_sum(row16_sum(ll));
             if (lane == 0) {
                 s_M[wave] = mm;
@@ -626,6 +649,15 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         } else {
             o[lane] = v0;
             o[lane + 64] = v1;
+        }
+    }
+    // departure, off the critical path: the last block of the row to leave
+    // resets both counters for the next call (no block polls them any more)
+    if (a.nblk > 1 && tid == 0) {
+        uint32_t *arrive = a.sync + 2 * row, *depart = arrive + 1;
+        if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == uint32_t(a.nblk) - 1) {
+            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

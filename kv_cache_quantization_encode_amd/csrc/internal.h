@@ -65,6 +65,7 @@ AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int
 // Tokens per block and block size limits of the single-launch kernel.
 constexpr int kFusedSlice = 512;
 constexpr int kFusedMaxTokens = 4096;
+constexpr int kFusedMaxBlocks = 256;  // blocks per row (statistics read in one pass)
 // Prefill queries of one sequence that share a scores pass: the largest of
 // 8/g, ..., 2, 1 (g = query heads per kv head) dividing Tq, so that the
 // group's g * qp rows fill at most the 8 query rows of one pass.

@@ -209,3 +209,15 @@ def test_attention_q8_v_large_values_peaked(ctx, oracle_tables):
     gp = out.cpu().numpy()
     assert np.isfinite(gp).all()
     assert np.max(np.abs(gp[:, -1] - ref)) <= G.ATTN_ATOL + 1e-5 * scale
+
+
+@pytest.mark.parametrize("kf", [("prod", 1), ("prod", 2), ("prod", 3), ("mse", 1), ("mse", 2), ("mse", 4),
+                                ("q8", 8)])
+@pytest.mark.parametrize("vf", [("mse", 2), ("q8", 8)])
+def test_attention_eight_heads_key_formats(ctx, oracle_tables, kf, vf):
+    """Every K codec on the single-launch path (8 query heads per KV head):
+    1- and 2-bit codebooks score through bit-plane products, 3- and 4-bit
+    through level tables, q8 through int8 operands; a ragged length and a
+    row split over several blocks."""
+    c = W.llama70b_layer(21, T=1500, Hkv=2, Hq=16)
+    _run(ctx, oracle_tables, c, kf, vf, 1e-6, seq_lens=np.array([1333], np.int32))
