@@ -145,8 +145,11 @@ tq_status tq_decode_kv(const tq_ctx *ctx, const void *packed, tq_format f, int64
  * softmax over each sequence; V rows whose normalised weight is below tau
  * are skipped and not renormalised (tau = 0 keeps every row).
  * out_f32: device [B, Hq, d].  workspace: device, at least
- * tq_attn_workspace_bytes(...) bytes, 256-byte aligned; its contents need no
- * initialisation and are clobbered.  K: MSE, PROD or Q8; V: MSE or Q8.
+ * tq_attn_workspace_bytes(...) bytes, 256-byte aligned, zero-filled once
+ * before its first use.  Its first 68 KiB hold barrier counters and flags
+ * that every call leaves at zero; the rest is clobbered.  So one workspace serves calls
+ * of any shape, format and Tq in turn without clearing it again (sized for
+ * the largest).  K: MSE, PROD or Q8; V: MSE or Q8.
  * out_f32 is written as a sum of per-chunk shares added with fp32 atomics,
  * so repeated calls may differ in the last bits.  Calls that share one
  * workspace or one output must be ordered on one stream. */
@@ -183,9 +186,10 @@ size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_f
  * B*Tq*Hkv must not exceed 65535.  Other arguments, formats, ownership and
  * the last-bit nondeterminism of the fp32 atomics as for tq_attn_decode;
  * workspace: tq_attn_prefill_workspace_bytes(...) bytes, 256-byte aligned.
- * Tq = 1 is exactly tq_attn_decode.  Each query reads its visible K rows and
- * kept V rows itself (no sharing of loads between the queries of a sequence
- * beyond what the caches hold). */
+ * Tq = 1 is exactly tq_attn_decode.  Queries are taken in groups of up to
+ * 8 / (Hq / Hkv) per kv head; the queries of a group are stacked as extra
+ * MFMA rows and share every K and V load of their scores and values passes,
+ * while separate groups each read the prefix again. */
 tq_status tq_attn_prefill(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
                           const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
                           int T, int Tq, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,

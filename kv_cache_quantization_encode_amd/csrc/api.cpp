@@ -81,7 +81,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     p.n_chunks = int(nc);
     p.chunk = int(chunk);
     const int64_t heads = int64_t(B) * Hq;
-    int64_t off = 0;
+    int64_t off = int64_t(kSyncBytes);  // barrier counters of the single-launch path, never written here
     // score rows padded to 32 tokens, so that a 32-token group of a row can
     // be read whole (16-byte aligned) near the end of the sequence
     p.ld_scores = int((int64_t(T) + 31) / 32 * 32);
@@ -109,14 +109,14 @@ AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int
     const int64_t tb = (slices + nblk - 1) / nblk * kFusedSlice;
     if (tb > kFusedMaxTokens) return p;
     nblk = (int64_t(T) + tb - 1) / tb;
+    if (nblk > 1 && (rows > kSyncRows || rows * nblk > kFusedMaxGrid)) return p;
     AttnPlan f{};
     f.fused = 1;
     f.nblk = int(nblk);
     f.tb = int(tb);
-    int64_t off = 0;
-    f.off_sync = size_t(off); off = align256(rows * 2 * 4);
-    f.off_stats = size_t(off); off = align256(off + rows * nblk * 8 * 2 * 4);
-    f.total = size_t(off);
+    f.off_sync = 0;
+    f.off_stats = kSyncCounterBytes;
+    f.total = kSyncBytes;
     return f;
 }
 

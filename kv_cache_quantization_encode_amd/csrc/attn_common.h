@@ -41,7 +41,8 @@ struct AttnArgs {
     int k_rotated;  // K codec works in the rotated domain
     int v_rotated;  // V codec works in the rotated domain
     // single-launch path: nblk blocks of tb tokens per (sequence, kv head)
-    // row, two barrier counters per row
+    // row; a departure counter per row at sync, and stats holds one 64-bit
+    // (max, sum) slot per block and head
     uint32_t *sync;
     int nblk, tb;
 };
@@ -402,100 +403,6 @@ __device__ __forceinline__ int plane_coord(int kq, int j, int k, int h) {
     return 32 * kq + 16 * h + k;  // 1-bit codes and QJL signs: one bit per coordinate
 }
 
-// Builds the plane operands from the stacked fp16 hi/lo query rows s_a
-// (q_rot) and s_ap (q_proj).  s_cst: 2 * G floats of LDS scratch, s_qmax: 2
-// floats, zero before the call.  Ends with a barrier.  NW = waves per block.
-template <int G, int BITS, bool PROJ, int NW>
-__device__ __forceinline__ void build_plane_ops(PlaneOps<G, BITS, PROJ> &po, const DevTables *tab,
-                                                const _Float16 (*s_a)[128], const _Float16 (*s_ap)[128],
-                                                float *s_cst, float *s_qmax) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, kq = lane >> 4;
-    auto q32 = [&](const _Float16 (*rows)[128], int h, int c) { return float(rows[h][c]) + float(rows[G + h][c]); };
-    // per-head sums and the largest |q| of each term (wave w takes heads w, w + NW, ..)
-    float mq = 0.0f, mp = 0.0f;
-    for (int h = wave; h < G; h += NW) {
-        const float x0 = q32(s_a, h, lane), x1 = q32(s_a, h, lane + 64);
-        float sx = x0 + x1;
-        mq = fmaxf(mq, fmaxf(fabsf(x0), fabsf(x1)));
-        float sp = 0.0f;
-        if constexpr (PROJ) {
-            const float p0 = q32(s_ap, h, lane), p1 = q32(s_ap, h, lane + 64);
-            sp = p0 + p1;
-            mp = fmaxf(mp, fmaxf(fabsf(p0), fabsf(p1)));
-        }
-        sx = quad_sum(row16_sum(sx));
-        sp = quad_sum(row16_sum(sp));
-        if (lane == 0) {
-            s_cst[h] = sx;
-            s_cst[G + h] = sp;
-        }
-    }
-    mq = quad_max(row16_max(mq));
-    mp = quad_max(row16_max(mp));
-    if (lane == 0) {
-        // non-negative floats order like their bit patterns
-        atomicMax(reinterpret_cast<int *>(&s_qmax[0]), __float_as_int(mq));
-        atomicMax(reinterpret_cast<int *>(&s_qmax[1]), __float_as_int(mp));
-    }
-    __syncthreads();
-    float a1, a0;
-    if constexpr (BITS == 2) {
-        a1 = 0.5f * (tab->levels[1][3] + tab->levels[1][2]);
-        a0 = 0.5f * (tab->levels[1][3] - tab->levels[1][2]);
-    } else {
-        a1 = a0 = tab->levels[0][1];
-    }
-    int e_cb = 0, e_q = 0;
-    (void)frexpf(s_qmax[0] * 2.0f * fmaxf(a1, a0), &e_cb);
-    (void)frexpf(s_qmax[1] * 2.0f, &e_q);
-    const int s0_cb = 14 - e_cb, s0_q = 14 - e_q;  // every |A| < 2^14
-    po.sc_cb = ldexpf(1.0f, 24 - s0_cb);
-    po.sc_q = ldexpf(1.0f, 24 - s0_q);
-    const bool arow = r < 2 * G, lo = r >= G;
-    const int hr = lo ? r - G : r;
-    auto part = [&](float x) -> _Float16 {
-        const _Float16 h = _Float16(x);
-        return !arow ? _Float16(0.0f) : (lo ? _Float16(x - float(h)) : h);
-    };
-#pragma unroll
-    for (int j = 0; j < BITS; ++j)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k = 4 * u + i;
-                    const int c = plane_coord<BITS>(kq, j, k, h);
-                    const float coef = 2.0f * ((BITS == 2 && (k & 1)) ? a1 : a0);
-                    const float x = arow ? q32(s_a, hr, c) * coef * ldexpf(1.0f, s0_cb - plane_pos(k)) : 0.0f;
-                    po.ab[4 * j + u][2 * i + h] = part(x);
-                }
-    if constexpr (PROJ) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k = 4 * u + i;
-                    const int c = plane_coord<1>(kq, 0, k, h);
-                    const float x = arow ? q32(s_ap, hr, c) * 2.0f * ldexpf(1.0f, s0_q - plane_pos(k)) : 0.0f;
-                    po.aq[u][2 * i + h] = part(x);
-                }
-    }
-    // constants: sum_i q c[idx] = sum (2 coef q) bit - (a1 + a0) sum q (1 bit:
-    // a sum q); sum_p q_proj (2 bit - 1) = sum 2 q_proj bit - sum q_proj
-#pragma unroll
-    for (int j = 0; j < kOwn<G>; ++j) {
-        const int h = own_head<G>(kq, j);
-        po.ccb[j] = (BITS == 2 ? a1 + a0 : a1) * s_cst[h];
-        po.cq[j] = PROJ ? s_cst[G + h] : 0.0f;
-    }
-    __syncthreads();
-}
-
 struct NoPlanes {};
 
 // Scores one slice (NT tiles per wave) and folds it into the running (max,
@@ -631,10 +538,10 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
 #pragma unroll
         for (int i = 1; i < KT::NT; ++i) mx = fmaxf(mx, scv[i][j]);
         const float nm = fmaxf(m[j], mx);
-        const float base = nm == -INFINITY ? 0.0f : nm;
-        float acc = l[j] * fast_exp2(m[j] - base);
+        const float mb = nm == -INFINITY ? 0.0f : nm;
+        float acc = l[j] * fast_exp2(m[j] - mb);
 #pragma unroll
-        for (int i = 0; i < KT::NT; ++i) acc += fast_exp2(scv[i][j] - base);
+        for (int i = 0; i < KT::NT; ++i) acc += fast_exp2(scv[i][j] - mb);
         l[j] = acc;
         m[j] = nm;
     }

@@ -53,9 +53,163 @@ __host__ __device__ constexpr float bitval(int k) {
                              : (k == 11 ? 1.0f / 8192.0f : (k == 12 ? 1.0f / 2048.0f : (k == 13 ? 1.0f / 128.0f : 2.0f))));
 }
 
+// Query operands of the single-launch kernel: 8 heads, 8 waves, wave w
+// owns head w (its q_rot in registers) and the q_proj rows 16 w .. 16 w + 15.
+// Fills s_a / s_ap (fp16 hi and lo rows of q_rot and q_proj, as the scores
+// MFMAs of every key format read them) and, for bit-plane keys, this lane's
+// PlaneOps.  Scratch (all of it may alias the score area; a barrier must
+// follow before the area is reused): fq, fp: fp32 q_rot and q_proj [8][128];
+// red: 88 floats of per-head sums and maxima; tab: the plane operand table,
+// (4 BITS + 4) x 64 half8 (operand u of lane l at u * 64 + l).  Four steps
+// and three barriers: rotation, projection, table, each lane's operands.
+template <bool PROJ, bool PLANES, int BITS, typename PO>
+__device__ __forceinline__ void fused_query_setup(const QueryLoads<8, PROJ, 8> &ql, const AttnArgs &a,
+                                                  _Float16 (*s_a)[128], _Float16 (*s_ap)[128], float (*fq)[128],
+                                                  float (*fp)[128], float *red, half8 *tab, PO &po) {
+    constexpr int G = 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, kq = lane >> 4;
+    // q_rot = H D q / sqrt(d) of head `wave` (q itself for unrotated keys)
+    {
+        float v0 = h2f(ql.q0[0]), v1 = h2f(ql.q1[0]);
+        if (a.k_rotated) {
+            v0 *= ql.sg0;
+            v1 *= ql.sg1;
+            fwht128_lanes(v0, v1, lane);
+            v0 *= kRsqrtD;
+            v1 *= kRsqrtD;
+        }
+        put_hi_lo(&s_a[wave][lane], &s_a[G + wave][lane], v0);
+        put_hi_lo(&s_a[wave][lane + 64], &s_a[G + wave][lane + 64], v1);
+        if constexpr (PLANES) {
+            fq[wave][lane] = v0;
+            fq[wave][lane + 64] = v1;
+            const float sx = quad_sum(row16_sum(v0 + v1));
+            const float mx = quad_max(row16_max(fmaxf(fabsf(v0), fabsf(v1))));
+            if (lane == 0) {
+                red[wave] = sx;
+                red[G + wave] = mx;
+            }
+        }
+    }
+    __syncthreads();
+    // q_proj = S q_rot on the matrix cores: rows = projections 16 wave + [0, 16),
+    // columns = the hi (c < 8) and lo (c >= 8) rows of every head
+    if constexpr (PROJ) {
+        half8 bq[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bq[st] = *reinterpret_cast<const half8 *>(&s_a[c][32 * kq + 8 * st]);
+        floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql.sf[st], bq[st], acc, 0, 0, 0);
+        // lane (c, kq) holds projections 16 wave + 4 kq + j of column c; the
+        // head's value is column c plus column c + 8 (row rotate by 8)
+        float ps = 0.0f, pm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float p = acc[j] + dpp_mov<0x128>(acc[j]);
+            const int idx = 16 * wave + 4 * kq + j;
+            if (c < G) {
+                put_hi_lo(&s_ap[c][idx], &s_ap[G + c][idx], p);
+                if constexpr (PLANES) fp[c][idx] = p;
+            }
+            ps += p;
+            pm = fmaxf(pm, fabsf(p));
+        }
+        if constexpr (PLANES) {
+            // this wave's partial sum of head c (lanes c, c + 16, c + 32, c + 48)
+            // and its largest |q_proj| over all heads
+            ps = quad_sum(ps);
+            pm = quad_max(row16_max(c < G ? pm : 0.0f));
+            if (kq == 0 && c < G) red[16 + wave * G + c] = ps;
+            if (lane == 0) red[80 + wave] = pm;
+        }
+        __syncthreads();
+    }
+    if constexpr (PLANES) {
+        float mq = 0.0f, mp = 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) mq = fmaxf(mq, red[G + h]);
+        if constexpr (PROJ) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) mp = fmaxf(mp, red[80 + w]);
+        }
+        float a1, a0;
+        if constexpr (BITS == 2) {
+            a1 = 0.5f * (a.tab->levels[1][3] + a.tab->levels[1][2]);
+            a0 = 0.5f * (a.tab->levels[1][3] - a.tab->levels[1][2]);
+        } else {
+            a1 = a0 = a.tab->levels[0][1];
+        }
+        int e_cb = 0, e_q = 0;
+        (void)frexpf(mq * 2.0f * fmaxf(a1, a0), &e_cb);
+        (void)frexpf(mp * 2.0f, &e_q);
+        const int s0_cb = 14 - e_cb, s0_q = 14 - e_q;  // every |A| < 2^14
+        po.sc_cb = ldexpf(1.0f, 24 - s0_cb);
+        po.sc_q = ldexpf(1.0f, 24 - s0_q);
+        const float f1 = 2.0f * a1 * ldexpf(1.0f, s0_cb), f0 = 2.0f * a0 * ldexpf(1.0f, s0_cb);
+        const float fpq = 2.0f * ldexpf(1.0f, s0_q);
+        // table entry e = (operand u, lane 16 ekq + r); row r < 8 takes the hi
+        // half of head r, row r >= 8 the lo half of head r - 8
+        constexpr int NOPS = 4 * BITS + (PROJ ? 4 : 0);
+        for (int e = tid; e < NOPS * 64; e += 8 * 64) {
+            const int u = e >> 6, ekq = (e >> 4) & 3, r = e & 15;
+            const bool lo = r >= G;
+            const int hr = r & (G - 1);
+            half8 v;
+            if (u >= 4 * BITS) {
+                const int uu = u - 4 * BITS;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int k = 4 * uu + i;
+                        const float x = fp[hr][plane_coord<1>(ekq, 0, k, h)] * fpq * ldexpf(1.0f, -plane_pos(k));
+                        const _Float16 xh = _Float16(x);
+                        v[2 * i + h] = lo ? _Float16(x - float(xh)) : xh;
+                    }
+            } else {
+                const int j = u >> 2, uu = u & 3;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int k = 4 * uu + i;
+                        const float f = (BITS == 2 && (k & 1)) ? f1 : f0;
+                        const float x = fq[hr][plane_coord<BITS>(ekq, j, k, h)] * f * ldexpf(1.0f, -plane_pos(k));
+                        const _Float16 xh = _Float16(x);
+                        v[2 * i + h] = lo ? _Float16(x - float(xh)) : xh;
+                    }
+            }
+            tab[e] = v;
+        }
+        // head constants: sum_i q c[idx] = sum (2 coef q) bit - (a1 + a0) sum q
+        // (1 bit: a sum q); sum_p q_proj (2 bit - 1) = sum 2 q_proj bit - sum q_proj
+#pragma unroll
+        for (int jo = 0; jo < kOwn<G>; ++jo) {
+            const int h = own_head<G>(kq, jo);
+            po.ccb[jo] = (BITS == 2 ? a1 + a0 : a1) * red[h];
+            float psum = 0.0f;
+            if constexpr (PROJ) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) psum += red[16 + w * G + h];
+            }
+            po.cq[jo] = psum;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4 * BITS; ++u) po.ab[u] = tab[u * 64 + lane];
+        if constexpr (PROJ) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) po.aq[u] = tab[(4 * BITS + u) * 64 + lane];
+        }
+    }
+}
+
 // Fused kernel for rows whose tokens fit the block range; rows of the grid y
-// = (sequence, kv head), x = block of the row.  a.sync: two counters per row
-// (arrivals, departures), zero between calls; a.stats: [rows][nblk][8] float2.
+// = (sequence, kv head), x = block of the row.  a.sync: a departure counter
+// per row; a.stats: [rows][nblk][8] 64-bit (max, sum) slots; both zero
+// between calls.
 template <int KK, int KB, int VK>
 __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
                                                                const uint8_t *__restrict__ ksign,
@@ -72,8 +226,7 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         half8 sgn[PROJ ? 256 : 1];
         float red[kFW][G][2];
         float M[G], invL[G], W[kFW][G], vmax[kFW];
-        float cst[2 * G], qmax[2];
-        int ok;
+        int ok, last, okw[G];
         __attribute__((aligned(16))) _Float16 a[16][128];
         __attribute__((aligned(16))) _Float16 ap[PROJ ? 16 : 1][128];
         // scores of the block: head h, token t0 + i at sc[h * kFLd + i];
@@ -92,6 +245,11 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     int &s_ok = lds.ok;
     static_assert(kFW * G * 128 <= G * kFLd, "partial sums fit the score area");
 
+    // every kernel argument of the first loads, requested together so that
+    // one wait covers them (else the compiler spreads them over several
+    // dependent round trips before the first query load)
+    asm volatile("" ::"s"(a.tab), "s"(a.q), "s"(a.vnorm), "s"(kidx), "s"(ksign), "s"(knorm), "s"(a.seq_lens),
+                 "s"(a.Hq), "s"(a.Hkv), "s"(a.T), "s"(a.tb), "s"(a.nblk), "s"(a.k_rotated));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = lane & 15, kq = lane >> 4;
     const int blk = blockIdx.x, row = blockIdx.y;  // row = b * Hkv + kvh
@@ -135,18 +293,7 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     const bool whole = n_tok % kFSlice == 0;
     KTiles<KK, KB> ta, tb, tc;
     load_ktiles<kFW>(ta, t0, tmax, wave, t, kq, kid, ksg, knm);
-    load_ktiles<kFW>(tb, t0 + kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-    // (the scale words were requested first: reducing them now waits for
-    // them only, not for the K tiles behind them)
-    uint32_t vmx = 0;
-#pragma unroll
-    for (int r = 0; r < kVR; ++r) {
-        if constexpr (VQ8) {
-            vmx = max(vmx, max(max(vraw[r][0] & 0xFFFFu, vraw[r][0] >> 16), max(vraw[r][1] & 0xFFFFu, vraw[r][1] >> 16)));
-        } else {
-            vmx = max(vmx, vraw[r][0]);
-        }
-    }
+    if (t0 + kFSlice < t1) load_ktiles<kFW>(tb, t0 + kFSlice, tmax, wave, t, kq, kid, ksg, knm);
 
     // a row shared by several blocks is summed with atomics: block 0 zeroes
     // it before the barrier
@@ -180,13 +327,27 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             s_pair[tid] = uint2{hp, lp};
         }
     }
-    if (tid < 2) lds.qmax[tid] = 0.0f;
-    build_query_rows<G>(ql, a, s_a, s_ap);
-    // 1- and 2-bit codebook keys: bit-plane products (code words as B operands)
+    // query operands; 1- and 2-bit codebook keys take bit-plane products
+    // (code words as B operands).  Scratch in the score area: fp32 q_rot and
+    // q_proj rows (8 KB), sums (576 B), the plane operand table (12 KB).
     constexpr bool USE_PLANES = KK != TQ_KIND_Q8 && KB <= 2;
     using PO = typename std::conditional<USE_PLANES, PlaneOps<G, (KB <= 2 ? KB : 1), PROJ>, NoPlanes>::type;
     PO po;
-    if constexpr (USE_PLANES) build_plane_ops<G, KB, PROJ, kFW>(po, a.tab, s_a, s_ap, lds.cst, lds.qmax);
+    static_assert(2304 + (4 * 2 + 4) * 64 * 4 <= G * kFLd, "setup scratch fits the score area");
+    fused_query_setup<PROJ, USE_PLANES, (KB <= 2 ? KB : 1)>(
+        ql, a, s_a, s_ap, reinterpret_cast<float (*)[128]>(s_sc), reinterpret_cast<float (*)[128]>(s_sc + 1024),
+        s_sc + 2048, reinterpret_cast<half8 *>(s_sc + 2304), po);
+    // V scale bound of the block (its words were requested before the K
+    // tiles, so they have long landed)
+    uint32_t vmx = 0;
+#pragma unroll
+    for (int r = 0; r < kVR; ++r) {
+        if constexpr (VQ8) {
+            vmx = max(vmx, max(max(vraw[r][0] & 0xFFFFu, vraw[r][0] >> 16), max(vraw[r][1] & 0xFFFFu, vraw[r][1] >> 16)));
+        } else {
+            vmx = max(vmx, vraw[r][0]);
+        }
+    }
 
     half8 aq[8], ap[4];
     {
@@ -210,6 +371,8 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         }
     }
 
+    __syncthreads();  // the setup scratch in the score area is free again
+
     // ---- phase 1: scores into LDS, running (max, sum) per own head
     float m[kOwn<G>], l[kOwn<G>];
     int lim[kOwn<G>];
@@ -224,16 +387,18 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     auto scan = [&](auto full_c) {
         constexpr bool F = decltype(full_c)::value;
         if (t0 >= t1) return;
+        // slices are requested two ahead, and only inside the range: the
+        // arrival below waits for every outstanding access of the block
         for (int base = t0;;) {
-            load_ktiles<kFW>(tc, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+            if (base + 2 * kFSlice < t1) load_ktiles<kFW>(tc, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
             score_ktiles<F, false, G, kFW>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
             base += kFSlice;
             if (base >= t1) break;
-            load_ktiles<kFW>(ta, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+            if (base + 2 * kFSlice < t1) load_ktiles<kFW>(ta, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
             score_ktiles<F, false, G, kFW>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
             base += kFSlice;
             if (base >= t1) break;
-            load_ktiles<kFW>(tb, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+            if (base + 2 * kFSlice < t1) load_ktiles<kFW>(tb, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
             score_ktiles<F, false, G, kFW>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
             base += kFSlice;
             if (base >= t1) break;
@@ -258,6 +423,12 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     }
     __syncthreads();
     // block statistics per head, in natural-log units
+    if (a.nblk > 1 && blk == 0) {
+        // the zeroed output is visible before this block's statistics are
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+    }
+    uint64_t *slots = reinterpret_cast<uint64_t *>(a.stats) + int64_t(row) * a.nblk * G;  // [nblk][G]
     float bm = -INFINITY, bl = 0.0f;
     if (tid < G) {
         for (int w = 0; w < kFW; ++w) bm = fmaxf(bm, s_red[w][tid][0]);
@@ -265,52 +436,48 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             for (int w = 0; w < kFW; ++w) bl += s_red[w][tid][1] * fast_exp2(s_red[w][tid][0] - bm);
         bm = bm == -INFINITY ? bm : bm / kLog2e;
         if (a.nblk > 1) {
-            float *st = a.stats + ((int64_t(row) * a.nblk + blk) * G + tid) * 2;
-            __hip_atomic_store(st, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(st + 1, bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // one 64-bit slot carries both values and marks them written: a
+            // written slot is never zero (an empty block stores -inf, 0)
+            const uint64_t v = uint64_t(__float_as_uint(bm)) | (uint64_t(__float_as_uint(bl)) << 32);
+            __hip_atomic_store(slots + int64_t(blk) * G + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
-    // ---- barrier of the row's blocks (arrive, wait with a bounded spin,
-    // depart; the last block to depart resets both counters for the next call).
-    // Everything exchanged between blocks (statistics, counters, the zeroed
-    // output) goes through device-coherent atomic accesses, ordered by waiting
-    // for this thread's stores to complete before the arrival; acquire/release
-    // fences would write back and invalidate the whole L2 instead.
+    // ---- barrier of the row's blocks: wave h waits (bounded spin) until
+    // every block's slot of head h is written and reduces them to the exact
+    // softmax statistics; the poll returns the data itself, so the wait ends
+    // one device-coherent round trip after the last block's store lands.
+    // Everything exchanged between blocks goes through device-coherent
+    // atomic accesses; acquire/release fences would write back and
+    // invalidate the whole L2 instead.
     if (a.nblk > 1) {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have landed
-        asm volatile("" ::: "memory");
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t *arrive = a.sync + 2 * row;
-            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wave < G) {
+            const uint64_t *sl = slots + wave;
+            uint64_t v[4];
             const uint64_t tstart = __builtin_amdgcn_s_memrealtime();
             int ok = 1;
-            while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < uint32_t(a.nblk)) {
+            for (;;) {
+                bool missing = false;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = lane + 64 * i;
+                    v[i] = c < a.nblk ? __hip_atomic_load(sl + int64_t(c) * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : ~uint64_t(0);
+                    missing |= v[i] == 0;
+                }
+                if (__ballot(missing) == 0) break;
                 __builtin_amdgcn_s_sleep(1);
                 if (__builtin_amdgcn_s_memrealtime() - tstart > kSpinTicks) {
                     ok = 0;
                     break;
                 }
             }
-            s_ok = ok;
-        }
-        __syncthreads();
-        // exact softmax statistics of every head from all blocks of the row:
-        // lane c of wave h reads block c's (max, sum) of head h once
-        if (wave < G) {
-            const float *st = a.stats + int64_t(row) * a.nblk * G * 2 + wave * 2;
             float mc[4], lc[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int c = lane + 64 * i;
-                mc[i] = -INFINITY;
-                lc[i] = 0.0f;
-                if (c < a.nblk) {
-                    mc[i] = __hip_atomic_load(st + c * G * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    lc[i] = __hip_atomic_load(st + c * G * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                const bool real = lane + 64 * i < a.nblk;
+                mc[i] = real ? __uint_as_float(uint32_t(v[i])) : -INFINITY;
+                lc[i] = real ? __uint_as_float(uint32_t(v[i] >> 32)) : 0.0f;
             }
             float mm = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
             mm = quad_max(row16_max(mm));
@@ -322,14 +489,21 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             if (lane == 0) {
                 s_M[wave] = mm;
                 s_invL[wave] = ll > 0.0f ? 1.0f / ll : 0.0f;
+                lds.okw[wave] = ok;
             }
         }
     } else {
         if (tid < G) {
             s_M[tid] = bm;
             s_invL[tid] = bl > 0.0f ? 1.0f / bl : 0.0f;
+            lds.okw[tid] = 1;
         }
-        if (tid == 0) s_ok = 1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int ok = 1;
+        for (int w = 0; w < G; ++w) ok &= lds.okw[w];
+        s_ok = ok;
     }
     __syncthreads();
 
@@ -651,13 +825,18 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             o[lane + 64] = v1;
         }
     }
-    // departure, off the critical path: the last block of the row to leave
-    // resets both counters for the next call (no block polls them any more)
-    if (a.nblk > 1 && tid == 0) {
-        uint32_t *arrive = a.sync + 2 * row, *depart = arrive + 1;
-        if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == uint32_t(a.nblk) - 1) {
-            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // departure: the last block of the row to leave clears the row's slots
+    // and its counter for the next call (no block reads them any more)
+    if (a.nblk > 1) {
+        uint32_t *depart = a.sync + row;
+        if (tid == 0)
+            lds.last = __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       uint32_t(a.nblk) - 1;
+        __syncthreads();
+        if (lds.last) {
+            for (int i = tid; i < a.nblk * G; i += kFThreads)
+                __hip_atomic_store(slots + i, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

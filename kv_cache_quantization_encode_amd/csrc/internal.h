@@ -53,7 +53,8 @@ struct AttnPlan {
     int ld_scores;   // score row stride in floats: T rounded up to 32
     size_t off_scores, off_stats, total;
     // single-launch path (decode, 8 query heads per kv head, 2-bit codebook or
-    // q8 V): nblk blocks of tb tokens per row; barrier counters at off_sync
+    // q8 V): nblk blocks of tb tokens per row; departure counters at
+    // off_sync, (max, sum) slots at off_stats
     int fused, nblk, tb;
     size_t off_sync;
 };
@@ -66,6 +67,16 @@ AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int
 constexpr int kFusedSlice = 512;
 constexpr int kFusedMaxTokens = 4096;
 constexpr int kFusedMaxBlocks = 256;  // blocks per row (statistics read in one pass)
+// Every attention workspace plan starts with kSyncBytes for the barrier of
+// the single-launch path: a departure counter per row (rows < kSyncRows),
+// then a 64-bit (max, sum) slot per block and head (grids of up to
+// kFusedMaxGrid blocks).  Nothing else is ever stored there and every call
+// leaves it zero, so a workspace zero-filled once stays valid for calls of
+// any shape and path.
+constexpr int kSyncRows = 1024;
+constexpr int kFusedMaxGrid = 1024;
+constexpr size_t kSyncCounterBytes = size_t(kSyncRows) * 4;
+constexpr size_t kSyncBytes = kSyncCounterBytes + size_t(kFusedMaxGrid) * 8 * 8;
 // Prefill queries of one sequence that share a scores pass: the largest of
 // 8/g, ..., 2, 1 (g = query heads per kv head) dividing Tq, so that the
 // group's g * qp rows fill at most the 8 query rows of one pass.

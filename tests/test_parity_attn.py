@@ -176,6 +176,38 @@ def test_attention_eight_heads_repeated_calls_one_workspace(ctx, oracle_tables):
         assert np.max(np.abs(o - ref)) <= G.ATTN_ATOL
 
 
+def test_attention_workspace_shared_across_paths_and_shapes(ctx, oracle_tables):
+    """One workspace, zero-filled once, serves in turn: a single-launch call
+    (rows spread over several blocks), a two-pass call (4 query heads per KV
+    head, scores written over most of the workspace), a single-launch call
+    with another row count and block split, and the first call again.  Every
+    call matches the oracle: nothing but the barrier counters, which each
+    call leaves at zero, survives from one call to the next."""
+    import torch
+    from kv_cache_quantization_encode_amd import turbokv as T
+    kf, vf = ("prod", 2), ("mse", 2)
+    K, V = G.tf(*kf), G.tf(*vf)
+    cases = [W.llama70b_layer(21, T=3000, Hkv=2, Hq=16), W.llama70b_layer(22, T=2500, Hkv=2, Hq=8),
+             W.llama70b_layer(23, T=1900, Hkv=4, Hq=32)]
+    need = max(T.tq_attn_workspace_bytes(*c.shape, K, V) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    prepared = []
+    for c in cases:
+        kp, vp = _encode_case(ctx, c, kf, vf)
+        ref = G.oracle_attention(c, kp, vp, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6)
+        prepared.append((c, G.to_dev_f16(c.q), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), ref))
+    for i in (0, 1, 2, 0):
+        c, q, kd, vd, ref = prepared[i]
+        B, Hq, Hkv, Tn = c.shape
+        out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        G.note(f"shared workspace: case {i} B={B} Hq={Hq} Hkv={Hkv} T={Tn}")
+        T.tq_attn_decode(ctx, q, kd, vd, K, V, B, Hq, Hkv, Tn, None, 1e-6, out, ws, need)
+        got = out.cpu().numpy()
+        assert np.isfinite(got).all()
+        err = np.max(np.abs(got - ref))
+        assert err <= G.ATTN_ATOL, f"case {i}: max abs error {err:.3g}"
+
+
 def test_attention_q8_v_large_values_peaked(ctx, oracle_tables):
     """q8 V rows with |v| up to ~6e4 under a needle-peaked softmax, 8 query
     heads per KV head: the A operands (weight x block scale) must stay inside
