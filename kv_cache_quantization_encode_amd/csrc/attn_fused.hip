@@ -45,6 +45,7 @@ constexpr int kFTokens = kFusedMaxTokens;        // most tokens per block (score
 constexpr int kFLd = kFTokens + 16;              // LDS score row stride: head rows 16 banks apart
 constexpr float kAMax = 16384.0f;                // V-product A operands stay below 2^14
 constexpr uint64_t kSpinTicks = 25000000;        // barrier spin budget: 0.25 s of the 100 MHz clock
+constexpr int kQRow = 132;                       // fp32 query row stride of the setup scratch
 
 // fp16 value of a half whose only set bit is bit k (k <= 14)
 __host__ __device__ constexpr float bitval(int k) {
@@ -58,14 +59,15 @@ __host__ __device__ constexpr float bitval(int k) {
 // Fills s_a / s_ap (fp16 hi and lo rows of q_rot and q_proj, as the scores
 // MFMAs of every key format read them) and, for bit-plane keys, this lane's
 // PlaneOps.  Scratch (all of it may alias the score area; a barrier must
-// follow before the area is reused): fq, fp: fp32 q_rot and q_proj [8][128];
+// follow before the area is reused): fq, fp: fp32 q_rot and q_proj [8][128]
+// in rows of kQRow floats (the padding puts the 8 rows in different banks);
 // red: 88 floats of per-head sums and maxima; tab: the plane operand table,
 // (4 BITS + 4) x 64 half8 (operand u of lane l at u * 64 + l).  Four steps
 // and three barriers: rotation, projection, table, each lane's operands.
 template <bool PROJ, bool PLANES, int BITS, typename PO>
 __device__ __forceinline__ void fused_query_setup(const QueryLoads<8, PROJ, 8> &ql, const AttnArgs &a,
-                                                  _Float16 (*s_a)[128], _Float16 (*s_ap)[128], float (*fq)[128],
-                                                  float (*fp)[128], float *red, half8 *tab, PO &po) {
+                                                  _Float16 (*s_a)[128], _Float16 (*s_ap)[128], float (*fq)[kQRow],
+                                                  float (*fp)[kQRow], float *red, half8 *tab, PO &po) {
     constexpr int G = 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, kq = lane >> 4;
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     const uint8_t *ksg = ksign + int64_t(row) * a.T * 16;
     const uint8_t *knm = knorm + int64_t(row) * a.T * (KK == TQ_KIND_Q8 ? 8 : (PROJ ? 4 : 2));
 
-    // ---- global reads first: query, tables, V scale bound, first K slices
+    // ---- global reads first: query, tables, V scale words, first K slices
     QueryLoads<G, PROJ, kFW> ql;
     load_query(ql, a, b, kvh);
     float lv[2] = {0.0f, 0.0f};
@@ -275,18 +277,40 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         }
     }
     // largest V norm (codebook V) or block scale (q8 V) of the block's tokens,
-    // as fp16 bits (non-negative halves order like their bit patterns)
-    constexpr int kVR = kFTokens / kFThreads;  // tokens per thread
-    uint32_t vraw[kVR][VQ8 ? 2 : 1];
+    // as fp16 bits (non-negative halves order like their bit patterns):
+    // thread i takes tokens t0 + 8 i .. t0 + 8 i + 7, in one or four 16-byte
+    // loads when they all lie in the range and the address is 16-byte
+    // aligned (else one clamped load each)
+    static_assert(8 * kFThreads >= kFTokens, "eight scale words per thread cover the block");
+    constexpr int kVW = VQ8 ? 16 : 4;  // dwords per thread
+    uint32_t vraw[kVW];
+    {
+        const int tk = t0 + 8 * tid;
+        const uint8_t *vp = a.vnorm + (int64_t(row) * a.T + tk) * (VQ8 ? 8 : 2);
+        if (tk + 8 <= t1 && (reinterpret_cast<uintptr_t>(vp) & 15) == 0) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(vp);
 #pragma unroll
-    for (int r = 0; r < kVR; ++r) {
-        const int tok = min(t0 + kFThreads * r + tid, tmax);
-        if constexpr (VQ8) {
-            const uint2 u = reinterpret_cast<const uint2 *>(a.vnorm)[int64_t(row) * a.T + tok];
-            vraw[r][0] = u.x;
-            vraw[r][1] = u.y;
+            for (int i = 0; i < kVW / 4; ++i) {
+                const uint4 u = src[i];
+                vraw[4 * i] = u.x;
+                vraw[4 * i + 1] = u.y;
+                vraw[4 * i + 2] = u.z;
+                vraw[4 * i + 3] = u.w;
+            }
         } else {
-            vraw[r][0] = reinterpret_cast<const uint16_t *>(a.vnorm)[int64_t(row) * a.T + tok];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int tok = min(tk + r, tmax);
+                if constexpr (VQ8) {
+                    const uint2 u = reinterpret_cast<const uint2 *>(a.vnorm)[int64_t(row) * a.T + tok];
+                    vraw[2 * r] = u.x;
+                    vraw[2 * r + 1] = u.y;
+                } else {
+                    const uint32_t h = reinterpret_cast<const uint16_t *>(a.vnorm)[int64_t(row) * a.T + tok];
+                    if (r & 1) vraw[r >> 1] |= h << 16;
+                    else vraw[r >> 1] = h;
+                }
+            }
         }
     }
     asm volatile("" ::: "memory");
@@ -329,25 +353,19 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     }
     // query operands; 1- and 2-bit codebook keys take bit-plane products
     // (code words as B operands).  Scratch in the score area: fp32 q_rot and
-    // q_proj rows (8 KB), sums (576 B), the plane operand table (12 KB).
+    // q_proj rows (8.25 KB), sums (512 B), the plane operand table (12 KB).
     constexpr bool USE_PLANES = KK != TQ_KIND_Q8 && KB <= 2;
     using PO = typename std::conditional<USE_PLANES, PlaneOps<G, (KB <= 2 ? KB : 1), PROJ>, NoPlanes>::type;
     PO po;
-    static_assert(2304 + (4 * 2 + 4) * 64 * 4 <= G * kFLd, "setup scratch fits the score area");
+    static_assert(16 * kQRow + 128 + (4 * 2 + 4) * 64 * 4 <= G * kFLd, "setup scratch fits the score area");
     fused_query_setup<PROJ, USE_PLANES, (KB <= 2 ? KB : 1)>(
-        ql, a, s_a, s_ap, reinterpret_cast<float (*)[128]>(s_sc), reinterpret_cast<float (*)[128]>(s_sc + 1024),
-        s_sc + 2048, reinterpret_cast<half8 *>(s_sc + 2304), po);
+        ql, a, s_a, s_ap, reinterpret_cast<float (*)[kQRow]>(s_sc), reinterpret_cast<float (*)[kQRow]>(s_sc + 8 * kQRow),
+        s_sc + 16 * kQRow, reinterpret_cast<half8 *>(s_sc + 16 * kQRow + 128), po);
     // V scale bound of the block (its words were requested before the K
     // tiles, so they have long landed)
     uint32_t vmx = 0;
 #pragma unroll
-    for (int r = 0; r < kVR; ++r) {
-        if constexpr (VQ8) {
-            vmx = max(vmx, max(max(vraw[r][0] & 0xFFFFu, vraw[r][0] >> 16), max(vraw[r][1] & 0xFFFFu, vraw[r][1] >> 16)));
-        } else {
-            vmx = max(vmx, vraw[r][0]);
-        }
-    }
+    for (int r = 0; r < kVW; ++r) vmx = max(vmx, max(vraw[r] & 0xFFFFu, vraw[r] >> 16));
 
     half8 aq[8], ap[4];
     {
