@@ -41,6 +41,12 @@ Readings where the pages are silent (each is listed in the design notes):
     outputs give the signs (top bit set -> -1), the next m*d outputs feed the
     Box-Muller transform (Box & Muller 1958) pairwise, row-major into S.
   * q8 boundary blocks: symmetric absmax int8, blocks of 32, fp16 scale.
+  * Block-32 norm storage (formats 'mse32', 'prod32'): the rotation stays
+    over all d coordinates; the Stage-1 norm is kept per block of 32 rotated
+    coordinates (n_b = ||(R x)_b||, fp16), each block standardised by its own
+    norm, z = sqrt(32) (R x)_b / n_b.  K's residual r = R x - x_hat_1 (x
+    units, rotated) keeps one fp16 norm gamma per vector; its QJL sketch is
+    sign(S r).
   * min-max: fp16 scale = (max - min)/(2^b - 1) and fp16 zero = min, codes
     decided in float32 (the kernel's precision, the pages fix none).
 
@@ -245,6 +251,80 @@ def qjl_projection_from_codes(x: np.ndarray, idx: np.ndarray, bits: int, tab: Ta
 
 
 # --------------------------------------------------------------------------
+# Block-32 norm storage  [yeyulingfeng.com "TurboQuant+: 3.8x compression
+# ...", technical highlights: block-32 storage; quidproquo.cc format table:
+# 6.4x for turbo2, 4.6-5.1x for turbo3]
+# --------------------------------------------------------------------------
+BLOCK = 32
+
+
+def block_standardised_rotation(x: np.ndarray, tab: Tables, block: int = BLOCK):
+    """u = R x; per block of `block` rotated coordinates n_b = ||u_b|| and
+    z = sqrt(block) u_b / n_b (z = 0 in a zero block).  Returns (u, n_b, z)."""
+    x = np.asarray(x, dtype=np.float64)
+    u = x @ tab.R.T
+    ub = u.reshape(*u.shape[:-1], tab.d // block, block)
+    nb = np.sqrt(np.sum(ub * ub, axis=-1))
+    safe = np.where(nb > 0, nb, 1.0)
+    z = np.where((nb > 0)[..., None], ub / safe[..., None], 0.0) * math.sqrt(block)
+    return u, nb, z.reshape(u.shape)
+
+
+def _per_coordinate(nb, block: int = BLOCK):
+    """Block values [.., d/block] -> per-coordinate values [.., d]."""
+    return np.repeat(np.asarray(nb, dtype=np.float64), block, axis=-1)
+
+
+def encode_block32(x: np.ndarray, bits: int, prod: bool, tab: Tables, block: int = BLOCK) -> dict:
+    """Block-32 encode of rows of x ([n, d]).
+
+    'mse32': idx and the fp16 block norms.  'prod32': additionally the QJL
+    sign bits of S r, r = u - (n_b / sqrt(block)) c[idx] the rotated
+    Stage-1 residual (exact n_b), and its fp16 norm gamma = ||r||.  P is
+    returned in z-units of the whole vector, sqrt(d) (S r) / ||x||, for the
+    near-zero exemption of the parity checks (its sign is that of S r)."""
+    u, nb, z = block_standardised_rotation(x, tab, block)
+    c = tab.levels[bits]
+    idx = quantise_index(z, tab.bounds[bits])
+    out = {"idx": idx, "bnorm": nb.astype(np.float16), "bn64": nb, "z": z}
+    if prod:
+        r = u - _per_coordinate(nb / math.sqrt(block), block) * c[idx]
+        gamma = np.sqrt(np.sum(r * r, axis=-1))
+        n = np.sqrt(np.sum(u * u, axis=-1))
+        zs = np.where(n > 0, math.sqrt(tab.d) / np.where(n > 0, n, 1.0), 0.0)
+        P = (r @ tab.S.T) * zs[..., None]
+        out.update(bits_qjl=(P > 0).astype(np.uint8), rnorm=gamma.astype(np.float16),
+                   gamma64=gamma, P=P, r=r)
+    return out
+
+
+def qjl_projection_from_codes_block32(x: np.ndarray, idx: np.ndarray, bits: int, tab: Tables,
+                                      block: int = BLOCK):
+    """P (as in encode_block32) for the given codes."""
+    u, nb, _ = block_standardised_rotation(x, tab, block)
+    r = u - _per_coordinate(nb / math.sqrt(block), block) * tab.levels[bits][idx]
+    n = np.sqrt(np.sum(u * u, axis=-1))
+    zs = np.where(n > 0, math.sqrt(tab.d) / np.where(n > 0, n, 1.0), 0.0)
+    return (r @ tab.S.T) * zs[..., None]
+
+
+def dequant_mse32(idx, bnorm16, bits, tab: Tables, block: int = BLOCK) -> np.ndarray:
+    """v_hat = R^T ( (n_b / sqrt(block)) c[idx] ) per block."""
+    zhat = tab.levels[bits][idx]
+    return (_per_coordinate(np.asarray(bnorm16, np.float64) / math.sqrt(block), block) * zhat) @ tab.R
+
+
+def dequant_prod32(idx, bits_qjl, bnorm16, rnorm16, bits, tab: Tables, block: int = BLOCK) -> np.ndarray:
+    """k_hat = R^T ( (n_b / sqrt(block)) c[idx] + sqrt(pi/2)/m * gamma * S^T (2 bit - 1) )."""
+    zhat = tab.levels[bits][idx]
+    g = np.asarray(rnorm16, dtype=np.float64)
+    sgn = 2.0 * np.asarray(bits_qjl, dtype=np.float64) - 1.0
+    rot = _per_coordinate(np.asarray(bnorm16, np.float64) / math.sqrt(block), block) * zhat + \
+        (math.sqrt(math.pi / 2.0) / tab.m) * g[..., None] * (sgn @ tab.S)
+    return rot @ tab.R
+
+
+# --------------------------------------------------------------------------
 # Dequant  [QPQ: Stage-1 reconstruction; QJL estimate of the residual]
 # --------------------------------------------------------------------------
 def dequant_mse(idx, norm16, bits, tab: Tables) -> np.ndarray:
@@ -303,6 +383,9 @@ def tq_plane_layout(kind: str, bits: int, d: int, n_vec: int, m: int | None = No
 
     kind 'mse': [IDX n_vec*(b*d/8)] [NORM n_vec*2]
     kind 'prod': [IDX] [SIGN n_vec*m/8] [NORM n_vec*4: fp16 n then fp16 gamma]
+    kind 'mse32': [IDX] [NORM n_vec*(d/32)*2: fp16 block norms]
+    kind 'prod32': [IDX] [SIGN] [NORM n_vec*(d/32)*2 block norms, then
+                   n_vec*2 fp16 gamma]
     kind 'q8':   [Q n_vec*d int8] [SCALE n_vec*(d/32)*2]
     Each plane starts on a 256-byte boundary.
     """
@@ -318,14 +401,12 @@ def tq_plane_layout(kind: str, bits: int, d: int, n_vec: int, m: int | None = No
     ib = n_vec * bits * d // 8
     planes["idx"] = (off, ib)
     off = _align256(off + ib)
-    if kind == "prod":
+    if kind in ("prod", "prod32"):
         planes["sign"] = (off, n_vec * m // 8)
         off = _align256(off + n_vec * m // 8)
-        planes["norm"] = (off, n_vec * 4)
-        off = _align256(off + n_vec * 4)
-    else:
-        planes["norm"] = (off, n_vec * 2)
-        off = _align256(off + n_vec * 2)
+    nb = {"mse": 2, "prod": 4, "mse32": 2 * (d // BLOCK), "prod32": 2 * (d // BLOCK) + 2}[kind]
+    planes["norm"] = (off, n_vec * nb)
+    off = _align256(off + n_vec * nb)
     return {"planes": planes, "total": off}
 
 
@@ -335,15 +416,20 @@ def pack_tq(enc: dict, kind: str, bits: int, d: int, m: int | None = None) -> np
     buf = np.zeros(lay["total"], dtype=np.uint8)
     o, s = lay["planes"]["idx"]
     buf[o:o + s] = pack_bitstream(enc["idx"], bits).reshape(-1)
-    if kind == "prod":
+    if kind in ("prod", "prod32"):
         o, s = lay["planes"]["sign"]
         buf[o:o + s] = pack_bitstream(enc["bits_qjl"], 1).reshape(-1)
-        o, s = lay["planes"]["norm"]
+    o, s = lay["planes"]["norm"]
+    if kind == "prod":
         pair = np.stack([enc["norm"], enc["rnorm"]], axis=1).astype(np.float16)
         buf[o:o + s] = pair.view(np.uint8).reshape(-1)
-    else:
-        o, s = lay["planes"]["norm"]
+    elif kind == "mse":
         buf[o:o + s] = enc["norm"].astype(np.float16).view(np.uint8).reshape(-1)
+    else:
+        blk = np.ascontiguousarray(enc["bnorm"], dtype=np.float16).view(np.uint8).reshape(-1)
+        buf[o:o + blk.size] = blk
+        if kind == "prod32":
+            buf[o + blk.size:o + s] = np.ascontiguousarray(enc["rnorm"], dtype=np.float16).view(np.uint8).reshape(-1)
     return buf
 
 
@@ -353,15 +439,20 @@ def unpack_tq(buf: np.ndarray, kind: str, bits: int, d: int, n_vec: int, m: int 
     buf = np.asarray(buf, dtype=np.uint8)
     o, s = lay["planes"]["idx"]
     out = {"idx": unpack_bitstream(buf[o:o + s].reshape(n_vec, bits * d // 8), bits, d)}
-    if kind == "prod":
+    if kind in ("prod", "prod32"):
         o, s = lay["planes"]["sign"]
         out["bits_qjl"] = unpack_bitstream(buf[o:o + s].reshape(n_vec, m // 8), 1, m)
-        o, s = lay["planes"]["norm"]
+    o, s = lay["planes"]["norm"]
+    if kind == "prod":
         pair = buf[o:o + s].copy().view(np.float16).reshape(n_vec, 2)
         out["norm"], out["rnorm"] = pair[:, 0].copy(), pair[:, 1].copy()
-    else:
-        o, s = lay["planes"]["norm"]
+    elif kind == "mse":
         out["norm"] = buf[o:o + s].copy().view(np.float16)
+    else:
+        nbk = d // BLOCK
+        out["bnorm"] = buf[o:o + n_vec * nbk * 2].copy().view(np.float16).reshape(n_vec, nbk)
+        if kind == "prod32":
+            out["rnorm"] = buf[o + n_vec * nbk * 2:o + s].copy().view(np.float16)
     return out
 
 
@@ -373,6 +464,10 @@ def dequant_packed(buf, kind: str, bits: int, tab: Tables, n_vec: int) -> np.nda
     u = unpack_tq(buf, kind, bits, tab.d, n_vec, tab.m)
     if kind == "prod":
         return dequant_prod(u["idx"], u["bits_qjl"], u["norm"], u["rnorm"], bits, tab)
+    if kind == "prod32":
+        return dequant_prod32(u["idx"], u["bits_qjl"], u["bnorm"], u["rnorm"], bits, tab)
+    if kind == "mse32":
+        return dequant_mse32(u["idx"], u["bnorm"], bits, tab)
     return dequant_mse(u["idx"], u["norm"], bits, tab)
 
 
@@ -551,6 +646,11 @@ def bytes_per_vector(kind: str, bits: int, d: int = 128, m: int | None = None) -
     m = d if m is None else m
     if kind == "q8":
         return d + (d // 32) * 2
+    if kind in ("mse32", "prod32"):
+        base = bits * d // 8 + 2 * (d // BLOCK)
+        if kind == "prod32":
+            base += m // 8 + 2
+        return base
     base = bits * d // 8 + 2
     if kind == "prod":
         base += m // 8 + 2

@@ -21,7 +21,9 @@ from tests import test_oracle_pins as P
 _orig = {name: getattr(O, name) for name in (
     "rotation", "encode", "qjl_projection_from_codes", "dequant_mse", "dequant_prod", "qjl_inner_product",
     "quantise_index", "minmax_quant", "attention_decode", "attention_prefill", "pack_bitstream", "q8_quant",
-    "quality", "lloyd_max_gaussian", "splitmix64_outputs", "standardised_rotation")}
+    "quality", "lloyd_max_gaussian", "splitmix64_outputs", "standardised_rotation",
+    "block_standardised_rotation", "encode_block32", "qjl_projection_from_codes_block32", "dequant_mse32",
+    "dequant_prod32")}
 
 
 def m_rotation_transposed(signs):
@@ -203,6 +205,42 @@ def m_standardised_no_normalise(x, tab):
     return n, math.sqrt(tab.d) * (x @ tab.R.T)
 
 
+def m_block_scale_sqrt_d(x, tab, block=32):
+    u, nb, z = _orig["block_standardised_rotation"](x, tab, block)
+    return u, nb, z * math.sqrt(tab.d / block)
+
+
+def m_block_norms_before_rotation(x, tab, block=32):
+    x = np.asarray(x, dtype=np.float64)
+    u = x @ tab.R.T
+    nb = np.sqrt(np.sum(x.reshape(*x.shape[:-1], tab.d // block, block) ** 2, axis=-1))
+    safe = np.where(nb > 0, nb, 1.0)
+    z = u.reshape(*u.shape[:-1], tab.d // block, block) / safe[..., None] * math.sqrt(block)
+    return u, nb, z.reshape(u.shape)
+
+
+def m_block_residual_in_block_units(x, bits, prod, tab, block=32):
+    out = _orig["encode_block32"](x, bits, prod, tab, block)
+    if prod:
+        r = out["z"] - tab.levels[bits][out["idx"]]
+        g = np.sqrt(np.sum(r * r, axis=-1))
+        out.update(gamma64=g, rnorm=g.astype(np.float16))
+    return out
+
+
+def m_block_check_without_scale(x, idx, bits, tab, block=32):
+    _, _, z = O.block_standardised_rotation(x, tab, block)
+    return (z - tab.levels[bits][idx]) @ tab.S.T
+
+
+def m_dequant_mse32_sqrt_d(idx, bnorm16, bits, tab, block=32):
+    return _orig["dequant_mse32"](idx, np.asarray(bnorm16, np.float64) * math.sqrt(block / tab.d), bits, tab, block)
+
+
+def m_dequant_prod32_no_qjl(idx, bits_qjl, bnorm16, rnorm16, bits, tab, block=32):
+    return _orig["dequant_mse32"](idx, bnorm16, bits, tab, block)
+
+
 # ------------------------------------------------------------------- pins
 def _tab():
     return O.Tables(128, seed=42)
@@ -232,6 +270,11 @@ PINS = {
     "codebook": lambda: [P.test_codebook_textbook_levels(b, _tab()) for b in (1, 2, 3, 4)],
     "splitmix": lambda: P.test_splitmix64_published_vectors(),
     "rotated_scores": lambda: P.test_rotated_domain_scores_equal_dense_scores(_tab()),
+    "block32_equal_norms": lambda: [P.test_block32_equal_block_norms_reduce_to_per_vector_codec(b, _tab())
+                                    for b in (1, 2, 3, 4)],
+    "block32_independent": lambda: P.test_block32_blocks_are_independent(_tab()),
+    "block32_gamma": lambda: [P.test_block32_gamma_is_stage1_residual_norm(b, _tab()) for b in (1, 2, 3)],
+    "block32_from_codes": lambda: P.test_block32_qjl_projection_from_codes(_tab()),
 }
 
 # mistake -> (oracle function replaced, replacement, pins expected to catch it)
@@ -260,6 +303,18 @@ MUTATIONS = {
     "splitmix64 first shift 31": ("splitmix64_outputs", m_splitmix_wrong_shift, ["splitmix"]),
     "rotation not normalised by the norm": ("standardised_rotation", m_standardised_no_normalise,
                                             ["rotation_direction", "mse_distortion"]),
+    "block standardised with sqrt(d)": ("block_standardised_rotation", m_block_scale_sqrt_d,
+                                        ["block32_equal_norms"]),
+    "block norms taken before the rotation": ("block_standardised_rotation", m_block_norms_before_rotation,
+                                              ["block32_equal_norms", "block32_independent"]),
+    "block-32 K residual in block z-units": ("encode_block32", m_block_residual_in_block_units,
+                                             ["block32_gamma", "block32_equal_norms"]),
+    "block-32 QJL check without block scales": ("qjl_projection_from_codes_block32", m_block_check_without_scale,
+                                                ["block32_from_codes"]),
+    "block-32 V dequant with sqrt(d)": ("dequant_mse32", m_dequant_mse32_sqrt_d,
+                                        ["block32_equal_norms", "block32_gamma"]),
+    "block-32 K dequant without the QJL term": ("dequant_prod32", m_dequant_prod32_no_qjl,
+                                                ["block32_equal_norms"]),
 }
 
 

@@ -348,7 +348,8 @@ def test_prod_dequant_inner_product_is_stage1_plus_qjl(oracle_tables):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("kind,bits,size", [("prod", 1, 36), ("prod", 2, 52), ("prod", 3, 68),
                                             ("mse", 1, 18), ("mse", 2, 34), ("mse", 3, 50),
-                                            ("mse", 4, 66), ("q8", 8, 136)])
+                                            ("mse", 4, 66), ("q8", 8, 136), ("mse32", 2, 40), ("mse32", 3, 56),
+                                            ("prod32", 2, 58)])
 def test_bytes_per_vector(kind, bits, size):
     assert O.bytes_per_vector(kind, bits) == size
 
@@ -364,6 +365,28 @@ def test_pack_unpack_roundtrip(kind, bits, oracle_tables):
     if kind == "prod":
         assert np.array_equal(u["bits_qjl"], enc["bits_qjl"])
         assert np.array_equal(u["rnorm"].view(np.uint16), enc["rnorm"].view(np.uint16))
+
+
+@pytest.mark.parametrize("kind,bits", [("prod32", 2), ("prod32", 1), ("mse32", 2), ("mse32", 4)])
+def test_pack_unpack_roundtrip_block32(kind, bits, oracle_tables):
+    """Block-32 planes: block norms of every vector, then (K) every gamma;
+    the plane sizes add up to bytes_per_vector."""
+    x = np.random.default_rng(bits + 7).standard_normal((37, 128)).astype(np.float16)
+    enc = O.encode_block32(x, bits, kind == "prod32", oracle_tables)
+    buf = O.pack_tq(enc, kind, bits, 128)
+    lay = O.tq_plane_layout(kind, bits, 128, 37)
+    assert sum(sz for _, sz in lay["planes"].values()) == 37 * O.bytes_per_vector(kind, bits)
+    u = O.unpack_tq(buf, kind, bits, 128, 37)
+    assert np.array_equal(u["idx"], enc["idx"])
+    assert np.array_equal(u["bnorm"].view(np.uint16), enc["bnorm"].view(np.uint16))
+    o, _ = lay["planes"]["norm"]
+    first = buf[o:o + 8].copy().view(np.float16)  # vector 0: its four block norms
+    assert np.array_equal(first.view(np.uint16), enc["bnorm"][0].view(np.uint16))
+    if kind == "prod32":
+        assert np.array_equal(u["bits_qjl"], enc["bits_qjl"])
+        assert np.array_equal(u["rnorm"].view(np.uint16), enc["rnorm"].view(np.uint16))
+        g0 = buf[o + 37 * 8:o + 37 * 8 + 2].copy().view(np.float16)
+        assert g0.view(np.uint16)[0] == enc["rnorm"][0].view(np.uint16)
 
 
 # ----------------------------------------------------------------------------
@@ -634,3 +657,133 @@ def test_attention_decode_clamps_lengths():
     full, _ = O.attention_decode(q, k, v, tau=1e-6)
     assert np.all(out[0] == 0)
     assert np.array_equal(out[1], full[1])
+
+
+# ----------------------------------------------------------------------------
+# Block-32 norm storage (yeyulingfeng.com "TurboQuant+: 3.8x compression ...",
+# technical highlights: block-32 storage; quidproquo.cc format table)
+# ----------------------------------------------------------------------------
+def test_block32_ratio_arithmetic():
+    """One fp16 norm per 32 coordinates adds 16/32 = 0.5 bits per element: the
+    pages' 6.4x for turbo2 is 16/(2+0.5) and the low end of their 4.6-5.1x for
+    turbo3 is 16/(3+0.5) = 4.57.  K keeps one fp16 residual norm per vector on
+    top (turbo3 K: 16/(3+0.625))."""
+    def ratio(kind, bits):
+        return 16.0 / (O.bytes_per_vector(kind, bits) * 8 / 128)
+    assert ratio("mse32", 2) == pytest.approx(6.4, abs=1e-12)
+    assert ratio("mse32", 3) == pytest.approx(16 / 3.5, abs=1e-12)
+    assert round(ratio("mse32", 3), 2) == 4.57
+    assert ratio("prod32", 2) == pytest.approx(16 / 3.625, abs=1e-12)
+    assert ratio("prod32", 1) == pytest.approx(16 / 2.625, abs=1e-12)
+    assert O.bytes_per_vector("mse32", 4) == 64 + 8
+
+
+def _equal_block_norm_rows(tab, n, seed):
+    """Rows x whose rotated coordinates have the same norm in every block of
+    32 (x = u R with u built block by block)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((n, 128))
+    ub = u.reshape(n, 4, 32)
+    ub /= np.linalg.norm(ub, axis=-1, keepdims=True)
+    ub *= rng.uniform(0.5, 3.0, (n, 1, 1))
+    return ub.reshape(n, 128) @ tab.R
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_block32_equal_block_norms_reduce_to_per_vector_codec(bits, oracle_tables):
+    """With equal block norms n_b = ||x|| / 2, the block standardisation
+    sqrt(32) u_b / n_b equals the per-vector sqrt(128) u / ||x||: codes, the
+    projection P, gamma and both reconstructions coincide with the per-vector
+    codec (fp16(n/2) = fp16(n)/2 exactly)."""
+    tab = oracle_tables
+    x = _equal_block_norm_rows(tab, 40, 7 + bits)
+    a = O.encode(x, bits, True, tab)
+    b = O.encode_block32(x, bits, True, tab)
+    np.testing.assert_allclose(b["z"], a["z"], rtol=0, atol=1e-12)
+    assert (b["idx"] == a["idx"]).all()
+    np.testing.assert_allclose(b["P"], a["P"], rtol=0, atol=1e-9)
+    assert (b["bits_qjl"] == a["bits_qjl"]).all()
+    np.testing.assert_allclose(b["gamma64"], a["gamma64"], rtol=1e-12)
+    assert (b["bnorm"] == (a["norm"][:, None] / 2).astype(np.float16)).all()
+    np.testing.assert_allclose(O.dequant_mse32(b["idx"], b["bnorm"], bits, tab),
+                               O.dequant_mse(a["idx"], a["norm"], bits, tab), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.dequant_prod32(b["idx"], b["bits_qjl"], b["bnorm"], b["rnorm"], bits, tab),
+                               O.dequant_prod(a["idx"], a["bits_qjl"], a["norm"], a["rnorm"], bits, tab),
+                               rtol=0, atol=1e-12)
+
+
+def test_block32_blocks_are_independent(oracle_tables):
+    """Scaling one block of the rotated vector by a > 0 scales only that
+    block's norm: every code is unchanged (the per-vector codec, whose single
+    norm mixes the blocks, changes codes)."""
+    tab = oracle_tables
+    rng = np.random.default_rng(11)
+    u = rng.standard_normal((30, 128))
+    x = u @ tab.R
+    u2 = u.copy()
+    u2[:, 32:64] *= 9.0
+    x2 = u2 @ tab.R
+    a, b = O.encode_block32(x, 3, False, tab), O.encode_block32(x2, 3, False, tab)
+    assert (a["idx"] == b["idx"]).all()
+    np.testing.assert_allclose(b["bn64"][:, 1], 9.0 * a["bn64"][:, 1], rtol=1e-12)
+    np.testing.assert_allclose(b["bn64"][:, [0, 2, 3]], a["bn64"][:, [0, 2, 3]], rtol=1e-12)
+    assert (O.encode(x, 3, False, tab)["idx"] != O.encode(x2, 3, False, tab)["idx"]).any()
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_block32_gamma_is_stage1_residual_norm(bits, oracle_tables):
+    """gamma = ||x - x_hat_1|| with x_hat_1 the Stage-1 reconstruction from
+    the exact block norms (R is orthonormal), on rows with very uneven
+    blocks; and the Stage-1 reconstruction error is below ||x||."""
+    tab = oracle_tables
+    rng = np.random.default_rng(21 + bits)
+    u = rng.standard_normal((25, 128)) * np.repeat([0.01, 1.0, 30.0, 3.0], 32)
+    x = u @ tab.R
+    e = O.encode_block32(x, bits, True, tab)
+    x1 = O.dequant_mse32(e["idx"], e["bn64"], bits, tab)
+    np.testing.assert_allclose(e["gamma64"], np.linalg.norm(x - x1, axis=1), rtol=1e-10)
+    assert (np.linalg.norm(x - x1, axis=1) < np.linalg.norm(x, axis=1)).all()
+
+
+def test_block32_zero_vector(oracle_tables):
+    """A zero vector has zero block norms, z = 0 (the upper middle index),
+    no sign bit and gamma 0, and reconstructs to zero in both formats."""
+    tab = oracle_tables
+    x = np.zeros((2, 128))
+    e = O.encode_block32(x, 2, True, tab)
+    assert (e["idx"] == 2).all() and (e["bn64"] == 0).all()
+    assert e["bits_qjl"].sum() == 0 and (e["gamma64"] == 0).all()
+    np.testing.assert_allclose(O.dequant_mse32(e["idx"], e["bnorm"], 2, tab), 0.0, atol=0)
+    np.testing.assert_allclose(O.dequant_prod32(e["idx"], e["bits_qjl"], e["bnorm"], e["rnorm"], 2, tab), 0.0,
+                               atol=0)
+
+
+def test_block32_finer_norms_help_uneven_vectors(oracle_tables):
+    """On rows whose energy is concentrated in one block of the rotated
+    coordinates, per-block norms cut the Stage-1 error at equal code bits (the
+    codebook no longer sees a mixture of scales)."""
+    tab = oracle_tables
+    rng = np.random.default_rng(3)
+    u = rng.standard_normal((400, 128)) * np.repeat([0.05, 0.05, 1.0, 0.05], 32)
+    x = u @ tab.R
+    e1, e2 = O.encode(x, 2, False, tab), O.encode_block32(x, 2, False, tab)
+    m1 = O.quality(x, O.dequant_mse(e1["idx"], e1["norm"], 2, tab))["mse"]
+    m2 = O.quality(x, O.dequant_mse32(e2["idx"], e2["bnorm"], 2, tab))["mse"]
+    assert m2 < 0.5 * m1
+
+
+def test_block32_qjl_projection_from_codes(oracle_tables):
+    """The block-32 projection recomputed from the encoder's own codes is the
+    encoder's P; with one block's codes moved one level its block residual,
+    and so P, changes."""
+    tab = oracle_tables
+    x = np.random.default_rng(9).standard_normal((12, 128))
+    e = O.encode_block32(x, 2, True, tab)
+    np.testing.assert_allclose(O.qjl_projection_from_codes_block32(x, e["idx"], 2, tab), e["P"], rtol=0, atol=1e-12)
+    idx2 = e["idx"].copy()
+    idx2[:, 40] = np.where(idx2[:, 40] < 3, idx2[:, 40] + 1, idx2[:, 40] - 1)
+    P2 = O.qjl_projection_from_codes_block32(x, idx2, 2, tab)
+    u, nb, _ = O.block_standardised_rotation(x, tab)
+    step = (tab.levels[2][idx2[:, 40]] - tab.levels[2][e["idx"][:, 40]]) * nb[:, 1] / math.sqrt(32)
+    zs = math.sqrt(128) / np.linalg.norm(x, axis=1)
+    np.testing.assert_allclose(P2 - e["P"], -(step * zs)[:, None] * tab.S[:, 40][None, :], rtol=1e-9, atol=1e-12)
