@@ -59,8 +59,22 @@ typedef enum tq_status {
  *                 1 sign bit per projection, fp16 norm, fp16 residual norm.
  *                 turboN K = {TQ_KIND_PROD, N-1}.              bits = 1..3
  *   TQ_KIND_Q8  : boundary-layer blocks ([YYL] item 3): int8 per element,
- *                 fp16 absmax/127 scale per block of 32.       bits = 8     */
-typedef enum tq_kind { TQ_KIND_MSE = 0, TQ_KIND_PROD = 1, TQ_KIND_Q8 = 2 } tq_kind;
+ *                 fp16 absmax/127 scale per block of 32.       bits = 8
+ *   TQ_KIND_MSE32, TQ_KIND_PROD32: block-32 norm storage ([YYL] technical
+ *                 highlights, "block-32 storage"; the [QPQ] format-table
+ *                 ratios 16/(2+0.5) = 6.4 and 16/(3+0.5) = 4.57): as MSE and
+ *                 PROD, but the Stage-1 norm is kept per block of 32 rotated
+ *                 coordinates, n_b = ||(R x)_b||, and each block is
+ *                 standardised by its own norm, z = sqrt(32) (R x)_b / n_b.
+ *                 PROD32 keeps one residual norm per vector.
+ *                                           bits: MSE32 1..4, PROD32 1..3   */
+typedef enum tq_kind {
+    TQ_KIND_MSE = 0,
+    TQ_KIND_PROD = 1,
+    TQ_KIND_Q8 = 2,
+    TQ_KIND_MSE32 = 3,
+    TQ_KIND_PROD32 = 4
+} tq_kind;
 
 typedef struct tq_format {
     int32_t kind; /* tq_kind */
@@ -77,7 +91,12 @@ typedef struct tq_ctx tq_ctx;
  *   PROD: idx plane as MSE; sign plane n_vec * m/8 bytes (bit p = [(S e)_p > 0]);
  *         norm plane  n_vec * 4 bytes (fp16 ||x|| then fp16 residual norm).
  *   Q8  : idx plane   n_vec * d int8 values; norm plane n_vec * d/32 fp16
- *         block scales; no sign plane.                                      */
+ *         block scales; no sign plane.
+ *   MSE32: idx plane as MSE; norm plane n_vec * 8 bytes (the d/32 = 4 fp16
+ *         block norms of each vector, block order).
+ *   PROD32: idx and sign planes as PROD; norm plane n_vec * 10 bytes: the
+ *         four fp16 block norms of every vector (n_vec * 8 bytes), then the
+ *         fp16 residual norm of every vector (n_vec * 2 bytes).              */
 typedef struct tq_planes_desc {
     int64_t idx_offset, idx_bytes;
     int64_t sign_offset, sign_bytes;

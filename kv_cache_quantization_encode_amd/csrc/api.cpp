@@ -20,6 +20,8 @@ static bool format_ok(tq_format f) {
         case TQ_KIND_MSE: return f.bits >= 1 && f.bits <= 4;
         case TQ_KIND_PROD: return f.bits >= 1 && f.bits <= 3;
         case TQ_KIND_Q8: return f.bits == 8;
+        case TQ_KIND_MSE32: return f.bits >= 1 && f.bits <= 4;
+        case TQ_KIND_PROD32: return f.bits >= 1 && f.bits <= 3;
         default: return false;
     }
 }
@@ -40,15 +42,17 @@ bool plane_layout(tq_format f, int d, int64_t n_vec, tq_planes_desc *out) {
         p.idx_offset = 0;
         p.idx_bytes = n_vec * f.bits * d / 8;
         off = align256(p.idx_bytes);
-        if (f.kind == TQ_KIND_PROD) {
+        if (f.kind == TQ_KIND_PROD || f.kind == TQ_KIND_PROD32) {
             p.sign_offset = off;
             p.sign_bytes = n_vec * d / 8;
             off = align256(off + p.sign_bytes);
-            p.norm_offset = off;
-            p.norm_bytes = n_vec * 4;
-        } else {
-            p.norm_offset = off;
-            p.norm_bytes = n_vec * 2;
+        }
+        p.norm_offset = off;
+        switch (f.kind) {
+            case TQ_KIND_PROD: p.norm_bytes = n_vec * 4; break;
+            case TQ_KIND_MSE32: p.norm_bytes = n_vec * (d / 32) * 2; break;
+            case TQ_KIND_PROD32: p.norm_bytes = n_vec * ((d / 32) * 2 + 2); break;
+            default: p.norm_bytes = n_vec * 2; break;
         }
         off = align256(off + p.norm_bytes);
     }
@@ -91,10 +95,11 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     return p;
 }
 
-AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int capacity) {
+AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity) {
     const int g = Hq / Hkv;
     const int qp = prefill_group(g, Tq);
     AttnPlan p = attn_plan(B * (Tq / qp), Hq * qp, Hkv, T);
+    if (block32_format(kf) || block32_format(vf)) return p;  // scores + values passes
     // single launch: decode with 8 query heads per kv head and a V codec the
     // fused kernel reads (2-bit codebook, q8); every block of a row is resident
     // at once, and a block's scores (tb tokens x 8 heads) fit its LDS
@@ -284,7 +289,7 @@ size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq
     (void)kf;
     if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return 0;
     if (int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
-    return attn_call_plan(B, Hq, Hkv, T, Tq, vf, fused_capacity()).total;
+    return attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity()).total;
 }
 
 // Decode (Tq = 1) and causal prefill (Tq queries per sequence) share one path:
@@ -300,7 +305,8 @@ static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_p
         !aligned(out_f32, 16) || (seq_lens && !aligned(seq_lens, 4)))
         return TQ_ERR_INVALID_ARG;
     if (!format_ok(kf) || !format_ok(vf)) return TQ_ERR_INVALID_ARG;
-    if (vf.kind == TQ_KIND_PROD) return TQ_ERR_UNSUPPORTED;
+    if (vf.kind == TQ_KIND_PROD || vf.kind == TQ_KIND_PROD32) return TQ_ERR_UNSUPPORTED;
+    if ((block32_format(kf) || block32_format(vf)) && Tq != 1) return TQ_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
     if (g != 1 && g != 2 && g != 4 && g != 8) return TQ_ERR_UNSUPPORTED;
     if (int64_t(B) * Hkv * T > kMaxRows || int64_t(T) * 128 >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
@@ -309,7 +315,7 @@ static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_p
     tq_planes_desc kl{}, vl{};
     if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))
         return TQ_ERR_INVALID_ARG;
-    const AttnPlan plan = attn_call_plan(B, Hq, Hkv, T, Tq, vf, fused_capacity());
+    const AttnPlan plan = attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity());
     if (!workspace || !aligned(workspace, 256) || ws_bytes < plan.total) return TQ_ERR_WORKSPACE;
     return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, Tq, seq_lens,
                        sparse_v_tau, out_f32, workspace, plan, stream) == 0

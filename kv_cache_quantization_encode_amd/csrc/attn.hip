@@ -966,6 +966,7 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.ld_scores = plan.ld_scores;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
+    if (block32_format(kf) || block32_format(vf)) return launch_attn_generic(a, kf, vf, stream);
     if (plan.fused) {
         a.sync = reinterpret_cast<uint32_t *>(w + plan.off_sync);
         a.nblk = plan.nblk;

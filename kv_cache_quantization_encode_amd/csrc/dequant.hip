@@ -10,6 +10,8 @@
 // transform leaves it holding 8*(l>>4) + [0,8) + 32k of the output row.  The QJL term S^T (2b - 1) for the
 // 16 tokens of a wave is one [128 x 128] x [128 x 16] fp16 MFMA product
 // (entries of S and +-1 are exact in fp16; fp32 accumulation).
+// Block-32 norm storage: lane group q holds rotated block q, whose scale is
+// its own norm, n_q / sqrt(32).
 #include <type_traits>
 
 #include "device_common.h"
@@ -19,7 +21,7 @@ namespace tq {
 constexpr float kRsqrtD = 0.08838834764831845f;        // 1/sqrt(128)
 constexpr float kQjlScale = 1.2533141373155003f / 128;  // sqrt(pi/2)/m
 
-template <int BITS, bool PROD>
+template <int BITS, bool PROD, bool B32>
 __global__ __launch_bounds__(256) void decode_tq_kernel(const DevTables *__restrict__ tab,
                                                         const uint8_t *__restrict__ idx_plane,
                                                         const uint8_t *__restrict__ sign_plane,
@@ -52,7 +54,14 @@ __global__ __launch_bounds__(256) void decode_tq_kernel(const DevTables *__restr
             const uint32_t *src = reinterpret_cast<const uint32_t *>(idx_plane + tok * (16 * BITS) + q * (4 * BITS));
 #pragma unroll
             for (int i = 0; i < BITS; ++i) w[i] = src[i];
-            if constexpr (PROD) {
+            if constexpr (B32) {
+                // block norm q; K: the residual norms follow all block norms
+                nrm = h2f(reinterpret_cast<const uint16_t *>(norm_plane)[tok * 4 + q]);
+                if constexpr (PROD) {
+                    gam = h2f(reinterpret_cast<const uint16_t *>(norm_plane + n_vec * 8)[tok]);
+                    sbits = reinterpret_cast<const uint32_t *>(sign_plane + tok * 16)[q];
+                }
+            } else if constexpr (PROD) {
                 const uint32_t nn = reinterpret_cast<const uint32_t *>(norm_plane)[tok];
                 nrm = h2f(nn & 0xFFFFu);
                 gam = h2f(nn >> 16);
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_tq_kernel(const DevTables *__restr
             for (int i = 0; i < BITS; ++i) w[i] = 0;
         }
         float v[32];
-        const float sc = nrm * kRsqrtD;
+        const float sc = nrm * (B32 ? 0.17677669529663687f : kRsqrtD);  // 1/sqrt(32) or 1/sqrt(d)
         Unroll<32>::run([&](auto I) {
             constexpr int j = decltype(I)::value;
             v[j] = sc * s_levels[code_at<BITS, j>(w)];
@@ -132,14 +141,14 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(const int8_t *__restrict
     for (int c = 0; c < 4; ++c) dst[c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
 }
 
-template <int BITS, bool PROD>
+template <int BITS, bool PROD, bool B32 = false>
 static int launch_dec(const DevTables *tab, const uint8_t *base, int64_t n_vec, const tq_planes_desc &lay,
                       uint16_t *out, hipStream_t s) {
     const int64_t n_tiles = (n_vec + 15) / 16;
     int64_t blocks = (n_tiles + 3) / 4;
     if (PROD && blocks > 1024) blocks = 1024;
     if (blocks > (int64_t(1) << 30)) blocks = int64_t(1) << 30;
-    hipLaunchKernelGGL((decode_tq_kernel<BITS, PROD>), dim3(unsigned(blocks)), dim3(256), 0, s, tab,
+    hipLaunchKernelGGL((decode_tq_kernel<BITS, PROD, B32>), dim3(unsigned(blocks)), dim3(256), 0, s, tab,
                        base + lay.idx_offset, PROD ? base + lay.sign_offset : nullptr,
                        base + lay.norm_offset, n_vec, out, n_tiles);
     return int(hipGetLastError());
@@ -156,6 +165,23 @@ int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t
                            reinterpret_cast<const int8_t *>(base + lay.idx_offset),
                            reinterpret_cast<const uint16_t *>(base + lay.norm_offset), n_vec, out);
         return int(hipGetLastError());
+    }
+    if (f.kind == TQ_KIND_PROD32) {
+        switch (f.bits) {
+            case 1: return launch_dec<1, true, true>(tab, base, n_vec, lay, out, s);
+            case 2: return launch_dec<2, true, true>(tab, base, n_vec, lay, out, s);
+            case 3: return launch_dec<3, true, true>(tab, base, n_vec, lay, out, s);
+        }
+        return int(hipErrorInvalidValue);
+    }
+    if (f.kind == TQ_KIND_MSE32) {
+        switch (f.bits) {
+            case 1: return launch_dec<1, false, true>(tab, base, n_vec, lay, out, s);
+            case 2: return launch_dec<2, false, true>(tab, base, n_vec, lay, out, s);
+            case 3: return launch_dec<3, false, true>(tab, base, n_vec, lay, out, s);
+            case 4: return launch_dec<4, false, true>(tab, base, n_vec, lay, out, s);
+        }
+        return int(hipErrorInvalidValue);
     }
     if (f.kind == TQ_KIND_PROD) {
         switch (f.bits) {

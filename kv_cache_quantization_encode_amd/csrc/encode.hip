@@ -18,6 +18,11 @@
 // The norm is a packed fp16 dot product of the row with itself (fp32
 // accumulation); z = y / n is quantised against the fp32 Lloyd-Max
 // boundaries (bucket lookup for 3-4 bits).
+// Block-32 norm storage (yeyulingfeng.com "TurboQuant+: 3.8x compression
+// ...", technical highlights): lane group q holds exactly the rotated block
+// q, so its norm ||y_q|| is a sum over the lane's own 32 values and
+// z = sqrt(32) y / ||y_q||; K's residual enters the projection in units of
+// the whole vector, scaled per block by rho_q = 2 ||y_q|| / ||y||.
 #include <type_traits>
 
 #include "device_common.h"
@@ -73,11 +78,14 @@ __device__ __forceinline__ int dest_row(const RowMap &m, int tok, bool &valid) {
 
 // The encode of one packed tensor by a block of 256 threads (4 waves), the
 // waves of the grid striding over 16-row tiles.
-template <int BITS, bool PROD, bool APPEND>
+// B32: block-32 norms (norm_plane: four fp16 per row; rnorm_plane: the K
+// residual norms, one fp16 per row).
+template <int BITS, bool PROD, bool APPEND, bool B32 = false>
 __device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, const uint16_t *__restrict__ x,
                                             int64_t n_vec, uint8_t *__restrict__ idx_plane,
                                             uint8_t *__restrict__ sign_plane, uint8_t *__restrict__ norm_plane,
-                                            int64_t n_tiles, const RowMap &map) {
+                                            int64_t n_tiles, const RowMap &map,
+                                            uint8_t *__restrict__ rnorm_plane = nullptr) {
     __shared__ float s_levels[16];
     __shared__ __attribute__((aligned(16))) QBucket s_lut[kBuckets];
     __shared__ half8 s_frag[PROD ? 32 * 64 : 1];
@@ -167,8 +175,8 @@ __device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, c
                 ss = __builtin_amdgcn_fdot2(h, h, ss, false);
             }
         ss = quad_sum(ss);
-        const float n = sqrtf(ss);
-        const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+        float n = sqrtf(ss);
+        float inv = n > 0.0f ? 1.0f / n : 0.0f;
         // y = H D x; lane (t, q) ends with coordinates 32q + 4rb + j in yb[rb][j]
         floatx4 yb[8];
 #pragma unroll
@@ -185,6 +193,20 @@ __device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, c
             for (int rb = 0; rb < 8; ++rb)
                 yb[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     pat[rb & 1][__builtin_popcount(unsigned((rb >> 1) & s)) & 1], xd, yb[rb], 0, 0, 0);
+        }
+        // block-32: this lane's block norm from its rotated values
+        float rho = 1.0f, nb = 0.0f;
+        if constexpr (B32) {
+            float sb = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sb = fmaf(yb[rb][j], yb[rb][j], sb);
+            const float yq = sqrtf(sb), yall = sqrtf(quad_sum(sb));
+            nb = yq * kInvSqrtD;                           // ||(R x)_q||
+            inv = yq > 0.0f ? 5.656854249492381f / yq : 0.0f;  // sqrt(32) / ||y_q||
+            rho = yall > 0.0f ? 2.0f * yq / yall : 0.0f;
+            n = yall * kInvSqrtD;                          // ||x||, for gamma
         }
         uint32_t packed[BITS];
 #pragma unroll
@@ -221,7 +243,7 @@ __device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, c
                 const uint32_t c = quantise<BITS>(z, bnd, s_levels, s_lut, zhat);
                 put_code<BITS, j>(packed, c);
                 if constexpr (PROD) {
-                    const float es = fmaf(z, 256.0f, -zhat);
+                    const float es = B32 ? rho * fmaf(z, 256.0f, -zhat) : fmaf(z, 256.0f, -zhat);
                     se = fmaf(es, es, se);
                     if constexpr (j & 1) {
                         const half2v hi = __builtin_convertvector(float2v{es_prev, es}, half2v);
@@ -258,8 +280,11 @@ __device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, c
 #pragma unroll
             for (int i = 0; i < BITS; ++i) out[i] = packed[i];
         }
+        if constexpr (B32) {
+            if (valid) reinterpret_cast<uint16_t *>(norm_plane)[size_t(dst) * 4 + q] = uint16_t(f2h(nb));
+        }
         if constexpr (!PROD) {
-            if (valid && q == 0)
+            if (!B32 && valid && q == 0)
                 reinterpret_cast<uint16_t *>(norm_plane)[dst] = uint16_t(f2h(n));
         } else {
             se = quad_sum(se);
@@ -276,21 +301,24 @@ __device__ __forceinline__ void encode_rows(const DevTables *__restrict__ tab, c
             const uint32_t bits = se > 0.0f ? ~neg : 0u;
             if (valid) {
                 reinterpret_cast<uint32_t *>(sign_plane + size_t(dst) * 16)[q] = bits;
-                if (q == 0)
-                    reinterpret_cast<uint32_t *>(norm_plane)[dst] = f2h(n) | (f2h(gamma) << 16);
+                if (q == 0) {
+                    if constexpr (B32) reinterpret_cast<uint16_t *>(rnorm_plane)[dst] = uint16_t(f2h(gamma));
+                    else reinterpret_cast<uint32_t *>(norm_plane)[dst] = f2h(n) | (f2h(gamma) << 16);
+                }
             }
         }
     }
 }
 
-template <int BITS, bool PROD, bool APPEND>
+template <int BITS, bool PROD, bool APPEND, bool B32>
 __global__ __launch_bounds__(256) void encode_tq_kernel(const DevTables *__restrict__ tab,
                                                         const uint16_t *__restrict__ x, int64_t n_vec,
                                                         uint8_t *__restrict__ idx_plane,
                                                         uint8_t *__restrict__ sign_plane,
                                                         uint8_t *__restrict__ norm_plane, int64_t n_tiles,
-                                                        RowMap map) {
-    encode_rows<BITS, PROD, APPEND>(tab, x, n_vec, idx_plane, sign_plane, norm_plane, n_tiles, map);
+                                                        RowMap map, uint8_t *__restrict__ rnorm_plane) {
+    encode_rows<BITS, PROD, APPEND, B32>(tab, x, n_vec, idx_plane, sign_plane, norm_plane, n_tiles, map,
+                                         rnorm_plane);
 }
 
 // K (Stage 1 + QJL) and V (Stage 1) rows in a single launch, for encodes
@@ -358,7 +386,7 @@ __global__ __launch_bounds__(256) void encode_q8_kernel(const uint16_t *__restri
     scale_plane[dst * 4 + blk] = uint16_t(sbits);
 }
 
-template <int BITS, bool PROD, bool APPEND>
+template <int BITS, bool PROD, bool APPEND, bool B32 = false>
 static int launch_tq(const DevTables *tab, const uint16_t *x, int64_t n_vec, uint8_t *base,
                      const tq_planes_desc &lay, const RowMap &map, hipStream_t s) {
     const int64_t n_tiles = (n_vec + 15) / 16;
@@ -366,10 +394,13 @@ static int launch_tq(const DevTables *tab, const uint16_t *x, int64_t n_vec, uin
     // as are resident at once, each wave striding over the tiles
     static int cache[kMaxDevices];
     const int64_t blocks =
-        persistent_grid(n_tiles, resident_blocks(encode_tq_kernel<BITS, PROD, APPEND>, 256, cache));
-    hipLaunchKernelGGL((encode_tq_kernel<BITS, PROD, APPEND>), dim3(unsigned(blocks)), dim3(256), 0, s, tab, x,
-                       n_vec, base + lay.idx_offset, PROD ? base + lay.sign_offset : nullptr,
-                       base + lay.norm_offset, n_tiles, map);
+        persistent_grid(n_tiles, resident_blocks(encode_tq_kernel<BITS, PROD, APPEND, B32>, 256, cache));
+    // block-32 K: the residual norms follow the block norms of every row of
+    // the packed tensor (lay.norm_bytes = rows * 10)
+    uint8_t *rnorm = B32 && PROD ? base + lay.norm_offset + lay.norm_bytes / 10 * 8 : nullptr;
+    hipLaunchKernelGGL((encode_tq_kernel<BITS, PROD, APPEND, B32>), dim3(unsigned(blocks)), dim3(256), 0, s, tab,
+                       x, n_vec, base + lay.idx_offset, PROD ? base + lay.sign_offset : nullptr,
+                       base + lay.norm_offset, n_tiles, map, rnorm);
     return int(hipGetLastError());
 }
 
@@ -383,6 +414,23 @@ static int launch_format(const DevTables *tab, const uint16_t *x, int64_t n_vec,
                            reinterpret_cast<int8_t *>(base + lay.idx_offset),
                            reinterpret_cast<uint16_t *>(base + lay.norm_offset), map);
         return int(hipGetLastError());
+    }
+    if (f.kind == TQ_KIND_PROD32) {
+        switch (f.bits) {
+            case 1: return launch_tq<1, true, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+            case 2: return launch_tq<2, true, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+            case 3: return launch_tq<3, true, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+        }
+        return int(hipErrorInvalidValue);
+    }
+    if (f.kind == TQ_KIND_MSE32) {
+        switch (f.bits) {
+            case 1: return launch_tq<1, false, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+            case 2: return launch_tq<2, false, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+            case 3: return launch_tq<3, false, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+            case 4: return launch_tq<4, false, APPEND, true>(tab, x, n_vec, base, lay, map, s);
+        }
+        return int(hipErrorInvalidValue);
     }
     if (f.kind == TQ_KIND_PROD) {
         switch (f.bits) {

@@ -62,7 +62,8 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
 // The plan of one attention call: the single-launch path when its shape and
 // the device allow it, else the two-pass plan.  capacity = blocks of the
 // single-launch kernel resident at once on the current device (0: unknown).
-AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format vf, int capacity);
+AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity);
+inline bool block32_format(tq_format f) { return f.kind == TQ_KIND_MSE32 || f.kind == TQ_KIND_PROD32; }
 // Tokens per block and block size limits of the single-launch kernel.
 constexpr int kFusedSlice = 512;
 constexpr int kFusedMaxTokens = 4096;
@@ -103,6 +104,9 @@ int launch_append_kv(const DevTables *tab, const void *k, const void *v, int B, 
                      const tq_planes_desc &kl, const tq_planes_desc &vl, void *stream);
 int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t n_vec,
                   const tq_planes_desc &lay, void *out, void *stream);
+// Decode attention when K or V uses block-32 norms (attn_generic.hip): a
+// scores and a values pass over the two-pass workspace.
+int launch_attn_generic(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
                 tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
                 int Hkv, int T, int tq, const int32_t *seq_lens, float tau, float *out, void *ws,

@@ -22,7 +22,7 @@ TQ_ERR_HIP = -3
 TQ_ERR_ALLOC = -4
 TQ_ERR_WORKSPACE = -5
 
-KIND_MSE, KIND_PROD, KIND_Q8 = 0, 1, 2
+KIND_MSE, KIND_PROD, KIND_Q8, KIND_MSE32, KIND_PROD32 = 0, 1, 2, 3, 4
 HEAD_DIM = 128
 
 
@@ -58,6 +58,16 @@ def turbo_k(n: int) -> tq_format:
 def mse(bits: int) -> tq_format:
     """b-bit codebook only (the V codec)."""
     return tq_format(KIND_MSE, bits)
+
+
+def mse32(bits: int) -> tq_format:
+    """b-bit codebook with one fp16 norm per block of 32 rotated coordinates."""
+    return tq_format(KIND_MSE32, bits)
+
+
+def turbo_k32(n: int) -> tq_format:
+    """turboN K with block-32 norms: (N-1)-bit codebook + 1-bit QJL."""
+    return tq_format(KIND_PROD32, n - 1)
 
 
 Q8 = tq_format(KIND_Q8, 8)

@@ -22,7 +22,7 @@ import torch
 from kv_cache_quantization_encode_amd import turbokv as T
 from oracle import turbokv_oracle as O
 
-KIND = {"prod": T.KIND_PROD, "mse": T.KIND_MSE, "q8": T.KIND_Q8}
+KIND = {"prod": T.KIND_PROD, "mse": T.KIND_MSE, "q8": T.KIND_Q8, "mse32": T.KIND_MSE32, "prod32": T.KIND_PROD32}
 GUARD = 4096
 FILL = 0xA5
 
@@ -131,6 +131,8 @@ def check_encode(x16: np.ndarray, kind: str, bits: int, packed: np.ndarray, tab:
     u = O.unpack_tq(packed, kind, bits, 128, n)
     sel = np.arange(n) if rows is None else np.asarray(rows)
     xs = x16[sel]
+    if kind in ("mse32", "prod32"):
+        return _check_encode_block32(xs, kind, bits, u, sel, tab, max_exempt)
     enc = O.encode(xs, bits, kind == "prod", tab)
     gidx = u["idx"][sel]
     t = tab.bounds[bits]
@@ -166,6 +168,37 @@ def check_encode(x16: np.ndarray, kind: str, bits: int, packed: np.ndarray, tab:
         gamma = n64 * np.sqrt(np.sum(e * e, axis=-1)) / math.sqrt(128)
         assert np.all(_ulp_diff16(u["rnorm"][sel], gamma.astype(np.float16)) <= 1), "residual norm off"
         stats.update(sign_exempt=float((~ok).mean()), sign_mismatch=int(((sb != (P > 0))).sum()))
+    return stats
+
+
+def _check_encode_block32(xs, kind, bits, u, sel, tab, max_exempt):
+    """check_encode for block-32 norms: codes against the block-standardised
+    z, block norms and gamma within one fp16 ulp, sign bits against the
+    oracle's projection recomputed from the GPU's own codes."""
+    enc = O.encode_block32(xs, bits, kind == "prod32", tab)
+    gidx = u["idx"][sel]
+    t = tab.bounds[bits]
+    near = np.min(np.abs(enc["z"][..., None] - t), axis=-1) < BOUNDARY_TOL
+    mism = gidx != enc["idx"]
+    assert not (mism & ~near).any(), f"{int((mism & ~near).sum())} code mismatches away from boundaries"
+    cap = max(max_exempt * near.size, 1.0)
+    band_cap = cap + 3.0 * math.sqrt(cap)
+    assert mism.sum() <= cap, f"{int(mism.sum())} code mismatches in the band (cap {cap:.1f})"
+    assert near.sum() <= band_cap, f"{int(near.sum())} coordinates near a boundary (cap {band_cap:.1f})"
+    assert np.all(_ulp_diff16(u["bnorm"][sel], enc["bnorm"]) <= 1), "block norm differs by more than 1 fp16 ulp"
+    stats = {"rows": int(len(sel)), "code_exempt": float(near.mean()), "code_mismatch": int(mism.sum())}
+    if kind == "prod32":
+        P = O.qjl_projection_from_codes_block32(xs, gidx, bits, tab)
+        ok = np.abs(P) >= PROJ_TOL
+        sb = u["bits_qjl"][sel]
+        assert not ((sb != (P > 0)) & ok).any(), "QJL sign mismatches away from zero"
+        assert (sb != (P > 0)).sum() <= cap
+        assert (~ok).sum() <= band_cap, f"{int((~ok).sum())} projections near zero (cap {band_cap:.1f})"
+        uu, nb, _ = O.block_standardised_rotation(xs, tab)
+        r = uu - np.repeat(nb / math.sqrt(32), 32, axis=-1) * tab.levels[bits][gidx]
+        gamma = np.sqrt(np.sum(r * r, axis=-1))
+        assert np.all(_ulp_diff16(u["rnorm"][sel], gamma.astype(np.float16)) <= 1), "residual norm off"
+        stats.update(sign_exempt=float((~ok).mean()), sign_mismatch=int((sb != (P > 0)).sum()))
     return stats
 
 
@@ -244,6 +277,13 @@ def sub_packed(packed, kind, bits, n_total, start, count):
     part = O.tq_plane_layout(kind, bits, 128, count)
     out = np.zeros(part["total"], np.uint8)
     for name, (off, size) in part["planes"].items():
+        if kind == "prod32" and name == "norm":
+            # block norms of every row (8 bytes each), then every gamma (2 bytes)
+            fo = full[name][0]
+            out[off:off + 8 * count] = packed[fo + 8 * start:fo + 8 * (start + count)]
+            go = fo + 8 * n_total
+            out[off + 8 * count:off + size] = packed[go + 2 * start:go + 2 * (start + count)]
+            continue
         per_row = size // count if count else 0
         src_off = full[name][0] + start * per_row
         out[off:off + size] = packed[src_off:src_off + size]

@@ -14,7 +14,8 @@ from tests import gpu_helpers as G
 pytestmark = pytest.mark.gpu
 
 FORMATS = [(("prod", 3), ("mse", 4)), (("prod", 2), ("mse", 2)), (("prod", 1), ("mse", 3)),
-           (("mse", 1), ("q8", 8)), (("q8", 8), ("mse", 2))]
+           (("mse", 1), ("q8", 8)), (("q8", 8), ("mse", 2)), (("prod32", 2), ("mse32", 2)),
+           (("mse32", 3), ("mse32", 4))]
 
 
 @pytest.fixture(scope="module")
