@@ -643,8 +643,8 @@ def bench_quality(TK, ctx, dev):
     outlier channels the rotation spreads out.  Bits per element include the
     stored norms / scales; ratio = 16 / bits."""
     import torch
-    res = {"workload": "reconstruction quality: turboN K (QJL), b-bit V, q8 and min-max (group 64) on the "
-                       "min-max workload's K tensor and on llama8b-like K"}
+    res = {"workload": "reconstruction quality: turboN K (QJL), b-bit V, their block-32 norm variants, q8 and "
+                       "min-max (group 64) on the min-max workload's K tensor and on llama8b-like K"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(303)
     n_a = 32 * 8 * 4096 * 128
@@ -665,8 +665,12 @@ def bench_quality(TK, ctx, dev):
         cv = float((torch.sum(xf * yf, 1) / (xf.norm(dim=1) * yf.norm(dim=1)).clamp_min(1e-30)).mean())
         return {"mse": float(((xf - yf) ** 2).mean()), "cosine": round(cos, 5), "cosine_per_vector": round(cv, 5)}
 
+    # block-32 formats (one fp16 Stage-1 norm per 32 rotated coordinates): the
+    # pages' 6.4x / 4.57x for 2 / 3 bits, K with one residual norm on top
     fmts = [("turbo2_k", TK.turbo_k(2), 2.25), ("turbo3_k", TK.turbo_k(3), 3.25), ("turbo4_k", TK.turbo_k(4), 4.25),
-            ("v2", TK.mse(2), 2.125), ("v3", TK.mse(3), 3.125), ("v4", TK.mse(4), 4.125), ("q8", TK.Q8, 8.5)]
+            ("v2", TK.mse(2), 2.125), ("v3", TK.mse(3), 3.125), ("v4", TK.mse(4), 4.125), ("q8", TK.Q8, 8.5),
+            ("turbo2_k_block32", TK.turbo_k32(2), 2.625), ("turbo3_k_block32", TK.turbo_k32(3), 3.625),
+            ("v2_block32", TK.mse32(2), 2.5), ("v3_block32", TK.mse32(3), 3.5), ("v4_block32", TK.mse32(4), 4.5)]
     for name, data in (("minmax_data", data_a), ("llama8b_k", data_b)):
         n_vec = data.shape[0]
         out = {}
