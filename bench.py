@@ -326,6 +326,26 @@ def bench_70b(TK, ctx, dev, reps=10, warm=3):
     t_mid = graph_time(calls(lambda l: l not in boundary), reps, warm, None) / (L - len(boundary))
     t_bnd = graph_time(calls(lambda l: l in boundary), reps, warm, None) / len(boundary)
     per_mid, per_bnd = alg_mid / (L - len(boundary)), alg_bnd / len(boundary)
+    # the same step as a decode loop runs it: each layer's call also appends
+    # the step's new K/V at the last position (tq_attn_decode_append; the q8
+    # boundary layers append in a launch of their own).  Timed last: it
+    # rewrites that position of every cache.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(909)
+    news = [(torch.randn((B, Hkv, 128), generator=gen, device=dev).half(),
+             torch.randn((B, Hkv, 128), generator=gen, device=dev).half()) for _ in range(L)]
+    last = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+
+    def appending(which):
+        def run():
+            for (l, q, kp, vp, kf, vf, out), (kn, vn) in zip(layers, news):
+                if which(l):
+                    TK.tq_attn_decode_append(ctx, q, kn, vn, last, kp.buf, vp.buf, kf, vf, B, Hq, Hkv, T, tau, out,
+                                             ws, wsb)
+        return run
+
+    t_app = graph_time(appending(lambda l: True), reps, warm, None)
+    t_app_mid = graph_time(appending(lambda l: l not in boundary), reps, warm, None) / (L - len(boundary))
     res = {"workload": "70B-like decode step: 80 layers x 8 KV / 64 q heads x 131072 tokens, batch 1; "
                        "turbo3 K + 2-bit V, layers 0,1,78,79 q8 K and V; sparse V tau 1e-6; one HIP graph of 80 calls",
            "step_ms": round(t * 1e3, 4), "alg_gb": round(alg / 1e9, 4), "logical_gb": round(logical / 1e9, 4),
@@ -335,6 +355,7 @@ def bench_70b(TK, ctx, dev, reps=10, warm=3):
            "middle_layer_frac_hbm": round(per_mid / t_mid / 1e9 / HBM_PEAK_GBS, 4),
            "boundary_layer_us": round(t_bnd * 1e6, 2), "boundary_layer_alg_bytes": int(per_bnd),
            "boundary_layer_frac_hbm": round(per_bnd / t_bnd / 1e9 / HBM_PEAK_GBS, 4),
+           "step_with_append_ms": round(t_app * 1e3, 4), "middle_layer_with_append_us": round(t_app_mid * 1e6, 2),
            "_t": t, "_alg": alg, "_t_mid": t_mid, "_per_mid": per_mid, "_t_bnd": t_bnd, "_per_bnd": per_bnd}
     del layers, ws
     torch.cuda.empty_cache()
@@ -527,16 +548,36 @@ def bench_decode_loop(TK, ctx, dev, reps=10, warm=3):
         for c in range(copies):
             TK.tq_append_kv(ctx, k_new, v_new, B, Hkv, T, pos, kf, vf, kps[c].buf, vps[c].buf)
 
-    def steps():
+    def attends():
+        for c in range(copies):
+            TK.tq_attn_decode(ctx, q, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T, lens, tau, out, ws, wsb)
+
+    def separate():
         for c in range(copies):
             TK.tq_append_kv(ctx, k_new, v_new, B, Hkv, T, pos, kf, vf, kps[c].buf, vps[c].buf)
             TK.tq_attn_decode(ctx, q, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T, lens, tau, out, ws, wsb)
 
+    def fused():
+        for c in range(copies):
+            TK.tq_attn_decode_append(ctx, q, k_new, v_new, pos, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T,
+                                     tau, out, ws, wsb)
+
     t_app = graph_time(appends, reps, warm, None) / copies
-    t_step = graph_time(steps, reps, warm, None) / copies
+    t_att = graph_time(attends, reps, warm, None) / copies
+    t_sep = graph_time(separate, reps, warm, None) / copies
+    t_step = graph_time(fused, reps, warm, None) / copies
+    # the same loop three quarters into the cache (the later chunks idle)
+    pos.fill_(3 * T // 4 - 1)
+    lens.fill_(3 * T // 4)
+    t_att34 = graph_time(attends, reps, warm, None) / copies
+    t_step34 = graph_time(fused, reps, warm, None) / copies
     return {"workload": "decode loop, llama8b-like layer: append 1 token (K+V, 8 KV heads) then attend over "
                         "32768 tokens; turbo4 K + 4-bit V, tau 1e-6",
-            "append_us": round(t_app * 1e6, 2), "step_us": round(t_step * 1e6, 2)}
+            "step_us": round(t_step * 1e6, 2), "attn_only_us": round(t_att * 1e6, 2),
+            "separate_launches_us": round(t_sep * 1e6, 2), "append_alone_us": round(t_app * 1e6, 2),
+            "at_24576": {"step_us": round(t_step34 * 1e6, 2), "attn_only_us": round(t_att34 * 1e6, 2)},
+            "note": "step = tq_attn_decode_append (the append inside the attention launch); separate = "
+                    "tq_append_kv then tq_attn_decode; attn_only = tq_attn_decode over the same cache"}
 
 
 def bench_prefill(TK, ctx, dev, reps=10, warm=3, Tq=16):

@@ -11,7 +11,8 @@
  *         (turbo2/3/4), K/V asymmetric strategy (K = both stages, V = Stage 1).
  *   [CXT] chenxutan.com, "TurboQuant+ deep dive": 1.1 cached decode attention,
  *         1.2 KV-cache size, 2.3 QJL (one fixed-seed matrix at both ends,
- *         bit = projection > 0), 3.3 sparse V (no renormalisation).
+ *         bit = projection > 0), 3.3 sparse V (no renormalisation), 3.4
+ *         backend matrix (each step's new K/V rows written into the cache).
  *   [YYL] yeyulingfeng.com, TurboQuant+ introduction: core item 3 (Boundary V:
  *         first 2 + last 2 layers at q8_0), item 4 (Sparse V below 1e-6).
  *   [MAC] mac-code GitHub issue #1, technical analysis, section 2.1
@@ -190,6 +191,28 @@ tq_status tq_attn_decode_noalloc(const tq_ctx *ctx, const void *q_f16, const voi
                                  const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
                                  int T, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,
                                  void *stream);
+/* One decode step with the append of its new token ([CXT] 3.4: every step
+ * writes the new K/V rows into the quantised cache; [CXT] 1.1, [YYL] item 4,
+ * [CXT] 3.3 as tq_attn_decode): the new K and V of every (sequence, kv head)
+ * are encoded into the caches at position pos[b], then every query head of
+ * sequence b attends over its first pos[b] + 1 cached tokens, the new one
+ * included.  Same result as tq_append_kv(k_new, v_new, pos) followed by
+ * tq_attn_decode with seq_lens[b] = pos[b] + 1 and T = T_cap: identical cache
+ * bytes, outputs equal up to the last bits.  A sequence whose pos[b] lies
+ * outside [0, T_cap) gets nothing written and attends over its first
+ * clamp(pos[b] + 1, 0, T_cap) tokens.
+ * q_f16: device [B, Hq, d]; k_new_f16, v_new_f16: device [B, Hkv, d] fp16,
+ * 16-byte aligned; pos: device int32 [B]; k_packed, v_packed: device, the
+ * [B, Hkv, T_cap] caches (tq_packed_layout over B*Hkv*T_cap rows), read and
+ * written; out_f32, workspace (tq_attn_workspace_bytes(B, Hq, Hkv, T_cap,
+ * kf, vf)), tau and ordering as tq_attn_decode.  TurboQuant K (PROD) with
+ * codebook V (MSE) is encoded inside the attention launch, by one block of
+ * each row; other formats take one append launch ahead of it. */
+tq_status tq_attn_decode_append(const tq_ctx *ctx, const void *q_f16, const void *k_new_f16,
+                                const void *v_new_f16, const int32_t *pos, void *k_packed, void *v_packed,
+                                tq_format kf, tq_format vf, int B, int Hq, int Hkv, int T_cap,
+                                float sparse_v_tau, float *out_f32, void *workspace, size_t ws_bytes,
+                                void *stream);
 /* Workspace of tq_attn_decode (0 for an invalid shape, or when B*Hkv > 65535). */
 size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_format vf);
 

@@ -90,7 +90,9 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     // be read whole (16-byte aligned) near the end of the sequence
     p.ld_scores = int((int64_t(T) + 31) / 32 * 32);
     p.off_scores = size_t(off); off = align256(off + heads * int64_t(p.ld_scores) * 4);
-    p.off_stats = size_t(off); off = align256(off + heads * nc * 2 * 4);
+    // chunk statistics: one column more than chunks, for the new token of a
+    // decode step that appends it (scored by an extra block)
+    p.off_stats = size_t(off); off = align256(off + heads * (nc + 1) * 2 * 4);
     p.total = size_t(off);
     return p;
 }
@@ -294,10 +296,11 @@ size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq
 
 // Decode (Tq = 1) and causal prefill (Tq queries per sequence) share one path:
 // query i of sequence b becomes virtual sequence b * Tq + i over b's cache.
-static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_packed, const void *v_packed,
-                           tq_format kf, tq_format vf, int B, int Hq, int Hkv, int T, int Tq,
-                           const int32_t *seq_lens, float sparse_v_tau, float *out_f32, void *workspace,
-                           size_t ws_bytes, void *stream) {
+// Every argument check, nothing launched.
+static tq_status attn_check(const tq_ctx *ctx, const void *q_f16, const void *k_packed, const void *v_packed,
+                            tq_format kf, tq_format vf, int B, int Hq, int Hkv, int T, int Tq,
+                            const int32_t *seq_lens, float sparse_v_tau, float *out_f32, void *workspace,
+                            size_t ws_bytes, tq_planes_desc *kl, tq_planes_desc *vl, AttnPlan *plan) {
     if (!ctx || !q_f16 || !k_packed || !v_packed || !out_f32) return TQ_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return TQ_ERR_INVALID_ARG;
     if (!(sparse_v_tau >= 0.0f) || !std::isfinite(sparse_v_tau)) return TQ_ERR_INVALID_ARG;
@@ -312,13 +315,59 @@ static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_p
     if (int64_t(B) * Hkv * T > kMaxRows || int64_t(T) * 128 >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
     if (int64_t(B) * Tq * Hkv > kMaxGridY) return TQ_ERR_UNSUPPORTED;
     const int64_t n_vec = int64_t(B) * Hkv * T;
-    tq_planes_desc kl{}, vl{};
-    if (!plane_layout(kf, ctx->head_dim, n_vec, &kl) || !plane_layout(vf, ctx->head_dim, n_vec, &vl))
+    if (!plane_layout(kf, ctx->head_dim, n_vec, kl) || !plane_layout(vf, ctx->head_dim, n_vec, vl))
         return TQ_ERR_INVALID_ARG;
-    const AttnPlan plan = attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity());
-    if (!workspace || !aligned(workspace, 256) || ws_bytes < plan.total) return TQ_ERR_WORKSPACE;
+    *plan = attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity());
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < plan->total) return TQ_ERR_WORKSPACE;
+    return TQ_OK;
+}
+
+static tq_status attn_call(const tq_ctx *ctx, const void *q_f16, const void *k_packed, const void *v_packed,
+                           tq_format kf, tq_format vf, int B, int Hq, int Hkv, int T, int Tq,
+                           const int32_t *seq_lens, float sparse_v_tau, float *out_f32, void *workspace,
+                           size_t ws_bytes, void *stream) {
+    tq_planes_desc kl{}, vl{};
+    AttnPlan plan{};
+    const tq_status st = attn_check(ctx, q_f16, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, Tq, seq_lens,
+                                    sparse_v_tau, out_f32, workspace, ws_bytes, &kl, &vl, &plan);
+    if (st != TQ_OK) return st;
     return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T, Tq, seq_lens,
-                       sparse_v_tau, out_f32, workspace, plan, stream) == 0
+                       sparse_v_tau, out_f32, workspace, plan, 0, nullptr, stream) == 0
+               ? TQ_OK
+               : TQ_ERR_HIP;
+}
+
+tq_status tq_attn_decode_append(const tq_ctx *ctx, const void *q_f16, const void *k_new_f16,
+                                const void *v_new_f16, const int32_t *pos, void *k_packed, void *v_packed,
+                                tq_format kf, tq_format vf, int B, int Hq, int Hkv, int T_cap,
+                                float sparse_v_tau, float *out_f32, void *workspace, size_t ws_bytes,
+                                void *stream) {
+    if (!ctx || !k_new_f16 || !v_new_f16 || !pos) return TQ_ERR_INVALID_ARG;
+    if (!aligned(k_new_f16, 16) || !aligned(v_new_f16, 16)) return TQ_ERR_INVALID_ARG;
+    tq_planes_desc kl{}, vl{};
+    AttnPlan plan{};
+    const tq_status st = attn_check(ctx, q_f16, k_packed, v_packed, kf, vf, B, Hq, Hkv, T_cap, 1, pos,
+                                    sparse_v_tau, out_f32, workspace, ws_bytes, &kl, &vl, &plan);
+    if (st != TQ_OK) return st;
+    // (the two-pass kernels put the rows' extra blocks in grid rows of their
+    // own: at most twice B * Hkv grid rows)
+    if (append_in_attention(kf, vf) && (plan.fused || 2 * int64_t(B) * Hkv <= kMaxGridY)) {
+        const AttnAppend app{k_new_f16, v_new_f16, k_packed, v_packed};
+        return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T_cap, 1, pos,
+                           sparse_v_tau, out_f32, workspace, plan, 0, &app, stream) == 0
+                   ? TQ_OK
+                   : TQ_ERR_HIP;
+    }
+    // other formats: the append launch first, then attention over pos + 1
+    int r = launch_append_kv(ctx->dev, k_new_f16, v_new_f16, B, Hkv, T_cap, pos, kf, vf, k_packed, v_packed, kl,
+                             vl, stream);
+    if (r == kPairDeclined) {
+        r = launch_append(ctx->dev, k_new_f16, B, Hkv, T_cap, pos, kf, k_packed, kl, stream);
+        if (r == 0) r = launch_append(ctx->dev, v_new_f16, B, Hkv, T_cap, pos, vf, v_packed, vl, stream);
+    }
+    if (r != 0) return TQ_ERR_HIP;
+    return launch_attn(ctx->dev, q_f16, k_packed, v_packed, kf, vf, kl, vl, B, Hq, Hkv, T_cap, 1, pos,
+                       sparse_v_tau, out_f32, workspace, plan, 1, nullptr, stream) == 0
                ? TQ_OK
                : TQ_ERR_HIP;
 }

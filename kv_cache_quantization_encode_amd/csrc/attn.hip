@@ -36,12 +36,122 @@
 
 namespace tq {
 
-template <int G, int KIND, int BITS>
+// The extra block of an appending decode step (256 threads): encodes the
+// new token of its row at position pos (K by wave 0, V by wave 1, with the
+// encode kernels' tile code) while waves 2 and 3 form the query operands of
+// the row's G heads, q_rot = R q and q_proj = S q_rot, in fp32; then wave 0
+// scores the stored token for every head with the rotated-domain formula of
+// the scan,
+//   s_h = (1/sqrt d) [ n/sqrt(d) <q_rot, c[idx]> + sqrt(pi/2)/m gamma <q_proj, 2 bit - 1> ],
+// and writes the scores at position pos and the statistics (max = the score,
+// sum = 1) of the extra chunk column.  LDS scratch: et (two EncodeTables),
+// frag (2048 half8), qr ([2G][128] fp32: q_rot rows, then q_proj rows).
+template <int G, int KB, int VB>
+__device__ __forceinline__ void append_and_score(const AttnArgs &a, int b, int kvh, int row, int pos,
+                                                 int64_t head0, float *scores, EncodeTables *et, half8 *frag,
+                                                 float (*qr)[128], int tid) {
+    constexpr float kQjl = 1.2533141373155003f / 128.0f;  // sqrt(pi/2) / m
+    const int wave = tid >> 6, lane = tid & 63;
+    // waves 2 and 3: the query rows of heads wave - 2, wave, ... (in flight
+    // with the encode's loads)
+    constexpr int kH = (G + 1) / 2;
+    uint32_t q0[kH], q1[kH];
+    float d0 = 0.0f, d1 = 0.0f;
+    if (wave >= 2) {
+#pragma unroll
+        for (int i = 0; i < kH; ++i) {
+            const int h = wave - 2 + 2 * i;
+            const uint16_t *q = a.q + io_row(a, b, kvh, h < G ? h : 0) * kHeadDim;
+            q0[i] = q[lane];
+            q1[i] = q[lane + 64];
+        }
+        d0 = a.tab->signs[lane];
+        d1 = a.tab->signs[lane + 64];
+    }
+    append_new_token<KB, VB, 256>(a, row, pos, et, frag, tid);
+    if (wave >= 2) {
+#pragma unroll
+        for (int i = 0; i < kH; ++i) {
+            const int h = wave - 2 + 2 * i;
+            if (h >= G) break;
+            float v0 = h2f(q0[i]) * d0, v1 = h2f(q1[i]) * d1;
+            fwht128_lanes(v0, v1, lane);
+            qr[h][lane] = v0 * kRsqrtD;
+            qr[h][lane + 64] = v1 * kRsqrtD;
+        }
+        // q_proj rows p = lane, lane + 64 of this wave's heads, S from row-major [m][d]
+        const half8 *S8 = reinterpret_cast<const half8 *>(a.tab->S);
+        float pr[kH][2];
+#pragma unroll
+        for (int i = 0; i < kH; ++i) pr[i][0] = pr[i][1] = 0.0f;
+#pragma unroll 2
+        for (int k8 = 0; k8 < 16; ++k8) {
+            const half8 sa = S8[lane * 16 + k8], sb = S8[(lane + 64) * 16 + k8];
+#pragma unroll
+            for (int i = 0; i < kH; ++i) {
+                const int h = wave - 2 + 2 * i;
+                if (h >= G) break;
+                const float4 qa = *reinterpret_cast<const float4 *>(&qr[h][8 * k8]);
+                const float4 qb = *reinterpret_cast<const float4 *>(&qr[h][8 * k8 + 4]);
+                const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pr[i][0] = fmaf(float(sa[j]), qv[j], pr[i][0]);
+                    pr[i][1] = fmaf(float(sb[j]), qv[j], pr[i][1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kH; ++i) {
+            const int h = wave - 2 + 2 * i;
+            if (h >= G) break;
+            qr[G + h][lane] = pr[i][0];
+            qr[G + h][lane + 64] = pr[i][1];
+        }
+    }
+    __syncthreads();  // the new rows are stored, the query rows are in LDS
+    if (wave != 0) return;
+    const int dst = row * a.T + pos;
+    const uint32_t *iw = reinterpret_cast<const uint32_t *>(a.kw.idx + size_t(dst) * (16 * KB));
+    const uint4 sg = *reinterpret_cast<const uint4 *>(a.kw.sign + size_t(dst) * 16);
+    const uint32_t nn = reinterpret_cast<const uint32_t *>(a.kw.norm)[dst];
+    const float n = h2f(nn & 0xFFFFu), gamma = h2f(nn >> 16);
+    float lev[2], sgn[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = lane + 64 * u;
+        // code i: bits i*KB .. i*KB + KB - 1 of the row's bitstream
+        const int o = i * KB, w = o >> 5, sh = o & 31;
+        uint32_t c = iw[w] >> sh;
+        if (sh + KB > 32) c |= iw[w + 1] << (32 - sh);
+        lev[u] = a.tab->levels[KB - 1][c & ((1u << KB) - 1u)];
+        const uint32_t word = u == 0 ? (lane < 32 ? sg.x : sg.y) : (lane < 32 ? sg.z : sg.w);
+        sgn[u] = ((word >> (lane & 31)) & 1u) ? 1.0f : -1.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float dc = quad_sum(row16_sum(qr[h][lane] * lev[0] + qr[h][lane + 64] * lev[1]));
+        const float dq = quad_sum(row16_sum(qr[G + h][lane] * sgn[0] + qr[G + h][lane + 64] * sgn[1]));
+        const float sc = kRsqrtD * (n * kRsqrtD * dc + kQjl * gamma * dq);
+        if (lane == 0) {
+            scores[(head0 + h) * a.ld_scores + pos] = sc;
+            float *stt = a.stats + ((head0 + h) * a.n_chunks + a.n_chunks - 1) * 2;
+            stt[0] = sc;
+            stt[1] = 1.0f;
+        }
+    }
+}
+
+// APPEND: a decode step that also appends the new token (AttnArgs::append
+// 1): one extra block per row, in grid rows after the chunks' rows, encodes
+// it and scores only it (append_and_score).
+template <int G, int KIND, int BITS, bool APPEND = false>
 __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
                                                           const uint8_t *__restrict__ ksign,
                                                           const uint8_t *__restrict__ knorm,
                                                           float *__restrict__ scores) {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "1, 2, 4 or 8 query heads per kv head");
+    static_assert(!APPEND || KIND == TQ_KIND_PROD, "the append encodes TurboQuant K");
     // s_pair[f]: fp16 hi halves and fp16 lo halves of the two levels of a
     // 2-code field f = c0 | c1 << BITS; s_sgn[byte]: eight fp16 +-1 (bit set -> +1)
     constexpr int kPairs = KIND == TQ_KIND_Q8 ? 1 : 1 << (2 * BITS);
@@ -50,8 +160,40 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
     __shared__ float s_red[4][16][2];  // per wave, per head: (max, sum)
     __shared__ __attribute__((aligned(16))) _Float16 s_a[16][128];
     __shared__ __attribute__((aligned(16))) _Float16 s_ap[KIND == TQ_KIND_PROD ? 16 : 1][128];
+    __shared__ EncodeTables s_et[APPEND ? 2 : 1];
+    __shared__ half8 s_fr[APPEND ? 2048 : 1];
+    __shared__ float s_qr[APPEND ? 2 * G : 1][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = lane & 15, kq = lane >> 4;
+    if constexpr (APPEND) {
+        // the extra blocks (grid rows past the B * Hkv rows of chunks, so
+        // that they are dispatched last): block r of them encodes the new
+        // token of row r at position seq_lens[b] (none outside [0, T)) and
+        // scores it as the one-token chunk a.n_chunks - 1; the other chunks
+        // end before it (L = the clamped seq_lens[b])
+        const int rows = a.B * a.Hkv;
+        if (int(blockIdx.y) >= rows) {
+            const int row = (int(blockIdx.y) - rows) * int(gridDim.x) + int(blockIdx.x);
+            if (row >= rows) return;
+            const int b = row / a.Hkv, kvh = row - b * a.Hkv;
+            const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
+            const int chunk_id = a.n_chunks - 1;
+            const int pos = a.seq_lens[b];
+            if (pos >= 0 && pos < a.T) {
+                switch (a.vbits) {
+                    case 1: append_and_score<G, BITS, 1>(a, b, kvh, row, pos, head0, scores, s_et, s_fr, s_qr, tid); break;
+                    case 2: append_and_score<G, BITS, 2>(a, b, kvh, row, pos, head0, scores, s_et, s_fr, s_qr, tid); break;
+                    case 3: append_and_score<G, BITS, 3>(a, b, kvh, row, pos, head0, scores, s_et, s_fr, s_qr, tid); break;
+                    default: append_and_score<G, BITS, 4>(a, b, kvh, row, pos, head0, scores, s_et, s_fr, s_qr, tid); break;
+                }
+            } else if (tid < G) {
+                float *st = a.stats + ((head0 + tid) * a.n_chunks + chunk_id) * 2;
+                st[0] = -INFINITY;
+                st[1] = 0.0f;
+            }
+            return;
+        }
+    }
     const int chunk_id = blockIdx.x, row = blockIdx.y;  // row = b*Hkv + kvh
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
     const int64_t head0 = int64_t(b) * a.Hq + int64_t(kvh) * G;
@@ -877,12 +1019,32 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
 
 // ------------------------------------------------------------------ launch
 template <int G, int KK, int KB, int VK, int VB>
-static int launch_passes(const AttnArgs &a, hipStream_t s) {
-    dim3 grid(unsigned(a.n_chunks), unsigned(a.B * a.Hkv));
-    hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, a, a.kidx, a.ksign, a.knorm,
-                       a.scores);
+static int launch_passes(const AttnArgs &as, hipStream_t s) {
+    dim3 grid(unsigned(as.n_chunks), unsigned(as.B * as.Hkv));
+    if constexpr (KK == TQ_KIND_PROD) {
+        if (as.append) {
+            // the chunks of every row, then the rows' extra blocks (the last
+            // chunk column of the statistics) in grid rows of their own
+            const unsigned nc = unsigned(as.n_chunks - 1), rows = unsigned(as.B * as.Hkv);
+            const dim3 sgrid(nc, rows + (rows + nc - 1) / nc);
+            hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB, true>), sgrid, dim3(256), 0, s, as, as.kidx, as.ksign,
+                               as.knorm, as.scores);
+        } else
+            hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, as, as.kidx, as.ksign,
+                               as.knorm, as.scores);
+    } else {
+        hipLaunchKernelGGL((attn_scores_kernel<G, KK, KB>), grid, dim3(256), 0, s, as, as.kidx, as.ksign, as.knorm,
+                           as.scores);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return int(e);
+    // with an append the values pass sees the new token too (in the chunk
+    // that holds its position; the statistics have one column more)
+    AttnArgs a = as;
+    if (a.append) {
+        a.len_add = 1;
+        grid.x = unsigned(a.n_chunks - 1);
+    }
     if constexpr (G == 8 && ((VK == TQ_KIND_MSE && VB == 2) || VK == TQ_KIND_Q8)) {
         // 8 query heads: the kept rows of all heads together are most of the
         // tokens unless attention is very peaked, and the per-row cost of the
@@ -935,7 +1097,7 @@ static int dispatch_k(const AttnArgs &a, tq_format kf, tq_format vf, hipStream_t
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
                 tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
                 int Hkv, int T, int tq, const int32_t *seq_lens, float tau, float *out, void *ws,
-                const AttnPlan &plan, void *stream) {
+                const AttnPlan &plan, int len_add, const AttnAppend *app, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *w = static_cast<uint8_t *>(ws);
     const uint8_t *kb = static_cast<const uint8_t *>(kp), *vb = static_cast<const uint8_t *>(vp);
@@ -966,6 +1128,21 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
     a.ld_scores = plan.ld_scores;
     a.k_rotated = kf.kind != TQ_KIND_Q8;
     a.v_rotated = vf.kind != TQ_KIND_Q8;
+    a.len_add = len_add;
+    if (app) {
+        // the new token of each row goes to position seq_lens[b]: the
+        // single-launch kernel encodes it in the block that owns that
+        // position; the two-pass scores kernel in an extra chunk column
+        uint8_t *kw = static_cast<uint8_t *>(app->k_packed), *vw = static_cast<uint8_t *>(app->v_packed);
+        a.k_new = static_cast<const uint16_t *>(app->k_new);
+        a.v_new = static_cast<const uint16_t *>(app->v_new);
+        a.kw = EncodePlanes{kw + klay.idx_offset, kw + klay.sign_offset, kw + klay.norm_offset, nullptr};
+        a.vw = EncodePlanes{vw + vlay.idx_offset, nullptr, vw + vlay.norm_offset, nullptr};
+        a.vbits = vf.bits;
+        a.append = plan.fused ? 2 : 1;
+        if (plan.fused) a.len_add = 1;
+        else a.n_chunks = plan.n_chunks + 1;
+    }
     if (block32_format(kf) || block32_format(vf)) return launch_attn_generic(a, kf, vf, stream);
     if (plan.fused) {
         a.sync = reinterpret_cast<uint32_t *>(w + plan.off_sync);

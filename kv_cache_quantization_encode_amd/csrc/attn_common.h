@@ -7,7 +7,7 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "device_common.h"
+#include "encode_common.h"
 
 namespace tq {
 
@@ -45,6 +45,19 @@ struct AttnArgs {
     // (max, sum) slot per block and head
     uint32_t *sync;
     int nblk, tb;
+    // decode step with append (chenxutan.com, "TurboQuant+ deep dive", 3.4:
+    // the backends write each step's new K/V rows into the quantised cache):
+    // the new token of row (b, kv head) goes to position seq_lens[b] of the
+    // cache, encoded in the attention launch itself by one block of its row.
+    //   append 1: that block is an extra one of the scores pass (its
+    //             statistics are the last of a.n_chunks columns) which
+    //             scores only the new token; the other chunks scan the
+    //             seq_lens[b] tokens before it;
+    //   append 2: the block whose token range holds the new position.
+    // len_add: added to seq_lens[b] before clamping to [0, T].
+    int append, len_add, vbits;
+    const uint16_t *k_new, *v_new;  // [B * Hkv][128] fp16
+    EncodePlanes kw, vw;            // the K and V planes, writable
 };
 
 // Query i of sequence s sits at position L_s - tq + i and sees the first
@@ -54,7 +67,9 @@ struct AttnArgs {
 __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
     if (a.tq == 1) {  // decode: no integer divisions on the setup path
         if (!a.seq_lens) return a.T;
-        const int L = a.seq_lens[b];
+        int L = a.seq_lens[b];
+        if (L >= a.T) return a.T;
+        L += a.len_add;
         return L < 0 ? 0 : (L > a.T ? a.T : L);
     }
     const int groups = a.tq / a.qp;
@@ -65,6 +80,48 @@ __device__ __forceinline__ int seq_len_of(const AttnArgs &a, int b) {
     return L < 0 ? 0 : L;
 }
 __device__ __forceinline__ int row_shift(const AttnArgs &a, int g) { return a.qp - 1 - g / a.qg; }
+
+// The new token of decode row `row` (b * Hkv + kv head) encoded into cache
+// row row * T + pos: K (Stage 1 + QJL, KB bits) by wave 0, V (Stage 1, VB
+// bits) by wave 1, with the encode kernels' own tile code, so the bytes are
+// those of tq_append_kv.  Every global read (quantiser tables, the 32 KB of
+// S fragments, the two new rows, the lane constants) is issued before one
+// barrier; et (two EncodeTables) and frag (2048 half8) are LDS scratch.
+// Every thread of the block (NT threads) calls this; after the barrier that
+// the caller places next, the block's own loads see the stored rows (no other
+// block reads them in this launch).
+template <int KB, int VB, int NT>
+__device__ __forceinline__ void append_new_token(const AttnArgs &a, int row, int pos, EncodeTables *et,
+                                                 half8 *frag, int tid) {
+    static_assert(2048 % NT == 0, "S fragments split evenly over the threads");
+    constexpr int kPer = 2048 / NT;
+    const int wave = tid >> 6, lane = tid & 63, q = lane >> 4;
+    half8 fr[kPer];
+    const half8 *src = reinterpret_cast<const half8 *>(a.tab->S_enc);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) fr[i] = src[tid + i * NT];
+    half8 xb[4];
+    EncodeLane el;
+    if (wave < 2) {
+        const uint16_t *x = (wave == 0 ? a.k_new : a.v_new) + size_t(row) * kHeadDim + 32 * q;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xb[s] = *reinterpret_cast<const half8 *>(x + 8 * s);
+        if (wave == 0) encode_lane<KB>(a.tab, lane, el);
+        else encode_lane<VB>(a.tab, lane, el);
+    }
+    fill_encode_tables<KB, true>(a.tab, &et[0], tid, NT);
+    fill_encode_tables<VB, false>(a.tab, &et[1], tid, NT);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) frag[tid + i * NT] = fr[i];
+    __syncthreads();
+    const int dst = row * a.T + pos;  // cache rows < 2^31 (checked on the host)
+    const bool first = (lane & 15) == 0;
+    auto fget = [&](int i) { return frag[i]; };
+    if (wave == 0)
+        encode_tile<KB, true, false>(xb, el, et[0].levels, et[0].lut, fget, lane, first, dst, a.kw, [] {});
+    else if (wave == 1)
+        encode_tile<VB, false, false>(xb, el, et[1].levels, et[1].lut, fget, lane, first, dst, a.vw, [] {});
+}
 
 // Packed K/V row (batch * Hkv + kv head) of virtual row b * Hkv + kvh: the
 // queries of one sequence share its cache.

@@ -212,11 +212,14 @@ __device__ __forceinline__ void fused_query_setup(const QueryLoads<8, PROJ, 8> &
 // = (sequence, kv head), x = block of the row.  a.sync: a departure counter
 // per row; a.stats: [rows][nblk][8] 64-bit (max, sum) slots; both zero
 // between calls.
-template <int KK, int KB, int VK>
+// APPEND: a decode step that also appends the new token (AttnArgs::append
+// 2): the block whose range holds the new position encodes it first.
+template <int KK, int KB, int VK, bool APPEND = false>
 __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
                                                                const uint8_t *__restrict__ ksign,
                                                                const uint8_t *__restrict__ knorm) {
     constexpr int G = 8;
+    static_assert(!APPEND || (KK == TQ_KIND_PROD && VK == TQ_KIND_MSE), "the append encodes TurboQuant K and V");
     constexpr bool PROJ = KK == TQ_KIND_PROD;
     constexpr bool VQ8 = VK == TQ_KIND_Q8;
     static_assert(VK == TQ_KIND_Q8 || VK == TQ_KIND_MSE, "2-bit codebook V or q8 V");
@@ -274,6 +277,17 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         if (tid < kPairs) {
             lv[0] = a.tab->levels[KB - 1][tid & ((1 << KB) - 1)];
             lv[1] = a.tab->levels[KB - 1][tid >> KB];
+        }
+    }
+    if constexpr (APPEND) {
+        // the new token at position seq_lens[b] (none outside [0, T); L
+        // counts it: len_add = 1): the block whose range holds it encodes it
+        // before any load of its range; its reads travel with the query's
+        const int pos = a.seq_lens[b];
+        if (pos >= 0 && pos < a.T && pos >= blk * a.tb && pos < (blk + 1) * a.tb) {
+            append_new_token<KB, 2, kFThreads>(a, row, pos, reinterpret_cast<EncodeTables *>(lds.sc),
+                                               reinterpret_cast<half8 *>(lds.sc + 1024), tid);
+            __syncthreads();
         }
     }
     // largest V norm (codebook V) or block scale (q8 V) of the block's tokens,
@@ -863,6 +877,13 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
 template <int KK, int KB, int VK>
 static int launch_fused_t(const AttnArgs &a, hipStream_t s) {
     dim3 grid(unsigned(a.nblk), unsigned(a.B * a.Hkv));
+    if constexpr (KK == TQ_KIND_PROD && VK == TQ_KIND_MSE) {
+        if (a.append) {
+            hipLaunchKernelGGL((attn_fused_kernel<KK, KB, VK, true>), grid, dim3(kFThreads), 0, s, a, a.kidx,
+                               a.ksign, a.knorm);
+            return int(hipGetLastError());
+        }
+    }
     hipLaunchKernelGGL((attn_fused_kernel<KK, KB, VK>), grid, dim3(kFThreads), 0, s, a, a.kidx, a.ksign, a.knorm);
     return int(hipGetLastError());
 }

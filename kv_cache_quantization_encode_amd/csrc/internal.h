@@ -107,10 +107,24 @@ int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t
 // Decode attention when K or V uses block-32 norms (attn_generic.hip): a
 // scores and a values pass over the two-pass workspace.
 int launch_attn_generic(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
+// A decode step's new tokens ([B * Hkv][128] fp16 each), encoded by the
+// attention launch into the caches it reads (writable aliases of kp, vp).
+struct AttnAppend {
+    const void *k_new, *v_new;
+    void *k_packed, *v_packed;
+};
+// True when the attention kernels can encode the new token themselves
+// (TurboQuant K and codebook V with 128-element norms); other formats take a
+// separate append launch first.
+inline bool append_in_attention(tq_format kf, tq_format vf) {
+    return kf.kind == TQ_KIND_PROD && vf.kind == TQ_KIND_MSE;
+}
+// len_add: each seq_lens[b] counts len_add more tokens (clamped to [0, T]);
+// app: the append of a decode step (nullptr: none).
 int launch_attn(const DevTables *tab, const void *q, const void *kp, const void *vp, tq_format kf,
                 tq_format vf, const tq_planes_desc &klay, const tq_planes_desc &vlay, int B, int Hq,
                 int Hkv, int T, int tq, const int32_t *seq_lens, float tau, float *out, void *ws,
-                const AttnPlan &plan, void *stream);
+                const AttnPlan &plan, int len_add, const AttnAppend *app, void *stream);
 // Single-launch decode attention (attn_fused.hip); capacity of the current
 // device for it (0 when it cannot run).
 int launch_attn_fused(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);

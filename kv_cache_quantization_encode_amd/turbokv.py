@@ -95,6 +95,8 @@ def load() -> ctypes.CDLL:
                                    ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.tq_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, tq_format, tq_format, i32, i32, i32, i32, vp,
                                            ctypes.c_float, vp, vp]
+    lib.tq_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, tq_format, tq_format, i32, i32, i32, i32,
+                                          ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.tq_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, tq_format, tq_format]
     lib.tq_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_attn_prefill.argtypes = [vp, vp, vp, vp, tq_format, tq_format, i32, i32, i32, i32, i32, vp,
@@ -107,7 +109,7 @@ def load() -> ctypes.CDLL:
     lib.tq_status_str.restype = ctypes.c_char_p
     for name in ("tq_codebook_init", "tq_ctx_destroy", "tq_host_tables", "tq_packed_layout",
                  "tq_encode_kv", "tq_append_kv", "tq_decode_kv", "tq_attn_decode", "tq_attn_decode_noalloc",
-                 "tq_attn_prefill",
+                 "tq_attn_decode_append", "tq_attn_prefill",
                  "tq_minmax_quant",
                  "tq_minmax_dequant"):
         getattr(lib, name).restype = ctypes.c_int
@@ -198,6 +200,13 @@ def tq_attn_decode(ctx, q, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, seq_lens, 
     _check(load().tq_attn_decode(ctx, _ptr(q), _ptr(k_packed), _ptr(v_packed), kf, vf, B, Hq, Hkv, T,
                                  _ptr(seq_lens), float(tau), _ptr(out), _ptr(workspace), ws_bytes,
                                  _stream(stream)), "tq_attn_decode")
+
+
+def tq_attn_decode_append(ctx, q, k_new, v_new, pos, k_packed, v_packed, kf, vf, B, Hq, Hkv, T_cap, tau, out,
+                          workspace, ws_bytes, stream=None) -> None:
+    _check(load().tq_attn_decode_append(ctx, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(k_packed),
+                                        _ptr(v_packed), kf, vf, B, Hq, Hkv, T_cap, float(tau), _ptr(out),
+                                        _ptr(workspace), ws_bytes, _stream(stream)), "tq_attn_decode_append")
 
 
 def tq_attn_decode_noalloc(ctx, q, k_packed, v_packed, kf, vf, B, Hq, Hkv, T, seq_lens, tau, out,

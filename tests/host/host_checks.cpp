@@ -90,6 +90,22 @@ int main() {
            TQ_ERR_UNSUPPORTED);
     EXPECT(tq_attn_decode(&fake, A, A, A, k3, v2, 1, 32, 8, 32768, nullptr, 1e-6f, o, A, ws, nullptr) ==
            TQ_ERR_HIP);
+    const int32_t *P = static_cast<const int32_t *>(A);
+    EXPECT(tq_attn_decode_append(&fake, A, A, A, P, A, A, k3, v2, 1, 32, 8, 32768, 1e-6f, o, A, ws, nullptr) ==
+           TQ_ERR_HIP);
+    EXPECT(tq_attn_decode_append(&fake, A, A, A, nullptr, A, A, k3, v2, 1, 32, 8, 32768, 1e-6f, o, A, ws,
+                                 nullptr) == TQ_ERR_INVALID_ARG);
+    EXPECT(tq_attn_decode_append(&fake, A, nullptr, A, P, A, A, k3, v2, 1, 32, 8, 32768, 1e-6f, o, A, ws,
+                                 nullptr) == TQ_ERR_INVALID_ARG);
+    EXPECT(tq_attn_decode_append(&fake, A, A, A, P, A, A, k3, v2, 1, 32, 8, 32768, 1e-6f, o, A, 1024,
+                                 nullptr) == TQ_ERR_WORKSPACE);
+    EXPECT(tq_attn_decode_append(&fake, A, A, A, P, A, A, k3, {TQ_KIND_PROD, 2}, 1, 32, 8, 32768, 1e-6f, o, A, ws,
+                                 nullptr) == TQ_ERR_UNSUPPORTED);
+    // q8 caches take the separate append launch (the stub fails it first)
+    const tq_format q8{TQ_KIND_Q8, 8};
+    const size_t qws = tq_attn_workspace_bytes(1, 32, 8, 4096, q8, q8);
+    EXPECT(tq_attn_decode_append(&fake, A, A, A, P, A, A, q8, q8, 1, 32, 8, 4096, 1e-6f, o, A, qws, nullptr) ==
+           TQ_ERR_HIP);
     const size_t pws = tq_attn_prefill_workspace_bytes(2, 32, 8, 4096, 16, k3, v2);
     EXPECT(pws > 0);
     EXPECT(tq_attn_prefill(&fake, A, A, A, k3, v2, 2, 32, 8, 4096, 16, nullptr, 1e-6f, o, A, pws, nullptr) ==

@@ -25,7 +25,7 @@ int launch_decode(const DevTables *, const void *, tq_format, int64_t, const tq_
 }
 int launch_attn(const DevTables *, const void *, const void *, const void *, tq_format, tq_format,
                 const tq_planes_desc &, const tq_planes_desc &, int, int, int, int, int, const int32_t *, float,
-                float *, void *, const AttnPlan &, void *) {
+                float *, void *, const AttnPlan &, int, const AttnAppend *, void *) {
     return 1;
 }
 int launch_attn_fused(const AttnArgs &, tq_format, tq_format, void *) { return 1; }

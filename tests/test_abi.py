@@ -25,7 +25,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "turbokv.h")).read()
     names = sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", hdr)))
-    assert len(names) == 15 and "tq_attn_decode" in names and "tq_attn_decode_noalloc" in names
+    assert len(names) == 16 and "tq_attn_decode" in names and "tq_attn_decode_noalloc" in names
+    assert "tq_attn_decode_append" in names
     assert "tq_attn_prefill" in names and "tq_attn_prefill_workspace_bytes" in names and "tq_status_str" in names
     for n in names:
         assert hasattr(lib, n), n

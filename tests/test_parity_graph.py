@@ -1,6 +1,7 @@
-"""HIP-graph replays of a decode step (append, then attention) must equal the
-eager result on every replay, with eager work and synchronisations between
-replays (the benchmark captures attention calls in graphs)."""
+"""HIP-graph replays of a decode step (append, then attention; or both in
+one call, tq_attn_decode_append) must equal the eager result on every
+replay, with eager work and synchronisations between replays (the benchmark
+captures attention calls in graphs)."""
 import numpy as np
 import pytest
 import torch
@@ -12,9 +13,13 @@ from tests import gpu_helpers as G
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kf,vf,hq", [(("prod", 3), ("mse", 4), 8), (("prod", 2), ("mse", 2), 16),
-                                      (("q8", 8), ("q8", 8), 16)])
-def test_graph_replays_match_eager(oracle_tables, kf, vf, hq):
+@pytest.mark.parametrize("kf,vf,hq,one_call", [(("prod", 3), ("mse", 4), 8, False),
+                                               (("prod", 2), ("mse", 2), 16, False),
+                                               (("q8", 8), ("q8", 8), 16, False),
+                                               (("prod", 3), ("mse", 4), 8, True),
+                                               (("prod", 2), ("mse", 2), 16, True),
+                                               (("q8", 8), ("q8", 8), 16, True)])
+def test_graph_replays_match_eager(oracle_tables, kf, vf, hq, one_call):
     B, Hkv, Tc = 2, 2, 2100
     c = W.llama8b(T=Tc, Hq=hq, Hkv=Hkv, B=B)
     K, V = G.tf(*kf), G.tf(*vf)
@@ -33,10 +38,14 @@ def test_graph_replays_match_eager(oracle_tables, kf, vf, hq):
         out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
 
         def step():
-            T.tq_append_kv(ctx, k_new, v_new, B, Hkv, Tc, pos, K, V, kp.buf, vp.buf)
-            T.tq_attn_decode(ctx, q, kp.buf, vp.buf, K, V, B, hq, Hkv, Tc, lens, 1e-6, out, ws, wsb)
+            if one_call:
+                T.tq_attn_decode_append(ctx, q, k_new, v_new, pos, kp.buf, vp.buf, K, V, B, hq, Hkv, Tc, 1e-6, out,
+                                        ws, wsb)
+            else:
+                T.tq_append_kv(ctx, k_new, v_new, B, Hkv, Tc, pos, K, V, kp.buf, vp.buf)
+                T.tq_attn_decode(ctx, q, kp.buf, vp.buf, K, V, B, hq, Hkv, Tc, lens, 1e-6, out, ws, wsb)
 
-        G.note(f"graph eager kf={kf} vf={vf} Hq={hq}")
+        G.note(f"graph eager kf={kf} vf={vf} Hq={hq} one_call={one_call}")
         step()
         torch.cuda.synchronize()
         ref = out.clone()
