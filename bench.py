@@ -580,12 +580,14 @@ def bench_decode_loop(TK, ctx, dev, reps=10, warm=3):
                     "tq_append_kv then tq_attn_decode; attn_only = tq_attn_decode over the same cache"}
 
 
-def bench_prefill(TK, ctx, dev, reps=10, warm=3, Tq=16):
+def bench_prefill(TK, ctx, dev, reps=10, warm=3, tqs=(16, 64, 128, 2048)):
     """Causal prefill attention on the llama8b-like layer (32 q / 8 KV heads,
     32768 tokens, turbo4 K + 4-bit V, tau 1e-6): the last Tq positions attend
-    to their prefixes (tq_attn_prefill).  Eight rotating caches, one HIP graph
-    of eight calls; inputs drawn on the GPU from a seeded generator (K
-    lognormal(0, 0.5) per (head, channel) x Student-t(3), V and q N(0, 1))."""
+    to their prefixes (tq_attn_prefill), for each Tq in tqs.  Eight rotating
+    caches, one HIP graph of eight calls; inputs drawn on the GPU from a
+    seeded generator (K lognormal(0, 0.5) per (head, channel) x Student-t(3),
+    V and q N(0, 1)).  attn_tflops counts 4 d Hq flops per (query, visible
+    token): the QK and PV products of dense causal attention."""
     import torch
     B, Hq, Hkv, T, copies = 1, 32, 8, 32768, 8
     n_vec = B * Hkv * T
@@ -604,22 +606,27 @@ def bench_prefill(TK, ctx, dev, reps=10, warm=3, Tq=16):
         kps.append(kp)
         vps.append(vp)
         del k, v, z, chi
-    q = torch.randn((B, Tq, Hq, 128), generator=gen, device=dev).half()
-    wsb = TK.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, Tq, kf, vf)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-    out = torch.empty((B, Tq, Hq, 128), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
+    res = {"workload": "causal prefill attention, llama8b-like layer: last Tq of 32768 positions as queries, "
+                       "32 q / 8 KV heads; turbo4 K + 4-bit V, tau 1e-6"}
+    for Tq in tqs:
+        q = torch.randn((B, Tq, Hq, 128), generator=gen, device=dev).half()
+        wsb = TK.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, T, Tq, kf, vf)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        out = torch.empty((B, Tq, Hq, 128), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
 
-    def calls():
-        for c in range(copies):
-            TK.tq_attn_prefill(ctx, q, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T, Tq, None, tau, out, ws, wsb)
+        def calls():
+            for c in range(copies):
+                TK.tq_attn_prefill(ctx, q, kps[c].buf, vps[c].buf, kf, vf, B, Hq, Hkv, T, Tq, None, tau, out, ws,
+                                   wsb)
 
-    t = graph_time(calls, reps, warm, None) / copies
-    k_bytes = n_vec * 68
-    return {"workload": f"causal prefill attention, llama8b-like layer: last {Tq} of 32768 positions as queries, "
-                        "32 q / 8 KV heads; turbo4 K + 4-bit V, tau 1e-6",
-            "us": round(t * 1e6, 2), "queries_per_s": round(Tq / t, 1),
-            "k_read_gbs_per_query": round(k_bytes * Tq / t / 1e9, 1)}
+        t = graph_time(calls, reps, warm, None) / copies
+        seen = sum(T - Tq + i + 1 for i in range(Tq))  # visible tokens summed over the queries
+        res[f"tq{Tq}"] = {"us": round(t * 1e6, 2), "queries_per_s": round(Tq / t, 1),
+                          "attn_tflops": round(4 * 128 * Hq * seen / t / 1e12, 1),
+                          "k_read_gbs_per_query": round(n_vec * 68 * Tq / t / 1e9, 1)}
+        del q, ws, out
+    return res
 
 
 def bench_minmax(TK, dev, reps=10, warm=3):

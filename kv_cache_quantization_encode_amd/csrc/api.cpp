@@ -97,7 +97,30 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int T) {
     return p;
 }
 
+// Prompt-scale prefill: blocks of 64 (query, head) rows; enough token
+// ranges that the grid has ~512 blocks (two per CU), ranges of at least 512
+// tokens (multiples of 64).
+static AttnPlan prefill_plan(int B, int Hq, int Hkv, int T, int Tq) {
+    AttnPlan p{};
+    p.tiled = 1;
+    const int64_t qblocks = (int64_t(Tq) * (Hq / Hkv) + 63) / 64;
+    const int64_t blocks = qblocks * B * Hkv;
+    int64_t ns = (512 + blocks - 1) / blocks;
+    const int64_t maxs = (int64_t(T) + 511) / 512;
+    if (ns > maxs) ns = maxs;
+    if (ns < 1) ns = 1;
+    int64_t span = (int64_t(T) + ns - 1) / ns;
+    span = (span + 63) / 64 * 64;
+    ns = (int64_t(T) + span - 1) / span;
+    p.n_chunks = int(ns);
+    p.chunk = int(span);
+    p.off_stats = kSyncBytes;
+    p.total = align256(int64_t(kSyncBytes) + int64_t(B) * Tq * Hq * ns * 2 * 4);
+    return p;
+}
+
 AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity) {
+    if (Tq > 1 && prefill_tiled_formats(kf, vf)) return prefill_plan(B, Hq, Hkv, T, Tq);
     const int g = Hq / Hkv;
     const int qp = prefill_group(g, Tq);
     AttnPlan p = attn_plan(B * (Tq / qp), Hq * qp, Hkv, T);
@@ -290,7 +313,9 @@ size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_f
 size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf) {
     (void)kf;
     if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Tq < 1 || Hq % Hkv) return 0;
-    if (int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
+    if (int64_t(B) * Hkv > kMaxGridY) return 0;
+    // the grouped prefill path puts (sequence, query group, kv head) on grid y
+    if (!(Tq > 1 && prefill_tiled_formats(kf, vf)) && int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
     return attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity()).total;
 }
 
@@ -313,7 +338,8 @@ static tq_status attn_check(const tq_ctx *ctx, const void *q_f16, const void *k_
     const int g = Hq / Hkv;
     if (g != 1 && g != 2 && g != 4 && g != 8) return TQ_ERR_UNSUPPORTED;
     if (int64_t(B) * Hkv * T > kMaxRows || int64_t(T) * 128 >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
-    if (int64_t(B) * Tq * Hkv > kMaxGridY) return TQ_ERR_UNSUPPORTED;
+    if (int64_t(B) * Hkv > kMaxGridY) return TQ_ERR_UNSUPPORTED;
+    if (!(Tq > 1 && prefill_tiled_formats(kf, vf)) && int64_t(B) * Tq * Hkv > kMaxGridY) return TQ_ERR_UNSUPPORTED;
     const int64_t n_vec = int64_t(B) * Hkv * T;
     if (!plane_layout(kf, ctx->head_dim, n_vec, kl) || !plane_layout(vf, ctx->head_dim, n_vec, vl))
         return TQ_ERR_INVALID_ARG;

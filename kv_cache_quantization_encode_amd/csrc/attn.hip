@@ -1143,6 +1143,14 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
         if (plan.fused) a.len_add = 1;
         else a.n_chunks = plan.n_chunks + 1;
     }
+    if (plan.tiled) {
+        // prompt-scale prefill: real sequences and heads, token ranges
+        a.B = B;
+        a.Hq = Hq;
+        a.chunk = plan.chunk;
+        a.n_chunks = plan.n_chunks;
+        return launch_attn_prefill(a, kf, vf, stream);
+    }
     if (block32_format(kf) || block32_format(vf)) return launch_attn_generic(a, kf, vf, stream);
     if (plan.fused) {
         a.sync = reinterpret_cast<uint32_t *>(w + plan.off_sync);

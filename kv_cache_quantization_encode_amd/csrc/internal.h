@@ -57,6 +57,9 @@ struct AttnPlan {
     // off_sync, (max, sum) slots at off_stats
     int fused, nblk, tb;
     size_t off_sync;
+    // prompt-scale prefill (attn_prefill.hip): n_chunks token ranges of
+    // chunk tokens, (max, sum) statistics per row and range at off_stats
+    int tiled;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
 // The plan of one attention call: the single-launch path when its shape and
@@ -104,6 +107,12 @@ int launch_append_kv(const DevTables *tab, const void *k, const void *v, int B, 
                      const tq_planes_desc &kl, const tq_planes_desc &vl, void *stream);
 int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t n_vec,
                   const tq_planes_desc &lay, void *out, void *stream);
+// Causal prefill with many queries per block (attn_prefill.hip): K PROD or
+// MSE, V MSE; a.chunk / a.n_chunks = token range length / count.
+inline bool prefill_tiled_formats(tq_format kf, tq_format vf) {
+    return (kf.kind == TQ_KIND_PROD || kf.kind == TQ_KIND_MSE) && vf.kind == TQ_KIND_MSE;
+}
+int launch_attn_prefill(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
 // Decode attention when K or V uses block-32 norms (attn_generic.hip): a
 // scores and a values pass over the two-pass workspace.
 int launch_attn_generic(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);

@@ -159,12 +159,15 @@ def test_invalid_arguments_are_rejected_on_host(lib):
     assert attn(ws=A + 128) == T.TQ_ERR_WORKSPACE
     assert T.tq_attn_workspace_bytes(16384, 32, 8, 64, f3, v2) == 0  # 131072 (batch, kv head) pairs
     assert attn(B=16384) == T.TQ_ERR_UNSUPPORTED
-    # prefill: Tq queries per sequence share its cache
+    # prefill: Tq queries per sequence share its cache.  TurboQuant / codebook
+    # K with codebook V take the prompt-scale kernels (statistics only in the
+    # workspace, no limit on B * Tq * Hkv); q8 the grouped decode kernels
     pws = T.tq_attn_prefill_workspace_bytes(1, 32, 8, 1024, 16, f3, v2)
-    assert pws > ws
+    assert pws > 0
     assert T.tq_attn_prefill_workspace_bytes(1, 32, 8, 1024, 1, f3, v2) == ws
     assert T.tq_attn_prefill_workspace_bytes(1, 32, 8, 1024, 0, f3, v2) == 0
-    assert T.tq_attn_prefill_workspace_bytes(2, 32, 8, 1024, 4096, f3, v2) == 0  # 65536 pairs
+    assert T.tq_attn_prefill_workspace_bytes(2, 32, 8, 1024, 4096, f3, v2) > 0
+    assert T.tq_attn_prefill_workspace_bytes(2, 32, 8, 1024, 4096, T.Q8, T.Q8) == 0  # 65536 grid rows
 
     def prefill(**kw):
         a = dict(ctx=cp, q=A, k=A, v=A, kf=f3, vf=v2, B=1, Hq=32, Hkv=8, T=1024, Tq=16, lens=None, tau=1e-6,
@@ -182,9 +185,9 @@ def test_invalid_arguments_are_rejected_on_host(lib):
     assert prefill(tau=float("inf")) == T.TQ_ERR_INVALID_ARG
     assert prefill(Hq=24) == T.TQ_ERR_UNSUPPORTED
     assert prefill(vf=T.turbo_k(3)) == T.TQ_ERR_UNSUPPORTED
-    assert prefill(B=2, Tq=4096) == T.TQ_ERR_UNSUPPORTED
+    assert prefill(B=2, Tq=4096, kf=T.Q8, vf=T.Q8) == T.TQ_ERR_UNSUPPORTED
     assert prefill(wsb=pws - 1) == T.TQ_ERR_WORKSPACE
-    assert prefill(wsb=ws) == T.TQ_ERR_WORKSPACE  # the decode workspace is too small for 16 queries
+    assert prefill(wsb=0) == T.TQ_ERR_WORKSPACE
     # min-max
     mq = L.tq_minmax_quant
     assert mq(None, 64, 64, 3, A, A, A, None) == T.TQ_ERR_INVALID_ARG

@@ -107,3 +107,96 @@ def test_prefill_query_grouping_shapes(ctx, oracle_tables, tq, hq, hkv):
     c = W.llama8b(T=900, Hq=hq, Hkv=hkv, B=2)
     q = _queries(705 + tq, 2, tq, hq)
     _prefill(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), 1e-6, [900, tq + 2])
+
+
+def _prefill_sampled(ctx, tab, case, q, kf, vf, tau, lens, samples):
+    """GPU prefill of every query; the oracle's decode step of a sample of
+    (sequence, query) pairs at their own causal lengths (the oracle's prefill
+    is that decode step per query)."""
+    B, _, Hkv, Tn = case.shape
+    Tq, Hq = q.shape[1], q.shape[2]
+    kp, _ = G.gpu_encode(ctx, np.ascontiguousarray(case.k.reshape(-1, 128)), *kf)
+    vp, _ = G.gpu_encode(ctx, np.ascontiguousarray(case.v.reshape(-1, 128)), *vf, as_v=True)
+    K, V = G.tf(*kf), G.tf(*vf)
+    wsb = T.tq_attn_prefill_workspace_bytes(B, Hq, Hkv, Tn, Tq, K, V)
+    assert wsb > 0
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    out = G.Guarded(B * Tq * Hq * 128 * 4)
+    lt = None if lens is None else torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    G.note(f"prefill (sampled check) B={B} Tq={Tq} Hq={Hq} Hkv={Hkv} T={Tn} kf={kf} vf={vf} lens={lens}")
+    T.tq_attn_prefill(ctx, G.to_dev_f16(q), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), K, V, B, Hq,
+                      Hkv, Tn, Tq, lt, tau, out.ptr, ws, wsb)
+    h = out.host()
+    out.check_guard(h)
+    got = h[: B * Tq * Hq * 128 * 4].view(np.float32).reshape(B, Tq, Hq, 128)
+    n_per, n_all = Hkv * Tn, B * Hkv * Tn
+    worst = 0.0
+    for b in sorted({b for b, _ in samples}):
+        ks = G._dequant_rows(kp, kf[0], kf[1], tab, n_all, b * n_per, n_per).reshape(1, Hkv, Tn, 128)
+        vs = G._dequant_rows(vp, vf[0], vf[1], tab, n_all, b * n_per, n_per).reshape(1, Hkv, Tn, 128)
+        L = Tn if lens is None else min(max(int(lens[b]), 0), Tn)
+        for bb, i in samples:
+            if bb != b:
+                continue
+            n = max(L - Tq + i + 1, 0)
+            ref, _ = O.attention_decode(q[b:b + 1, i].astype(np.float64), ks, vs, tau, [n])
+            worst = max(worst, float(np.max(np.abs(got[b, i] - ref[0]))))
+    assert worst <= G.ATTN_ATOL, f"max abs error {worst:.3g} over the sampled queries"
+    return got
+
+
+@pytest.mark.parametrize("tq", [128, 1024])
+def test_prefill_prompt_scale(ctx, oracle_tables, tq):
+    """Prompt-scale prefill: the last 128 or 1024 positions of an
+    8192-token llama8b-like sequence (32 query / 8 KV heads, turbo4 K +
+    4-bit V) as queries; 48 queries checked against the oracle, among them
+    the first and the last."""
+    c = W.llama8b(T=8192, Hq=32, Hkv=8, B=1)
+    q = _queries(706 + tq, 1, tq, 32)
+    rng = np.random.default_rng(tq)
+    idx = sorted({0, 1, tq - 1, tq // 2} | set(rng.choice(tq, 44, replace=False).tolist()))
+    _prefill_sampled(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 4), 1e-6, None, [(0, i) for i in idx])
+
+
+@pytest.mark.parametrize("hq,hkv,kf,vf", [(64, 8, ("prod", 2), ("mse", 2)), (4, 4, ("prod", 1), ("mse", 3)),
+                                          (8, 4, ("mse", 3), ("mse", 1))],
+                         ids=["gqa8-turbo3", "gqa1-turbo2", "gqa2-codebook-k"])
+def test_prefill_many_queries_ragged(ctx, oracle_tables, hq, hkv, kf, vf):
+    """200 queries of two sequences (one 150 tokens long, so its first 50
+    queries see nothing), GQA 8 / 1 / 2, codebook-only K; every query of
+    both sequences checked."""
+    c = W.llama8b(T=1200, Hq=hq, Hkv=hkv, B=2)
+    q = _queries(707 + hq, 2, 200, hq)
+    lens = [1200, 150]
+    got = _prefill_sampled(ctx, oracle_tables, c, q, kf, vf, 1e-6, lens,
+                           [(b, i) for b in range(2) for i in range(0, 200, 3)] + [(1, 199), (0, 199)])
+    assert np.all(got[1, :50] == 0.0)
+
+
+def test_prefill_beyond_grid_limit(ctx, oracle_tables):
+    """Every position of an 8192-token sequence as a query (B * Tq * Hkv =
+    65536 (sequence, query, kv head) triples, past the 65535 grid rows the
+    grouped path allows), sampled against the oracle."""
+    c = W.llama8b(T=8192, Hq=32, Hkv=8, B=1)
+    q = _queries(708, 1, 8192, 32)
+    rng = np.random.default_rng(8192)
+    idx = sorted({0, 1, 8191} | set(rng.choice(8192, 29, replace=False).tolist()))
+    _prefill_sampled(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 4), 1e-6, None, [(0, i) for i in idx])
+
+
+def test_prefill_peaked_attention_skips_groups(ctx, oracle_tables):
+    """Needle-like queries (each aimed at one key) keep a handful of V rows:
+    most 32-token groups are skipped; tau 1e-6 and tau 0 (nothing skipped)."""
+    c = W.llama8b(T=2048, Hq=16, Hkv=4, B=1)
+    rng = np.random.default_rng(709)
+    tq = 64
+    q = np.zeros((1, tq, 16, 128), np.float32)
+    for i in range(tq):
+        for h in range(16):
+            tok = int(rng.integers(0, 2048 - tq + i + 1))
+            kk = c.k[0, h // 4, tok].astype(np.float32)
+            q[0, i, h] = 4.0 * kk / max(np.linalg.norm(kk), 1e-6) * np.sqrt(128)
+    q = q.astype(np.float16)
+    for tau in (1e-6, 0.0):
+        _prefill_sampled(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), tau, None,
+                         [(0, i) for i in range(0, tq, 4)] + [(0, tq - 1)])
