@@ -580,14 +580,16 @@ def bench_decode_loop(TK, ctx, dev, reps=10, warm=3):
                     "tq_append_kv then tq_attn_decode; attn_only = tq_attn_decode over the same cache"}
 
 
-def bench_prefill(TK, ctx, dev, reps=10, warm=3, tqs=(16, 64, 128, 2048)):
+def bench_prefill(TK, ctx, dev, reps=10, warm=3, tqs=(16, 128, 2048, 8192)):
     """Causal prefill attention on the llama8b-like layer (32 q / 8 KV heads,
     32768 tokens, turbo4 K + 4-bit V, tau 1e-6): the last Tq positions attend
     to their prefixes (tq_attn_prefill), for each Tq in tqs.  Eight rotating
     caches, one HIP graph of eight calls; inputs drawn on the GPU from a
     seeded generator (K lognormal(0, 0.5) per (head, channel) x Student-t(3),
     V and q N(0, 1)).  attn_tflops counts 4 d Hq flops per (query, visible
-    token): the QK and PV products of dense causal attention."""
+    token): the QK and PV products of dense causal attention.  Up to Tq 8191
+    the call takes the grouped decode kernels; Tq 8192 (65536 sequence,
+    query and kv head rows) the prompt-scale kernels."""
     import torch
     B, Hq, Hkv, T, copies = 1, 32, 8, 32768, 8
     n_vec = B * Hkv * T
@@ -622,7 +624,8 @@ def bench_prefill(TK, ctx, dev, reps=10, warm=3, tqs=(16, 64, 128, 2048)):
 
         t = graph_time(calls, reps, warm, None) / copies
         seen = sum(T - Tq + i + 1 for i in range(Tq))  # visible tokens summed over the queries
-        res[f"tq{Tq}"] = {"us": round(t * 1e6, 2), "queries_per_s": round(Tq / t, 1),
+        res[f"tq{Tq}"] = {"path": "prompt-scale kernels" if B * Tq * Hkv > 65535 else "grouped decode kernels",
+                          "us": round(t * 1e6, 2), "queries_per_s": round(Tq / t, 1),
                           "attn_tflops": round(4 * 128 * Hq * seen / t / 1e12, 1),
                           "k_read_gbs_per_query": round(n_vec * 68 * Tq / t / 1e9, 1)}
         del q, ws, out

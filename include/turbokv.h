@@ -225,13 +225,16 @@ size_t tq_attn_workspace_bytes(int B, int Hq, int Hkv, int T, tq_format kf, tq_f
  * L_b = seq_lens[b] clamped to [0, T] (or T when seq_lens is NULL), query i
  * of sequence b sits at position L_b - Tq + i and sees the first
  * L_b - Tq + i + 1 tokens; a query that sees none gets a zero row.
- * B*Tq*Hkv must not exceed 65535.  Other arguments, formats, ownership and
- * the last-bit nondeterminism of the fp32 atomics as for tq_attn_decode;
- * workspace: tq_attn_prefill_workspace_bytes(...) bytes, 256-byte aligned.
- * Tq = 1 is exactly tq_attn_decode.  Queries are taken in groups of up to
- * 8 / (Hq / Hkv) per kv head; the queries of a group are stacked as extra
- * MFMA rows and share every K and V load of their scores and values passes,
- * while separate groups each read the prefix again. */
+ * Other arguments, formats, ownership and the last-bit nondeterminism of
+ * the fp32 atomics as for tq_attn_decode; workspace:
+ * tq_attn_prefill_workspace_bytes(...) bytes, 256-byte aligned.  Tq = 1 is
+ * exactly tq_attn_decode.  Up to B*Tq*Hkv = 65535, queries are taken in
+ * groups of up to 8 / (Hq / Hkv) per kv head; the queries of a group are
+ * stacked as extra MFMA rows and share every K and V load of their scores
+ * and values passes, while separate groups each read the prefix again.
+ * Past that, calls with TurboQuant or codebook K and codebook V run the
+ * prompt-scale kernels (64 (query, head) rows per block share each K tile;
+ * any B*Hkv <= 65535); other formats return TQ_ERR_UNSUPPORTED there. */
 tq_status tq_attn_prefill(const tq_ctx *ctx, const void *q_f16, const void *k_packed,
                           const void *v_packed, tq_format kf, tq_format vf, int B, int Hq, int Hkv,
                           int T, int Tq, const int32_t *seq_lens, float sparse_v_tau, float *out_f32,

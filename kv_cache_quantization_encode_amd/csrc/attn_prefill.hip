@@ -478,31 +478,32 @@ __global__ __launch_bounds__(kPThreads) void attn_prefill_values_kernel(AttnArgs
     const int tq4 = tid & 7, jv = tid >> 3;  // V staging: token quad, coordinate quad
     if (p.t0 < p.t1) {
         const int tmax = p.t1 - 1;
-        PTile<KB> cur[2], nxt[2];
-        uint32_t vc[4], vcn[4];
-        auto load_group = [&](int base, PTile<KB> (&d)[2], uint32_t (&c)[4]) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) load_ptile<KK, KB>(d[i], a, p.kvbase, min(base + 16 * i + t, tmax), kq);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) c[u] = load_vcodes<VB>(a, p.kvbase + min(base + 4 * tq4 + u, tmax), jv);
+        // a group's loads one group ahead, in two named buffers (no copies,
+        // so no wait is forced before the data is used)
+        struct Grp {
+            PTile<KB> k[2];
+            uint32_t vc[4];
         };
-        load_group(p.t0, cur, vc);
-        int gi = 0;
-        for (int base = p.t0; base < p.t1; base += kPGroup, ++gi) {
-            const int buf = gi & 1;
-            if (base + kPGroup < p.t1) load_group(base + kPGroup, nxt, vcn);
+        Grp g0, g1;
+        auto load_group = [&](int base, Grp &g) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) load_ptile<KK, KB>(g.k[i], a, p.kvbase, min(base + 16 * i + t, tmax), kq);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) g.vc[u] = load_vcodes<VB>(a, p.kvbase + min(base + 4 * tq4 + u, tmax), jv);
+        };
+        auto process = [&](const Grp &g, int base, int buf) {
             // transposed V levels of the group (before its weights are known,
             // so one barrier per group serves both stagings; a group whose
             // weights all drop is then skipped at the products): rows =
             // coordinates 4 jv + i, columns = tokens 4 tq4 .. 4 tq4 + 3 (fp16
             // hi and lo, 8 bytes a store: rows 4 apart fall 16 banks apart).
-            // Buffer buf was last read by the products of group gi - 2, which
-            // every wave finished before the barrier of group gi - 1.
+            // Buffer buf was last read by the products two groups back, which
+            // every wave finished before the previous group's barrier.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t lv[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) lv[u] = s_vlev[(vc[u] >> (VB * i)) & ((1u << VB) - 1u)];
+                for (int u = 0; u < 4; ++u) lv[u] = s_vlev[(g.vc[u] >> (VB * i)) & ((1u << VB) - 1u)];
                 *reinterpret_cast<uint2 *>(&sg.vh[buf][4 * jv + i][4 * tq4]) =
                     make_uint2((lv[0] & 0xFFFFu) | (lv[1] << 16), (lv[2] & 0xFFFFu) | (lv[3] << 16));
                 *reinterpret_cast<uint2 *>(&sg.vl[buf][4 * jv + i][4 * tq4]) =
@@ -513,18 +514,16 @@ __global__ __launch_bounds__(kPThreads) void attn_prefill_values_kernel(AttnArgs
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 float o[2][2];
-                prefill_score<KK, KB>(cur[i], s_pair, s_sgn, aq, ap, lane, o);
+                prefill_score<KK, KB>(g.k[i], s_pair, s_sgn, aq, ap, lane, o);
                 const int tok = base + 16 * i + t;
-                const float nv = h2f(cur[i].vn);
+                const float nv = h2f(g.k[i].vn);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        float w = 0.0f;
-                        if (tok < p.t1 && tok < lim[rb][j]) {
-                            const float pw = fast_exp2(fmaf(o[rb][j], kLog2e, -M2[rb][j])) * invL[rb][j];
-                            w = pw >= a.tau ? pw * nv : 0.0f;
-                        }
+                        const bool in = tok < p.t1 && tok < lim[rb][j];
+                        const float pw = fast_exp2(fmaf(o[rb][j], kLog2e, -M2[rb][j])) * invL[rb][j];
+                        const float w = in && pw >= a.tau ? pw * nv : 0.0f;
                         any |= w != 0.0f;
                         sg.w[buf][16 * wave + 8 * rb + own_head<8>(kq, j)][16 * i + t] = w;
                     }
@@ -532,40 +531,45 @@ __global__ __launch_bounds__(kPThreads) void attn_prefill_values_kernel(AttnArgs
             const bool wave_any = __builtin_amdgcn_ballot_w64(any) != 0;
             if (lane == 0) s_flag[buf][wave] = wave_any ? 1 : 0;
             __syncthreads();
-            const bool keep = (s_flag[buf][0] | s_flag[buf][1] | s_flag[buf][2] | s_flag[buf][3]) != 0;
-            if (keep) {
-                // O_rot += w V on the matrix cores: A row mr = lane & 15 is
-                // row mr & 7 of the row block as the fp16 hi (mr < 8) or lo
-                // half of its weights, k = tokens 8 kq .. 8 kq + 7
-                const int mr = lane & 15;
-                half8 A[2];
+            if ((s_flag[buf][0] | s_flag[buf][1] | s_flag[buf][2] | s_flag[buf][3]) == 0) return;
+            // O_rot += w V on the matrix cores: A row mr = lane & 15 is row
+            // mr & 7 of the row block as the fp16 hi (mr < 8) or lo half of
+            // its weights, k = tokens 8 kq .. 8 kq + 7
+            const int mr = lane & 15;
+            half8 A[2];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    const float *wr = &sg.w[buf][16 * wave + 8 * rb + (mr & 7)][8 * kq];
-                    const float4 w0 = *reinterpret_cast<const float4 *>(wr);
-                    const float4 w1 = *reinterpret_cast<const float4 *>(wr + 4);
-                    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            for (int rb = 0; rb < 2; ++rb) {
+                const float *wr = &sg.w[buf][16 * wave + 8 * rb + (mr & 7)][8 * kq];
+                const float4 w0 = *reinterpret_cast<const float4 *>(wr);
+                const float4 w1 = *reinterpret_cast<const float4 *>(wr + 4);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const _Float16 h = _Float16(wv[k]);
-                        A[rb][k] = mr < 8 ? h : _Float16(wv[k] - float(h));
-                    }
-                }
-#pragma unroll
-                for (int cb = 0; cb < 8; ++cb) {
-                    const half8 bh = *reinterpret_cast<const half8 *>(&sg.vh[buf][16 * cb + mr][8 * kq]);
-                    const half8 bl = *reinterpret_cast<const half8 *>(&sg.vl[buf][16 * cb + mr][8 * kq]);
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rb], bh, acc[rb][cb], 0, 0, 0);
-                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rb], bl, acc[rb][cb], 0, 0, 0);
-                    }
+                for (int k = 0; k < 8; ++k) {
+                    const _Float16 h = _Float16(wv[k]);
+                    A[rb][k] = mr < 8 ? h : _Float16(wv[k] - float(h));
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) cur[i] = nxt[i];
+            for (int cb = 0; cb < 8; ++cb) {
+                const half8 bh = *reinterpret_cast<const half8 *>(&sg.vh[buf][16 * cb + mr][8 * kq]);
+                const half8 bl = *reinterpret_cast<const half8 *>(&sg.vl[buf][16 * cb + mr][8 * kq]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) vc[u] = vcn[u];
+                for (int rb = 0; rb < 2; ++rb) {
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rb], bh, acc[rb][cb], 0, 0, 0);
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rb], bl, acc[rb][cb], 0, 0, 0);
+                }
+            }
+        };
+        load_group(p.t0, g0);
+        for (int base = p.t0;;) {
+            if (base + kPGroup < p.t1) load_group(base + kPGroup, g1);
+            process(g0, base, 0);
+            base += kPGroup;
+            if (base >= p.t1) break;
+            if (base + kPGroup < p.t1) load_group(base + kPGroup, g0);
+            process(g1, base, 1);
+            base += kPGroup;
+            if (base >= p.t1) break;
         }
     }
     __syncthreads();  // the staging buffers are done with

@@ -112,6 +112,11 @@ int launch_decode(const DevTables *tab, const void *packed, tq_format f, int64_t
 inline bool prefill_tiled_formats(tq_format kf, tq_format vf) {
     return (kf.kind == TQ_KIND_PROD || kf.kind == TQ_KIND_MSE) && vf.kind == TQ_KIND_MSE;
 }
+// The prefill calls that take those kernels: the ones past the grouped
+// path's grid limit (B * Tq * Hkv grid rows).
+inline bool prefill_tiled_call(int B, int Hkv, int Tq, tq_format kf, tq_format vf) {
+    return Tq > 1 && prefill_tiled_formats(kf, vf) && int64_t(B) * Tq * Hkv > kMaxGridY;
+}
 int launch_attn_prefill(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
 // Decode attention when K or V uses block-32 norms (attn_generic.hip): a
 // scores and a values pass over the two-pass workspace.

@@ -147,10 +147,10 @@ def _prefill_sampled(ctx, tab, case, q, kf, vf, tau, lens, samples):
 
 @pytest.mark.parametrize("tq", [128, 1024])
 def test_prefill_prompt_scale(ctx, oracle_tables, tq):
-    """Prompt-scale prefill: the last 128 or 1024 positions of an
-    8192-token llama8b-like sequence (32 query / 8 KV heads, turbo4 K +
-    4-bit V) as queries; 48 queries checked against the oracle, among them
-    the first and the last."""
+    """The last 128 or 1024 positions of an 8192-token llama8b-like
+    sequence (32 query / 8 KV heads, turbo4 K + 4-bit V) as queries (the
+    grouped decode kernels at this size); 48 queries checked against the
+    oracle, among them the first and the last."""
     c = W.llama8b(T=8192, Hq=32, Hkv=8, B=1)
     q = _queries(706 + tq, 1, tq, 32)
     rng = np.random.default_rng(tq)
@@ -158,25 +158,31 @@ def test_prefill_prompt_scale(ctx, oracle_tables, tq):
     _prefill_sampled(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 4), 1e-6, None, [(0, i) for i in idx])
 
 
-@pytest.mark.parametrize("hq,hkv,kf,vf", [(64, 8, ("prod", 2), ("mse", 2)), (4, 4, ("prod", 1), ("mse", 3)),
-                                          (8, 4, ("mse", 3), ("mse", 1))],
-                         ids=["gqa8-turbo3", "gqa1-turbo2", "gqa2-codebook-k"])
-def test_prefill_many_queries_ragged(ctx, oracle_tables, hq, hkv, kf, vf):
-    """200 queries of two sequences (one 150 tokens long, so its first 50
-    queries see nothing), GQA 8 / 1 / 2, codebook-only K; every query of
-    both sequences checked."""
-    c = W.llama8b(T=1200, Hq=hq, Hkv=hkv, B=2)
-    q = _queries(707 + hq, 2, 200, hq)
+# Calls with B * Tq * Hkv past 65535 (sequence, query, kv head) rows take the
+# prompt-scale kernels (attn_prefill.hip); below that the grouped decode
+# kernels.  The shapes below are chosen past the limit with short caches and
+# many kv heads, so that they exercise the prompt-scale kernels cheaply.
+@pytest.mark.parametrize("g,kf,vf", [(8, ("prod", 2), ("mse", 2)), (1, ("prod", 1), ("mse", 3)),
+                                     (2, ("mse", 3), ("mse", 1)), (4, ("prod", 3), ("mse", 4))],
+                         ids=["gqa8-turbo3", "gqa1-turbo2", "gqa2-codebook-k", "gqa4-turbo4"])
+def test_prefill_many_queries_ragged(ctx, oracle_tables, g, kf, vf):
+    """1024 queries of two sequences over 32 kv heads (65536 grid rows: the
+    prompt-scale kernels); the second sequence is 150 tokens long, so its
+    first 874 queries see nothing.  Sampled queries of both sequences
+    against the oracle."""
+    hkv = 32
+    c = W.llama8b(T=1200, Hq=g * hkv, Hkv=hkv, B=2)
+    q = _queries(707 + g, 2, 1024, g * hkv)
     lens = [1200, 150]
-    got = _prefill_sampled(ctx, oracle_tables, c, q, kf, vf, 1e-6, lens,
-                           [(b, i) for b in range(2) for i in range(0, 200, 3)] + [(1, 199), (0, 199)])
-    assert np.all(got[1, :50] == 0.0)
+    samples = [(b, i) for b in range(2) for i in range(0, 1024, 37)] + [(0, 1023), (1, 1023), (1, 873), (1, 874)]
+    got = _prefill_sampled(ctx, oracle_tables, c, q, kf, vf, 1e-6, lens, samples)
+    assert np.all(got[1, :874] == 0.0)
 
 
 def test_prefill_beyond_grid_limit(ctx, oracle_tables):
     """Every position of an 8192-token sequence as a query (B * Tq * Hkv =
-    65536 (sequence, query, kv head) triples, past the 65535 grid rows the
-    grouped path allows), sampled against the oracle."""
+    65536 (sequence, query, kv head) rows, past the grouped path's grid):
+    the prompt-scale kernels, sampled against the oracle."""
     c = W.llama8b(T=8192, Hq=32, Hkv=8, B=1)
     q = _queries(708, 1, 8192, 32)
     rng = np.random.default_rng(8192)
@@ -185,18 +191,18 @@ def test_prefill_beyond_grid_limit(ctx, oracle_tables):
 
 
 def test_prefill_peaked_attention_skips_groups(ctx, oracle_tables):
-    """Needle-like queries (each aimed at one key) keep a handful of V rows:
-    most 32-token groups are skipped; tau 1e-6 and tau 0 (nothing skipped)."""
-    c = W.llama8b(T=2048, Hq=16, Hkv=4, B=1)
+    """Needle-like queries (each aimed at one key) keep a handful of V rows,
+    so the prompt-scale values pass skips most 32-token groups; 1025 queries
+    over 64 kv heads (GQA 2), tau 1e-6 and tau 0 (nothing skipped)."""
+    hkv, g, T_, tq = 64, 2, 1100, 1025
+    c = W.llama8b(T=T_, Hq=g * hkv, Hkv=hkv, B=1)
     rng = np.random.default_rng(709)
-    tq = 64
-    q = np.zeros((1, tq, 16, 128), np.float32)
+    q = np.zeros((1, tq, g * hkv, 128), np.float32)
     for i in range(tq):
-        for h in range(16):
-            tok = int(rng.integers(0, 2048 - tq + i + 1))
-            kk = c.k[0, h // 4, tok].astype(np.float32)
-            q[0, i, h] = 4.0 * kk / max(np.linalg.norm(kk), 1e-6) * np.sqrt(128)
+        toks = rng.integers(0, T_ - tq + i + 1, size=g * hkv)
+        kk = c.k[0, np.arange(g * hkv) // g, toks].astype(np.float32)
+        q[0, i] = 4.0 * kk / np.maximum(np.linalg.norm(kk, axis=-1, keepdims=True), 1e-6) * np.sqrt(128)
     q = q.astype(np.float16)
     for tau in (1e-6, 0.0):
         _prefill_sampled(ctx, oracle_tables, c, q, ("prod", 3), ("mse", 2), tau, None,
-                         [(0, i) for i in range(0, tq, 4)] + [(0, tq - 1)])
+                         [(0, i) for i in range(0, tq, 41)] + [(0, tq - 1)])
