@@ -65,28 +65,45 @@ __global__ __launch_bounds__(256) void minmax_quant_kernel(const uint16_t *__res
     }
 }
 
+// Dequant: a wave's 64 lanes write 64 consecutive half-groups (4 KB of
+// fp16).  Each lane forms its 32 outputs (64 contiguous bytes) in LDS, and
+// the wave stores them as 16-byte pieces, lane l taking bytes 16 l + 1024 c
+// (c = 0..3), so that every store instruction writes one contiguous 1 KB.
 template <int BITS>
 __global__ __launch_bounds__(256) void minmax_dequant_kernel(const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scale_in,
                                                              const uint16_t *__restrict__ zero_in,
                                                              int64_t n_half, uint16_t *__restrict__ out) {
-    const int64_t h = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (h >= n_half) return;
-    uint32_t w[BITS];
+    __shared__ uint4 s_o[4][256];  // per wave: 4 KB
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t h0 = (int64_t(blockIdx.x) * 4 + wave) * 64;
+    const int64_t h = h0 + lane;
+    if (h0 >= n_half) return;  // uniform over the wave
+    if (h < n_half) {
+        uint32_t w[BITS];
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) w[i] = codes[h * BITS + i];
-    const float scale = h2f(scale_in[h >> 1]);
-    const float zero = h2f(zero_in[h >> 1]);
-    uint32_t o[16];
-    Unroll<16>::run([&](auto I) {
-        constexpr int p = decltype(I)::value;
-        const float a = fmaf(float(code_at<BITS, 2 * p>(w)), scale, zero);
-        const float b = fmaf(float(code_at<BITS, 2 * p + 1>(w)), scale, zero);
-        o[p] = f2h(a) | (f2h(b) << 16);
-    });
-    uint4 *dst = reinterpret_cast<uint4 *>(out + h * 32);
+        for (int i = 0; i < BITS; ++i) w[i] = codes[h * BITS + i];
+        const float scale = h2f(scale_in[h >> 1]);
+        const float zero = h2f(zero_in[h >> 1]);
+        uint32_t o[16];
+        Unroll<16>::run([&](auto I) {
+            constexpr int p = decltype(I)::value;
+            const float a = fmaf(float(code_at<BITS, 2 * p>(w)), scale, zero);
+            const float b = fmaf(float(code_at<BITS, 2 * p + 1>(w)), scale, zero);
+            o[p] = f2h(a) | (f2h(b) << 16);
+        });
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dst[c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+        for (int c = 0; c < 4; ++c) s_o[wave][4 * lane + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    uint4 *dst = reinterpret_cast<uint4 *>(out + h0 * 32);
+    const int64_t n16 = (n_half - h0) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int i = lane + 64 * c;
+        if (i < n16) dst[i] = s_o[wave][i];
+    }
 }
 
 int launch_minmax_quant(const void *x, int64_t n, int bits, void *codes, void *scale, void *zero,
