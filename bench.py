@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the MI355X
 N_COPIES = 8
 LAG = 4
-KERNEL_SOURCES = ["encode.hip", "attn.hip", "attn_fused.hip", "attn_common.h", "device_common.h"]
+KERNEL_SOURCES = ["encode.hip", "encode_common.h", "attn.hip", "attn_fused.hip", "attn_common.h", "device_common.h"]
 
 
 def parse():
@@ -80,7 +80,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_profile(kernel: str, section: str = "kernels", name: str = "traffic_llama8b.json"):
+def load_profile(kernel: str, section: str = "kernels", name: str = "traffic_70b.json"):
     """Per-launch figures from a committed rocprofv3 --pmc summary under
     profiles/ (HBM bytes under "kernels", MFMA utilisation under "mfma"), if
     it was taken on the current kernel sources."""
