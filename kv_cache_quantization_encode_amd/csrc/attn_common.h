@@ -426,54 +426,16 @@ __device__ __forceinline__ void own_scores(const float (&e)[4], int lane, float 
     }
 }
 
-// ------------------------------------------------------- bit-plane scoring
-// 1- and 2-bit codebooks are sums of signed constants chosen by single code
-// bits: c[b] = a (2b - 1) (1 bit, a = c1) and c[2 b1 + b0] = a1 (2 b1 - 1) +
-// a0 (2 b0 - 1) (2 bits, a1 = (c3 + c2) / 2, a0 = (c3 - c2) / 2), and the QJL
-// term is sum_p q_proj,p (2 bit_p - 1).  So every K product is
-//   sum over bits of (2 coef q) x bit  -  a per-head constant,
-// and its MFMA B operand is the packed code word itself: w & (bit k of both
-// 16-bit halves) is two fp16 halves whose only set bit is bit k, i.e. the
-// code bit times the exact power of two 2^(k - 24) (subnormal for k <= 9;
-// bits 10..15 are first shifted down to 4..9).  The query operand of each
-// k-slot carries 2 coef q 2^(S0 - k), so every product has the same scale
-// 2^(S0 - 24), which the epilogue divides out.  One AND per two k-slots, no
-// table reads.  Lane (r, kq) of source dword j, product u (0..3) holds k-slot
-// pairs i = 0..3 from bit k = 4u + i of the dword's low half (slot 2i) and
-// high half (slot 2i + 1).
-template <int G, int BITS, bool PROJ>
-struct PlaneOps {
-    half8 ab[4 * BITS];              // codebook products
-    half8 aq[PROJ ? 4 : 1];          // QJL products
-    float sc_cb, sc_q;               // 2^(24 - S0) of each term
-    float ccb[kOwn<G>], cq[kOwn<G>]; // constants of the own heads
-};
-
-// Bit k of a 16-bit half after the shift that brings bits 10..15 to 4..9.
-__device__ __forceinline__ constexpr int plane_pos(int k) { return k <= 9 ? k : k - 6; }
-
-// Coordinate (or projection) of k-slot half h (0 low, 1 high) for bit k of
-// source dword j of lane group kq.
-template <int BITS>
-__device__ __forceinline__ int plane_coord(int kq, int j, int k, int h) {
-    if constexpr (BITS == 2) return 32 * kq + 16 * j + 8 * h + (k >> 1);
-    return 32 * kq + 16 * h + k;  // 1-bit codes and QJL signs: one bit per coordinate
-}
-
-struct NoPlanes {};
-
 // Scores one slice (NT tiles per wave) and folds it into the running (max,
 // sum) of each own head; store(h, tok, s) receives the score of head h (in
 // the block's head numbering) and token tok, -inf past a row's causal limit.
 // NW = waves per block (token layout as in load_ktiles).
-template <bool FULL, bool ROWLIM, int G, int NW = 4, int KIND, int BITS, typename Store, typename PL = NoPlanes>
+template <bool FULL, bool ROWLIM, int G, int NW = 4, int KIND, int BITS, typename Store>
 __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int base, int t1, int wave, int t,
                                              int kq, const uint2 *s_pair, const half8 *s_sgn,
                                              const half8 (&aq)[8], const half8 (&ap)[4], Store &&store,
                                              const int (&lim)[kOwn<G>], float (&m)[kOwn<G>],
-                                             float (&l)[kOwn<G>], const PL *pl = nullptr) {
-    constexpr bool PLANES = !std::is_same<PL, NoPlanes>::value;
-    static_assert(!PLANES || (KIND != TQ_KIND_Q8 && BITS <= 2), "bit planes: 1- and 2-bit codebooks");
+                                             float (&l)[kOwn<G>]) {
     using KT = KTiles<KIND, BITS>;
     float scv[KT::NT][kOwn<G>];  // this lane's scores of the slice in log2 units, -inf where absent
     // B operands of the rotated-key path.  Field f (codes 2f, 2f+1 of the
@@ -501,32 +463,7 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         const int tok = base + wave * 16 + 16 * NW * i + t;
         const bool valid = FULL || tok < t1;
         float e[4];
-        float cn = 0.0f, cg = 0.0f;  // plane path: per-token factors of the head constants
-        if constexpr (PLANES) {
-            floatx4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-            auto products = [&](uint32_t w, const half8 *A, floatx4 &acc) {
-                const uint32_t ws = w >> 6;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    uint32_t bw[4];
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int k = 4 * u + q4;
-                        bw[q4] = (k <= 9 ? w : ws) & (0x00010001u << plane_pos(k));
-                    }
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        A[u], __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc, 0, 0, 0);
-                }
-            };
-#pragma unroll
-            for (int j = 0; j < BITS; ++j) products(d.wk[i][j], pl->ab + 4 * j, d0);
-            if constexpr (KIND == TQ_KIND_PROD) products(d.sw[i], pl->aq, d1);
-            cn = h2f(d.nn[i] & 0xFFFFu) * (1.0f / 128.0f);
-            cg = KIND == TQ_KIND_PROD ? h2f(d.nn[i] >> 16) * kQjlOverSqrtD : 0.0f;
-            const float n = cn * pl->sc_cb, gq = cg * pl->sc_q;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (KIND == TQ_KIND_PROD) ? fmaf(n, d0[j], gq * d1[j]) : n * d0[j];
-        } else if constexpr (KIND == TQ_KIND_Q8) {
+        if constexpr (KIND == TQ_KIND_Q8) {
             const uint2 scl = d.q8s[i];
             const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
 #pragma unroll
@@ -571,10 +508,6 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
         fold_rows<G>(e);
         float o[kOwn<G>];
         own_scores<G>(e, 16 * kq + t, o);
-        if constexpr (PLANES) {
-#pragma unroll
-            for (int j = 0; j < kOwn<G>; ++j) o[j] -= fmaf(cn, pl->ccb[j], cg * pl->cq[j]);
-        }
         // lane (t, kq) now holds the scores of its own heads for token tok;
         // one store per head and lane (on the whole-slice path without a
         // branch, so the memory counters stay exact).  A row whose query sees

@@ -54,20 +54,71 @@ __host__ __device__ constexpr float bitval(int k) {
                              : (k == 11 ? 1.0f / 8192.0f : (k == 12 ? 1.0f / 2048.0f : (k == 13 ? 1.0f / 128.0f : 2.0f))));
 }
 
+// ------------------------------------------------------- bit-plane scoring
+// 1- and 2-bit codebooks are sums of signed constants chosen by single code
+// bits: c[b] = a (2b - 1) (1 bit, a = c1) and c[2 b1 + b0] = a1 (2 b1 - 1) +
+// a0 (2 b0 - 1) (2 bits, a1 = (c3 + c2) / 2, a0 = (c3 - c2) / 2).  So the
+// codebook product of a key is
+//   sum over bits of (2 coef q) x bit  -  (a1 + a0) sum q   (1 bit: a sum q),
+// and its MFMA B operand is the packed code word itself: w & (bit k of both
+// 16-bit halves) is two fp16 halves whose only set bit is bit k, i.e. the
+// code bit times the exact power of two 2^(k - 24) (subnormal for k <= 9;
+// bits 10..15 are first shifted down to 4..9).  The query operand of each
+// k-slot carries 2 coef q 2^(S0 - k), so every product has the same scale
+// 2^(S0 - 24), divided out in the epilogue.  One AND per two k-slots, no
+// table reads.  Lane (r, kq) of source dword j, product u (0..3) holds k-slot
+// pairs i = 0..3 from bit k = 4u + i of the dword's low half (slot 2i) and
+// high half (slot 2i + 1).  The QJL term takes its +-1 B operands from the
+// 256-entry sign table against the q_proj rows.
+//
+// Rows of these products come in head pairs: row 2h is the fp16 hi half of
+// head h, row 2h + 1 its lo half, so lane group kq (output rows 4kq..4kq+3)
+// holds both halves of heads 2kq and 2kq + 1, its own heads: the hi + lo
+// fold is two adds in the lane.
+template <int G, int BITS>
+struct PlaneOps {
+    half8 ab[4 * BITS];  // codebook products
+    float sc_cb;         // log2(e) 2^(24 - S0) / 128: accumulator to log2-unit score per unit of norm
+    float ccb[2];        // log2(e) (a1 + a0) sum q / 128 of the own heads
+};
+struct NoPlanes {};
+
+// Bit k of a 16-bit half after the shift that brings bits 10..15 to 4..9.
+__device__ __forceinline__ constexpr int plane_pos(int k) { return k <= 9 ? k : k - 6; }
+
+// Coordinate of k-slot half h (0 low, 1 high) for bit k of source dword j of
+// lane group kq.
+template <int BITS>
+__device__ __forceinline__ int plane_coord(int kq, int j, int k, int h) {
+    if constexpr (BITS == 2) return 32 * kq + 16 * j + 8 * h + (k >> 1);
+    return 32 * kq + 16 * h + k;  // 1-bit codes: one bit per coordinate
+}
+
+// Own head j (0, 1) of lane group kq: on the bit-plane path the head pair of
+// the group's output rows, else the layout of own_scores.
+template <bool PLANES>
+__device__ __forceinline__ int fused_own_head(int kq, int j) {
+    if constexpr (PLANES) return 2 * kq + j;
+    return own_head<8>(kq, j);
+}
+
+// MFMA row r of the bit-plane products: head r / 2, lo half when r is odd.
+__device__ __forceinline__ int plane_row(int r) { return (r & 1) ? 8 + (r >> 1) : (r >> 1); }
+
 // Query operands of the single-launch kernel: 8 heads, 8 waves, wave w
 // owns head w (its q_rot in registers) and the q_proj rows 16 w .. 16 w + 15.
 // Fills s_a / s_ap (fp16 hi and lo rows of q_rot and q_proj, as the scores
 // MFMAs of every key format read them) and, for bit-plane keys, this lane's
 // PlaneOps.  Scratch (all of it may alias the score area; a barrier must
-// follow before the area is reused): fq, fp: fp32 q_rot and q_proj [8][128]
-// in rows of kQRow floats (the padding puts the 8 rows in different banks);
-// red: 88 floats of per-head sums and maxima; tab: the plane operand table,
-// (4 BITS + 4) x 64 half8 (operand u of lane l at u * 64 + l).  Four steps
-// and three barriers: rotation, projection, table, each lane's operands.
+// follow before the area is reused): fq: fp32 q_rot [8][128] in rows of kQRow
+// floats (the padding puts the 8 rows in different banks); red: 16 floats of
+// per-head sums and maxima; tab: the plane operand table, 4 BITS x 64 half8
+// (operand u of lane l at u * 64 + l).  Four steps and three barriers:
+// rotation, projection, table, each lane's operands.
 template <bool PROJ, bool PLANES, int BITS, typename PO>
 __device__ __forceinline__ void fused_query_setup(const QueryLoads<8, PROJ, 8> &ql, const AttnArgs &a,
                                                   _Float16 (*s_a)[128], _Float16 (*s_ap)[128], float (*fq)[kQRow],
-                                                  float (*fp)[kQRow], float *red, half8 *tab, PO &po) {
+                                                  float *red, half8 *tab, PO &po) {
     constexpr int G = 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, kq = lane >> 4;
@@ -106,36 +157,18 @@ __device__ __forceinline__ void fused_query_setup(const QueryLoads<8, PROJ, 8> &
         for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql.sf[st], bq[st], acc, 0, 0, 0);
         // lane (c, kq) holds projections 16 wave + 4 kq + j of column c; the
         // head's value is column c plus column c + 8 (row rotate by 8)
-        float ps = 0.0f, pm = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float p = acc[j] + dpp_mov<0x128>(acc[j]);
             const int idx = 16 * wave + 4 * kq + j;
-            if (c < G) {
-                put_hi_lo(&s_ap[c][idx], &s_ap[G + c][idx], p);
-                if constexpr (PLANES) fp[c][idx] = p;
-            }
-            ps += p;
-            pm = fmaxf(pm, fabsf(p));
-        }
-        if constexpr (PLANES) {
-            // this wave's partial sum of head c (lanes c, c + 16, c + 32, c + 48)
-            // and its largest |q_proj| over all heads
-            ps = quad_sum(ps);
-            pm = quad_max(row16_max(c < G ? pm : 0.0f));
-            if (kq == 0 && c < G) red[16 + wave * G + c] = ps;
-            if (lane == 0) red[80 + wave] = pm;
+            if (c < G) put_hi_lo(&s_ap[c][idx], &s_ap[G + c][idx], p);
         }
         __syncthreads();
     }
     if constexpr (PLANES) {
-        float mq = 0.0f, mp = 0.0f;
+        float mq = 0.0f;
 #pragma unroll
         for (int h = 0; h < G; ++h) mq = fmaxf(mq, red[G + h]);
-        if constexpr (PROJ) {
-#pragma unroll
-            for (int w = 0; w < 8; ++w) mp = fmaxf(mp, red[80 + w]);
-        }
         float a1, a0;
         if constexpr (BITS == 2) {
             a1 = 0.5f * (a.tab->levels[1][3] + a.tab->levels[1][2]);
@@ -143,68 +176,133 @@ __device__ __forceinline__ void fused_query_setup(const QueryLoads<8, PROJ, 8> &
         } else {
             a1 = a0 = a.tab->levels[0][1];
         }
-        int e_cb = 0, e_q = 0;
+        int e_cb = 0;
         (void)frexpf(mq * 2.0f * fmaxf(a1, a0), &e_cb);
-        (void)frexpf(mp * 2.0f, &e_q);
-        const int s0_cb = 14 - e_cb, s0_q = 14 - e_q;  // every |A| < 2^14
-        po.sc_cb = ldexpf(1.0f, 24 - s0_cb);
-        po.sc_q = ldexpf(1.0f, 24 - s0_q);
+        const int s0_cb = 14 - e_cb;  // every |A| < 2^14
+        // the epilogue scales by the fp16 norm itself: 1/128 = 1/sqrt(d)^2
+        // and the change to log2 units go into the constants
+        po.sc_cb = ldexpf(1.0f, 24 - s0_cb) * (kLog2e / 128.0f);
         const float f1 = 2.0f * a1 * ldexpf(1.0f, s0_cb), f0 = 2.0f * a0 * ldexpf(1.0f, s0_cb);
-        const float fpq = 2.0f * ldexpf(1.0f, s0_q);
-        // table entry e = (operand u, lane 16 ekq + r); row r < 8 takes the hi
-        // half of head r, row r >= 8 the lo half of head r - 8
-        constexpr int NOPS = 4 * BITS + (PROJ ? 4 : 0);
-        for (int e = tid; e < NOPS * 64; e += 8 * 64) {
+        // table entry e = (operand u, lane 16 ekq + r); row r is half r & 1
+        // (hi, lo) of head r / 2
+        for (int e = tid; e < 4 * BITS * 64; e += 8 * 64) {
             const int u = e >> 6, ekq = (e >> 4) & 3, r = e & 15;
-            const bool lo = r >= G;
-            const int hr = r & (G - 1);
+            const bool lo = (r & 1) != 0;
+            const int hr = r >> 1;
             half8 v;
-            if (u >= 4 * BITS) {
-                const int uu = u - 4 * BITS;
+            const int j = u >> 2, uu = u & 3;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int k = 4 * uu + i;
-                        const float x = fp[hr][plane_coord<1>(ekq, 0, k, h)] * fpq * ldexpf(1.0f, -plane_pos(k));
-                        const _Float16 xh = _Float16(x);
-                        v[2 * i + h] = lo ? _Float16(x - float(xh)) : xh;
-                    }
-            } else {
-                const int j = u >> 2, uu = u & 3;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int k = 4 * uu + i;
-                        const float f = (BITS == 2 && (k & 1)) ? f1 : f0;
-                        const float x = fq[hr][plane_coord<BITS>(ekq, j, k, h)] * f * ldexpf(1.0f, -plane_pos(k));
-                        const _Float16 xh = _Float16(x);
-                        v[2 * i + h] = lo ? _Float16(x - float(xh)) : xh;
-                    }
-            }
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 4 * uu + i;
+                    const float f = (BITS == 2 && (k & 1)) ? f1 : f0;
+                    const float x = fq[hr][plane_coord<BITS>(ekq, j, k, h)] * f * ldexpf(1.0f, -plane_pos(k));
+                    const _Float16 xh = _Float16(x);
+                    v[2 * i + h] = lo ? _Float16(x - float(xh)) : xh;
+                }
             tab[e] = v;
         }
         // head constants: sum_i q c[idx] = sum (2 coef q) bit - (a1 + a0) sum q
-        // (1 bit: a sum q); sum_p q_proj (2 bit - 1) = sum 2 q_proj bit - sum q_proj
+        // (1 bit: a sum q)
 #pragma unroll
-        for (int jo = 0; jo < kOwn<G>; ++jo) {
-            const int h = own_head<G>(kq, jo);
-            po.ccb[jo] = (BITS == 2 ? a1 + a0 : a1) * red[h];
-            float psum = 0.0f;
-            if constexpr (PROJ) {
-#pragma unroll
-                for (int w = 0; w < 8; ++w) psum += red[16 + w * G + h];
-            }
-            po.cq[jo] = psum;
-        }
+        for (int jo = 0; jo < 2; ++jo)
+            po.ccb[jo] = (BITS == 2 ? a1 + a0 : a1) * red[fused_own_head<true>(kq, jo)] * (kLog2e / 128.0f);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < 4 * BITS; ++u) po.ab[u] = tab[u * 64 + lane];
+    }
+}
+
+// Scores one slice of 1- or 2-bit codebook keys on the bit-plane path (the
+// products and epilogue of score_ktiles with its PlaneOps) with the tiles
+// software-pipelined: the matrix products of tile i + 1 are issued before
+// the epilogue of tile i (token scales, row fold, head constants, LDS
+// store), so that the epilogue's vector work runs while the matrix cores are
+// busy instead of after them.  Then the slice's (max, sum) update.
+template <bool FULL, int BITS, bool PROJ, typename KT, typename Store, typename PO>
+__device__ __forceinline__ void score_planes_slice(const KT &d, int base, int t1, int wave, int t, int kq,
+                                                   const half8 *s_sgn, const half8 (&ap)[4], Store &&store,
+                                                   float (&m)[2], float (&l)[2], const PO &po) {
+    constexpr int G = 8, NT = KT::NT;
+    static_assert(kOwn<G> == 2, "two own heads per lane");
+    float scv[NT][2];
+    floatx4 d0[NT], d1[NT];
+    auto products = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        d0[i] = d1[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) {
+            const uint32_t w = d.wk[i][j], ws = w >> 6;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t bw[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int k = 4 * u + q4;
+                    bw[q4] = (k <= 9 ? w : ws) & (0x00010001u << plane_pos(k));
+                }
+                d0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    po.ab[4 * j + u], __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3])), d0[i], 0, 0,
+                    0);
+            }
+        }
         if constexpr (PROJ) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) po.aq[u] = tab[(4 * BITS + u) * 64 + lane];
+            for (int s = 0; s < 4; ++s)
+                d1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[s], s_sgn[(d.sw[i] >> (8 * s)) & 0xFFu], d1[i], 0, 0,
+                                                               0);
         }
+    };
+    // scores in log2 units: log2(e) s, with s = (n/d) <q_rot, c> +
+    // (sqrt(pi/2)/m)(gamma/sqrt d) <q_proj, sign>
+    auto epilogue = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int tok = base + wave * 16 + 16 * kFW * i + t;
+        const bool valid = FULL || tok < t1;
+        const float cn = h2f(d.nn[i] & 0xFFFFu);
+        const float cg = PROJ ? h2f(d.nn[i] >> 16) * (kQjlOverSqrtD * kLog2e) : 0.0f;
+        const float n = cn * po.sc_cb;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            // rows 4kq + 2j (hi) and 4kq + 2j + 1 (lo) of head 2kq + j
+            const float cb = d0[i][2 * j] + d0[i][2 * j + 1];
+            float o = PROJ ? fmaf(n, cb, cg * (d1[i][2 * j] + d1[i][2 * j + 1])) : n * cb;
+            o = fmaf(-cn, po.ccb[j], o);
+            if (valid) store(2 * kq + j, tok, o);
+            scv[i][j] = valid ? o : -INFINITY;
+        }
+    };
+    constexpr int kMfma = 4 * BITS + (PROJ ? 4 : 0);
+    Unroll<NT>::run([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        products(I);
+        if constexpr (i > 0) {
+            epilogue(std::integral_constant<int, i - 1>{});
+            // ask the scheduler to spread the vector work over the products:
+            // the table reads first, then one product after every few
+            // vector instructions
+            if constexpr (PROJ) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int r = 0; r < kMfma; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        }
+    });
+    epilogue(std::integral_constant<int, NT - 1>{});
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float mx = scv[0][j];
+#pragma unroll
+        for (int i = 1; i < NT; ++i) mx = fmaxf(mx, scv[i][j]);
+        const float nm = fmaxf(m[j], mx);
+        const float mb = nm == -INFINITY ? 0.0f : nm;
+        float acc = l[j] * fast_exp2(m[j] - mb);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc += fast_exp2(scv[i][j] - mb);
+        l[j] = acc;
+        m[j] = nm;
     }
 }
 
@@ -234,7 +332,8 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         int ok, last, okw[G];
         __attribute__((aligned(16))) _Float16 a[16][128];
         __attribute__((aligned(16))) _Float16 ap[PROJ ? 16 : 1][128];
-        // scores of the block: head h, token t0 + i at sc[h * kFLd + i];
+        // scores of the block: head h, token t0 + i at sc[h * kFLd + i]
+        // (log2 units on the bit-plane path, natural units otherwise);
         // after the V products, the per-wave partial sums [kFW][G][128]
         __attribute__((aligned(16))) float sc[G * kFLd];
     };
@@ -329,9 +428,13 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     }
     asm volatile("" ::: "memory");
     const bool whole = n_tok % kFSlice == 0;
-    KTiles<KK, KB> ta, tb, tc;
-    load_ktiles<kFW>(ta, t0, tmax, wave, t, kq, kid, ksg, knm);
-    if (t0 + kFSlice < t1) load_ktiles<kFW>(tb, t0 + kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+    // K slices in flight ahead of the one being scored
+    constexpr int kAhead = 2;
+    KTiles<KK, KB> kt[kAhead + 1];
+    Unroll<kAhead>::run([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if (i == 0 || t0 + i * kFSlice < t1) load_ktiles<kFW>(kt[i], t0 + i * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
+    });
 
     // a row shared by several blocks is summed with atomics: block 0 zeroes
     // it before the barrier
@@ -369,12 +472,12 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     // (code words as B operands).  Scratch in the score area: fp32 q_rot and
     // q_proj rows (8.25 KB), sums (512 B), the plane operand table (12 KB).
     constexpr bool USE_PLANES = KK != TQ_KIND_Q8 && KB <= 2;
-    using PO = typename std::conditional<USE_PLANES, PlaneOps<G, (KB <= 2 ? KB : 1), PROJ>, NoPlanes>::type;
+    using PO = typename std::conditional<USE_PLANES, PlaneOps<G, (KB <= 2 ? KB : 1)>, NoPlanes>::type;
     PO po;
-    static_assert(16 * kQRow + 128 + (4 * 2 + 4) * 64 * 4 <= G * kFLd, "setup scratch fits the score area");
-    fused_query_setup<PROJ, USE_PLANES, (KB <= 2 ? KB : 1)>(
-        ql, a, s_a, s_ap, reinterpret_cast<float (*)[kQRow]>(s_sc), reinterpret_cast<float (*)[kQRow]>(s_sc + 8 * kQRow),
-        s_sc + 16 * kQRow, reinterpret_cast<half8 *>(s_sc + 16 * kQRow + 128), po);
+    static_assert(8 * kQRow + 128 + 4 * 2 * 64 * 4 <= G * kFLd, "setup scratch fits the score area");
+    fused_query_setup<PROJ, USE_PLANES, (KB <= 2 ? KB : 1)>(ql, a, s_a, s_ap, reinterpret_cast<float (*)[kQRow]>(s_sc),
+                                                           s_sc + 8 * kQRow,
+                                                           reinterpret_cast<half8 *>(s_sc + 8 * kQRow + 128), po);
     // V scale bound of the block (its words were requested before the K
     // tiles, so they have long landed)
     uint32_t vmx = 0;
@@ -397,7 +500,8 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             }
         }
         if constexpr (PROJ) {
-            const _Float16 *rp = s_ap[lane & 15];
+            // the bit-plane products take their rows in head pairs
+            const _Float16 *rp = s_ap[USE_PLANES ? plane_row(lane & 15) : lane & 15];
 #pragma unroll
             for (int s = 0; s < 4; ++s) ap[s] = *reinterpret_cast<const half8 *>(rp + 32 * kq + 8 * s);
         }
@@ -415,25 +519,27 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         lim[j] = L;
     }
     auto sink = [&](int h, int tok, float v) { s_sc[h * kFLd + (tok - t0)] = v; };
-    const PO *pop = USE_PLANES ? &po : nullptr;
     auto scan = [&](auto full_c) {
         constexpr bool F = decltype(full_c)::value;
         if (t0 >= t1) return;
-        // slices are requested two ahead, and only inside the range: the
+        // slices are requested kAhead ahead, and only inside the range: the
         // arrival below waits for every outstanding access of the block
+        constexpr int NS = kAhead + 1, A = kAhead * kFSlice;
         for (int base = t0;;) {
-            if (base + 2 * kFSlice < t1) load_ktiles<kFW>(tc, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, false, G, kFW>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
-            base += kFSlice;
-            if (base >= t1) break;
-            if (base + 2 * kFSlice < t1) load_ktiles<kFW>(ta, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, false, G, kFW>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
-            base += kFSlice;
-            if (base >= t1) break;
-            if (base + 2 * kFSlice < t1) load_ktiles<kFW>(tb, base + 2 * kFSlice, tmax, wave, t, kq, kid, ksg, knm);
-            score_ktiles<F, false, G, kFW>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l, pop);
-            base += kFSlice;
-            if (base >= t1) break;
+            bool done = false;
+            Unroll<NS>::run([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                if (done) return;
+                if (base + A < t1) load_ktiles<kFW>(kt[(i + kAhead) % NS], base + A, tmax, wave, t, kq, kid, ksg, knm);
+                if constexpr (USE_PLANES)
+                    score_planes_slice<F, KB, PROJ>(kt[i], base, t1, wave, t, kq, s_sgn, ap, sink, m, l, po);
+                else
+                    score_ktiles<F, false, G, kFW>(kt[i], base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m,
+                                                   l);
+                base += kFSlice;
+                done = base >= t1;
+            });
+            if (done) break;
         }
     };
     if (whole) scan(std::true_type{});
@@ -444,8 +550,8 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         l[j] = row16_sum(m[j] == -INFINITY ? 0.0f : l[j] * fast_exp2(m[j] - mx));
         m[j] = mx;
         if (t == 0) {
-            s_red[wave][own_head<G>(kq, j)][0] = m[j];
-            s_red[wave][own_head<G>(kq, j)][1] = l[j];
+            s_red[wave][fused_own_head<USE_PLANES>(kq, j)][0] = m[j];
+            s_red[wave][fused_own_head<USE_PLANES>(kq, j)][1] = l[j];
         }
     }
     // V scale bound of the block
@@ -630,7 +736,7 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         bool kj[4], kept = false;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[j] = fmaf(sv[j], kLog2e, -Ml2);
+            x[j] = fmaf(sv[j], USE_PLANES ? 1.0f : kLog2e, -Ml2);
             kj[j] = x[j] >= keep_x;
             if constexpr (!decltype(whole_c)::value) kj[j] = kj[j] && tbs + 8 * kq + jo + j < t1;
             kept |= kj[j];
