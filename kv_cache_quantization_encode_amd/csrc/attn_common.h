@@ -334,26 +334,30 @@ template <int NW = 4, int KIND, int BITS>
 __device__ __forceinline__ void load_ktiles(KTiles<KIND, BITS> &d, int base, int tmax, int wave, int t, int kq,
                                             const uint8_t *kid, const uint8_t *ksg, const uint8_t *knm) {
     using KT = KTiles<KIND, BITS>;
+    // byte offsets within the row are non-negative and below 2^32: unsigned
+    // 32-bit offsets from the uniform row pointers, so each load is one
+    // scalar-base + vector-offset access with no 64-bit address arithmetic
 #pragma unroll
     for (int i = 0; i < KT::NT; ++i) {
-        const int tok = min(base + wave * 16 + 16 * NW * i + t, tmax);
+        const uint32_t tok = uint32_t(min(base + wave * 16 + 16 * NW * i + t, tmax));
         if constexpr (KIND == TQ_KIND_Q8) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint2 u = *reinterpret_cast<const uint2 *>(kid + tok * 128 + 32 * s + 8 * kq);
+                const uint2 u = *reinterpret_cast<const uint2 *>(kid + (tok * 128u + uint32_t(32 * s + 8 * kq)));
                 d.wk[i][2 * s] = u.x;
                 d.wk[i][2 * s + 1] = u.y;
             }
-            d.q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8);
+            d.q8s[i] = *reinterpret_cast<const uint2 *>(knm + tok * 8u);
         } else {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(kid + tok * (16 * BITS) + 4 * BITS * kq);
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(kid + (tok * uint32_t(16 * BITS) + uint32_t(4 * BITS * kq)));
 #pragma unroll
             for (int w = 0; w < KT::W; ++w) d.wk[i][w] = src[w];
             if constexpr (KIND == TQ_KIND_PROD) {
-                d.sw[i] = reinterpret_cast<const uint32_t *>(ksg + tok * 16)[kq];
-                d.nn[i] = reinterpret_cast<const uint32_t *>(knm)[tok];
+                d.sw[i] = *reinterpret_cast<const uint32_t *>(ksg + (tok * 16u + uint32_t(4 * kq)));
+                d.nn[i] = *reinterpret_cast<const uint32_t *>(knm + tok * 4u);
             } else {
-                d.nn[i] = reinterpret_cast<const uint16_t *>(knm)[tok];
+                d.nn[i] = *reinterpret_cast<const uint16_t *>(knm + tok * 2u);
             }
         }
     }

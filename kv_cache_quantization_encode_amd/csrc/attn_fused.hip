@@ -657,15 +657,22 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     const bool lo_half = n >= G;
     const int hn = n & (G - 1);
     const int jo = lo_half ? 4 : 0;  // lanes n and n + 8 weigh tokens 0-3 and 4-7 of their eight
-    const float Ml2 = s_M[hn] * kLog2e;
-    const float invL = s_invL[hn] * vsh;
-    const float keep_x = log2f(a.tau) - log2f(s_invL[hn]);  // p >= tau  <=>  x >= log2(tau L)
+    // A value of a token = p vsh = exp2(s log2(e) - Cy) with p = exp(s - M)/L
+    // (1/L and vsh = 2^(14 - vexp) in the exponent); kept when p >= tau, i.e.
+    // when the exponent is at least log2(tau) + 14 - vexp
+    const float lsh = float(14 - vexp);
+    const float Cy = s_M[hn] * kLog2e - log2f(s_invL[hn]) - lsh;
+    const float keep_y = log2f(a.tau) + lsh;
     const int vrow = row;
-    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 8 + (n >> 1);
+    // uniform row bases and unsigned 32-bit byte offsets (one scalar-base +
+    // vector-offset access per load)
+    const uint8_t *vrow_codes = a.vidx + int64_t(vrow) * a.T * (VQ8 ? 128 : 32);
+    const uint32_t lane_cw = VQ8 ? uint32_t(4 * n) : uint32_t(4 * (n >> 1));  // this lane's word of a token row
     const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
-    const uint16_t *vn = reinterpret_cast<const uint16_t *>(a.vnorm) + int64_t(vrow) * a.T;
-    const uint32_t *q8w = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 32 + n;
-    const uint2 *q8s = reinterpret_cast<const uint2 *>(a.vnorm) + int64_t(vrow) * a.T;
+    const uint8_t *vrow_scl = a.vnorm + int64_t(vrow) * a.T * (VQ8 ? 8 : 2);
+    auto code_word = [&](int tok, uint32_t w) {
+        return *reinterpret_cast<const uint32_t *>(vrow_codes + (uint32_t(tok) * (VQ8 ? 128u : 32u) + lane_cw + w));
+    };
     constexpr int NC = VQ8 ? 16 : 8;  // code dwords per lane and group
     constexpr int NA = VQ8 ? 16 : 4;  // A-operand dwords
 
@@ -677,47 +684,45 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     auto load_q8scl = [&](int tbs, uint2 (&sc)[4], bool tail) {
         const int tk = tbs + 8 * kq + jo;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sc[j] = q8s[tail ? min(tk + j, tmax) : tk + j];
+        for (int j = 0; j < 4; ++j)
+            sc[j] = *reinterpret_cast<const uint2 *>(vrow_scl + uint32_t(tail ? min(tk + j, tmax) : tk + j) * 8u);
     };
     auto load_norms = [&](int tbs, uint32_t (&nr)[2], bool tail) {
         const int tk = tbs + 8 * kq + jo;
         if (tail) {
             uint32_t h[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = vn[min(tk + j, tmax)];
+            for (int j = 0; j < 4; ++j)
+                h[j] = *reinterpret_cast<const uint16_t *>(vrow_scl + uint32_t(min(tk + j, tmax)) * 2u);
             nr[0] = h[0] | (h[1] << 16);
             nr[1] = h[2] | (h[3] << 16);
         } else {
-            __builtin_memcpy(nr, vn + tk, 8);
+            __builtin_memcpy(nr, vrow_scl + uint32_t(tk) * 2u, 8);
         }
     };
     auto load_codes = [&](int tbs, bool real, uint32_t (&c)[NC]) {
         const int tk = real ? tbs + 8 * kq : t0;
-        if constexpr (VQ8) {
-            const uint32_t *cp = q8w + int64_t(tk) * 32;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                c[2 * j] = cp[32 * j];
-                c[2 * j + 1] = cp[32 * j + 16];
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (VQ8) {
+                c[2 * j] = code_word(tk + j, 0);
+                c[2 * j + 1] = code_word(tk + j, 64);
+            } else {
+                c[j] = code_word(tk + j, 0);
             }
-        } else {
-            const uint32_t *cp = cwd32 + int64_t(tk) * 8;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = cp[8 * j];
         }
     };
     auto load_tail_codes = [&](int tbs, uint32_t (&c)[NC]) {
         const int tk = tbs + 8 * kq;
-        if constexpr (VQ8) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t *cp = q8w + int64_t(min(tk + j, tmax)) * 32;
-                c[2 * j] = cp[0];
-                c[2 * j + 1] = cp[16];
+        for (int j = 0; j < 8; ++j) {
+            const int tok = min(tk + j, tmax);
+            if constexpr (VQ8) {
+                c[2 * j] = code_word(tok, 0);
+                c[2 * j + 1] = code_word(tok, 64);
+            } else {
+                c[j] = code_word(tok, 0);
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = cwd32[int64_t(min(tk + j, tmax)) * 8];
         }
     };
 
@@ -732,19 +737,19 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
                        auto whole_c) -> bool {
         const float4 sd = *reinterpret_cast<const float4 *>(&s_sc[hn * kFLd + (tbs - t0) + 8 * kq + jo]);
         const float sv[4] = {sd.x, sd.y, sd.z, sd.w};
-        float x[4];
+        float y[4];
         bool kj[4], kept = false;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[j] = fmaf(sv[j], USE_PLANES ? 1.0f : kLog2e, -Ml2);
-            kj[j] = x[j] >= keep_x;
+            y[j] = fmaf(sv[j], USE_PLANES ? 1.0f : kLog2e, -Cy);
+            kj[j] = y[j] >= keep_y;
             if constexpr (!decltype(whole_c)::value) kj[j] = kj[j] && tbs + 8 * kq + jo + j < t1;
             kept |= kj[j];
         }
         if (__ballot(kept) == 0) return false;
         float ws[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ws[j] = kj[j] ? fast_exp2(x[j]) * invL : 0.0f;
+        for (int j = 0; j < 4; ++j) ws[j] = kj[j] ? fast_exp2(y[j]) : 0.0f;
 #pragma unroll
         for (int blkq = 0; blkq < NA / 4; ++blkq) {
             float v[4];
