@@ -48,14 +48,31 @@ __global__ __launch_bounds__(256) void minmax_quant_kernel(const uint16_t *__res
     const uint32_t sbits = double_to_half_bits((double(mx) - double(mn)) / double(kQmax));
     const float scale = h2f(sbits);
     const float zero = mn;  // already an fp16 value
+    // code = rint(fl32(v - zero) / scale), the quotient rounded to float32
+    // first.  With rs = fl32(1/scale) the product (v - zero) rs is within
+    // three float32 ulps of that quotient, so both round to the same integer
+    // unless the product lies within 2^-17 of a half-integer (an ulp is at
+    // most 2^-19 below 32); only then, in any of the lane's 32 values, the
+    // lane redoes its values with the division itself.
+    const float rs = scale > 0.0f ? 1.0f / scale : 0.0f;
+    float code[32];
+    bool tie = false;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float q = (v[j] - zero) * rs;
+        code[j] = rintf(q);
+        tie |= !(fabsf(fabsf(q - code[j]) - 0.5f) > 0x1p-17f);  // also NaN
+    }
+    if (tie && scale > 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) code[j] = rintf((v[j] - zero) / scale);
+    }
     uint32_t packed[BITS];
 #pragma unroll
     for (int i = 0; i < BITS; ++i) packed[i] = 0;
     Unroll<32>::run([&](auto I) {
         constexpr int j = decltype(I)::value;
-        float r = scale > 0.0f ? rintf((v[j] - zero) / scale) : 0.0f;
-        r = fminf(fmaxf(r, 0.0f), kQmax);
-        put_code<BITS, j>(packed, uint32_t(r));
+        put_code<BITS, j>(packed, uint32_t(fminf(fmaxf(code[j], 0.0f), kQmax)));
     });
 #pragma unroll
     for (int i = 0; i < BITS; ++i) codes[h * BITS + i] = packed[i];

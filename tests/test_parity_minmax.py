@@ -89,3 +89,32 @@ def test_minmax_full_size_sampled():
     cg = codes.reshape(-1, 64 * bits // 8)[groups]
     got = O.unpack_bitstream(cg, bits, 64).reshape(-1)
     assert np.array_equal(got, rc)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_minmax_exact_ties(bits):
+    """Values whose float32 quotient (v - zero)/scale is exactly k + 0.5 with a
+    scale whose reciprocal is inexact (3, 5, 7, 11): the code is round half to
+    even of the quotient itself, which a product with the rounded reciprocal
+    misses (it lands one ulp above or below the tie)."""
+    qmax = (1 << bits) - 1
+    groups = []
+    for s in (3.0, 5.0, 7.0, 11.0):
+        for off in (0.0, -64.0, 256.0):
+            g = np.empty(64)
+            g[0], g[1] = off, off + s * qmax  # min and max fix zero = off and scale = s
+            k = np.arange(62) % qmax
+            g[2:] = off + s * (k + 0.5)
+            groups.append(g)
+    x = np.concatenate(groups).astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), np.concatenate(groups))  # every value exact in fp16
+    codes, scale, zero, _ = _gpu_minmax(x, bits)
+    rc, rs, rz = O.minmax_quant(x, 64, bits)
+    assert np.array_equal(scale.view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(zero.view(np.uint16), rz.view(np.uint16))
+    got = O.unpack_minmax_codes(codes, bits, x.size)
+    assert np.array_equal(got, rc)
+    # half to even: k + 0.5 goes to the even neighbour
+    g2 = got.reshape(-1, 64)[:, 2:]
+    k = np.arange(62) % qmax
+    assert np.array_equal(g2, np.broadcast_to(np.where(k % 2 == 0, k, k + 1), g2.shape))
