@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libturbokv.so")
-SOURCES = ["attn.hip", "attn_fused.hip", "attn_generic.hip", "attn_prefill.hip", "encode.hip", "tables.cpp", "api.cpp", "dequant.hip", "minmax.hip",
+SOURCES = ["attn.hip", "attn_fused.hip", "attn_fused4.hip", "attn_generic.hip", "attn_prefill.hip", "encode.hip", "tables.cpp", "api.cpp", "dequant.hip", "minmax.hip",
            "scratch.hip"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 (v_pk_*_f32)

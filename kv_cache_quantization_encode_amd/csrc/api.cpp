@@ -119,7 +119,8 @@ static AttnPlan prefill_plan(int B, int Hq, int Hkv, int T, int Tq) {
     return p;
 }
 
-AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity) {
+AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity,
+                        int capacity4) {
     // prompt-scale prefill kernels past the grouped path's grid limit (within
     // it the grouped decode kernels are faster: measured on the llama8b-like
     // layer, Tq 2048: 11.4 ms against 15.7 ms)
@@ -128,6 +129,27 @@ AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_
     const int qp = prefill_group(g, Tq);
     AttnPlan p = attn_plan(B * (Tq / qp), Hq * qp, Hkv, T);
     if (block32_format(kf) || block32_format(vf)) return p;  // scores + values passes
+    // single launch with 4 query heads per kv head: decode, every block of a
+    // row resident at once, a block's scores (tb tokens x 4 heads) in its LDS
+    if (Tq == 1 && g == 4 && capacity4 > 0 && fused4_formats(kf, vf)) {
+        const int64_t rows = int64_t(B) * Hkv;
+        const int64_t slices = (int64_t(T) + kFusedSlice - 1) / kFusedSlice;
+        int64_t nblk = capacity4 / rows;
+        if (nblk < 1) nblk = 1;
+        if (nblk > slices) nblk = slices;
+        if (nblk > kFusedMaxBlocks) nblk = kFusedMaxBlocks;
+        const int64_t tb = (slices + nblk - 1) / nblk * kFusedSlice;
+        nblk = (int64_t(T) + tb - 1) / tb;
+        if (tb <= kFusedMaxTokens && rows * nblk <= capacity4 && rows <= kSyncRows &&
+            rows * nblk <= kFusedMaxGrid) {
+            AttnPlan f = p;
+            f.fused4 = 1;
+            f.nblk = int(nblk);
+            f.tb = int(tb);
+            return f;
+        }
+        return p;
+    }
     // single launch: decode with 8 query heads per kv head and a V codec the
     // fused kernel reads (2-bit codebook, q8); every block of a row is resident
     // at once, and a block's scores (tb tokens x 8 heads) fit its LDS
@@ -319,7 +341,7 @@ size_t tq_attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int T, int Tq, tq
     if (int64_t(B) * Hkv > kMaxGridY) return 0;
     // the grouped prefill path puts (sequence, query group, kv head) on grid y
     if (!prefill_tiled_call(B, Hkv, Tq, kf, vf) && int64_t(B) * Tq * Hkv > kMaxGridY) return 0;
-    return attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity()).total;
+    return attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity(), fused4_capacity()).total;
 }
 
 // Decode (Tq = 1) and causal prefill (Tq queries per sequence) share one path:
@@ -346,7 +368,7 @@ static tq_status attn_check(const tq_ctx *ctx, const void *q_f16, const void *k_
     const int64_t n_vec = int64_t(B) * Hkv * T;
     if (!plane_layout(kf, ctx->head_dim, n_vec, kl) || !plane_layout(vf, ctx->head_dim, n_vec, vl))
         return TQ_ERR_INVALID_ARG;
-    *plan = attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity());
+    *plan = attn_call_plan(B, Hq, Hkv, T, Tq, kf, vf, fused_capacity(), fused4_capacity());
     if (!workspace || !aligned(workspace, 256) || ws_bytes < plan->total) return TQ_ERR_WORKSPACE;
     return TQ_OK;
 }
@@ -378,6 +400,9 @@ tq_status tq_attn_decode_append(const tq_ctx *ctx, const void *q_f16, const void
     const tq_status st = attn_check(ctx, q_f16, k_packed, v_packed, kf, vf, B, Hq, Hkv, T_cap, 1, pos,
                                     sparse_v_tau, out_f32, workspace, ws_bytes, &kl, &vl, &plan);
     if (st != TQ_OK) return st;
+    // the 4-head single launch has no append: the two-pass plan of the same
+    // call (its fields are kept in the plan) appends in its scores pass
+    plan.fused4 = 0;
     // (the two-pass kernels put the rows' extra blocks in grid rows of their
     // own: at most twice B * Hkv grid rows)
     if (append_in_attention(kf, vf) && (plan.fused || 2 * int64_t(B) * Hkv <= kMaxGridY)) {

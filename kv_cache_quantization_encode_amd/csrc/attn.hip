@@ -363,12 +363,9 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
     constexpr int R = kSuper / kVThreads;  // tokens per thread per super-slice
     // s_vpair[f]: the two levels of a 2-code field f = c0 | c1 << BITS
     constexpr int kVPairs = KIND == TQ_KIND_Q8 ? 1 : 1 << (2 * BITS);
-    __shared__ float2 s_vpair[kVPairs];
     __shared__ float s_M[G], s_invL[G];
-    __shared__ float s_w[G][kSuper];
-    __shared__ int s_tok[kSuper];
-    __shared__ int s_wcount[R][kVWaves];
-    __shared__ float s_acc[kVWaves][G][128];
+    __shared__ ValuesLds<G, KIND, BITS, kSuper> lds;
+    float2 *s_vpair = lds.vpair;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk_id = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv, kvh = row - b * a.Hkv;
@@ -427,182 +424,7 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    // V accumulation layout: CPL coordinates per lane, LPT lanes per token,
-    // TPW tokens per wave and pass (fewer coordinates per lane for 8 heads,
-    // whose accumulators take twice the registers)
-    constexpr int CPL = G >= 8 ? 4 : 8, LPT = 128 / CPL, TPW = 64 / LPT;
-    const int tk = lane / LPT, cg = lane % LPT;  // token slot within the wave, coordinate group
-    float acc[G][CPL];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) acc[g][j] = 0.0f;
-
-    bool kept_any = false;  // uniform over the block
-    for (int base = t0; base < t1; base += kSuper) {
-        // 1) weights and the keep decision, R tokens per thread
-        bool keep[R];
-        uint64_t bal[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            keep[r] = false;
-            if (base + kVThreads * r < t1) {  // uniform
-                const bool ok = base + kVThreads * r + tid < t1;
-                const float vsc = KIND == TQ_KIND_Q8 ? 1.0f : h2f(vraw[r]) * kRsqrtD;
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float p = fast_exp2((sv[r][g] - s_M[g]) * kLog2e) * s_invL[g];
-                    const bool k = ok && p >= a.tau;
-                    keep[r] |= k;
-                    sv[r][g] = k ? p * vsc : 0.0f;  // reuse as the weight
-                }
-            }
-            bal[r] = __ballot(keep[r]);
-            if (lane == 0) s_wcount[r][wave] = __popcll(bal[r]);
-        }
-        __syncthreads();
-        // 2) compaction in token order
-        int total = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            int off = total;
-#pragma unroll
-            for (int w = 0; w < kVWaves; ++w) {
-                const int c = s_wcount[r][w];
-                off += (w < wave) ? c : 0;
-                total += c;
-            }
-            if (keep[r]) {
-                const int slot = off + __popcll(bal[r] & ((uint64_t(1) << lane) - 1));
-                s_tok[slot] = base + kVThreads * r + tid;
-#pragma unroll
-                for (int g = 0; g < G; ++g) s_w[g][slot] = sv[r][g];
-            }
-        }
-        kept_any |= total > 0;
-        __syncthreads();
-        if (base + kSuper < t1) load_super(base + kSuper);  // next super-slice in flight
-        // 3) accumulate kept rows: TPW tokens per wave and pass, CPL
-        //    coordinates per lane.  All row loads of a batch are issued before
-        //    any is used (a slot past `total` reads a kept row), and passes run
-        //    four at a time without branches (such slots carry weight 0); the
-        //    number of groups of four is uniform over the block.
-        constexpr int PASSES = 8, PER_PASS = TPW * kVWaves;
-        // codes of this lane: CPL * BITS bits from bit CPL * BITS * cg of the
-        // row; within one dword unless 3-bit codes straddle two
-        constexpr int NB = CPL * (KIND == TQ_KIND_Q8 ? 8 : BITS);
-        constexpr bool TWO = (32 % NB) != 0;
-        const int bit0 = NB * cg;
-        for (int k0 = 0; k0 < total; k0 += PER_PASS * PASSES) {
-            const int npass = min((total - k0 + PER_PASS - 1) / PER_PASS, PASSES);
-            uint32_t raw[PASSES][2];
-            float bsc[PASSES];
-            Unroll<PASSES>::run([&](auto P) {
-                constexpr int ps = decltype(P)::value;
-                {
-                    const int slot = min(k0 + PER_PASS * ps + wave * TPW + tk, total - 1);
-                    const int64_t vec = int64_t(vrow) * a.T + s_tok[slot];
-                    raw[ps][1] = 0u;
-                    if constexpr (KIND == TQ_KIND_Q8) {
-                        if constexpr (CPL == 8) {
-                            const uint2 u = *reinterpret_cast<const uint2 *>(a.vidx + vec * 128 + 8 * cg);
-                            raw[ps][0] = u.x;
-                            raw[ps][1] = u.y;
-                        } else {
-                            raw[ps][0] = *reinterpret_cast<const uint32_t *>(a.vidx + vec * 128 + 4 * cg);
-                        }
-                        bsc[ps] = h2f(reinterpret_cast<const uint16_t *>(a.vnorm)[vec * 4 + ((CPL * cg) >> 5)]);
-                    } else {
-                        const uint32_t *wp = reinterpret_cast<const uint32_t *>(a.vidx + vec * (16 * BITS));
-                        raw[ps][0] = wp[bit0 >> 5];
-                        if constexpr (TWO) raw[ps][1] = wp[(bit0 + NB - 1) >> 5];
-                    }
-                }
-            });
-            // every row load above is issued before the first use below
-            asm volatile("" ::: "memory");
-            Unroll<PASSES / 4>::run([&](auto Q) {
-                constexpr int q4 = decltype(Q)::value;
-                if (4 * q4 < npass) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int ps = 4 * q4 + u;
-                        const int slot = k0 + PER_PASS * ps + wave * TPW + tk;
-                        const bool live = slot < total;
-                        float val[CPL];
-                        if constexpr (KIND == TQ_KIND_Q8) {
-#pragma unroll
-                            for (int j = 0; j < CPL; ++j)
-                                val[j] = float(int8_t((raw[ps][j >> 2] >> (8 * (j & 3))) & 0xFFu)) * bsc[ps];
-                        } else {
-                            uint32_t bitsw;
-                            if constexpr (TWO) {
-                                bitsw = __builtin_amdgcn_alignbit(raw[ps][1], raw[ps][0], bit0 & 31);
-                            } else {
-                                bitsw = raw[ps][0] >> (bit0 & 31);
-                            }
-                            // 2-code fields: one table read gives two levels
-#pragma unroll
-                            for (int f = 0; f < CPL / 2; ++f) {
-                                const float2 lv = s_vpair[(bitsw >> (2 * BITS * f)) & ((1u << (2 * BITS)) - 1u)];
-                                val[2 * f] = lv.x;
-                                val[2 * f + 1] = lv.y;
-                            }
-                        }
-#pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            const float wg = live ? s_w[g][slot] : 0.0f;
-#pragma unroll
-                            for (int j = 0; j < CPL; ++j) acc[g][j] = fmaf(wg, val[j], acc[g][j]);
-                        }
-                    }
-                }
-            });
-        }
-        __syncthreads();
-    }
-    // reduce over the token slots of each wave, then over the waves
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            if constexpr (TPW == 4) {
-                acc[g][j] = quad_sum(acc[g][j]);
-            } else {
-                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[g][j]),
-                                                                __float_as_uint(acc[g][j]), false, false);
-                acc[g][j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-            }
-        }
-    if (tk == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) s_acc[wave][g][CPL * cg + j] = acc[g][j];
-    }
-    __syncthreads();
-    // the chunk's share of each head, rotated back (out = R^T acc = D H acc /
-    // sqrt(d) for rotated V codecs; R^T is linear, so shares rotate one by
-    // one) and added into the output, which the scores pass zeroed.  A chunk
-    // that kept no row adds nothing.
-    if (kept_any) {
-        for (int g = wave; g < G; g += kVWaves) {
-            float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kVWaves; ++w) {
-                v0 += s_acc[w][g][lane];
-                v1 += s_acc[w][g][lane + 64];
-            }
-            if (a.v_rotated) {
-                fwht128_lanes(v0, v1, lane);
-                v0 *= a.tab->signs[lane] * kRsqrtD;
-                v1 *= a.tab->signs[lane + 64] * kRsqrtD;
-            }
-            float *o = a.out + io_row(a, b, kvh, g) * 128;
-            __hip_atomic_fetch_add(o + lane, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(o + lane + 64, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    values_compact<G, KIND, BITS, kSuper, true>(a, b, kvh, vrow, t0, t1, s_M, s_invL, sv, vraw, load_super, lds);
 }
 
 // ------------------------------------- values pass on MFMA: 2-bit V and q8 V
@@ -1157,6 +979,15 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
         a.nblk = plan.nblk;
         a.tb = plan.tb;
         return launch_attn_fused(a, kf, vf, stream);
+    }
+    if (plan.fused4 && !app) {
+        // the barrier region at the start of the workspace (counters, then
+        // the (max, sum) slots), as for the 8-head kernel
+        a.sync = reinterpret_cast<uint32_t *>(w);
+        a.stats = reinterpret_cast<float *>(w + kSyncCounterBytes);
+        a.nblk = plan.nblk;
+        a.tb = plan.tb;
+        return launch_attn_fused4(a, kf, vf, stream);
     }
     switch (a.Hq / Hkv) {
         case 1: return dispatch_k<1>(a, kf, vf, s);

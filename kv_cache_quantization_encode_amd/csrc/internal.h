@@ -60,12 +60,19 @@ struct AttnPlan {
     // prompt-scale prefill (attn_prefill.hip): n_chunks token ranges of
     // chunk tokens, (max, sum) statistics per row and range at off_stats
     int tiled;
+    // single launch with 4 query heads per kv head (attn_fused4.hip): nblk
+    // blocks of tb tokens per row, departure counters at the start of the
+    // workspace and (max, sum) slots after them; the other fields keep the
+    // two-pass plan of the same call (same workspace size), which a decode
+    // step that appends takes instead
+    int fused4;
 };
 AttnPlan attn_plan(int B, int Hq, int Hkv, int T);
 // The plan of one attention call: the single-launch path when its shape and
 // the device allow it, else the two-pass plan.  capacity = blocks of the
 // single-launch kernel resident at once on the current device (0: unknown).
-AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity);
+AttnPlan attn_call_plan(int B, int Hq, int Hkv, int T, int Tq, tq_format kf, tq_format vf, int capacity,
+                        int capacity4 = 0);
 inline bool block32_format(tq_format f) { return f.kind == TQ_KIND_MSE32 || f.kind == TQ_KIND_PROD32; }
 // Tokens per block and block size limits of the single-launch kernel.
 constexpr int kFusedSlice = 512;
@@ -143,6 +150,14 @@ int launch_attn(const DevTables *tab, const void *q, const void *kp, const void 
 // device for it (0 when it cannot run).
 int launch_attn_fused(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
 int fused_capacity();
+// Single-launch decode attention with 4 query heads per kv head
+// (attn_fused4.hip): TurboQuant K, 2/3/4-bit codebook V; capacity as above.
+inline bool fused4_formats(tq_format kf, tq_format vf) {
+    return kf.kind == TQ_KIND_PROD && kf.bits >= 1 && kf.bits <= 3 && vf.kind == TQ_KIND_MSE && vf.bits >= 2 &&
+           vf.bits <= 4;
+}
+int launch_attn_fused4(const struct AttnArgs &a, tq_format kf, tq_format vf, void *stream);
+int fused4_capacity();
 // Library-owned attention workspace (scratch.hip): kScratchBytes on every
 // GPU the library runs on.  scratch_prepare looks up this device's copy (the
 // device must be current); scratch_device_ptr returns it (nullptr if not

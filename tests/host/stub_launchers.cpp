@@ -31,8 +31,10 @@ int launch_attn(const DevTables *, const void *, const void *, const void *, tq_
 int launch_attn_fused(const AttnArgs &, tq_format, tq_format, void *) { return 1; }
 int launch_attn_generic(const AttnArgs &, tq_format, tq_format, void *) { return 1; }
 int launch_attn_prefill(const AttnArgs &, tq_format, tq_format, void *) { return 1; }
-// no device: the single-launch attention path is never planned
+int launch_attn_fused4(const AttnArgs &, tq_format, tq_format, void *) { return 1; }
+// no device: the single-launch attention paths are never planned
 int fused_capacity() { return 0; }
+int fused4_capacity() { return 0; }
 int scratch_prepare(int) { return 1; }
 void *scratch_device_ptr(int) { return nullptr; }
 int launch_minmax_quant(const void *, int64_t, int, void *, void *, void *, void *) { return 1; }

@@ -177,18 +177,20 @@ def test_attention_eight_heads_repeated_calls_one_workspace(ctx, oracle_tables):
 
 
 def test_attention_workspace_shared_across_paths_and_shapes(ctx, oracle_tables):
-    """One workspace, zero-filled once, serves in turn: a single-launch call
-    (rows spread over several blocks), a two-pass call (4 query heads per KV
-    head, scores written over most of the workspace), a single-launch call
-    with another row count and block split, and the first call again.  Every
-    call matches the oracle: nothing but the barrier counters, which each
-    call leaves at zero, survives from one call to the next."""
+    """One workspace, zero-filled once, serves in turn: an 8-head
+    single-launch call (rows spread over several blocks), a two-pass call (2
+    query heads per KV head, scores written over most of the workspace), a
+    4-head single-launch call, the two-pass call again, an 8-head
+    single-launch call with another row count and block split, and the first
+    call again.  Every call matches the oracle: nothing but the barrier
+    counters and slots, which each call leaves at zero, survives from one
+    call to the next."""
     import torch
     from kv_cache_quantization_encode_amd import turbokv as T
     kf, vf = ("prod", 2), ("mse", 2)
     K, V = G.tf(*kf), G.tf(*vf)
     cases = [W.llama70b_layer(21, T=3000, Hkv=2, Hq=16), W.llama70b_layer(22, T=2500, Hkv=2, Hq=8),
-             W.llama70b_layer(23, T=1900, Hkv=4, Hq=32)]
+             W.llama70b_layer(23, T=1900, Hkv=4, Hq=32), W.llama70b_layer(24, T=2200, Hkv=2, Hq=4)]
     need = max(T.tq_attn_workspace_bytes(*c.shape, K, V) for c in cases)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     prepared = []
@@ -196,7 +198,7 @@ def test_attention_workspace_shared_across_paths_and_shapes(ctx, oracle_tables):
         kp, vp = _encode_case(ctx, c, kf, vf)
         ref = G.oracle_attention(c, kp, vp, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6)
         prepared.append((c, G.to_dev_f16(c.q), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), ref))
-    for i in (0, 1, 2, 0):
+    for i in (0, 3, 1, 3, 2, 0):
         c, q, kd, vd, ref = prepared[i]
         B, Hq, Hkv, Tn = c.shape
         out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
@@ -253,3 +255,47 @@ def test_attention_eight_heads_key_formats(ctx, oracle_tables, kf, vf):
     row split over several blocks."""
     c = W.llama70b_layer(21, T=1500, Hkv=2, Hq=16)
     _run(ctx, oracle_tables, c, kf, vf, 1e-6, seq_lens=np.array([1333], np.int32))
+
+
+def test_attention_four_heads_single_launch_ragged(ctx, oracle_tables):
+    """4 query heads per KV head, few rows (6 x 8): the single-launch path
+    spreads each row over several 512-token blocks; lengths cut rows at 0, 1,
+    a slice edge and inside a block."""
+    c = W.llama8b(seed=206, T=3000, B=6)
+    lens = np.array([3000, 0, 1, 513, 1024, 2047], np.int32)
+    got, _, _ = _run(ctx, oracle_tables, c, ("prod", 3), ("mse", 4), 1e-6, seq_lens=lens)
+    assert np.all(got[1] == 0.0)
+
+
+@pytest.mark.parametrize("kf,vf", [(("prod", 1), ("mse", 2)), (("prod", 2), ("mse", 3))],
+                         ids=["turbo2K-2bitV", "turbo3K-3bitV"])
+def test_attention_four_heads_single_launch_formats(ctx, oracle_tables, kf, vf):
+    c = W.llama8b(seed=207, T=2600, B=2)
+    _run(ctx, oracle_tables, c, kf, vf, 1e-6)
+
+
+def test_attention_four_heads_repeated_calls_one_workspace(ctx, oracle_tables):
+    """The 4-head single launch leaves its barrier counters and slots at zero:
+    five calls on one workspace (each row over 10 blocks) agree with each
+    other and with the oracle, and the barrier region is zero afterwards."""
+    import torch
+    from kv_cache_quantization_encode_amd import turbokv as T
+    c = W.llama8b(seed=208, T=5000, B=1)
+    kf, vf = ("prod", 3), ("mse", 4)
+    kp, vp = _encode_case(ctx, c, kf, vf)
+    B, Hq, Hkv, Tn = c.shape
+    K, V = G.tf(*kf), G.tf(*vf)
+    ws, wsb = T.alloc_workspace(B, Hq, Hkv, Tn, K, V)
+    q, kd, vd = G.to_dev_f16(c.q), torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda()
+    outs = []
+    for r in range(5):
+        out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        G.note(f"4-head repeated call {r}")
+        T.tq_attn_decode(ctx, q, kd, vd, K, V, B, Hq, Hkv, Tn, None, 1e-6, out, ws, wsb)
+        outs.append(out.cpu().numpy())
+    ref = G.oracle_attention(c, kp, vp, kf[0], kf[1], vf[0], vf[1], oracle_tables, 1e-6)
+    for o in outs:
+        assert np.isfinite(o).all()
+        assert np.max(np.abs(o - outs[0])) <= 1e-5
+        assert np.max(np.abs(o - ref)) <= G.ATTN_ATOL
+    assert int(ws[:68 * 1024].count_nonzero().item()) == 0
