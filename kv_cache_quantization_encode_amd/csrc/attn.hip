@@ -146,9 +146,9 @@ __device__ __forceinline__ void append_and_score(const AttnArgs &a, int b, int k
 // 1): one extra block per row, in grid rows after the chunks' rows, encodes
 // it and scores only it (append_and_score).
 template <int G, int KIND, int BITS, bool APPEND = false>
-__global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint8_t *__restrict__ kidx,
-                                                          const uint8_t *__restrict__ ksign,
-                                                          const uint8_t *__restrict__ knorm,
+__global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint8_t *kidx,
+                                                          const uint8_t *ksign,
+                                                          const uint8_t *knorm,
                                                           float *__restrict__ scores) {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "1, 2, 4 or 8 query heads per kv head");
     static_assert(!APPEND || KIND == TQ_KIND_PROD, "the append encodes TurboQuant K");
@@ -301,21 +301,29 @@ __global__ __launch_bounds__(256) void attn_scores_kernel(AttnArgs a, const uint
 
     auto sink = [&](int h, int tok, float v) { scores[(head0 + h) * a.ld_scores + tok] = v; };
     // the scan: every load is unconditional (clamped rows), so the wait
-    // before scoring a slice covers exactly that slice's loads
+    // before scoring a slice covers exactly that slice's loads.  The K planes
+    // are not declared __restrict__, and a compiler barrier follows each
+    // request: otherwise the compiler is free to move a slice's loads past
+    // the loop exits to just before the slice is scored, and the scan then
+    // waits for each slice's loads in turn (the needle batch's scores pass:
+    // 84 us with the loads kept in place, 91 us with them moved)
     auto scan = [&](auto full_c, auto rowlim_c) {
         constexpr bool F = decltype(full_c)::value;
         constexpr bool RL = decltype(rowlim_c)::value;
         if (t0 >= t1) return;
         for (int base = t0;;) {
             load_ktiles(tc, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
+            asm volatile("" ::: "memory");  // issued here, two slices ahead
             score_ktiles<F, RL, G>(ta, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(ta, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
+            asm volatile("" ::: "memory");  // issued here, two slices ahead
             score_ktiles<F, RL, G>(tb, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
             base += kSlice;
             if (base >= t1) break;
             load_ktiles(tb, base + 2 * kSlice, tmax, wave, t, kq, kid, ksg, knm);
+            asm volatile("" ::: "memory");  // issued here, two slices ahead
             score_ktiles<F, RL, G>(tc, base, t1, wave, t, kq, s_pair, s_sgn, aq, ap, sink, lim, m, l);
             base += kSlice;
             if (base >= t1) break;

@@ -551,10 +551,12 @@ struct ValuesLds {
     static constexpr int R = kSuper / kVThreads;
     float2 vpair[kVPairs];  // the two levels of a 2-code field f = c0 | c1 << BITS (filled by the caller)
     int wcount[R][kVWaves];
+    // the kept list: up to two super-slices of kept rows (weights per head,
+    // token), drained when the next super-slice might not fit
     union {
         struct {
-            float w[G][kSuper];
-            int tok[kSuper];
+            float w[G][2 * kSuper];
+            int tok[2 * kSuper];
         } c;
         float acc[kVWaves][G][128];
     } u;
@@ -589,6 +591,7 @@ __device__ __forceinline__ void values_compact(const AttnArgs &a, int b, int kvh
         for (int j = 0; j < CPL; ++j) acc[g][j] = 0.0f;
 
     bool kept_any = false;  // uniform over the block
+    int total = 0;          // rows in the kept list, uniform over the block
     for (int base = t0; base < t1; base += kSuper) {
         // 1) weights and the keep decision, R tokens per thread
         bool keep[R];
@@ -611,16 +614,16 @@ __device__ __forceinline__ void values_compact(const AttnArgs &a, int b, int kvh
             if (lane == 0) lds.wcount[r][wave] = __popcll(bal[r]);
         }
         __syncthreads();
-        // 2) compaction in token order
-        int total = 0;
+        // 2) compaction in token order, appended to the kept list
+        int cnt = 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            int off = total;
+            int off = total + cnt;
 #pragma unroll
             for (int w = 0; w < kVWaves; ++w) {
                 const int c = lds.wcount[r][w];
                 off += (w < wave) ? c : 0;
-                total += c;
+                cnt += c;
             }
             if (keep[r]) {
                 const int slot = off + __popcll(bal[r] & ((uint64_t(1) << lane) - 1));
@@ -629,9 +632,14 @@ __device__ __forceinline__ void values_compact(const AttnArgs &a, int b, int kvh
                 for (int g = 0; g < G; ++g) lds.u.c.w[g][slot] = sv[r][g];
             }
         }
-        kept_any |= total > 0;
+        total += cnt;
+        kept_any |= cnt > 0;
         __syncthreads();
         if (base + kSuper < t1) load_super(base + kSuper);  // next super-slice in flight
+        // the list is drained after the last super-slice and whenever the
+        // next might not fit, so that with peaked attention the kept rows of
+        // many super-slices share one round of V row loads
+        if (total <= kSuper && base + kSuper < t1) continue;  // uniform
         // 3) accumulate kept rows: TPW tokens per wave and pass, CPL
         //    coordinates per lane.  All row loads of a batch are issued before
         //    any is used (a slot past `total` reads a kept row), and passes run
@@ -709,6 +717,7 @@ __device__ __forceinline__ void values_compact(const AttnArgs &a, int b, int kvh
                 }
             });
         }
+        total = 0;
         __syncthreads();
     }
     // reduce over the token slots of each wave, then over the waves

@@ -103,6 +103,49 @@ def test_attention_needle_batched_sampled(ctx, oracle_tables):
     _, _, err = _run(ctx, oracle_tables, c, ("prod", 3), ("mse", 2), 1e-6, batches=[0, 17, 42, 63])
 
 
+def _copies_case(g, B, T, layout, seed):
+    """Needle keys with copies: in sequence b, the key at position layout[b][0]
+    of every KV head is copied to the other positions of layout[b], and every
+    query head aims at it (as in the needle workload).  The copies encode to
+    the same bytes and score alike, so the weight spreads evenly over them;
+    every other key scores far below.  Sequences past len(layout) take a
+    random pick of 1 to 4 positions."""
+    c = W.needle(seed=seed, B=B, T=T, Hq=8 * g, Hkv=8)
+    k = c.k.astype(np.float32)
+    rng = np.random.default_rng(seed + 1)
+    ch_std = k.std(axis=(0, 2))  # [Hkv, D]: the x20 outlier channels stand out
+    q = np.zeros(c.q.shape, np.float32)
+    for b in range(B):
+        pos = layout[b] if b < len(layout) else list(rng.choice(T, rng.integers(1, 5), replace=False))
+        for kvh in range(8):
+            k[b, kvh, pos[1:]] = k[b, kvh, pos[0]]
+            kn = k[b, kvh, pos[0]].copy()
+            kn[ch_std[kvh] > 5.0] = 0.0
+            q[b, kvh * g:(kvh + 1) * g] = 3.0 * np.sqrt(128) * kn / np.linalg.norm(kn)
+    return W.AttnCase(f"copies.g{g}", k.astype(np.float16), c.v, q.astype(np.float16))
+
+
+@pytest.mark.parametrize("g,kf,vf", [(1, ("prod", 3), ("mse", 2)), (2, ("prod", 2), ("mse", 4)),
+                                     (4, ("mse", 3), ("mse", 2)), (8, ("prod", 3), ("mse", 3))])
+def test_attention_two_pass_kept_rows_across_super_slices(ctx, oracle_tables, g, kf, vf):
+    """The two-pass values pass keeps the rows of several super-slices in one
+    list and reads their V rows together.  512 rows (one chunk per row) and
+    256 rows (two chunks, the second starting at token 1536): keys copied to
+    the first and last token of 512-token stretches, to the last token of a
+    sequence and past a cut length, queries aimed at them, so a row keeps a
+    few tokens spread over its super-slices; at tau = 0.05 each copy carries
+    a weight of 1/4 to 1, so a kept row lost or added twice moves the output
+    by ~0.1.  Then tau = 1e-6 on the same caches."""
+    for B, T, layout, lens in (
+            (64, 2600, [[1023, 1536, 2599], [1024, 2047], [2560, 511, 2048], [1535, 2559, 2047], [2599]],
+             [2600, 2600, 2561, 2049, 2600]),
+            (32, 3000, [[2560, 2999], [1536, 2559, 1024], [2047, 2048, 2999, 100]], [3000, 2560, 3000])):
+        c = _copies_case(g, B, T, layout, seed=900 + g)
+        seq_lens = np.array(lens + [T] * (B - len(lens)), np.int32)
+        for tau in (0.05, 1e-6):
+            _run(ctx, oracle_tables, c, kf, vf, tau, seq_lens=seq_lens, batches=list(range(len(lens))))
+
+
 def test_attention_70b_boundary_and_middle_layers(ctx, oracle_tables):
     for layer in (0, 40, 79):
         c = W.llama70b_layer(layer, T=4096)
