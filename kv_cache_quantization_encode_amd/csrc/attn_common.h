@@ -472,14 +472,23 @@ __device__ __forceinline__ void score_ktiles(const KTiles<KIND, BITS> &d, int ba
             const float bs[4] = {h2f(scl.x & 0xFFFFu), h2f(scl.x >> 16), h2f(scl.y & 0xFFFFu), h2f(scl.y >> 16)};
 #pragma unroll
             for (int j = 0; j < 4; ++j) e[j] = 0.0f;
+            // int8 q as fp16, exactly: byte q ^ 0x80 = q + 128 as the low
+            // mantissa byte under exponent byte 0x64 is 1024 + q + 128, then
+            // one packed subtract of 1152 (one XOR per four bytes, one permute
+            // and one subtract per two)
+            const half2v k1152 = half2v{_Float16(1152.0f), _Float16(1152.0f)};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                half8 bv;
+                uint32_t bw[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t w = d.wk[i][2 * s + (j >> 2)];
-                    bv[j] = _Float16(float(int8_t((w >> (8 * (j & 3))) & 0xFFu)));
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t x = d.wk[i][2 * s + h] ^ 0x80808080u;
+                    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);  // q0, q1
+                    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);  // q2, q3
+                    bw[2 * h] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, lo) - k1152);
+                    bw[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, hi) - k1152);
                 }
+                const half8 bv = __builtin_bit_cast(half8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
                 floatx4 ds = {0.0f, 0.0f, 0.0f, 0.0f};
                 ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bv, ds, 0, 0, 0);  // aq[0..3] only
                 // scale of block s of token t
