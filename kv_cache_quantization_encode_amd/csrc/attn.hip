@@ -452,6 +452,13 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
 // word n of the token's row.  Every token of a chunk is stepped over; a group
 // in which no head keeps a token is skipped as a whole.
 //
+// 4-bit codebook V: B = the level of the token's code, as fp16 hi and lo
+// halves (two products per column block), read from a 16-entry LDS table;
+// the token's norm goes into A (weight x norm, scaled below 2^14 by the
+// block's largest norm); the sum is the rotated-domain V sum times that
+// scale and sqrt(d).  Coordinates 8n + [0, 8) of a token are dword n of its
+// 64-byte row.
+//
 // q8 V (boundary layers): x = q s_blk with int8 q and one fp16 scale per 32
 // coordinates.  B = q as fp16 (exact: the byte becomes the mantissa of
 // 1024 + (q + 128) through v_perm and an xor, then one packed fp16 subtract
@@ -464,16 +471,19 @@ constexpr int kMThreads = 256;
 constexpr int kMWaves = kMThreads / 64;
 constexpr float kWScale = 32768.0f;  // 2^15
 
-template <int G, int VK>
+template <int G, int VK, int VB>
 __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a) {
     static_assert(G == 8, "rows: 8 heads x (hi, lo)");
-    static_assert(VK == TQ_KIND_MSE || VK == TQ_KIND_Q8, "2-bit codebook V or q8 V");
+    static_assert(VK == TQ_KIND_Q8 || (VK == TQ_KIND_MSE && (VB == 2 || VB == 4)), "2/4-bit codebook V or q8 V");
     constexpr bool Q8 = VK == TQ_KIND_Q8;
+    constexpr bool LUT = VK == TQ_KIND_MSE && VB == 4;  // levels from the table, norms in A
+    constexpr bool SCL = Q8 || LUT;                     // A = weight x a per-token factor
     constexpr int NC = Q8 ? 16 : 8;  // code dwords per lane and group
-    constexpr int NN = Q8 ? 1 : 4;   // norm dwords per lane and group
+    constexpr int NN = LUT || Q8 ? 1 : 4;  // norm dwords per lane and group (2-bit: in B)
     constexpr int NA = Q8 ? 16 : 4;  // A-operand dwords (q8: one operand per block)
-    constexpr int NS = Q8 ? 4 : 1;   // q8 scale pairs (uint2) per lane and group
+    constexpr int NS = Q8 ? 4 : 1;   // q8 scale pairs or (4-bit) four norms, uint2, per lane and group
     __shared__ float s_M[G], s_invL[G], s_qmax[kMWaves];
+    __shared__ uint32_t s_lvl[16];  // 4-bit: level c as fp16 hi | lo << 16
     __shared__ int s_any[kMWaves];
     __shared__ __attribute__((aligned(16))) float s_acc[kMWaves][G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -493,7 +503,10 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     const int hn = n < G ? n : (n < 2 * G ? n - G : 0);
     const float *srow = a.scores + (head0 + hn) * int64_t(a.ld_scores);
     const int vrow = kv_row(a, row);
-    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * 8 + (n >> 1);
+    // 2-bit: the dword that holds 16-bit word n of each 32-byte row; 4-bit:
+    // dword n of each 64-byte row
+    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) +
+                            (LUT ? int64_t(vrow) * a.T * 16 + n : int64_t(vrow) * a.T * 8 + (n >> 1));
     // v_perm selector joining half (n & 1) of two dwords: that half of the
     // second operand (bytes 0-3) in bits 0-15, of the first (bytes 4-7) in 16-31
     const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
@@ -524,6 +537,11 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
         if constexpr (Q8) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sc[j] = q8s[min(tb + 8 * kq + jo + j, tmax)];
+        } else if constexpr (LUT) {
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = vn[min(tb + 8 * kq + jo + j, tmax)];
+            sc[0] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
     };
     // code words and norms of a whole group; a group that keeps no token
@@ -541,6 +559,10 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 c[2 * j] = cp[32 * j];
                 c[2 * j + 1] = cp[32 * j + 16];
             }
+        } else if constexpr (LUT) {
+            const uint32_t *cp = cwd32 + int64_t(tk) * 16;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = cp[16 * j];
         } else {
             const uint32_t *cp = cwd32 + int64_t(tk) * 8;
 #pragma unroll
@@ -557,6 +579,9 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 c[2 * j] = cp[0];
                 c[2 * j + 1] = cp[16];
             }
+        } else if constexpr (LUT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = cwd32[int64_t(min(tk + j, tmax)) * 16];
         } else {
             uint32_t h[8];
 #pragma unroll
@@ -573,17 +598,31 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
         load_scores(gbase(0), S[0], SC[0]);
         load_scores(gbase(1), S[1], SC[1]);
     }
-    const float c2 = Q8 ? 0.0f : a.tab->levels[1][2], c3 = Q8 ? 0.0f : a.tab->levels[1][3];
+    const float c2 = SCL ? 0.0f : a.tab->levels[1][2], c3 = SCL ? 0.0f : a.tab->levels[1][3];
+    if constexpr (LUT) {
+        if (tid < 16) {
+            const float lv = a.tab->levels[3][tid];
+            const _Float16 hi = _Float16(lv);
+            const _Float16 lo = _Float16(lv - float(hi));
+            s_lvl[tid] = uint32_t(__builtin_bit_cast(uint16_t, hi)) | (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
+        }
+    }
     const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
     const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
     asm volatile("" ::: "memory");
-    // q8 V: the A operands are weight x block scale; the block's largest scale
-    // bounds them (codebook V: weights <= 1, scaled by 2^15)
-    if constexpr (Q8) {
+    // q8 V: the A operands are weight x block scale, 4-bit V weight x norm;
+    // the block's largest scale or norm bounds them (fp16 bits of
+    // non-negative halves order like the values; 2-bit V: weights <= 1,
+    // scaled by 2^15)
+    if constexpr (SCL) {
         uint32_t mx = 0;
         for (int tk = t0 + tid; tk < t1; tk += kMThreads) {
-            const uint2 u = q8s[tk];
-            mx = max(mx, max(max(u.x & 0xFFFFu, u.x >> 16), max(u.y & 0xFFFFu, u.y >> 16)));
+            if constexpr (Q8) {
+                const uint2 u = q8s[tk];
+                mx = max(mx, max(max(u.x & 0xFFFFu, u.x >> 16), max(u.y & 0xFFFFu, u.y >> 16)));
+            } else {
+                mx = max(mx, uint32_t(vn[tk]));
+            }
         }
         const float mf = quad_max(row16_max(h2f(mx)));
         if (lane == 0) s_qmax[wave] = mf;
@@ -610,7 +649,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     __syncthreads();
     const float Ml2 = s_M[hn] * kLog2e;
     float ash = kWScale;
-    if constexpr (Q8) {
+    if constexpr (SCL) {
         float mf = 0.0f;
 #pragma unroll
         for (int w = 0; w < kMWaves; ++w) mf = fmaxf(mf, s_qmax[w]);
@@ -651,9 +690,12 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
             float v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if constexpr (Q8) {
+                if constexpr (Q8) {  // the token's scale of block blk
                     const uint32_t sp = blk < 2 ? sc[j].x : sc[j].y;
                     v[j] = ws[j] * h2f((sp >> (16 * (blk & 1))) & 0xFFFFu);
+                } else if constexpr (LUT) {  // the token's norm
+                    const uint32_t sp = j < 2 ? sc[0].x : sc[0].y;
+                    v[j] = ws[j] * h2f((sp >> (16 * (j & 1))) & 0xFFFFu);
                 } else {
                     v[j] = ws[j];
                 }
@@ -707,6 +749,26 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
                 for (int p = 0; p < 2; ++p)
                     acc[m][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2 * w + p], B, acc[m][p], 0, 0, 0);
             }
+        } else if constexpr (LUT) {
+            const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                // the levels of coordinate 8n + m (nibble m) of the eight
+                // tokens; hi halves into one B operand, lo halves into another
+                uint32_t x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = s_lvl[(c[j] >> (4 * m)) & 15u];
+                uint32_t bh[4], bl[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bh[i] = __builtin_amdgcn_perm(x[2 * i + 1], x[2 * i], 0x05040100u);
+                    bl[i] = __builtin_amdgcn_perm(x[2 * i + 1], x[2 * i], 0x07060302u);
+                }
+                acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    A, __builtin_bit_cast(half8, make_uint4(bh[0], bh[1], bh[2], bh[3])), acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    A, __builtin_bit_cast(half8, make_uint4(bl[0], bl[1], bl[2], bl[3])), acc[m][1], 0, 0, 0);
+            }
         } else {
             const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
             uint32_t cwd[4];
@@ -735,7 +797,7 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
         if constexpr (Q8)
             asm volatile("" ::"v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]), "v"(c[14]),
                          "v"(c[15]));
-        else
+        else if constexpr (!LUT)
             asm volatile("" ::"v"(nr[0]), "v"(nr[1]), "v"(nr[2]), "v"(nr[3]));
     };
     // software pipeline over this wave's whole groups k = 0 .. ng-1, two
@@ -794,7 +856,9 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            y[m][j] = Q8 ? (n >= 8 ? acc[m][1][j] : acc[m][0][j]) : fmaf(a1, acc[m][1][j], a0 * acc[m][0][j]);
+            y[m][j] = Q8    ? (n >= 8 ? acc[m][1][j] : acc[m][0][j])
+                      : LUT ? acc[m][0][j] + acc[m][1][j]
+                            : fmaf(a1, acc[m][1][j], a0 * acc[m][0][j]);
     // rows 4kq + j and 4(kq + 2) + j are the hi and lo rows of head 4kq + j
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -824,7 +888,8 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     // V is not rotated) and added into the output, which the scores pass
     // zeroed
     if (kept_any) {
-        const float sc = -kRsqrtD * kRsqrtD / ash;
+        // 2-bit: -(a1 X1 + a0 X0); 4-bit: the sum itself
+        const float sc = (LUT ? kRsqrtD : -kRsqrtD) * kRsqrtD / ash;
         for (int g = wave; g < G; g += kMWaves) {
             float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
@@ -875,7 +940,7 @@ static int launch_passes(const AttnArgs &as, hipStream_t s) {
         a.len_add = 1;
         grid.x = unsigned(a.n_chunks - 1);
     }
-    if constexpr (G == 8 && ((VK == TQ_KIND_MSE && VB == 2) || VK == TQ_KIND_Q8)) {
+    if constexpr (G == 8 && ((VK == TQ_KIND_MSE && (VB == 2 || VB == 4)) || VK == TQ_KIND_Q8)) {
         // 8 query heads: the kept rows of all heads together are most of the
         // tokens unless attention is very peaked, and the per-row cost of the
         // compacting pass grows with the head count, so the whole range goes
@@ -885,7 +950,7 @@ static int launch_passes(const AttnArgs &as, hipStream_t s) {
         AttnArgs v = a;
         v.vsub = int(std::min<int64_t>(std::max<int64_t>((per + 255) / 256 * 256, 256), (int64_t(a.T) + 31) / 32 * 32));
         const dim3 vgrid(unsigned((a.T + v.vsub - 1) / v.vsub), unsigned(rows));
-        hipLaunchKernelGGL((attn_values_mfma_kernel<G, VK>), vgrid, dim3(kMThreads), 0, s, v);
+        hipLaunchKernelGGL((attn_values_mfma_kernel<G, VK, VB>), vgrid, dim3(kMThreads), 0, s, v);
     } else {
         hipLaunchKernelGGL((attn_values_kernel<G, VK, VB>), grid, dim3(kVThreads), 0, s, a);
     }
