@@ -453,7 +453,8 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
 // in which no head keeps a token is skipped as a whole.
 //
 // 4-bit codebook V: B = the level of the token's code, as fp16 hi and lo
-// halves (two products per column block), read from a 16-entry LDS table;
+// halves (two products per column block), two tokens at a time from a
+// 256-entry LDS table indexed by both codes;
 // the token's norm goes into A (weight x norm, scaled below 2^14 by the
 // block's largest norm); the sum is the rotated-domain V sum times that
 // scale and sqrt(d).  Coordinates 8n + [0, 8) of a token are dword n of its
@@ -483,7 +484,9 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     constexpr int NA = Q8 ? 16 : 4;  // A-operand dwords (q8: one operand per block)
     constexpr int NS = Q8 ? 4 : 1;   // q8 scale pairs or (4-bit) four norms, uint2, per lane and group
     __shared__ float s_M[G], s_invL[G], s_qmax[kMWaves];
-    __shared__ uint32_t s_lvl[16];  // 4-bit: level c as fp16 hi | lo << 16
+    // 4-bit: entry c0 | c1 << 4 = the levels of codes c0, c1 as fp16 (hi
+    // halves, lo halves): one B dword of a token pair for each product
+    __shared__ uint2 s_lv2[LUT ? 256 : 1];
     __shared__ int s_any[kMWaves];
     __shared__ __attribute__((aligned(16))) float s_acc[kMWaves][G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -600,12 +603,17 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
     }
     const float c2 = SCL ? 0.0f : a.tab->levels[1][2], c3 = SCL ? 0.0f : a.tab->levels[1][3];
     if constexpr (LUT) {
-        if (tid < 16) {
-            const float lv = a.tab->levels[3][tid];
+        static_assert(kMThreads == 256, "one pair-table entry per thread");
+        uint32_t h2[2], l2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float lv = a.tab->levels[3][(tid >> (4 * u)) & 15];
             const _Float16 hi = _Float16(lv);
             const _Float16 lo = _Float16(lv - float(hi));
-            s_lvl[tid] = uint32_t(__builtin_bit_cast(uint16_t, hi)) | (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
+            h2[u] = __builtin_bit_cast(uint16_t, hi);
+            l2[u] = __builtin_bit_cast(uint16_t, lo);
         }
+        s_lv2[tid] = make_uint2(h2[0] | (h2[1] << 16), l2[0] | (l2[1] << 16));
     }
     const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
     const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
@@ -751,18 +759,26 @@ __global__ __launch_bounds__(kMThreads) void attn_values_mfma_kernel(AttnArgs a)
             }
         } else if constexpr (LUT) {
             const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+            // token pair i (tokens 2i, 2i + 1): byte k of pe[i] is code 2k of
+            // the first | code 2k of the second << 4, of po[i] the same for
+            // code 2k + 1 (coordinates 8n + 2k and 8n + 2k + 1)
+            uint32_t pe[4], po[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pe[i] = (c[2 * i] & 0x0F0F0F0Fu) | ((c[2 * i + 1] & 0x0F0F0F0Fu) << 4);
+                po[i] = ((c[2 * i] >> 4) & 0x0F0F0F0Fu) | (c[2 * i + 1] & 0xF0F0F0F0u);
+            }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                // the levels of coordinate 8n + m (nibble m) of the eight
-                // tokens; hi halves into one B operand, lo halves into another
-                uint32_t x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = s_lvl[(c[j] >> (4 * m)) & 15u];
+                // coordinate 8n + m of the eight tokens: hi halves into one B
+                // operand, lo halves into another, a token pair per table read
                 uint32_t bh[4], bl[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bh[i] = __builtin_amdgcn_perm(x[2 * i + 1], x[2 * i], 0x05040100u);
-                    bl[i] = __builtin_amdgcn_perm(x[2 * i + 1], x[2 * i], 0x07060302u);
+                    const uint32_t e = (((m & 1) ? po[i] : pe[i]) >> (8 * (m >> 1))) & 0xFFu;
+                    const uint2 v = s_lv2[e];
+                    bh[i] = v.x;
+                    bl[i] = v.y;
                 }
                 acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     A, __builtin_bit_cast(half8, make_uint4(bh[0], bh[1], bh[2], bh[3])), acc[m][0], 0, 0, 0);
