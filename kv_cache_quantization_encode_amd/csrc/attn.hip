@@ -452,13 +452,14 @@ __global__ __launch_bounds__(kVThreads) void attn_values_kernel(AttnArgs a) {
 // word n of the token's row.  Every token of a chunk is stepped over; a group
 // in which no head keeps a token is skipped as a whole.
 //
-// 4-bit codebook V: B = the level of the token's code, as fp16 hi and lo
-// halves (two products per column block), two tokens at a time from a
-// 256-entry LDS table indexed by both codes;
+// 3- and 4-bit codebook V: B = the level of the token's code, as fp16 hi
+// and lo halves (two products per column block), two tokens at a time from
+// an LDS table indexed by both codes (64 / 256 entries);
 // the token's norm goes into A (weight x norm, scaled below 2^14 by the
 // block's largest norm); the sum is the rotated-domain V sum times that
 // scale and sqrt(d).  Coordinates 8n + [0, 8) of a token are dword n of its
-// 64-byte row.
+// 64-byte row (4-bit), or bits 24n + [0, 24) of its 48-byte row (3-bit: two
+// dwords, the second clamped to the row, joined by one funnel shift).
 //
 // q8 V (boundary layers): x = q s_blk with int8 q and one fp16 scale per 32
 // coordinates.  B = q as fp16 (exact: the byte becomes the mantissa of
@@ -473,23 +474,24 @@ constexpr int kMWaves = kMThreads / 64;
 constexpr float kWScale = 32768.0f;  // 2^15
 
 // (the 4-bit instance is held to three waves per SIMD, 168 registers: the
-// grouped prefill at Tq 2048 takes 9.0-9.1 ms against 9.8-10.0 ms at two)
+// grouped prefill at Tq 2048 takes 9.0-9.1 ms against 9.8-10.0 ms at two;
+// the 3-bit one, with twice the code dwords in flight, would spill there)
 template <int G, int VK, int VB>
 __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(VK == TQ_KIND_MSE && VB == 4 ? 3 : 1)))
 void attn_values_mfma_kernel(AttnArgs a) {
     static_assert(G == 8, "rows: 8 heads x (hi, lo)");
-    static_assert(VK == TQ_KIND_Q8 || (VK == TQ_KIND_MSE && (VB == 2 || VB == 4)), "2/4-bit codebook V or q8 V");
+    static_assert(VK == TQ_KIND_Q8 || (VK == TQ_KIND_MSE && VB >= 2 && VB <= 4), "2/3/4-bit codebook V or q8 V");
     constexpr bool Q8 = VK == TQ_KIND_Q8;
-    constexpr bool LUT = VK == TQ_KIND_MSE && VB == 4;  // levels from the table, norms in A
+    constexpr bool LUT = VK == TQ_KIND_MSE && VB >= 3;  // levels from the table, norms in A
     constexpr bool SCL = Q8 || LUT;                     // A = weight x a per-token factor
-    constexpr int NC = Q8 ? 16 : 8;  // code dwords per lane and group
+    constexpr int NC = Q8 || VB == 3 ? 16 : 8;  // code dwords per lane and group
     constexpr int NN = LUT || Q8 ? 1 : 4;  // norm dwords per lane and group (2-bit: in B)
     constexpr int NA = Q8 ? 16 : 4;  // A-operand dwords (q8: one operand per block)
     constexpr int NS = Q8 ? 4 : 1;   // q8 scale pairs or (4-bit) four norms, uint2, per lane and group
     __shared__ float s_M[G], s_invL[G], s_qmax[kMWaves];
-    // 4-bit: entry c0 | c1 << 4 = the levels of codes c0, c1 as fp16 (hi
+    // 3/4-bit: entry c0 | c1 << VB = the levels of codes c0, c1 as fp16 (hi
     // halves, lo halves): one B dword of a token pair for each product
-    __shared__ uint2 s_lv2[LUT ? 256 : 1];
+    __shared__ uint2 s_lv2[LUT ? 1 << (2 * VB) : 1];
     __shared__ int s_any[kMWaves];
     __shared__ __attribute__((aligned(16))) float s_acc[kMWaves][G][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,9 +512,13 @@ void attn_values_mfma_kernel(AttnArgs a) {
     const float *srow = a.scores + (head0 + hn) * int64_t(a.ld_scores);
     const int vrow = kv_row(a, row);
     // 2-bit: the dword that holds 16-bit word n of each 32-byte row; 4-bit:
-    // dword n of each 64-byte row
-    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) +
-                            (LUT ? int64_t(vrow) * a.T * 16 + n : int64_t(vrow) * a.T * 8 + (n >> 1));
+    // dword n of each 64-byte row; 3-bit: the dword that holds bit 24n of
+    // each 48-byte row (and the next one, clamped to the row: c3n1)
+    constexpr int kRowDw = 4 * VB;  // code dwords per row (codebook V)
+    const int c3n0 = VB == 3 ? (3 * n) >> 2 : 0, c3n1 = VB == 3 ? min(c3n0 + 1, kRowDw - 1) - c3n0 : 0;
+    const uint32_t c3sh = VB == 3 ? uint32_t(24 * n) & 31u : 0u;
+    const uint32_t *cwd32 = reinterpret_cast<const uint32_t *>(a.vidx) + int64_t(vrow) * a.T * kRowDw +
+                            (VB == 4 ? n : VB == 3 ? c3n0 : (n >> 1));
     // v_perm selector joining half (n & 1) of two dwords: that half of the
     // second operand (bytes 0-3) in bits 0-15, of the first (bytes 4-7) in 16-31
     const uint32_t half_sel = (n & 1) ? 0x07060302u : 0x05040100u;
@@ -565,6 +571,13 @@ void attn_values_mfma_kernel(AttnArgs a) {
                 c[2 * j] = cp[32 * j];
                 c[2 * j + 1] = cp[32 * j + 16];
             }
+        } else if constexpr (LUT && VB == 3) {
+            const uint32_t *cp = cwd32 + int64_t(tk) * kRowDw;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                c[2 * j] = cp[kRowDw * j];
+                c[2 * j + 1] = cp[kRowDw * j + c3n1];
+            }
         } else if constexpr (LUT) {
             const uint32_t *cp = cwd32 + int64_t(tk) * 16;
 #pragma unroll
@@ -584,6 +597,13 @@ void attn_values_mfma_kernel(AttnArgs a) {
                 const uint32_t *cp = q8w + int64_t(min(tk + j, tmax)) * 32;
                 c[2 * j] = cp[0];
                 c[2 * j + 1] = cp[16];
+            }
+        } else if constexpr (LUT && VB == 3) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t *cp = cwd32 + int64_t(min(tk + j, tmax)) * kRowDw;
+                c[2 * j] = cp[0];
+                c[2 * j + 1] = cp[c3n1];
             }
         } else if constexpr (LUT) {
 #pragma unroll
@@ -606,17 +626,19 @@ void attn_values_mfma_kernel(AttnArgs a) {
     }
     const float c2 = SCL ? 0.0f : a.tab->levels[1][2], c3 = SCL ? 0.0f : a.tab->levels[1][3];
     if constexpr (LUT) {
-        static_assert(kMThreads == 256, "one pair-table entry per thread");
-        uint32_t h2[2], l2[2];
+        static_assert(kMThreads >= (1 << (2 * VB)), "one pair-table entry per thread");
+        if (tid < (1 << (2 * VB))) {
+            uint32_t h2[2], l2[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float lv = a.tab->levels[3][(tid >> (4 * u)) & 15];
-            const _Float16 hi = _Float16(lv);
-            const _Float16 lo = _Float16(lv - float(hi));
-            h2[u] = __builtin_bit_cast(uint16_t, hi);
-            l2[u] = __builtin_bit_cast(uint16_t, lo);
+            for (int u = 0; u < 2; ++u) {
+                const float lv = a.tab->levels[VB - 1][(tid >> (VB * u)) & ((1 << VB) - 1)];
+                const _Float16 hi = _Float16(lv);
+                const _Float16 lo = _Float16(lv - float(hi));
+                h2[u] = __builtin_bit_cast(uint16_t, hi);
+                l2[u] = __builtin_bit_cast(uint16_t, lo);
+            }
+            s_lv2[tid] = make_uint2(h2[0] | (h2[1] << 16), l2[0] | (l2[1] << 16));
         }
-        s_lv2[tid] = make_uint2(h2[0] | (h2[1] << 16), l2[0] | (l2[1] << 16));
     }
     const float *st = a.stats + (head0 + min(wave, G - 1)) * a.n_chunks * 2;
     const float2 st0 = *reinterpret_cast<const float2 *>(st + 2 * min(lane, a.n_chunks - 1));
@@ -762,14 +784,20 @@ void attn_values_mfma_kernel(AttnArgs a) {
             }
         } else if constexpr (LUT) {
             const half8 A = __builtin_bit_cast(half8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
-            // token pair i (tokens 2i, 2i + 1): byte k of pe[i] is code 2k of
-            // the first | code 2k of the second << 4, of po[i] the same for
-            // code 2k + 1 (coordinates 8n + 2k and 8n + 2k + 1)
-            uint32_t pe[4], po[4];
+            // 4-bit, token pair i (tokens 2i, 2i + 1): byte k of pe[i] is
+            // code 2k of the first | code 2k of the second << 4, of po[i] the
+            // same for code 2k + 1 (coordinates 8n + 2k and 8n + 2k + 1).
+            // 3-bit: f[j] = the eight 3-bit codes of token j.
+            uint32_t pe[4], po[4], f[8];
+            if constexpr (VB == 4) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pe[i] = (c[2 * i] & 0x0F0F0F0Fu) | ((c[2 * i + 1] & 0x0F0F0F0Fu) << 4);
-                po[i] = ((c[2 * i] >> 4) & 0x0F0F0F0Fu) | (c[2 * i + 1] & 0xF0F0F0F0u);
+                for (int i = 0; i < 4; ++i) {
+                    pe[i] = (c[2 * i] & 0x0F0F0F0Fu) | ((c[2 * i + 1] & 0x0F0F0F0Fu) << 4);
+                    po[i] = ((c[2 * i] >> 4) & 0x0F0F0F0Fu) | (c[2 * i + 1] & 0xF0F0F0F0u);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) f[j] = __builtin_amdgcn_alignbit(c[2 * j + 1], c[2 * j], c3sh);
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -778,7 +806,11 @@ void attn_values_mfma_kernel(AttnArgs a) {
                 uint32_t bh[4], bl[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t e = (((m & 1) ? po[i] : pe[i]) >> (8 * (m >> 1))) & 0xFFu;
+                    uint32_t e;
+                    if constexpr (VB == 4)
+                        e = (((m & 1) ? po[i] : pe[i]) >> (8 * (m >> 1))) & 0xFFu;
+                    else
+                        e = ((f[2 * i] >> (3 * m)) & 7u) | (((f[2 * i + 1] >> (3 * m)) & 7u) << 3);
                     const uint2 v = s_lv2[e];
                     bh[i] = v.x;
                     bl[i] = v.y;
@@ -813,7 +845,7 @@ void attn_values_mfma_kernel(AttnArgs a) {
     // everything in flight
     auto take = [&](const uint32_t (&c)[NC], const uint32_t (&nr)[NN]) {
         asm volatile("" ::"v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(c[4]), "v"(c[5]), "v"(c[6]), "v"(c[7]));
-        if constexpr (Q8)
+        if constexpr (NC == 16)
             asm volatile("" ::"v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]), "v"(c[14]),
                          "v"(c[15]));
         else if constexpr (!LUT)
@@ -959,7 +991,7 @@ static int launch_passes(const AttnArgs &as, hipStream_t s) {
         a.len_add = 1;
         grid.x = unsigned(a.n_chunks - 1);
     }
-    if constexpr (G == 8 && ((VK == TQ_KIND_MSE && (VB == 2 || VB == 4)) || VK == TQ_KIND_Q8)) {
+    if constexpr (G == 8 && ((VK == TQ_KIND_MSE && VB >= 2) || VK == TQ_KIND_Q8)) {
         // 8 query heads: the kept rows of all heads together are most of the
         // tokens unless attention is very peaked, and the per-row cost of the
         // compacting pass grows with the head count, so the whole range goes

@@ -91,23 +91,24 @@ def test_attention_eight_heads_ragged_batch(ctx, oracle_tables):
     _run(ctx, oracle_tables, n, ("prod", 3), ("mse", 2), 1e-6)
 
 
-@pytest.mark.parametrize("kf", [("prod", 3), ("mse", 3)])
-def test_attention_eight_heads_four_bit_v(ctx, oracle_tables, kf):
-    """8 query heads per KV head with 4-bit codebook V: the matrix-core values
-    pass with level-table B operands and the V norms in A.  A batch of 4 whose
-    lengths give a partial last 32-token group, a one-token and an empty
-    sequence, at tau 0, 1e-6 and 0.5; a needle-peaked batch; and V rows
-    scaled by 500 (norms in the thousands, so the A operands' scale comes
-    from the block's largest norm)."""
+@pytest.mark.parametrize("kf,vb", [(("prod", 3), 4), (("mse", 3), 4), (("prod", 2), 3), (("mse", 3), 3)])
+def test_attention_eight_heads_three_and_four_bit_v(ctx, oracle_tables, kf, vb):
+    """8 query heads per KV head with 3- or 4-bit codebook V: the matrix-core
+    values pass with level-table B operands (3-bit codes straddling dwords)
+    and the V norms in A.  A batch of 4 whose lengths give a partial last
+    32-token group, a one-token and an empty sequence, at tau 0, 1e-6 and
+    0.5; a needle-peaked batch; and V rows scaled by 500 (norms in the
+    thousands, so the A operands' scale comes from the block's largest norm)."""
+    vf = ("mse", vb)
     c = W.llama8b(T=1100, Hq=16, Hkv=2, B=4)
     lens = np.array([1100, 33, 1, 0], np.int32)
     for tau in (0.0, 1e-6, 0.5):
-        got, _, _ = _run(ctx, oracle_tables, c, kf, ("mse", 4), tau, seq_lens=lens)
+        got, _, _ = _run(ctx, oracle_tables, c, kf, vf, tau, seq_lens=lens)
         assert np.all(got[3] == 0.0)
     n = W.needle(B=2, T=2048, Hq=16, Hkv=2)
-    _run(ctx, oracle_tables, n, kf, ("mse", 4), 1e-6)
+    _run(ctx, oracle_tables, n, kf, vf, 1e-6)
     big = W.AttnCase("llama8b.bigv", c.k, (c.v.astype(np.float32) * 500.0).astype(np.float16), c.q)
-    got, ref, _ = _run(ctx, oracle_tables, big, kf, ("mse", 4), 1e-6, seq_lens=lens, atol=G.ATTN_ATOL * 500.0)
+    got, ref, _ = _run(ctx, oracle_tables, big, kf, vf, 1e-6, seq_lens=lens, atol=G.ATTN_ATOL * 500.0)
     assert np.isfinite(got).all()
 
 
