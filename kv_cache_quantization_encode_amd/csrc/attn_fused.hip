@@ -733,9 +733,11 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     // weights of head hn for tokens tbs + 8kq + jo + [0, 4): p = exp(s - M)/L,
     // kept when p >= tau, times the token's V scale, as this row's fp16 half;
     // returns whether any lane of the wave keeps a token (uniform)
-    auto weights = [&](int tbs, const uint32_t (&nr)[2], const uint2 (&sc)[4], uint32_t (&aw)[NA],
+    auto read_sd = [&](int tbs) -> float4 {
+        return *reinterpret_cast<const float4 *>(&s_sc[hn * kFLd + (tbs - t0) + 8 * kq + jo]);
+    };
+    auto weights = [&](int tbs, const float4 &sd, const uint32_t (&nr)[2], const uint2 (&sc)[4], uint32_t (&aw)[NA],
                        auto whole_c) -> bool {
-        const float4 sd = *reinterpret_cast<const float4 *>(&s_sc[hn * kFLd + (tbs - t0) + 8 * kq + jo]);
         const float sv[4] = {sd.x, sd.y, sd.z, sd.w};
         float y[4];
         bool kj[4], kept = false;
@@ -838,11 +840,15 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
     };
     if (s_ok && ng > 0) {
         // software pipeline two groups deep: step k starts the scale words of
-        // group k + 4, forms the A operands of group k + 2 (scale words issued
-        // two steps earlier, scores from LDS), starts its code words, and runs
-        // the products of group k; three register sets rotate with k mod 3
+        // group k + 4 and the LDS read of group k + 3's scores, forms the A
+        // operands of group k + 2 (scale words issued two steps earlier, its
+        // scores one step earlier), starts its code words, and runs the
+        // products of group k; three register sets rotate with k mod 3 (the
+        // early score read: middle layer ~0.25 us faster over five A/B pairs)
         uint32_t aw[3][NA], c[3][NC];
         uint32_t NR[3][2];
+        float4 SD[3];  // scores of group g in slot g mod 3, read one step ahead
+        SD[0] = read_sd(gbase(0));
         uint2 SC[3][4];
         bool kp[3] = {false, false, false};
         auto load_scale = [&](int tbs, int p) {
@@ -857,7 +863,8 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
             load_scale(gbase(k + 4), p1);
             asm volatile("" ::: "memory");
             const bool more = k + 2 < ng;
-            kp[p2] = more && weights(gbase(k + 2), NR[p2], SC[p2], aw[p2], std::true_type{});
+            SD[p] = read_sd(gbase(k + 3));
+            kp[p2] = more && weights(gbase(k + 2), SD[p2], NR[p2], SC[p2], aw[p2], std::true_type{});
             load_codes(gbase(k + 2), kp[p2], c[p2]);
             asm volatile("" ::: "memory");
             if (kp[p]) {
@@ -880,7 +887,7 @@ __global__ __launch_bounds__(kFThreads) void attn_fused_kernel(AttnArgs a, const
         uint2 sc[4] = {};
         if constexpr (VQ8) load_q8scl(tbs, sc, true);
         else load_norms(tbs, nr, true);
-        if (weights(tbs, nr, sc, aw, std::false_type{})) {
+        if (weights(tbs, read_sd(tbs), nr, sc, aw, std::false_type{})) {
             load_tail_codes(tbs, c);
             products(aw, c);
         }
